@@ -1,0 +1,196 @@
+"""Benchmark: one forward of a tile graph as one persistent megakernel launch.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode]
+
+A step is one forward of the whole graph (every instruction of the plan) on
+seeded synthetic inputs already resident in HBM.  The default workload is
+the batch-1 decoder-layer GEMV chain (hidden 4096, QKV 6144, gate_up 28672,
+down 14336, bf16).  Prints one JSON line: µs per forward, achieved GB/s or
+TFLOP/s against the MI355X roofline, the same graph launched one op at a
+time, and the CPU oracle timed on the host as a reported baseline.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "µs/forward + TFLOP/s (% MFMA peak) or GB/s (% HBM) per graph, 1 MI355X"
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+PEAK_MFMA_TFLOPS = 2500.0   # MI355X dense fp16/bf16 MFMA
+
+DESCR = {
+    "mlp3": "3-layer MLP x=relu(x@W[i]+b[i]), x 1024x1024, fp16",
+    "decode": "decoder layer at batch 1: RMSNorm-fused QKV GEMV N=6144, O + residual N=4096, "
+              "RMSNorm-fused gate_up N=28672 with SiLU*mul, down K=14336 + residual; hidden 4096, bf16",
+    "prefill": "prefill GEMM chain M=8192: X[8192x8192]@W1[8192x8192], then @W2[8192x28672] "
+               "with ReLU, fp16",
+    "decode_gemm": "decode-shaped GEMM chain M=256, K=8192: QKV N=10240, attn-out N=8192, "
+                   "MLP up N=28672, MLP down K=28672, fp16",
+    "layer": "Llama-style decoder layer prefill, seq 2048, hidden 4096, 32/8 heads of 128, causal "
+             "attention, RMSNorm, rotary, SiLU*mul MLP inter 14336, bf16",
+}
+BOUND = dict(mlp3="mfma", decode="hbm", prefill="mfma", decode_gemm="hbm", layer="mfma")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def time_forwards(fn, steps, warmup):
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    for _ in range(steps):
+        fn()
+    e1.record(s)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps  # ms per forward
+
+
+def cpu_baseline(workload, dims, inp, budget_s):
+    """The oracle as it stands, timed on the host cores on a bounded sample."""
+    import numpy as np
+    from oracle import graphs as OG
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count()
+    rows_total = dims.get("m", dims.get("seq", 1))
+    if workload in ("prefill",):
+        rows = list(range(16))
+        t0 = time.perf_counter()
+        n = 0
+        while True:
+            OG.run(workload, inp, dims, rows=rows)
+            n += 1
+            if time.perf_counter() - t0 > budget_s:
+                break
+        dt = (time.perf_counter() - t0) / n * rows_total / len(rows)
+        sample = f"{n} oracle runs of {len(rows)} of {rows_total} rows, scaled to all rows"
+    else:
+        t0 = time.perf_counter()
+        n = 0
+        while True:
+            OG.run(workload, inp, dims)
+            n += 1
+            if time.perf_counter() - t0 > budget_s:
+                break
+        dt = (time.perf_counter() - t0) / n
+        sample = f"{n} full oracle forwards"
+    return {"value": dt * 1e6, "unit": "us/forward", "cores": int(cores), "kind": "oracle",
+            "sample": sample}
+
+
+def bench_one(workload, steps, warmup, cpu_budget, do_check=True):
+    import numpy as np
+    import torch
+
+    import workloads
+    from tiled_gemm_graph_amd import graphs as G
+
+    dims = workloads.default_dims(workload)
+    log(f"[bench] {workload} dims={dims}: drawing inputs")
+    inp = workloads.generate(workload, dims)
+    r = G.Runner(workload, dims, inp, device="cuda")
+    st = r.plan.stats()
+    log(f"[bench] plan: {st.n_instr} instructions, {st.n_iters} waves, {st.n_barriers} counters")
+    r.forward()
+    r.plan.check()
+    torch.cuda.synchronize()
+    out = {}
+    if do_check:
+        from oracle import graphs as OG
+        got = r.out.float().cpu().numpy().astype(np.float64)
+        if workload in ("prefill", "decode_gemm"):
+            rows = [0, dims["m"] // 2 + 1, dims["m"] - 1]
+            ref = OG.run(workload, inp, dims, rows=rows).astype(np.float64)
+            got = got[rows]
+        else:
+            ref = OG.run(workload, inp, dims).astype(np.float64)
+        rel = float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-12))
+        out["rel_err"] = rel
+        out["max_abs_err"] = float(np.max(np.abs(got - ref)))
+        log(f"[bench] parity vs oracle: rel {rel:.3e}")
+    ms = time_forwards(r.forward, steps, warmup)
+    r.plan.check()
+    ms_op = time_forwards(r.forward_per_op, steps, warmup)
+    us = ms * 1e3
+    gbs = st.bytes / (us * 1e-6) / 1e9
+    tfl = st.flops / (us * 1e-6) / 1e12
+    bound = BOUND[workload]
+    if bound == "hbm":
+        roof = {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": gbs / PEAK_HBM_GBS, "traffic": None}
+    else:
+        roof = {"bound": "mfma", "achieved": tfl, "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s",
+                "frac": tfl / PEAK_MFMA_TFLOPS, "traffic": None}
+    line = {
+        "metric": METRIC,
+        "value": us,
+        "unit": "us/forward",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": ms,
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if G.DTYPE[workload] == "bf16" else "f16",
+        "data": "synthetic (seeded torch CPU generator, normal distributions of the workload spec)",
+        "config": {"workload": DESCR[workload], "name": workload, "dims": dims,
+                   "instructions": int(st.n_instr), "counters": int(st.n_barriers),
+                   "launches_per_forward": 1},
+        "gbps": gbs,
+        "tflops": tfl,
+        "alg_bytes": st.bytes,
+        "alg_flops": st.flops,
+        "per_op_us": ms_op * 1e3,
+        "speedup_vs_per_op": ms_op / ms,
+        "roofline": roof,
+    }
+    line.update(out)
+    if cpu_budget > 0:
+        log(f"[bench] timing the CPU oracle (~{cpu_budget:.0f} s)")
+        line["cpu_baseline"] = cpu_baseline(workload, dims, inp, cpu_budget)
+    else:
+        line["cpu_baseline"] = None
+    return line
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="decode",
+                    choices=["mlp3", "decode", "prefill", "decode_gemm", "layer"])
+    ap.add_argument("--all", action="store_true", help="one JSON line per workload")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-check", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the tile-graph "
+              "megakernel is a single-GPU path", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    wls = ["decode", "mlp3", "prefill", "decode_gemm", "layer"] if args.all else [args.workload]
+    for wl in wls:
+        line = bench_one(wl, args.steps, args.warmup, args.cpu_seconds, not args.no_check)
+        print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

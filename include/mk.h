@@ -1,0 +1,271 @@
+/*
+ * mk.h — C ABI of the MI355X persistent tile-graph megakernel.
+ *
+ * A static graph of GEMMs (with bias / ReLU / residual / SiLU-mul /
+ * RMSNorm-input / rotary epilogues), RMSNorms, causal attention and
+ * elementwise ops is compiled on the host into a flat list of tile-sized
+ * instructions with per-tile int32 dependency counters, then executed by one
+ * persistent HIP kernel (one workgroup per compute unit) per forward.
+ *
+ * Design sources (web pages):
+ *   "MegaKittens Internals" — sections 02 (graph, views as ranges), 04
+ *     (scheduler: placement, tensor slots, fine-grained barriers), 05
+ *     (per-SM placement), 06 (256-byte instruction), 07 (dispatcher), 11
+ *     (global barriers, deadlock argument), 12-14 (instruction types).
+ *   "Implementing a Mega Kernel for B300" — sections 1-2 (graph builder,
+ *     epilogues as GEMV flags, 64-byte POD descriptors with buffer indices
+ *     instead of pointers, ABI size guards), 5-6 (buffer table, upload).
+ *   "Beating torch.compile with Megakernels in CuTe DSL" — "Cooperative
+ *     Kernel", "Dependency Management and Scheduling" (round-robin
+ *     placement, counter spin-wait with acquire loads).
+ *
+ * Conventions
+ *   - Every call returns an mk_status; mk_last_error() gives a message for
+ *     the calling thread's last non-OK status.  No C++ exception crosses
+ *     this boundary.
+ *   - Tensors are row-major and contiguous, of at most 4 dimensions,
+ *     left-padded to 4-D for ranges.  A GEMM computes out = A @ B with
+ *     A [M, K] and B [K, N] (weights stored K-major).
+ *   - Pointers passed to megakernel_run* are device pointers; every other
+ *     pointer argument is a host pointer.
+ *   - The graph and every input / weight / output device buffer belong to
+ *     the caller.  A plan owns its device copy of the instruction records,
+ *     its counters, its intermediate buffers and its error record; they are
+ *     allocated on the plan's first run and freed by mk_plan_destroy.
+ *   - A plan runs on one stream at a time: its counters and intermediates
+ *     are shared by every run of that plan.
+ */
+#ifndef MK_H
+#define MK_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MK_ABI_VERSION 1
+#define MK_MAX_TENSORS 64       /* graph tensors incl. views and internals */
+#define MK_MAX_SRC 16           /* counters one instruction waits on       */
+#define MK_MAX_DST 8            /* counters one instruction arrives on     */
+#define MK_INSTR_WORDS 64       /* int32 words per instruction record      */
+#define MK_NODE_WORDS 64        /* int32 words per node descriptor         */
+
+typedef enum {
+  MK_OK = 0,
+  MK_E_INVALID = 1,     /* bad argument, shape mismatch, non-topological */
+  MK_E_UNSUPPORTED = 2, /* valid graph the kernels do not implement      */
+  MK_E_LIMIT = 3,       /* a fixed limit (tensors, counters per instr)   */
+  MK_E_HIP = 4,         /* a HIP runtime call failed                     */
+  MK_E_DEADLOCK = 5     /* a counter wait exceeded the spin limit        */
+} mk_status;
+
+typedef enum { MK_F16 = 1, MK_BF16 = 2, MK_F32 = 3 } mk_dtype;
+
+typedef enum {
+  MK_INPUT = 0,        /* caller-owned activation input                  */
+  MK_WEIGHT = 1,       /* caller-owned constant input                    */
+  MK_OUTPUT = 2,       /* caller-owned output buffer                     */
+  MK_INTERMEDIATE = 3  /* plan-owned                                     */
+} mk_role;
+
+typedef enum {
+  MK_OP_GEMM = 1,      /* in: A, B [, bias][, residual][, gamma]         */
+  MK_OP_RMSNORM = 2,   /* in: x, gamma                                   */
+  MK_OP_ATTENTION = 3, /* in: q, k, v (column ranges of a QKV tensor)    */
+  MK_OP_ADD = 4,       /* in: a, b  (same shape, no broadcasting)        */
+  MK_OP_RELU = 5       /* in: a                                          */
+} mk_op_kind;
+
+/* GEMM epilogue flags ("Implementing a Mega Kernel for B300", section 2:
+ * fusions are flags on the GEMV; MegaKittens Internals section 02: bias then
+ * ReLU).  Order of application: RMSNORM_INPUT scales the A rows, then the
+ * fp32 product, then SILU_MUL, BIAS, RESIDUAL, ROPE, RELU, then one
+ * round-to-nearest-even cast to the output dtype. */
+enum {
+  MK_EP_BIAS = 1,          /* + bias, a full [M, N] tensor                 */
+  MK_EP_RELU = 2,          /* max(., 0)                                    */
+  MK_EP_RESIDUAL = 4,      /* + residual [M, N]                            */
+  MK_EP_SILU_MUL = 8,      /* B has 2N columns [gate | up]; out = silu(g)*u */
+  MK_EP_RMSNORM_INPUT = 16,/* A rows normalised: A*gamma/sqrt(mean(A^2)+eps) */
+  MK_EP_ROPE = 32,         /* rotate-half rotary embedding on the leading
+                              rope_cols columns, position = row index      */
+  MK_EP_PARTIAL = 64       /* internal: instruction writes fp32 split-K partial
+                              sums (set by the compiler, never by callers) */
+};
+
+/* Instruction opcodes (the record's first word). */
+enum {
+  MK_I_NOOP = 0, MK_I_GEMM = 1, MK_I_GEMV = 2, MK_I_REDUCE = 3,
+  MK_I_RMSNORM = 4, MK_I_ATTENTION = 5, MK_I_EW_ADD = 6, MK_I_EW_RELU = 7
+};
+
+/* Tile parameters of one op; 0 in any field = the compiler's choice.
+ * GEMM: bm x bn output tile (bn counts output columns, so a SILU_MUL tile
+ * reads 2*bn weight columns), split = K chunks (> 1 adds a REDUCE node over
+ * rbm x rbn tiles), dup = copies of each tile (cluster duplicate, host
+ * profile only), gemv = 1 selects the small-M streaming body.
+ * RMSNORM: rows per instruction.  ATTENTION: bq query rows per instruction.
+ * ADD / RELU: er x ec tiles. */
+typedef struct {
+  int32_t bm, bn, split, dup, gemv;
+  int32_t rbm, rbn;
+  int32_t rows;
+  int32_t bq;
+  int32_t er, ec;
+} mk_tile;
+
+typedef struct {
+  uint32_t epilogue;    /* MK_EP_* (GEMM only)                            */
+  float eps;            /* RMSNorm epsilon; 0 -> 1e-6                      */
+  float rope_theta;     /* 0 -> 10000                                      */
+  int32_t n_heads;      /* ATTENTION / ROPE: query heads                   */
+  int32_t n_kv_heads;   /* ATTENTION: kv heads (query head h reads h / (n_heads/n_kv_heads)) */
+  int32_t head_dim;     /* ATTENTION / ROPE                                */
+  int32_t causal;       /* ATTENTION: key j visible to query i iff j <= i  */
+  int32_t rope_cols;    /* ROPE: leading output columns rotated; 0 -> all  */
+  mk_tile tile;
+} mk_op_attrs;
+
+typedef struct {
+  int32_t num_cus;      /* 0 -> 256 (MI355X); placement modulus            */
+  int32_t cluster_size; /* 0 -> 1; node ranges padded to a multiple        */
+  int32_t reuse;        /* 0: no buffer pooling; 1: pool intermediates;
+                           2: also let outputs take pooled slots (host
+                           profile of dispatcher-owned outputs only)       */
+  int32_t gemv_max_m;   /* 0 -> 8: GEMMs with M <= this use the GEMV body  */
+  int64_t spin_limit_us;/* 0 -> 2000000: a counter wait longer than this
+                           aborts the run with MK_E_DEADLOCK               */
+} mk_build_options;
+
+typedef struct {
+  int64_t n_instr;        /* list length incl. Noop pads                   */
+  int64_t n_iters;        /* waves: ceil(n_instr / num_cus)                */
+  int64_t n_nodes;
+  int64_t n_barriers;
+  int64_t n_input_barriers;
+  int64_t n_reuse_barriers;
+  int64_t n_slots;        /* buffer slots of graph and node tensors        */
+  int64_t intermediate_bytes; /* plan-owned device bytes                   */
+  double flops;           /* algorithmic: 2MNK per GEMM + causal attention */
+  double bytes;           /* algorithmic HBM bytes: inputs/weights read once,
+                             every intermediate written once and read once
+                             per consuming node, outputs written once      */
+  int32_t num_cus;
+  int32_t reserved;
+} mk_plan_stats;
+
+/* Instruction record: exactly 256 bytes (MegaKittens Internals section 06:
+ * a fixed 256-byte POD loaded with coalesced per-lane words).  Packed
+ * [n_iters][num_cus] so record i sits at index i. */
+typedef struct {
+  int32_t opcode;      /* MK_I_*                                           */
+  int32_t flags;       /* MK_EP_* of this node                             */
+  int32_t node;        /* index into the node table                        */
+  int32_t n_src, n_dst;
+  int32_t coord[4];    /* tile coordinates (see mk_plan_instructions)      */
+  int32_t r0, r1;      /* output rows [r0, r1) (attention: query rows)     */
+  int32_t c0, c1;      /* output columns [c0, c1) (attention: head h in c0)*/
+  int32_t k0, k1;      /* K range of a GEMM / GEMV instruction             */
+  int32_t split_idx;   /* K chunk index (partials plane)                   */
+  int32_t src_id[MK_MAX_SRC];
+  int32_t src_target[MK_MAX_SRC];
+  int32_t dst_id[MK_MAX_DST];
+  int32_t reserved[MK_INSTR_WORDS - 16 - 2 * MK_MAX_SRC - MK_MAX_DST];
+} mk_instr;
+
+/* Operand of a node: buffer-table slot, element offset and row stride. */
+typedef struct {
+  int32_t slot;        /* -1 = absent                                      */
+  int32_t ld;          /* row stride in elements                           */
+  int64_t off;         /* element offset of logical element (0, 0)         */
+} mk_operand;
+
+/* Node descriptor: exactly 256 bytes, shared by a node's instructions. */
+typedef struct {
+  int32_t opcode, flags, dtype, node_start;
+  int32_t M, N, K, Nb;       /* GEMM: out [M,N], B [K,Nb]; others: rows, cols */
+  int32_t split, n_instr, heads, kv_heads;
+  int32_t head_dim, causal, rope_cols, seq;
+  float eps, scale, reserved_f0, reserved_f1;
+  mk_operand a, b, out, bias, res, gamma, part, aux;
+  int64_t part_plane;        /* elements between split-K planes of part     */
+  int32_t tile_m, tile_n;    /* GEMM kernel tile: rows x weight columns     */
+  int32_t reserved[MK_NODE_WORDS - 20 - 8 * 4 - 2 - 2];
+} mk_node;
+
+typedef struct mk_graph mk_graph;
+typedef struct mk_plan mk_plan;
+
+/* Error record of a failed run (filled when a wait times out). */
+typedef struct {
+  int32_t code;        /* MK_OK or MK_E_DEADLOCK                           */
+  int32_t cu;          /* virtual CU that gave up                          */
+  int32_t instr;       /* instruction index it was waiting in              */
+  int32_t barrier;     /* counter id                                       */
+  int32_t value;       /* counter value seen                               */
+  int32_t need;        /* value waited for (epoch * target)                */
+} mk_run_error;
+
+/* ---- graph building (host only; "Implementing a Mega Kernel for B300",
+ *      section 1) --------------------------------------------------------- */
+mk_status mk_graph_create(mk_graph **g);
+void mk_graph_destroy(mk_graph *g);
+/* New tensor; shape has ndim (1..4) entries.  Ids are dense from 0. */
+mk_status mk_graph_tensor(mk_graph *g, mk_dtype dt, int ndim, const int64_t *shape,
+                          mk_role role, int32_t *id);
+/* Step-1 range view [lo, hi) of tensor src in its left-padded 4-D
+ * coordinates (MegaKittens Internals section 02, step 4).  A view gets its
+ * own id and may be used wherever a tensor id is accepted. */
+mk_status mk_graph_view(mk_graph *g, int32_t src, const int64_t lo[4],
+                        const int64_t hi[4], int32_t *id);
+/* Append an op; ops must be added in topological order. */
+mk_status mk_graph_op(mk_graph *g, mk_op_kind kind, const int32_t *in, int n_in,
+                      int32_t out, const mk_op_attrs *attrs);
+
+/* ---- compile (host only, no GPU needed) -------------------------------- */
+mk_status megakernel_build(const mk_graph *g, const mk_build_options *opts,
+                           mk_plan **plan);
+void mk_plan_destroy(mk_plan *p);
+
+/* ---- run --------------------------------------------------------------- */
+/* One forward as one persistent cooperative launch on `stream` (a
+ * hipStream_t; 0 = null stream).  buffers[i] is the device pointer of tensor
+ * id i for every caller-owned tensor (inputs, weights, outputs); entries of
+ * views and intermediates are ignored.  Asynchronous: call mk_plan_check to
+ * learn whether a counter wait gave up. */
+mk_status megakernel_run(mk_plan *p, void *const *buffers, int n_buffers, void *stream);
+/* Same graph, same tile bodies, one launch per node and no counters. */
+mk_status megakernel_run_per_op(mk_plan *p, void *const *buffers, int n_buffers,
+                                void *stream);
+/* Synchronise `stream` and read the plan's error record. */
+mk_status mk_plan_check(mk_plan *p, void *stream, mk_run_error *err);
+
+/* ---- introspection ----------------------------------------------------- */
+mk_status mk_plan_stats_get(const mk_plan *p, mk_plan_stats *out);
+/* Records, n_instr of them, MK_INSTR_WORDS int32 each (pointer owned by the
+ * plan).  coord: GEMM/GEMV (tm, tn, s, dup copy); REDUCE (tm, tn, 0, 0);
+ * RMSNORM (row block, 0, 0, 0); ATTENTION (q block, head, 0, 0);
+ * EW_* (tile row, tile col, 0, 0). */
+mk_status mk_plan_instructions(const mk_plan *p, const int32_t **words,
+                               int64_t *n_instr, int32_t *words_per_instr);
+mk_status mk_plan_nodes(const mk_plan *p, const int32_t **words, int64_t *n_nodes,
+                        int32_t *words_per_node);
+mk_status mk_plan_barriers(const mk_plan *p, const int32_t **targets, int64_t *n);
+/* slot of each tensor id (-1 for views and unused tensors). */
+mk_status mk_plan_slots(const mk_plan *p, const int32_t **slot_of_tensor, int64_t *n);
+/* Tile parameters the compiler chose for graph op `op`. */
+mk_status mk_plan_op_tile(const mk_plan *p, int32_t op, mk_tile *out);
+/* Copy the counters to host memory after a run (synchronises `stream`).
+ * After e runs every counter equals e * its target. */
+mk_status mk_plan_read_counters(mk_plan *p, int32_t *host, int64_t n, void *stream);
+/* Runs so far (the epoch the next run waits against is this + 1). */
+mk_status mk_plan_epoch(const mk_plan *p, int64_t *epoch);
+
+const char *mk_last_error(void);
+int32_t mk_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MK_H */

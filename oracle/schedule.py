@@ -44,8 +44,10 @@ Lowering and tiling spec (the compiler implements the same rules):
   columns and gamma; writes rows x all columns.
 ``attention`` op, tile param bq: q blocks of bq rows; order: q block
   descending (longest first), head ascending; reads q rows [q0,q1) x head
-  columns, k and v rows [0, q1) (causal; all rows otherwise) x the kv head's
-  columns (kv head = h // (Hq/Hkv)); writes o rows [q0,q1) x head columns.
+  columns and k, v rows [0, S) x the kv head's columns (kv head =
+  h // (Hq/Hkv)); writes o rows [q0,q1) x head columns.  The k/v boxes cover
+  the whole sequence even under the causal mask, so every q block of a kv
+  head shares one dependency set and each k/v tile arrives on one counter.
 ``add`` / ``relu`` ops, tile params er, ec: row-major (er x ec) tiles.
 """
 from __future__ import annotations
@@ -193,14 +195,13 @@ def lower(g: Graph) -> List[Node]:
             q, k, v = op.ins["q"], op.ins["k"], op.ins["v"]
             Hq, Hkv = int(op.attrs["heads"]), int(op.attrs["kv_heads"])
             d = int(op.attrs["head_dim"])
-            causal = bool(op.attrs.get("causal", 1))
             S = q.rows
             bq = op.tile["bq"]
             o = g.full(op.out)
             ins = []
             for qb in reversed(range(_cdiv(S, bq))):
                 q0, q1 = qb * bq, min(S, qb * bq + bq)
-                kend = q1 if causal else S
+                kend = S
                 for h in range(Hq):
                     kh = h // (Hq // Hkv)
                     ins.append(Instr((qb, h, 0, 0),
@@ -565,10 +566,11 @@ def decode_graph(d: Dict[str, int], tiles: Sequence[Dict[str, int]]) -> Graph:
 
 
 def layer_graph(d: Dict[str, int], tiles: Sequence[Dict[str, int]]) -> Graph:
-    """Llama-style decoder layer prefill (bf16): rmsnorm, QKV GEMM with
-    rotary epilogue, causal GQA attention, O GEMM + residual, rmsnorm,
-    gate_up GEMM with SiLU-mul, down GEMM + residual.  ``tiles`` is in op
-    order (7 entries)."""
+    """Llama-style decoder layer prefill (bf16): rmsnorm; the QKV projection
+    as two GEMMs over column ranges of Wqkv (Q, and KV) with the rotary
+    epilogue on q and k; causal GQA attention; O GEMM + residual; rmsnorm;
+    gate_up GEMM with SiLU-mul; down GEMM + residual.  ``tiles`` is in op
+    order (8 entries)."""
     g = Graph()
     S, H = d["seq"], d["hidden"]
     Hq, Hkv, hd, I = d["heads"], d["kv_heads"], d["head_dim"], d["inter"]
@@ -581,7 +583,8 @@ def layer_graph(d: Dict[str, int], tiles: Sequence[Dict[str, int]]) -> Graph:
     Wgu = g.tensor("Wgu", "bf16", (H, 2 * I), "weight")
     Wd = g.tensor("Wd", "bf16", (I, H), "weight")
     xn = g.tensor("xn", "bf16", (S, H), "intermediate")
-    qkv = g.tensor("qkv", "bf16", (S, nq + 2 * nkv), "intermediate")
+    q = g.tensor("q", "bf16", (S, nq), "intermediate")
+    kv = g.tensor("kv", "bf16", (S, 2 * nkv), "intermediate")
     o = g.tensor("o", "bf16", (S, nq), "intermediate")
     h1 = g.tensor("h1", "bf16", (S, H), "intermediate")
     hn = g.tensor("hn", "bf16", (S, H), "intermediate")
@@ -589,17 +592,19 @@ def layer_graph(d: Dict[str, int], tiles: Sequence[Dict[str, int]]) -> Graph:
     out = g.tensor("out", "bf16", (S, H), "output")
     att = dict(heads=Hq, kv_heads=Hkv, head_dim=hd, causal=1)
     g.ops.append(Op("rmsnorm", dict(x=g.full(x), gamma=g.full(g1)), xn, 0, dict(tiles[0])))
-    g.ops.append(Op("gemm", dict(a=g.full(xn), b=g.full(Wqkv)), qkv, ROPE, dict(tiles[1]),
-                    dict(att)))
-    g.ops.append(Op("attention", dict(q=g.cols(qkv, 0, nq), k=g.cols(qkv, nq, nq + nkv),
-                                      v=g.cols(qkv, nq + nkv, nq + 2 * nkv)),
-                    o, 0, dict(tiles[2]), dict(att)))
+    g.ops.append(Op("gemm", dict(a=g.full(xn), b=g.cols(Wqkv, 0, nq)), q, ROPE,
+                    dict(tiles[1]), dict(att)))
+    g.ops.append(Op("gemm", dict(a=g.full(xn), b=g.cols(Wqkv, nq, nq + 2 * nkv)), kv, ROPE,
+                    dict(tiles[2]), dict(att)))
+    g.ops.append(Op("attention", dict(q=g.full(q), k=g.cols(kv, 0, nkv),
+                                      v=g.cols(kv, nkv, 2 * nkv)),
+                    o, 0, dict(tiles[3]), dict(att)))
     g.ops.append(Op("gemm", dict(a=g.full(o), b=g.full(Wo), residual=g.full(x)), h1,
-                    RESIDUAL, dict(tiles[3])))
-    g.ops.append(Op("rmsnorm", dict(x=g.full(h1), gamma=g.full(g2)), hn, 0, dict(tiles[4])))
-    g.ops.append(Op("gemm", dict(a=g.full(hn), b=g.full(Wgu)), a, SILU_MUL, dict(tiles[5])))
+                    RESIDUAL, dict(tiles[4])))
+    g.ops.append(Op("rmsnorm", dict(x=g.full(h1), gamma=g.full(g2)), hn, 0, dict(tiles[5])))
+    g.ops.append(Op("gemm", dict(a=g.full(hn), b=g.full(Wgu)), a, SILU_MUL, dict(tiles[6])))
     g.ops.append(Op("gemm", dict(a=g.full(a), b=g.full(Wd), residual=g.full(h1)), out,
-                    RESIDUAL, dict(tiles[6])))
+                    RESIDUAL, dict(tiles[7])))
     return g
 
 

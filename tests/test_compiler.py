@@ -1,0 +1,228 @@
+"""Host compiler (libmk.so) vs the brute-force schedule oracle, plus ABI
+guards.  CPU only: megakernel_build needs no GPU."""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import workloads
+from oracle import schedule as S
+from tiled_gemm_graph_amd import _lib as L
+from tiled_gemm_graph_amd import graphs as G
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mk.h")
+
+
+def test_library_exports_every_declared_symbol():
+    lib = L.load()
+    text = open(HEADER).read()
+    names = re.findall(r"^\s*(?:mk_status|void|const char|int32_t)\s*\**\s*(\w+)\(", text, re.M)
+    assert len(names) >= 18
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(L.EXPORTS) <= set(names)
+    assert lib.mk_abi_version() == 1
+
+
+def test_struct_layout_matches_decoder(tmp_path):
+    src = tmp_path / "layout.c"
+    src.write_text("""
+#include <stddef.h>
+#include <stdio.h>
+#include "mk.h"
+int main(void) {
+  printf("%zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu\\n", sizeof(mk_instr), sizeof(mk_node),
+    offsetof(mk_instr, opcode)/4, offsetof(mk_instr, n_src)/4, offsetof(mk_instr, coord)/4,
+    offsetof(mk_instr, r0)/4, offsetof(mk_instr, split_idx)/4, offsetof(mk_instr, src_id)/4,
+    offsetof(mk_instr, src_target)/4, offsetof(mk_instr, dst_id)/4,
+    sizeof(mk_tile), sizeof(mk_op_attrs));
+  printf("%zu %zu %zu\\n", sizeof(mk_build_options), sizeof(mk_plan_stats), sizeof(mk_run_error));
+  return 0;
+}
+""")
+    exe = tmp_path / "layout"
+    subprocess.check_call(["gcc", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)])
+    l1, l2 = subprocess.check_output([str(exe)]).decode().split("\n")[:2]
+    v = [int(x) for x in l1.split()]
+    assert v[:2] == [256, 256]
+    assert v[2:10] == [L.W_OPCODE, L.W_NSRC, L.W_COORD, L.W_R0, L.W_SPLIT, L.W_SRC_ID,
+                       L.W_SRC_TGT, L.W_DST_ID]
+    assert v[10] == ctypes.sizeof(L.Tile) and v[11] == ctypes.sizeof(L.OpAttrs)
+    w = [int(x) for x in l2.split()]
+    assert w == [ctypes.sizeof(L.BuildOptions), ctypes.sizeof(L.PlanStats),
+                 ctypes.sizeof(L.RunError)]
+
+
+def _gold():
+    vals = {}
+    for line in open(os.path.join(ROOT, "tests", "golden", "megakittens_mlp_schedule.txt")):
+        line = line.strip()
+        if line and not line.startswith("#"):
+            k, *v = line.split()
+            vals[k] = [float(x) if "." in x else int(x) for x in v]
+    return vals
+
+
+def test_megakittens_profile_through_libmk():
+    tiles = [dict(gemm=dict(bm=512, bn=256, dup=2, gemv=0), ew=dict(er=256, ec=128))]
+    g = G.build("mlp3", dict(layers=3, m=1024, h=1024), tiles, fused=False, w_first=True)
+    plan = g.build(num_cus=148, cluster_size=2, reuse=2)
+    st = plan.stats()
+    gv = _gold()
+    assert st.n_instr == gv["instructions"][0]
+    assert st.n_iters == gv["whole_waves"][0]
+    assert st.n_iters * 148 - st.n_instr == gv["zero_filled_slots"][0]
+    assert st.n_slots == gv["tensor_slots"][0]
+    assert st.n_input_barriers == gv["input_barriers"][0]
+    assert st.n_reuse_barriers == gv["reuse_barriers"][0]
+    assert st.n_barriers == gv["barriers"][0]
+    assert plan.slots()[g.ids["y2"]] == gv["final_relu_slot"][0]
+    # and the whole list equals the oracle's derivation
+    og = S.mlp3_graph(3, 1024, 1024, dict(gemm=dict(bm=512, bn=256, dup=2),
+                                          ew=dict(er=256, ec=128)),
+                      fused=False, names_w_first=True)
+    sc = S.schedule(og, ncu=148, cluster_size=2, reuse=2)
+    assert plan.decoded() == sc.records
+    assert list(plan.barriers()) == sc.targets
+
+
+def _oracle_tiles(tiles):
+    out = []
+    for t in tiles:
+        d = {k: v for k, v in t.items() if v}
+        d.setdefault("split", 1)
+        out.append(d)
+    return out
+
+
+def _compare(wl, dims, tiles=None, reuse=0, ncu=256):
+    g = G.build(wl, dims, tiles)
+    plan = g.build(num_cus=ncu, reuse=reuse)
+    chosen = _oracle_tiles(plan.op_tiles())
+    og = S.workload_graph(wl, dims, chosen if wl != "mlp3" else [chosen[0]])
+    sc = S.schedule(og, ncu=ncu, reuse=reuse)
+    got = plan.decoded()
+    assert len(got) == len(sc.records)
+    for a, b in zip(got, sc.records):
+        assert a == b, (wl, a, b)
+    assert list(plan.barriers()) == sc.targets
+    slots = plan.slots()
+    for ti, t in enumerate(og.tensors):
+        if t.name in g.ids and ti in sc.slots:
+            assert slots[g.ids[t.name]] == sc.slots[ti], t.name
+    st = plan.stats()
+    assert st.n_slots == sc.n_slots
+    assert st.n_reuse_barriers == sc.n_reuse_barriers
+    return plan, sc
+
+
+@pytest.mark.parametrize("wl", workloads.WORKLOADS)
+def test_full_size_lists_match_oracle(wl):
+    dims = workloads.default_dims(wl)
+    plan, sc = _compare(wl, dims)
+    # every counter's arrivals precede its first waiter (deadlock freedom)
+    for i, ds in sc.deps.items():
+        for st in ds.values():
+            assert max(st) < i
+
+
+@pytest.mark.parametrize("wl", workloads.WORKLOADS)
+@pytest.mark.parametrize("reuse", [0, 1])
+def test_small_lists_match_oracle(wl, reuse):
+    _compare(wl, workloads.small_dims(wl), reuse=reuse, ncu=16)
+
+
+def test_explicit_tiles_and_split_gemm_match_oracle():
+    d = dict(m=96, k=512, n_qkv=384, n_q=256, n_o=256, n_up=512, n_down=128)
+    tiles = [dict(bm=64, bn=128, split=2, rbm=32, rbn=64, gemv=0),
+             dict(bm=64, bn=64, gemv=0),
+             dict(bm=128, bn=128, split=4, rbm=64, rbn=128, gemv=0),
+             dict(bm=32, bn=1, gemv=1, split=1) if False else dict(bm=64, bn=64, gemv=0)]
+    _compare("decode_gemm", d, tiles, ncu=32)
+
+
+def test_algorithmic_counts():
+    for wl in workloads.WORKLOADS:
+        dims = workloads.default_dims(wl)
+        st = G.build(wl, dims).build().stats()
+        from oracle import graphs as OG
+        assert abs(st.flops - OG.flops(wl, dims)) / OG.flops(wl, dims) < 1e-9
+    # decode: weights 436.2 MB plus a few KB of activations
+    st = G.build("decode", workloads.default_dims("decode")).build().stats()
+    assert 436.2e6 < st.bytes < 436.5e6
+
+
+# --- negative tests: build must reject what the pages reject ---------------
+
+def test_rejects_non_topological_and_bad_views():
+    g = G.Graph()
+    x = g.tensor("x", "f16", (64, 64), "input")
+    w = g.tensor("w", "f16", (64, 64), "weight")
+    y = g.tensor("y", "f16", (64, 64), "intermediate")
+    z = g.tensor("z", "f16", (64, 64), "output")
+    with pytest.raises(L.MkError) as e:
+        g.gemm(y, w, z)            # y is never written before
+    assert e.value.status == L.MK_E_INVALID
+    with pytest.raises(L.MkError) as e:
+        g.view(x, (0, 0, 0, 0), (1, 1, 65, 64))
+    assert e.value.status == L.MK_E_INVALID
+    with pytest.raises(L.MkError):
+        g.gemm(x, w, x)            # output must not be an input
+    g.gemm(x, w, y)
+    with pytest.raises(L.MkError):
+        g.gemm(x, w, y)            # written twice
+
+
+def test_rejects_shape_mismatch_and_empty_split():
+    g = G.Graph()
+    x = g.tensor("x", "f16", (64, 128), "input")
+    w = g.tensor("w", "f16", (64, 64), "weight")
+    z = g.tensor("z", "f16", (64, 64), "output")
+    g.gemm(x, w, z)
+    with pytest.raises(L.MkError) as e:
+        g.build()
+    assert e.value.status == L.MK_E_INVALID
+    g = G.Graph()
+    x = g.tensor("x", "f16", (64, 256), "input")
+    w = g.tensor("w", "f16", (256, 64), "weight")
+    z = g.tensor("z", "f16", (64, 64), "output")
+    g.gemm(x, w, z, tile=dict(bm=64, bn=64, split=8))
+    with pytest.raises(L.MkError) as e:
+        g.build()
+    assert e.value.status == L.MK_E_INVALID
+
+
+def test_tensor_limit():
+    g = G.Graph()
+    for i in range(L.MAX_TENSORS):
+        g.tensor(f"t{i}", "f16", (8,), "input")
+    with pytest.raises(L.MkError) as e:
+        g.tensor("one_too_many", "f16", (8,), "input")
+    assert e.value.status == L.MK_E_LIMIT
+
+
+def test_empty_graph_and_empty_rows():
+    g = G.Graph()
+    plan = g.build()
+    assert plan.stats().n_instr == 0
+    g = G.Graph()
+    x = g.tensor("x", "f16", (0, 64), "input")
+    w = g.tensor("w", "f16", (64, 64), "weight")
+    z = g.tensor("z", "f16", (0, 64), "output")
+    g.gemm(x, w, z, tile=dict(bm=64, bn=64))
+    plan = g.build()
+    assert plan.stats().n_instr == 0 and plan.stats().n_barriers == 0
+
+
+def test_unsupported_profile_builds_but_does_not_run():
+    # the 512x256 duplicated tiles of the worked example are host-only
+    tiles = [dict(gemm=dict(bm=512, bn=256, dup=2), ew=dict(er=256, ec=128))]
+    g = G.build("mlp3", dict(layers=3, m=1024, h=1024), tiles, fused=False, w_first=True)
+    plan = g.build(num_cus=148, cluster_size=2, reuse=2)
+    with pytest.raises(L.MkError) as e:
+        plan.run([], stream=0)
+    assert e.value.status == L.MK_E_UNSUPPORTED

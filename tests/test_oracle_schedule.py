@@ -104,8 +104,8 @@ TINY = dict(
              dict(bm=1, bn=32, split=2, gemv=1, rbm=1, rbn=64),
              dict(bm=1, bn=64, split=3, gemv=1, rbm=1, rbn=64)]),
     layer=(dict(seq=40, hidden=32, heads=4, kv_heads=2, head_dim=8, inter=48),
-           [dict(rows=8), dict(bm=16, bn=16), dict(bq=16), dict(bm=16, bn=16),
-            dict(rows=16), dict(bm=16, bn=16), dict(bm=8, bn=16)]),
+           [dict(rows=8), dict(bm=16, bn=16), dict(bm=8, bn=16), dict(bq=16),
+            dict(bm=16, bn=16), dict(rows=16), dict(bm=16, bn=16), dict(bm=8, bn=16)]),
 )
 
 

@@ -1,0 +1,844 @@
+// Device side of the tile-graph megakernel for gfx950 (CDNA4).
+//
+// One persistent workgroup of 256 threads (4 wave64s) per compute unit walks
+// its share of the host-compiled instruction list ("MegaKittens Internals",
+// sections 05 and 08-11; "Beating torch.compile with Megakernels in CuTe DSL",
+// "Cooperative Kernel"): fetch the 256-byte record, wait until every source
+// counter reaches epoch * target (acquire, agent scope), run the tile body,
+// make the tile's stores visible (release, agent scope) and add 1 to every
+// destination counter.  Every wait is bounded in time: on expiry the
+// workgroup records the failure, raises a shared abort flag that every other
+// wait polls, and the whole grid drains.
+//
+// Tile bodies (all fp32 accumulate, one round-to-nearest-even cast):
+//   GEMM      C = A @ B on v_mfma_f32_32x32x16_{f16,bf16}, BM x BNK tile
+//             (64/128), K step 64, A and B staged through two LDS buffers;
+//             B (K-major weights) is transposed in registers on the way in;
+//             epilogue through an fp32 LDS tile.
+//   GEMV      M <= 8 rows: each thread streams 16-byte weight chunks of one
+//             K row, the activation chunk is staged in LDS, partial sums are
+//             reduced across the workgroup.
+//   REDUCE    sums split-K partials in a fixed order, then the epilogue.
+//   RMSNORM   rows of x * gamma / sqrt(mean(x^2) + eps).
+//   ATTENTION causal grouped-query flash attention, 128 queries x one head
+//             per instruction, 64-key steps, online softmax in exp2.
+//   EW_ADD / EW_RELU  elementwise tiles.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "mk.h"
+
+namespace mkd {
+
+constexpr int kThreads = 256;
+constexpr int kBK = 64;                 // GEMM K step
+constexpr int kLdsPad = 8;              // 16-bit elements of row padding
+constexpr int kSmemBytes = 144 * 1024;  // dynamic scratch per workgroup
+
+struct KArgs {
+  const mk_instr* instrs;   // [n_iters][ncu]
+  const mk_node* nodes;
+  int* counters;
+  int* err;                 // code, cu, instr, barrier, value, need, abort
+  long long spin_ticks;     // wall-clock ticks a wait may take
+  int n_iters, ncu, epoch;
+  int first, count;         // per-op mode: records [first, first + count)
+  void* bufs[MK_MAX_TENSORS];
+};
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned short u16;
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// ---------------------------------------------------------------- numerics
+__device__ __forceinline__ float bf16_to_f(u16 h) { return __uint_as_float((uint32_t)h << 16); }
+__device__ __forceinline__ float f16_to_f(u16 h) { return (float)__builtin_bit_cast(_Float16, h); }
+template <int DT>
+__device__ __forceinline__ float to_f(u16 h) { return DT == MK_BF16 ? bf16_to_f(h) : f16_to_f(h); }
+
+__device__ __forceinline__ u16 f_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;  // NaN
+  u += 0x7fffu + ((u >> 16) & 1u);                      // round to nearest even
+  return (u16)(u >> 16);
+}
+__device__ __forceinline__ u16 f_to_f16(float f) { return __builtin_bit_cast(u16, (_Float16)f); }
+template <int DT>
+__device__ __forceinline__ u16 from_f(float f) { return DT == MK_BF16 ? f_to_bf16(f) : f_to_f16(f); }
+
+__device__ __forceinline__ uint32_t word(const u32x4& v, int q) {
+  return q == 0 ? v.x : q == 1 ? v.y : q == 2 ? v.z : v.w;
+}
+// 16-bit columns 2q+h of rows r0, r1 packed as (row r0, row r1)
+__device__ __forceinline__ uint32_t pick2(const u32x4& r0, const u32x4& r1, int n) {
+  const uint32_t sel = (n & 1) ? 0x07060302u : 0x05040100u;
+  return __builtin_amdgcn_perm(word(r1, n >> 1), word(r0, n >> 1), sel);
+}
+
+template <int DT>
+__device__ __forceinline__ void unpack8(const u32x4& v, float* f) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t w = word(v, i);
+    f[2 * i] = to_f<DT>((u16)(w & 0xffff));
+    f[2 * i + 1] = to_f<DT>((u16)(w >> 16));
+  }
+}
+template <int DT>
+__device__ __forceinline__ u32x4 pack8(const float* f) {
+  uint32_t w[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) w[i] = (uint32_t)from_f<DT>(f[2 * i]) | ((uint32_t)from_f<DT>(f[2 * i + 1]) << 16);
+  return u32x4{w[0], w[1], w[2], w[3]};
+}
+
+template <int DT>
+__device__ __forceinline__ f32x16 mfma32(const u32x4& a, const u32x4& b, f32x16 c) {
+  if constexpr (DT == MK_BF16)
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                   __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// Sum over the workgroup; `red` holds at least 4 floats of LDS.
+__device__ __forceinline__ float block_sum(float v, float* red) {
+  v = wave_sum(v);
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  return red[0] + red[1] + red[2] + red[3];
+}
+
+template <typename T>
+__device__ __forceinline__ T* buf(const KArgs& a, const mk_operand& o) {
+  return reinterpret_cast<T*>(a.bufs[o.slot]) + o.off;
+}
+
+// ------------------------------------------------------------- epilogue
+// Applies the non-partial epilogue to 8 consecutive output columns of one
+// row and stores them.  raw(w) returns the 8 fp32 product values at
+// weight-tile column w (w = output column for plain tiles; gate at w and up
+// at w + half for SILU_MUL).  gr, gc: global row / output column.
+template <int DT, typename Raw>
+__device__ __forceinline__ void epilogue8(const KArgs& a, const mk_node& nd, int flags, int gr,
+                                          int gc, int w, int half, Raw raw) {
+  float v[8];
+  if (flags & MK_EP_SILU_MUL) {
+    float g[8], u[8];
+    raw(w, g);
+    raw(w + half, u);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = silu(g[e]) * u[e];
+  } else {
+    raw(w, v);
+  }
+  if (flags & MK_EP_BIAS) {
+    const u32x4 b = *reinterpret_cast<const u32x4*>(buf<u16>(a, nd.bias) + (long)gr * nd.bias.ld + gc);
+    float f[8];
+    unpack8<DT>(b, f);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] += f[e];
+  }
+  if (flags & MK_EP_RESIDUAL) {
+    const u32x4 b = *reinterpret_cast<const u32x4*>(buf<u16>(a, nd.res) + (long)gr * nd.res.ld + gc);
+    float f[8];
+    unpack8<DT>(b, f);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] += f[e];
+  }
+  if ((flags & MK_EP_ROPE) && gc < nd.rope_cols) {
+    const int hd = nd.head_dim, hh = hd >> 1;
+    const int i0 = gc % hd;  // 8 columns never straddle the half (hd % 16 == 0)
+    const bool lo = i0 < hh;
+    float p[8];
+    raw(lo ? w + hh : w - hh, p);
+    const float* tab = buf<float>(a, nd.aux) + (long)gr * hd;  // [cos(half) | sin(half)]
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int i = (i0 + e) % hh;
+      const float c = tab[i], s = tab[hh + i];
+      v[e] = lo ? v[e] * c - p[e] * s : v[e] * c + p[e] * s;
+    }
+  }
+  if (flags & MK_EP_RELU) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = fmaxf(v[e], 0.0f);
+  }
+  *reinterpret_cast<u32x4*>(buf<u16>(a, nd.out) + (long)gr * nd.out.ld + gc) = pack8<DT>(v);
+}
+
+// ------------------------------------------------------------------ GEMM
+// C[BM x BNK] = A[r0:r0+BM, k0:k1] @ B[k0:k1, cols], cols = c0.. (plain) or
+// gate c0.. and up N+c0.. (SILU_MUL, BNK/2 each).
+template <int BM, int BNK, int DT>
+__device__ void gemm_tile(const KArgs& a, const mk_instr& in, const mk_node& nd, char* smem) {
+  constexpr int LDS_ROW = kBK + kLdsPad;           // 72 elements = 144 B
+  constexpr int A_STAGE = BM * LDS_ROW;            // elements
+  constexpr int B_STAGE = BNK * LDS_ROW;
+  constexpr int WM = BM / 2, WN = BNK / 2, FM = WM / 32, FN = WN / 32;
+  constexpr int A_CHUNKS = BM * kBK / 8 / kThreads;  // 16-byte chunks per thread
+  constexpr int RB = BNK / 32;                       // B rows (k) per thread
+  constexpr int NCG = BNK / 8;                       // B column groups
+
+  u16* As = reinterpret_cast<u16*>(smem);
+  u16* Bs = As + 2 * A_STAGE;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int flags = in.flags;
+  const bool silu = flags & MK_EP_SILU_MUL;
+  const int half = silu ? BNK / 2 : BNK;
+  const int M = nd.M, N = nd.N;
+  const int r0 = in.r0, c0 = in.c0, k0 = in.k0, k1 = in.k1;
+  const u16* A = buf<const u16>(a, nd.a);
+  const u16* B = buf<const u16>(a, nd.b);
+  const long lda = nd.a.ld, ldb = nd.b.ld;
+
+  // per-thread global addresses
+  const u16* a_src[A_CHUNKS];
+  int a_dst[A_CHUNKS];
+#pragma unroll
+  for (int i = 0; i < A_CHUNKS; ++i) {
+    const int c = t + kThreads * i, row = c >> 3, kc = c & 7;
+    const int gr = min(r0 + row, M - 1);
+    a_src[i] = A + (long)gr * lda + k0 + kc * 8;
+    a_dst[i] = row * LDS_ROW + kc * 8;
+  }
+  const int ncg = t % NCG, kq = t / NCG;
+  int wcol = ncg * 8;  // weight-tile column of this thread's 8-column group
+  int gcol;
+  if (silu) {
+    const int j = wcol < half ? wcol : wcol - half;
+    const int cl = min(c0 + j, N - 8);
+    gcol = wcol < half ? cl : N + cl;
+  } else {
+    gcol = min(c0 + wcol, N - 8);
+  }
+  const u16* b_src = B + (long)(k0 + kq * RB) * ldb + gcol;
+
+  f32x16 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+  u32x4 ra[A_CHUNKS], rb[RB];
+  auto gload = [&](int kt) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < A_CHUNKS; ++i) ra[i] = *reinterpret_cast<const u32x4*>(a_src[i] + kt * kBK);
+#pragma unroll
+    for (int r = 0; r < RB; ++r) rb[r] = *reinterpret_cast<const u32x4*>(b_src + (long)(kt * kBK + r) * ldb);
+  };
+  auto swrite = [&](int st) __attribute__((always_inline)) {
+    u16* as = As + st * A_STAGE;
+#pragma unroll
+    for (int i = 0; i < A_CHUNKS; ++i) *reinterpret_cast<u32x4*>(as + a_dst[i]) = ra[i];
+    // transpose RB (k) x 8 (n) into 8 rows of Bt[n][k], RB k-values each
+    u16* bs = Bs + st * B_STAGE + wcol * LDS_ROW + kq * RB;
+#pragma unroll
+    for (int n = 0; n < 8; ++n) {
+      if constexpr (RB == 4) {
+        *reinterpret_cast<u32x2*>(bs + n * LDS_ROW) = u32x2{pick2(rb[0], rb[1], n), pick2(rb[2], rb[3], n)};
+      } else {
+        *reinterpret_cast<uint32_t*>(bs + n * LDS_ROW) = pick2(rb[0], rb[1], n);
+      }
+    }
+  };
+
+  const int nk = (k1 - k0) / kBK;
+  gload(0);
+  swrite(0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int st = kt & 1;
+    if (kt + 1 < nk) gload(kt + 1);
+    const u16* as = As + st * A_STAGE;
+    const u16* bs = Bs + st * B_STAGE;
+#pragma unroll
+    for (int kk = 0; kk < kBK / 16; ++kk) {
+      u32x4 af[FM], bf[FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+        af[i] = *reinterpret_cast<const u32x4*>(as + (wm * WM + i * 32 + (lane & 31)) * LDS_ROW + kk * 16 + (lane >> 5) * 8);
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        bf[j] = *reinterpret_cast<const u32x4*>(bs + (wn * WN + j * 32 + (lane & 31)) * LDS_ROW + kk * 16 + (lane >> 5) * 8);
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = mfma32<DT>(af[i], bf[j], acc[i][j]);
+    }
+    if (kt + 1 < nk) swrite(st ^ 1);
+    __syncthreads();
+  }
+
+  // accumulators -> fp32 LDS tile Cs[BM][BNK + 4]
+  constexpr int CS = BNK + 4;
+  float* Cs = reinterpret_cast<float*>(smem);
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int row = wm * WM + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+        const int col = wn * WN + j * 32 + (lane & 31);
+        Cs[row * CS + col] = acc[i][j][e];
+      }
+  __syncthreads();
+
+  const int r1 = in.r1, c1 = in.c1;
+  if (flags & MK_EP_PARTIAL) {
+    // fp32 partial sums of every weight column: P[s][row][weight col]
+    float* P = buf<float>(a, nd.part) + (long)in.split_idx * nd.part_plane;
+    constexpr int UNITS = BM * BNK / 8;
+    for (int u = t; u < UNITS; u += kThreads) {
+      const int row = u / (BNK / 8), w = (u % (BNK / 8)) * 8;
+      const int gr = r0 + row;
+      const int j = w < half ? w : w - half;
+      if (gr >= r1 || c0 + j >= c1) continue;
+      const int gc = (silu && w >= half) ? N + c0 + j : c0 + j;
+      float4* dst = reinterpret_cast<float4*>(P + (long)gr * nd.part.ld + gc);
+      const float* s = Cs + row * CS + w;
+      dst[0] = make_float4(s[0], s[1], s[2], s[3]);
+      dst[1] = make_float4(s[4], s[5], s[6], s[7]);
+    }
+    return;
+  }
+  constexpr int OUNITS_MAX = BM * BNK / 8;
+  const int ounits = BM * (half / 8);
+  for (int u = t; u < ounits && u < OUNITS_MAX; u += kThreads) {
+    const int row = u / (half / 8), w = (u % (half / 8)) * 8;
+    const int gr = r0 + row, gc = c0 + w;
+    if (gr >= r1 || gc >= c1) continue;
+    epilogue8<DT>(a, nd, flags, gr, gc, w, half, [&](int ww, float* o) {
+      const float* s = Cs + row * CS + ww;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = s[e];
+    });
+  }
+}
+
+// ------------------------------------------------------------------ GEMV
+// Rows [r0, r1) (at most 8), weight-tile columns wc = (c1 - c0) or twice that
+// under SILU_MUL, K rows [k0, k1).
+template <int DT, int MAXR>
+__device__ void gemv_tile(const KArgs& a, const mk_instr& in, const mk_node& nd, char* smem) {
+  constexpr int KB = 1024;  // K rows staged per pass
+  const int t = threadIdx.x;
+  const int flags = in.flags;
+  const bool silu = flags & MK_EP_SILU_MUL, rms = flags & MK_EP_RMSNORM_INPUT;
+  const int N = nd.N;
+  const int r0 = in.r0, rows = in.r1 - in.r0, c0 = in.c0, c1 = in.c1, k0 = in.k0, k1 = in.k1;
+  const int bw = c1 - c0;                       // output columns of this tile
+  const int wc = silu ? 2 * bw : bw;            // weight columns read
+  const int ncg = wc / 8;                       // 16-byte column groups
+  const int kpar = kThreads / ncg;              // K rows in flight at once
+  const int cg = t % ncg, kr = t / ncg;
+  const bool active = kr < kpar;
+  int gcol;
+  {
+    const int w = cg * 8;
+    gcol = (silu && w >= bw) ? N + c0 + (w - bw) : c0 + w;
+  }
+  const u16* A = buf<const u16>(a, nd.a) + (long)r0 * nd.a.ld;
+  const u16* G = rms ? buf<const u16>(a, nd.gamma) : nullptr;
+  const u16* W = buf<const u16>(a, nd.b) + gcol;
+  const long ldb = nd.b.ld, lda = nd.a.ld;
+
+  float* xs = reinterpret_cast<float*>(smem);          // [MAXR][KB] activation chunk
+  float* red = xs + 8 * KB;                            // [kpar][MAXR][wc] partial sums
+  float* misc = red + 8 * 8 * 256;                     // reductions
+  float acc[MAXR][8];
+#pragma unroll
+  for (int m = 0; m < MAXR; ++m)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[m][e] = 0.f;
+  float ssq[MAXR];
+#pragma unroll
+  for (int m = 0; m < MAXR; ++m) ssq[m] = 0.f;
+
+  for (int kb = k0; kb < k1; kb += KB) {
+    const int kn = min(KB, k1 - kb);
+    const int kc8 = kn / 8;
+    __syncthreads();
+    for (int i = t; i < rows * kc8; i += kThreads) {
+      const int m = i / kc8, kc = (i % kc8) * 8;
+      float f[8];
+      unpack8<DT>(*reinterpret_cast<const u32x4*>(A + (long)m * lda + kb + kc), f);
+      if (rms) {
+        float gm[8];
+        unpack8<DT>(*reinterpret_cast<const u32x4*>(G + kb + kc), gm);
+        float s = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          s += f[e] * f[e];
+          f[e] *= gm[e];
+        }
+#pragma unroll
+        for (int mm = 0; mm < MAXR; ++mm)
+          if (mm == m) ssq[mm] += s;
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) xs[m * KB + kc + e] = f[e];
+    }
+    __syncthreads();
+    if (active) {
+      int k = kr;
+      for (; k + 7 * kpar < kn; k += 8 * kpar) {
+        u32x4 wv[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) wv[u] = *reinterpret_cast<const u32x4*>(W + (long)(kb + k + u * kpar) * ldb);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          float f[8];
+          unpack8<DT>(wv[u], f);
+#pragma unroll
+          for (int m = 0; m < MAXR; ++m) {
+            if (m < rows) {
+              const float x = xs[m * KB + k + u * kpar];
+#pragma unroll
+              for (int e = 0; e < 8; ++e) acc[m][e] = fmaf(x, f[e], acc[m][e]);
+            }
+          }
+        }
+      }
+      for (; k < kn; k += kpar) {
+        float f[8];
+        unpack8<DT>(*reinterpret_cast<const u32x4*>(W + (long)(kb + k) * ldb), f);
+#pragma unroll
+        for (int m = 0; m < MAXR; ++m) {
+          if (m < rows) {
+            const float x = xs[m * KB + k];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[m][e] = fmaf(x, f[e], acc[m][e]);
+          }
+        }
+      }
+    }
+  }
+  __syncthreads();
+  if (active) {
+#pragma unroll
+    for (int m = 0; m < MAXR; ++m)
+      if (m < rows)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) red[(kr * MAXR + m) * wc + cg * 8 + e] = acc[m][e];
+  }
+  __syncthreads();
+  // sum the kpar partial rows: sum[m][w] for m < rows, w < wc
+  float* sum = xs;  // reuse: [MAXR][wc]
+  for (int i = t; i < rows * wc; i += kThreads) {
+    const int m = i / wc, w = i % wc;
+    float s = 0.f;
+    for (int q = 0; q < kpar; ++q) s += red[(q * MAXR + m) * wc + w];
+    sum[m * wc + w] = s;
+  }
+  // 1/rms per row when the instruction covers the whole K (no split)
+  float* rinv = misc;
+  if (rms && !(flags & MK_EP_PARTIAL)) {
+#pragma unroll
+    for (int m = 0; m < MAXR; ++m) {
+      if (m < rows) {
+        const float tot = block_sum(ssq[m], misc + 8);
+        if (t == 0) rinv[m] = 1.0f / sqrtf(tot / (float)nd.K + nd.eps);
+      }
+    }
+  }
+  __syncthreads();
+  if (flags & MK_EP_PARTIAL) {
+    float* P = buf<float>(a, nd.part) + (long)in.split_idx * nd.part_plane;
+    for (int i = t; i < rows * wc; i += kThreads) {
+      const int m = i / wc, w = i % wc;
+      const int gc = (silu && w >= bw) ? N + c0 + (w - bw) : c0 + w;
+      P[(long)(r0 + m) * nd.part.ld + gc] = sum[m * wc + w];
+    }
+    return;
+  }
+  const int units = rows * (bw / 8);
+  for (int u = t; u < units; u += kThreads) {
+    const int m = u / (bw / 8), w = (u % (bw / 8)) * 8;
+    const float sc = rms ? rinv[m] : 1.0f;
+    epilogue8<DT>(a, nd, flags, r0 + m, c0 + w, w, bw, [&](int ww, float* o) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = sum[m * wc + ww + e] * sc;
+    });
+  }
+}
+
+// ---------------------------------------------------------------- REDUCE
+template <int DT>
+__device__ void reduce_tile(const KArgs& a, const mk_instr& in, const mk_node& nd, char* smem) {
+  const int t = threadIdx.x;
+  const int flags = in.flags;
+  const bool silu = flags & MK_EP_SILU_MUL, rms = flags & MK_EP_RMSNORM_INPUT;
+  const int N = nd.N, S = nd.split, K = nd.K;
+  const int r0 = in.r0, rows = in.r1 - in.r0, c0 = in.c0, bw = in.c1 - in.c0;
+  float* rinv = reinterpret_cast<float*>(smem);
+  float* scratch = rinv + 256;
+  if (rms) {
+    const u16* X = buf<const u16>(a, nd.a);
+    for (int m = 0; m < rows; ++m) {
+      float s = 0.f;
+      for (int k = t * 8; k < K; k += kThreads * 8) {
+        float f[8];
+        unpack8<DT>(*reinterpret_cast<const u32x4*>(X + (long)(r0 + m) * nd.a.ld + k), f);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s += f[e] * f[e];
+      }
+      s = block_sum(s, scratch);
+      if (t == 0) rinv[m] = 1.0f / sqrtf(s / (float)K + nd.eps);
+    }
+    __syncthreads();
+  }
+  const float* P = buf<const float>(a, nd.part);
+  const long plane = nd.part_plane, ldp = nd.part.ld;
+  const int units = rows * (bw / 8);
+  for (int u = t; u < units; u += kThreads) {
+    const int m = u / (bw / 8), w = (u % (bw / 8)) * 8;
+    const int gr = r0 + m;
+    const float sc = rms ? rinv[m] : 1.0f;
+    epilogue8<DT>(a, nd, flags, gr, c0 + w, w, bw, [&](int ww, float* o) {
+      // weight-tile column ww: output column c0+ww (plain / gate) or the up
+      // column N + c0 + (ww - bw) under SILU_MUL
+      const int gc = (silu && ww >= bw) ? N + c0 + (ww - bw) : c0 + ww;
+      float s[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+      for (int p = 0; p < S; ++p) {
+        const float4* src = reinterpret_cast<const float4*>(P + p * plane + (long)gr * ldp + gc);
+        const float4 x0 = src[0], x1 = src[1];
+        s[0] += x0.x; s[1] += x0.y; s[2] += x0.z; s[3] += x0.w;
+        s[4] += x1.x; s[5] += x1.y; s[6] += x1.z; s[7] += x1.w;
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = s[e] * sc;
+    });
+  }
+}
+
+// --------------------------------------------------------------- RMSNORM
+template <int DT>
+__device__ void rmsnorm_tile(const KArgs& a, const mk_instr& in, const mk_node& nd, char* smem) {
+  const int t = threadIdx.x;
+  const int H = nd.N;
+  float* scratch = reinterpret_cast<float*>(smem);
+  const u16* X = buf<const u16>(a, nd.a);
+  const u16* G = buf<const u16>(a, nd.gamma);
+  u16* O = buf<u16>(a, nd.out);
+  for (int r = in.r0; r < in.r1; ++r) {
+    float s = 0.f;
+    for (int k = t * 8; k < H; k += kThreads * 8) {
+      float f[8];
+      unpack8<DT>(*reinterpret_cast<const u32x4*>(X + (long)r * nd.a.ld + k), f);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s += f[e] * f[e];
+    }
+    s = block_sum(s, scratch);
+    const float rinv = 1.0f / sqrtf(s / (float)H + nd.eps);
+    for (int k = t * 8; k < H; k += kThreads * 8) {
+      float f[8], g[8];
+      unpack8<DT>(*reinterpret_cast<const u32x4*>(X + (long)r * nd.a.ld + k), f);
+      unpack8<DT>(*reinterpret_cast<const u32x4*>(G + k), g);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) f[e] = f[e] * rinv * g[e];
+      *reinterpret_cast<u32x4*>(O + (long)r * nd.out.ld + k) = pack8<DT>(f);
+    }
+  }
+}
+
+// ------------------------------------------------------------- ATTENTION
+// Causal grouped-query attention for query rows [r0, r1) (at most 128) of
+// query head h = c0 (kv head c1), keys [0, k1).  Each wave owns 32 queries.
+// S^T = K Q^T is computed so that each lane holds one query's scores, which
+// then feed the P V product as the B operand straight from registers.
+template <int DT>
+__device__ void attention_tile(const KArgs& a, const mk_instr& in, const mk_node& nd, char* smem) {
+  constexpr int D = 128, KBLK = 64;
+  constexpr int KS = D + kLdsPad;      // K tile row: 136 elements
+  constexpr int VS = KBLK + kLdsPad;   // V^T tile row: 72 elements
+  u16* Ks = reinterpret_cast<u16*>(smem);            // [64][136]
+  u16* Vt = Ks + KBLK * KS;                           // [128][72]
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6, g = lane >> 5, l32 = lane & 31;
+  const int S = nd.seq, h = in.c0, kh = in.c1;
+  const int q0 = in.r0, q1 = in.r1, kend = in.k1;
+  const bool causal = nd.causal;
+  const u16* Q = buf<const u16>(a, nd.a) + h * D;
+  const u16* Kp = buf<const u16>(a, nd.b) + kh * D;
+  const u16* Vp = buf<const u16>(a, nd.aux) + kh * D;
+  const long ldq = nd.a.ld, ldk = nd.b.ld, ldv = nd.aux.ld;
+  const float c = nd.scale * 1.4426950408889634f;  // scale * log2(e)
+
+  const int qrow = q0 + wave * 32 + l32;             // this lane's query
+  const int qr = min(qrow, S - 1);
+  u32x4 qf[8];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) qf[s] = *reinterpret_cast<const u32x4*>(Q + (long)qr * ldq + s * 16 + g * 8);
+
+  f32x16 o[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) o[db][e] = 0.f;
+  float mrun = -INFINITY, lsum = 0.f;
+
+  for (int kb0 = 0; kb0 < kend; kb0 += KBLK) {
+    __syncthreads();
+    // stage K [64][128] and V^T [128][64]
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int cidx = t + kThreads * i, key = cidx >> 4, dc = (cidx & 15) * 8;
+      const int gk = min(kb0 + key, S - 1);
+      *reinterpret_cast<u32x4*>(Ks + key * KS + dc) = *reinterpret_cast<const u32x4*>(Kp + (long)gk * ldk + dc);
+    }
+    {
+      const int dblk = t & 15, kq = t >> 4;  // 8 d x 4 keys per thread
+      u32x4 v[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int gk = min(kb0 + kq * 4 + r, S - 1);
+        v[r] = *reinterpret_cast<const u32x4*>(Vp + (long)gk * ldv + dblk * 8);
+      }
+#pragma unroll
+      for (int n = 0; n < 8; ++n)
+        *reinterpret_cast<u32x2*>(Vt + (dblk * 8 + n) * VS + kq * 4) = u32x2{pick2(v[0], v[1], n), pick2(v[2], v[3], n)};
+    }
+    __syncthreads();
+    // S^T for 64 keys x 32 queries: two 32-key blocks
+    f32x16 sacc[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) sacc[kb][e] = 0.f;
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const u32x4 kf = *reinterpret_cast<const u32x4*>(Ks + (kb * 32 + l32) * KS + s * 16 + g * 8);
+        sacc[kb] = mfma32<DT>(kf, qf[s], sacc[kb]);
+      }
+    }
+    // mask, scale, running max
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int key = kb0 + kb * 32 + 8 * (e >> 2) + 4 * g + (e & 3);
+        float sv = sacc[kb][e] * c;
+        if (key >= kend || (causal && key > qrow)) sv = -INFINITY;
+        sacc[kb][e] = sv;
+        mloc = fmaxf(mloc, sv);
+      }
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
+    const float mnew = fmaxf(mrun, mloc);
+    const float muse = mnew == -INFINITY ? 0.f : mnew;
+    const float alpha = exp2f(mrun - muse);
+    mrun = mnew;
+    float psum = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const float p = exp2f(sacc[kb][e] - muse);
+        sacc[kb][e] = p;
+        psum += p;
+      }
+    lsum = lsum * alpha + psum;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) o[db][e] *= alpha;
+    // O^T += V^T P^T over four 16-key substeps
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      const int kb = st >> 1, hf = st & 1;
+      float pv[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pv[e] = sacc[kb][hf * 8 + e];
+      const u32x4 pf = pack8<DT>(pv);
+      const int kbase = kb * 32 + hf * 16 + 4 * g;  // keys kbase..+3 and kbase+8..+3
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        const u16* vrow = Vt + (db * 32 + l32) * VS;
+        const u32x2 v0 = *reinterpret_cast<const u32x2*>(vrow + kbase);
+        const u32x2 v1 = *reinterpret_cast<const u32x2*>(vrow + kbase + 8);
+        o[db] = mfma32<DT>(u32x4{v0.x, v0.y, v1.x, v1.y}, pf, o[db]);
+      }
+    }
+  }
+  lsum += __shfl_xor(lsum, 32, 64);
+  const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
+  // O^T (d rows x 32 queries per wave) -> LDS [128 q][136] -> coalesced stores
+  __syncthreads();
+  u16* Os = reinterpret_cast<u16*>(smem);
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int d = db * 32 + 8 * j + 4 * g;
+      const uint32_t w0 = (uint32_t)from_f<DT>(o[db][4 * j] * inv) | ((uint32_t)from_f<DT>(o[db][4 * j + 1] * inv) << 16);
+      const uint32_t w1 = (uint32_t)from_f<DT>(o[db][4 * j + 2] * inv) | ((uint32_t)from_f<DT>(o[db][4 * j + 3] * inv) << 16);
+      *reinterpret_cast<u32x2*>(Os + (wave * 32 + l32) * KS + d) = u32x2{w0, w1};
+    }
+  __syncthreads();
+  u16* O = buf<u16>(a, nd.out) + h * D;
+  for (int i = t; i < 128 * 16; i += kThreads) {
+    const int r = i >> 4, dc = (i & 15) * 8;
+    if (q0 + r >= q1) continue;
+    *reinterpret_cast<u32x4*>(O + (long)(q0 + r) * nd.out.ld + dc) = *reinterpret_cast<const u32x4*>(Os + r * KS + dc);
+  }
+}
+
+// ----------------------------------------------------------- elementwise
+template <int DT>
+__device__ void elementwise_tile(const KArgs& a, const mk_instr& in, const mk_node& nd) {
+  const int t = threadIdx.x;
+  const bool add = in.opcode == MK_I_EW_ADD;
+  const int wcols = in.c1 - in.c0, units = (in.r1 - in.r0) * (wcols / 8);
+  const u16* A = buf<const u16>(a, nd.a);
+  const u16* B = add ? buf<const u16>(a, nd.b) : nullptr;
+  u16* O = buf<u16>(a, nd.out);
+  for (int u = t; u < units; u += kThreads) {
+    const int r = in.r0 + u / (wcols / 8), c = in.c0 + (u % (wcols / 8)) * 8;
+    float x[8];
+    unpack8<DT>(*reinterpret_cast<const u32x4*>(A + (long)r * nd.a.ld + c), x);
+    if (add) {
+      float y[8];
+      unpack8<DT>(*reinterpret_cast<const u32x4*>(B + (long)r * nd.b.ld + c), y);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] += y[e];
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = fmaxf(x[e], 0.f);
+    }
+    *reinterpret_cast<u32x4*>(O + (long)r * nd.out.ld + c) = pack8<DT>(x);
+  }
+}
+
+// -------------------------------------------------------------- dispatch
+template <int DT>
+__device__ void run_body(const KArgs& a, const mk_instr& in, const mk_node& nd, char* smem) {
+  switch (in.opcode) {
+    case MK_I_GEMM:
+      if (nd.tile_m == 128 && nd.tile_n == 128) gemm_tile<128, 128, DT>(a, in, nd, smem);
+      else if (nd.tile_m == 64 && nd.tile_n == 128) gemm_tile<64, 128, DT>(a, in, nd, smem);
+      else if (nd.tile_m == 128 && nd.tile_n == 64) gemm_tile<128, 64, DT>(a, in, nd, smem);
+      else gemm_tile<64, 64, DT>(a, in, nd, smem);
+      break;
+    case MK_I_GEMV:
+      if (in.r1 - in.r0 == 1) gemv_tile<DT, 1>(a, in, nd, smem);
+      else gemv_tile<DT, 8>(a, in, nd, smem);
+      break;
+    case MK_I_REDUCE: reduce_tile<DT>(a, in, nd, smem); break;
+    case MK_I_RMSNORM: rmsnorm_tile<DT>(a, in, nd, smem); break;
+    case MK_I_ATTENTION: attention_tile<DT>(a, in, nd, smem); break;
+    case MK_I_EW_ADD:
+    case MK_I_EW_RELU: elementwise_tile<DT>(a, in, nd); break;
+    default: break;
+  }
+}
+
+__device__ __forceinline__ void run_instr(const KArgs& a, const mk_instr& in, const mk_node& nd, char* smem) {
+  if (nd.dtype == MK_BF16) run_body<MK_BF16>(a, in, nd, smem);
+  else run_body<MK_F16>(a, in, nd, smem);
+}
+
+// ----------------------------------------------------- counters and waits
+__device__ __forceinline__ void copy_words(int* dst, const int* src) {
+  if (threadIdx.x < 64) dst[threadIdx.x] = src[threadIdx.x];
+}
+
+// Thread 0 waits on every source counter; returns false (uniformly) if the
+// run was aborted.  `flag` is an LDS int.
+__device__ bool wait_sources(const KArgs& a, const mk_instr& in, int vcu, int gidx, int* flag) {
+  if (threadIdx.x == 0) {
+    int ok = 1;
+    const long long t0 = wall_clock64();
+    for (int k = 0; k < in.n_src && ok; ++k) {
+      const int id = in.src_id[k];
+      const int need = a.epoch * in.src_target[k];
+      int v;
+      while ((v = __hip_atomic_load(a.counters + id, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) < need) {
+        if (__hip_atomic_load(a.err + 6, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) { ok = 0; break; }
+        if (wall_clock64() - t0 > a.spin_ticks) {
+          if (atomicCAS(a.err, 0, (int)MK_E_DEADLOCK) == 0) {
+            a.err[1] = vcu; a.err[2] = gidx; a.err[3] = id; a.err[4] = v; a.err[5] = need;
+          }
+          __hip_atomic_store(a.err + 6, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          ok = 0;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+    }
+    if (ok && in.n_src) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    *flag = ok;
+  }
+  __syncthreads();
+  return *flag != 0;
+}
+
+__device__ __forceinline__ void release_dests(const KArgs& a, const mk_instr& in) {
+  // every wave: its stores have completed; then one lane makes them visible
+  // at agent scope and arrives on each destination counter
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0 && in.n_dst) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    for (int k = 0; k < in.n_dst; ++k)
+      __hip_atomic_fetch_add(a.counters + in.dst_id[k], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+}  // namespace mkd
+
+// One workgroup per CU; instruction `it * ncu + vcu` in iteration `it`.
+// Workgroups are dealt to the 8 XCDs round-robin, so the virtual CU index
+// groups each XCD's workgroups into one contiguous block of the placement.
+__global__ void __launch_bounds__(256, 1) mk_persistent(mkd::KArgs a) {
+  __shared__ mk_instr s_in;
+  __shared__ mk_node s_nd;
+  __shared__ int s_flag;
+  __shared__ __attribute__((aligned(16))) char smem[mkd::kSmemBytes];
+  const int b = blockIdx.x;
+  const int vcu = (a.ncu % 8 == 0) ? (b % 8) * (a.ncu / 8) + b / 8 : b;
+  for (int it = 0; it < a.n_iters; ++it) {
+    const int gidx = it * a.ncu + vcu;
+    __syncthreads();
+    mkd::copy_words(reinterpret_cast<int*>(&s_in), reinterpret_cast<const int*>(a.instrs + gidx));
+    __syncthreads();
+    if (s_in.opcode == MK_I_NOOP) continue;
+    mkd::copy_words(reinterpret_cast<int*>(&s_nd), reinterpret_cast<const int*>(a.nodes + s_in.node));
+    if (!mkd::wait_sources(a, s_in, vcu, gidx, &s_flag)) return;  // includes a barrier
+    mkd::run_instr(a, s_in, s_nd, smem);
+    mkd::release_dests(a, s_in);
+  }
+}
+
+// Per-op baseline: one launch per node, one workgroup per instruction, no
+// counters (stream order carries the dependencies).
+__global__ void __launch_bounds__(256, 1) mk_node_kernel(mkd::KArgs a) {
+  __shared__ mk_instr s_in;
+  __shared__ mk_node s_nd;
+  __shared__ __attribute__((aligned(16))) char smem[mkd::kSmemBytes];
+  const int gidx = a.first + blockIdx.x;
+  mkd::copy_words(reinterpret_cast<int*>(&s_in), reinterpret_cast<const int*>(a.instrs + gidx));
+  __syncthreads();
+  if (s_in.opcode == MK_I_NOOP) return;
+  mkd::copy_words(reinterpret_cast<int*>(&s_nd), reinterpret_cast<const int*>(a.nodes + s_in.node));
+  __syncthreads();
+  mkd::run_instr(a, s_in, s_nd, smem);
+}

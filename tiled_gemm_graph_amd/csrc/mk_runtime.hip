@@ -1,0 +1,266 @@
+// Runtime: device state of a plan, one-launch forward, per-op baseline.
+//
+// The plan's records, node table and counters are uploaded once on the first
+// run ("Implementing a Mega Kernel for B300", section 6: upload the
+// descriptors once; only addresses change per call).  Counters are never
+// reset between runs: run e waits for epoch * target, so after e runs every
+// counter equals e * target.  (MegaKittens Internals section 07 instead
+// zeroes them with a kernel before every launch.)
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "mk_internal.h"
+#include "mk_kernels.h"
+
+const char* mk_plan_unsupported_reason(const mk_plan* p);
+
+struct mk_plan_device {
+  int device = -1;
+  mk_instr* d_instrs = nullptr;
+  mk_node* d_nodes = nullptr;
+  int* d_counters = nullptr;
+  int* d_err = nullptr;
+  std::vector<void*> owned;   // by slot (plan-owned buffers), else nullptr
+  long long spin_ticks = 0;
+  int max_target = 1;
+};
+
+namespace {
+
+using mk::set_error;
+
+mk_status hip_fail(hipError_t e, const char* what) {
+  set_error(std::string(what) + ": " + hipGetErrorString(e));
+  return MK_E_HIP;
+}
+#define HIPCHK(x)                                        \
+  do {                                                   \
+    hipError_t e_ = (x);                                 \
+    if (e_ != hipSuccess) return hip_fail(e_, #x);       \
+  } while (0)
+
+void free_device(mk_plan_device* d) {
+  if (!d) return;
+  if (d->d_instrs) (void)hipFree(d->d_instrs);
+  if (d->d_nodes) (void)hipFree(d->d_nodes);
+  if (d->d_counters) (void)hipFree(d->d_counters);
+  if (d->d_err) (void)hipFree(d->d_err);
+  for (void* q : d->owned)
+    if (q) (void)hipFree(q);
+  delete d;
+}
+
+mk_status ensure_device(mk_plan* p) {
+  const char* why = mk_plan_unsupported_reason(p);
+  if (why && *why) {
+    set_error(std::string("plan cannot run on the GPU: ") + why);
+    return MK_E_UNSUPPORTED;
+  }
+  if (p->opts.reuse == 2) {
+    set_error("reuse mode 2 (outputs in pooled slots) is a host-only profile");
+    return MK_E_UNSUPPORTED;
+  }
+  int dev = 0;
+  HIPCHK(hipGetDevice(&dev));
+  if (p->dev) {
+    if (p->dev->device != dev) {
+      set_error("plan was uploaded to another device");
+      return MK_E_INVALID;
+    }
+    return MK_OK;
+  }
+  int ncu = 0;
+  HIPCHK(hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev));
+  if (ncu != p->opts.num_cus) {
+    set_error("plan was built for " + std::to_string(p->opts.num_cus) + " CUs, device has " +
+              std::to_string(ncu));
+    return MK_E_UNSUPPORTED;
+  }
+  int coop = 0;
+  HIPCHK(hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev));
+  if (!coop) {
+    set_error("device does not support cooperative launch");
+    return MK_E_UNSUPPORTED;
+  }
+  int blocks = 0;
+  HIPCHK(hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, mk_persistent, mkd::kThreads, 0));
+  if (blocks < 1) {
+    set_error("persistent kernel does not fit one workgroup per CU");
+    return MK_E_UNSUPPORTED;
+  }
+  auto* d = new mk_plan_device();
+  d->device = dev;
+  auto bail = [&](hipError_t e, const char* w) {
+    free_device(d);
+    return hip_fail(e, w);
+  };
+  hipError_t e;
+  const size_t rec_bytes = p->records.size() * sizeof(mk_instr);
+  if ((e = hipMalloc(&d->d_instrs, std::max<size_t>(rec_bytes, 256))) != hipSuccess) return bail(e, "hipMalloc records");
+  if (rec_bytes && (e = hipMemcpy(d->d_instrs, p->records.data(), rec_bytes, hipMemcpyHostToDevice)) != hipSuccess)
+    return bail(e, "hipMemcpy records");
+  const size_t nd_bytes = p->node_descs.size() * sizeof(mk_node);
+  if ((e = hipMalloc(&d->d_nodes, std::max<size_t>(nd_bytes, 256))) != hipSuccess) return bail(e, "hipMalloc nodes");
+  if (nd_bytes && (e = hipMemcpy(d->d_nodes, p->node_descs.data(), nd_bytes, hipMemcpyHostToDevice)) != hipSuccess)
+    return bail(e, "hipMemcpy nodes");
+  const size_t nb = std::max<size_t>(p->targets.size(), 1);
+  if ((e = hipMalloc(&d->d_counters, nb * sizeof(int))) != hipSuccess) return bail(e, "hipMalloc counters");
+  if ((e = hipMemset(d->d_counters, 0, nb * sizeof(int))) != hipSuccess) return bail(e, "hipMemset counters");
+  if ((e = hipMalloc(&d->d_err, 8 * sizeof(int))) != hipSuccess) return bail(e, "hipMalloc error record");
+  if ((e = hipMemset(d->d_err, 0, 8 * sizeof(int))) != hipSuccess) return bail(e, "hipMemset error record");
+  for (int32_t t : p->targets) d->max_target = std::max(d->max_target, (int)t);
+  // plan-owned buffers: intermediates, split-K partials, constant tables
+  d->owned.assign(p->slot_owner.size(), nullptr);
+  for (size_t s = 0; s < p->slot_owner.size(); ++s) {
+    const mk::Tensor& t = p->tensors[p->slot_owner[s]];
+    if (t.role != MK_INTERMEDIATE) continue;
+    size_t bytes = std::max<mk::I64>(p->slot_bytes[s], 16);
+    if ((e = hipMalloc(&d->owned[s], bytes)) != hipSuccess) return bail(e, "hipMalloc intermediate");
+    if (t.const_kind == 1) {
+      // rotary table: row p = [cos(p*th_i) for i < half | sin(p*th_i) for i < half],
+      // th_i = theta^(-2i / head_dim), evaluated in double
+      const int half = t.rope_half, rows = (int)t.shape[2];
+      std::vector<float> tab((size_t)rows * 2 * half);
+      for (int pos = 0; pos < rows; ++pos)
+        for (int i = 0; i < half; ++i) {
+          const double th = std::pow((double)t.rope_theta, -2.0 * i / (2.0 * half));
+          tab[(size_t)pos * 2 * half + i] = (float)std::cos(pos * th);
+          tab[(size_t)pos * 2 * half + half + i] = (float)std::sin(pos * th);
+        }
+      if ((e = hipMemcpy(d->owned[s], tab.data(), tab.size() * sizeof(float), hipMemcpyHostToDevice)) != hipSuccess)
+        return bail(e, "hipMemcpy rope table");
+    }
+  }
+  int rate_khz = 0;
+  if ((e = hipDeviceGetAttribute(&rate_khz, hipDeviceAttributeWallClockRate, dev)) != hipSuccess)
+    return bail(e, "wall clock rate");
+  if (rate_khz <= 0) rate_khz = 100000;
+  d->spin_ticks = (long long)(p->opts.spin_limit_us * (double)rate_khz / 1000.0);
+  p->dev = d;
+  return MK_OK;
+}
+
+mk_status fill_args(mk_plan* p, void* const* buffers, int n_buffers, mkd::KArgs& a) {
+  std::memset(&a, 0, sizeof(a));
+  if (n_buffers < p->n_graph_tensors) {
+    set_error("buffers must have one entry per graph tensor id");
+    return MK_E_INVALID;
+  }
+  for (size_t s = 0; s < p->slot_owner.size(); ++s) {
+    const int tid = p->slot_owner[s];
+    const mk::Tensor& t = p->tensors[tid];
+    if (t.role == MK_INTERMEDIATE) {
+      a.bufs[s] = p->dev->owned[s];
+    } else {
+      if (!buffers || !buffers[tid]) {
+        set_error("missing device buffer for tensor id " + std::to_string(tid));
+        return MK_E_INVALID;
+      }
+      if (reinterpret_cast<uintptr_t>(buffers[tid]) % 16) {
+        set_error("device buffer of tensor id " + std::to_string(tid) + " is not 16-byte aligned");
+        return MK_E_INVALID;
+      }
+      a.bufs[s] = buffers[tid];
+    }
+  }
+  a.instrs = p->dev->d_instrs;
+  a.nodes = p->dev->d_nodes;
+  a.counters = p->dev->d_counters;
+  a.err = p->dev->d_err;
+  a.spin_ticks = p->dev->spin_ticks;
+  a.n_iters = (int)p->stats.n_iters;
+  a.ncu = p->opts.num_cus;
+  return MK_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+mk_status megakernel_run(mk_plan* p, void* const* buffers, int n_buffers, void* stream) {
+  if (!p) { set_error("null plan"); return MK_E_INVALID; }
+  mk_status st = ensure_device(p);
+  if (st != MK_OK) return st;
+  mkd::KArgs a;
+  if ((st = fill_args(p, buffers, n_buffers, a)) != MK_OK) return st;
+  if (p->n_instr == 0) return MK_OK;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  // counters hold epoch * target; restart from zero well before int32 overflow
+  if ((p->epoch + 1) * (int64_t)p->dev->max_target > (1LL << 30)) {
+    HIPCHK(hipMemsetAsync(p->dev->d_counters, 0, std::max<size_t>(p->targets.size(), 1) * sizeof(int), s));
+    p->epoch = 0;
+  }
+  a.epoch = (int)(p->epoch + 1);
+  void* args[] = {&a};
+  HIPCHK(hipLaunchCooperativeKernel(reinterpret_cast<const void*>(mk_persistent), dim3(p->opts.num_cus),
+                                    dim3(mkd::kThreads), args, 0, s));
+  p->epoch += 1;
+  return MK_OK;
+}
+
+mk_status megakernel_run_per_op(mk_plan* p, void* const* buffers, int n_buffers, void* stream) {
+  if (!p) { set_error("null plan"); return MK_E_INVALID; }
+  mk_status st = ensure_device(p);
+  if (st != MK_OK) return st;
+  mkd::KArgs a;
+  if ((st = fill_args(p, buffers, n_buffers, a)) != MK_OK) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  for (const mk::Node& n : p->nodes) {
+    if (n.ins.empty()) continue;
+    a.first = n.start;
+    a.count = (int)n.ins.size();
+    hipLaunchKernelGGL(mk_node_kernel, dim3(a.count), dim3(mkd::kThreads), 0, s, a);
+    HIPCHK(hipGetLastError());
+  }
+  return MK_OK;
+}
+
+mk_status mk_plan_check(mk_plan* p, void* stream, mk_run_error* err) {
+  if (!p) { set_error("null plan"); return MK_E_INVALID; }
+  mk_run_error r{};
+  if (p->dev) {
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    HIPCHK(hipStreamSynchronize(s));
+    int h[8];
+    HIPCHK(hipMemcpy(h, p->dev->d_err, sizeof(h), hipMemcpyDeviceToHost));
+    r.code = h[0]; r.cu = h[1]; r.instr = h[2]; r.barrier = h[3]; r.value = h[4]; r.need = h[5];
+    if (h[0] != 0 || h[6] != 0) {
+      // the aborted run left counters mid-epoch: start over from zero
+      HIPCHK(hipMemset(p->dev->d_err, 0, 8 * sizeof(int)));
+      HIPCHK(hipMemset(p->dev->d_counters, 0, std::max<size_t>(p->targets.size(), 1) * sizeof(int)));
+      p->epoch = 0;
+      if (err) *err = r;
+      set_error("counter wait gave up: cu " + std::to_string(r.cu) + " instr " + std::to_string(r.instr) +
+                " counter " + std::to_string(r.barrier) + " value " + std::to_string(r.value) + " need " +
+                std::to_string(r.need));
+      return MK_E_DEADLOCK;
+    }
+  }
+  if (err) *err = r;
+  return MK_OK;
+}
+
+mk_status mk_plan_read_counters(mk_plan* p, int32_t* host, int64_t n, void* stream) {
+  if (!p || !host) { set_error("null argument"); return MK_E_INVALID; }
+  if (n < (int64_t)p->targets.size()) { set_error("host buffer too small"); return MK_E_INVALID; }
+  if (!p->dev) {
+    std::memset(host, 0, p->targets.size() * sizeof(int32_t));
+    return MK_OK;
+  }
+  HIPCHK(hipStreamSynchronize(reinterpret_cast<hipStream_t>(stream)));
+  if (!p->targets.empty())
+    HIPCHK(hipMemcpy(host, p->dev->d_counters, p->targets.size() * sizeof(int32_t), hipMemcpyDeviceToHost));
+  return MK_OK;
+}
+
+void mk_plan_destroy(mk_plan* p) {
+  if (!p) return;
+  free_device(p->dev);
+  delete p;
+}
+
+}  // extern "C"
