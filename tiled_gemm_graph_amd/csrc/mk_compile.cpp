@@ -137,11 +137,15 @@ struct Compiler {
     } else {
       if (t.bm <= 0 || t.bn <= 0) {
         // Largest kernel tile that still fills one wave of CUs.
+        // Rotary tiles must hold whole heads.
         const int cand[3][2] = {{128, 128}, {64, 128}, {64, 64}};
-        int pick = 2;
+        const bool rope = op.attrs.epilogue & MK_EP_ROPE;
+        const int hd = op.attrs.head_dim > 0 ? op.attrs.head_dim : 1;
+        int pick = rope ? 1 : 2;
         for (int c = 0; c < 3; ++c) {
           int bnk = cand[c][1];
           int bn = silu ? bnk / 2 : bnk;
+          if (rope && bn % hd) continue;
           if (cdiv(M, cand[c][0]) * cdiv(N, bn) >= ncu) {
             pick = c;
             break;
