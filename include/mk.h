@@ -235,6 +235,15 @@ void mk_plan_destroy(mk_plan *p);
  * views and intermediates are ignored.  Asynchronous: call mk_plan_check to
  * learn whether a counter wait gave up. */
 mk_status megakernel_run(mk_plan *p, void *const *buffers, int n_buffers, void *stream);
+/* megakernel_run that also writes four wall-clock stamps per executed
+ * instruction (fetched, counters satisfied, body done, released) to the
+ * caller-owned device array trace[4 * n_iters * num_cus] (uint64, indexed
+ * by instruction index; Noop slots are left untouched).  The stamps come
+ * from the GPU's constant-rate wall clock; a debugging aid after the
+ * intra-kernel timing of "Beating torch.compile with Megakernels in CuTe
+ * DSL", "Intrakernel Profiling". */
+mk_status megakernel_run_traced(mk_plan *p, void *const *buffers, int n_buffers, void *stream,
+                                uint64_t *trace);
 /* Same graph, same tile bodies, one launch per node and no counters. */
 mk_status megakernel_run_per_op(mk_plan *p, void *const *buffers, int n_buffers,
                                 void *stream);
@@ -261,6 +270,10 @@ mk_status mk_plan_op_tile(const mk_plan *p, int32_t op, mk_tile *out);
 mk_status mk_plan_read_counters(mk_plan *p, int32_t *host, int64_t n, void *stream);
 /* Runs so far (the epoch the next run waits against is this + 1). */
 mk_status mk_plan_epoch(const mk_plan *p, int64_t *epoch);
+
+/* Rate of the GPU wall clock that megakernel_run_traced stamps, in kHz, for
+ * the current device. */
+mk_status mk_wall_clock_khz(int32_t *khz);
 
 const char *mk_last_error(void);
 int32_t mk_abi_version(void);

@@ -72,10 +72,11 @@ class RunError(Structure):
 
 EXPORTS = [
     "mk_graph_create", "mk_graph_destroy", "mk_graph_tensor", "mk_graph_view", "mk_graph_op",
-    "megakernel_build", "mk_plan_destroy", "megakernel_run", "megakernel_run_per_op",
+    "megakernel_build", "mk_plan_destroy", "megakernel_run", "megakernel_run_traced",
+    "megakernel_run_per_op",
     "mk_plan_check", "mk_plan_stats_get", "mk_plan_instructions", "mk_plan_nodes",
     "mk_plan_barriers", "mk_plan_slots", "mk_plan_op_tile", "mk_plan_read_counters",
-    "mk_plan_epoch", "mk_last_error", "mk_abi_version",
+    "mk_plan_epoch", "mk_wall_clock_khz", "mk_last_error", "mk_abi_version",
 ]
 
 _lib = None
@@ -99,6 +100,7 @@ def load() -> ctypes.CDLL:
         "megakernel_build": ([vp, POINTER(BuildOptions), POINTER(c_void_p)], c_int),
         "mk_plan_destroy": ([vp], None),
         "megakernel_run": ([vp, POINTER(c_void_p), c_int, vp], c_int),
+        "megakernel_run_traced": ([vp, POINTER(c_void_p), c_int, vp, vp], c_int),
         "megakernel_run_per_op": ([vp, POINTER(c_void_p), c_int, vp], c_int),
         "mk_plan_check": ([vp, vp, POINTER(RunError)], c_int),
         "mk_plan_stats_get": ([vp, POINTER(PlanStats)], c_int),
@@ -109,6 +111,7 @@ def load() -> ctypes.CDLL:
         "mk_plan_op_tile": ([vp, c_int32, POINTER(Tile)], c_int),
         "mk_plan_read_counters": ([vp, i32p, c_int64, vp], c_int),
         "mk_plan_epoch": ([vp, i64p], c_int),
+        "mk_wall_clock_khz": ([i32p], c_int),
         "mk_last_error": ([], c_char_p),
         "mk_abi_version": ([], c_int32),
     }

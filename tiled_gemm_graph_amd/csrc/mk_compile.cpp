@@ -110,28 +110,39 @@ struct Compiler {
     if (!explicit_gemv && M <= p.opts.gemv_max_m) t.gemv = 1;
     if (t.gemv) {
       if (t.bm <= 0) t.bm = (int)std::max<I64>(M, 1);
-      if (t.bn <= 0) t.bn = silu ? 128 : 256;
-      I64 wcols = (I64)t.bn * (silu ? 2 : 1);
-      I64 tiles = cdiv(std::max<I64>(M, 1), t.bm) * cdiv(N, t.bn);
-      if (t.split <= 0) {
-        // Aim for ~64 KB of weights per instruction, then pick the split
-        // with the smallest per-CU makespan (wave quantisation included).
-        const double target = 65536.0;
-        double per_tile = (double)K * wcols * dtype_bytes((mk_dtype)dt);
-        I64 s0 = std::max<I64>(1, (I64)std::llround(per_tile / target));
-        I64 best = 1;
-        double best_cost = 1e300;
-        for (I64 s = std::max<I64>(1, s0 / 2); s <= std::max<I64>(1, 2 * s0); ++s) {
-          if (!chunks_ok(K, s) || cdiv(K, s) < 8) continue;
-          I64 kc = cdiv(cdiv(K, s), 64) * 64;
-          double cost = (double)cdiv(tiles * s, ncu) * (double)kc * wcols;
-          if (cost < best_cost * (1 - 1e-9)) {
-            best_cost = cost;
-            best = s;
+      const I64 rows = std::min<I64>(std::max<I64>(M, 1), t.bm);
+      // Streaming GEMV: pick the weight-tile width and the K split that
+      // minimise a makespan estimate: waves of CUs times (per-instruction
+      // overhead + bytes / per-CU bandwidth), with 32-512 KB of weights per
+      // instruction and the activation chunk small enough for LDS.
+      const double bw_cu = 22e3;   // bytes per microsecond per CU
+      const double ovh = 2.5;      // microseconds per instruction
+      const int eb = dtype_bytes((mk_dtype)dt);
+      double best = 1e300;
+      int best_bn = t.bn > 0 ? t.bn : (silu ? 128 : 256), best_s = t.split > 0 ? t.split : 1;
+      const int bns[] = {512, 448, 384, 320, 256, 224, 192, 128, 64};  // wide rows first on ties
+      for (int bn : bns) {
+        if (t.bn > 0 && bn != t.bn) continue;
+        const I64 wc = (I64)bn * (silu ? 2 : 1);
+        if (wc > 512 || bn > std::max<I64>(N, 8)) continue;
+        const I64 tiles = cdiv(std::max<I64>(M, 1), t.bm) * cdiv(N, bn);
+        for (I64 s = 1; s <= 128; ++s) {
+          if (t.split > 0 && s != t.split) continue;
+          if (!chunks_ok(K, s)) continue;
+          const I64 kc = std::min<I64>(K, cdiv(cdiv(K, s), 64) * 64);
+          if (kc * rows > 8192) continue;
+          const double bytes = (double)kc * wc * eb;
+          if (bytes > 512 * 1024.0 || (bytes < 32 * 1024.0 && s > 1)) continue;
+          const double cost = (double)cdiv(tiles * s, ncu) * (ovh + bytes / bw_cu);
+          if (cost < best * (1 - 1e-9)) {
+            best = cost;
+            best_bn = bn;
+            best_s = (int)s;
           }
         }
-        t.split = (int)best;
       }
+      if (t.bn <= 0) t.bn = best_bn;
+      if (t.split <= 0) t.split = best_s;
       if (t.rbm <= 0) t.rbm = t.bm;
       if (t.rbn <= 0) t.rbn = 256;
     } else {
@@ -220,8 +231,13 @@ struct Compiler {
     if (gemv) {
       int wc = t.bn * (silu ? 2 : 1);
       if (t.bm > 8) unsup("GEMV body handles at most 8 rows per tile");
-      if (wc > 256 || wc % 8) unsup("GEMV weight tile must be <= 256 columns, multiple of 8");
+      if (wc > 512 || wc % 8) unsup("GEMV weight tile must be <= 512 columns, multiple of 8");
       if (K % 8) unsup("GEMV K must be a multiple of 8");
+      {
+        const I64 kc = std::min<I64>(K, cdiv(cdiv(K, S), 64) * 64);
+        if (kc * std::min<I64>(std::max<I64>(M, 1), t.bm) > 8192)
+          unsup("GEMV activation chunk (rows x K chunk) exceeds 8192 elements");
+      }
     } else {
       int bnk = t.bn * (silu ? 2 : 1);
       if (!((t.bm == 64 || t.bm == 128) && (bnk == 64 || bnk == 128)))
@@ -819,6 +835,7 @@ struct Compiler {
     p.n_graph_tensors = (int)g.t.size();
     p.ops = g.ops;
     lower();
+    if (p.nodes.size() > 48) unsup("more than 48 lowered nodes (the LDS node cache)");
     place();
     assign_slots();
     derive_barriers();

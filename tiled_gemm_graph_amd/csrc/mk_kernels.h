@@ -34,7 +34,9 @@ namespace mkd {
 constexpr int kThreads = 256;
 constexpr int kBK = 64;                 // GEMM K step
 constexpr int kLdsPad = 8;              // 16-bit elements of row padding
-constexpr int kSmemBytes = 144 * 1024;  // dynamic scratch per workgroup
+constexpr int kSmemBytes = 140 * 1024;  // scratch per workgroup
+constexpr int kMaxNodes = 48;           // node descriptors cached in LDS
+constexpr int kGemvBatch = 8;           // 16-byte weight chunks per thread per batch
 
 struct KArgs {
   const mk_instr* instrs;   // [n_iters][ncu]
@@ -44,6 +46,8 @@ struct KArgs {
   long long spin_ticks;     // wall-clock ticks a wait may take
   int n_iters, ncu, epoch;
   int first, count;         // per-op mode: records [first, first + count)
+  int n_nodes;
+  unsigned long long* trace; // optional: 4 wall-clock stamps per instruction
   void* bufs[MK_MAX_TENSORS];
 };
 
@@ -124,6 +128,12 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
   return red[0] + red[1] + red[2] + red[3];
 }
 
+// Barrier that orders LDS traffic only (global loads stay in flight).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0); vmcnt and expcnt untouched
+  __builtin_amdgcn_s_barrier();
+}
+
 template <typename T>
 __device__ __forceinline__ T* buf(const KArgs& a, const mk_operand& o) {
   return reinterpret_cast<T*>(a.bufs[o.slot]) + o.off;
@@ -186,7 +196,7 @@ __device__ __forceinline__ void epilogue8(const KArgs& a, const mk_node& nd, int
 // C[BM x BNK] = A[r0:r0+BM, k0:k1] @ B[k0:k1, cols], cols = c0.. (plain) or
 // gate c0.. and up N+c0.. (SILU_MUL, BNK/2 each).
 template <int BM, int BNK, int DT>
-__device__ void gemm_tile(const KArgs& a, const mk_instr& in, const mk_node& nd, char* smem) {
+__device__ __forceinline__ void gemm_tile(const KArgs& a, const mk_instr& in, const mk_node& nd, char* smem) {
   constexpr int LDS_ROW = kBK + kLdsPad;           // 72 elements = 144 B
   constexpr int A_STAGE = BM * LDS_ROW;            // elements
   constexpr int B_STAGE = BNK * LDS_ROW;
@@ -336,121 +346,152 @@ __device__ void gemm_tile(const KArgs& a, const mk_instr& in, const mk_node& nd,
 }
 
 // ------------------------------------------------------------------ GEMV
-// Rows [r0, r1) (at most 8), weight-tile columns wc = (c1 - c0) or twice that
-// under SILU_MUL, K rows [k0, k1).
+// Small-M GEMM (M <= 8 rows) that streams its weight tile from HBM.
+// Thread layout: ncg 16-byte column groups of the weight tile and kpar K
+// rows in flight; thread t owns group t % ncg and rows kr + j * kpar of the
+// K chunk.  The weights are loaded in batches of kGemvBatch chunks per thread
+// through two register buffers, so every thread always has two batches in
+// flight.  The first two batches are issued before the counter wait (weights
+// are graph inputs and need no producer); the activation chunk is loaded
+// after it.  All loads are unconditional (rows past the chunk re-read a valid
+// row and idle threads re-read a valid column) so the count of outstanding
+// loads is the same on every path and each wait leaves the younger batch in
+// flight.
+struct GemvShape {
+  int bw, wc, ncg, kpar, cg, kr, gcol, kn, nb;
+  bool active;
+};
+__device__ __forceinline__ GemvShape gemv_shape(const mk_instr& in, const mk_node& nd) {
+  GemvShape g;
+  const bool silu = in.flags & MK_EP_SILU_MUL;
+  g.bw = in.c1 - in.c0;
+  g.wc = silu ? 2 * g.bw : g.bw;
+  g.ncg = g.wc / 8;
+  g.kpar = kThreads / g.ncg;
+  g.cg = threadIdx.x % g.ncg;
+  g.kr = threadIdx.x / g.ncg;
+  g.active = g.kr < g.kpar;
+  const int w = g.cg * 8;
+  g.gcol = (silu && w >= g.bw) ? nd.N + in.c0 + (w - g.bw) : in.c0 + w;
+  g.kn = in.k1 - in.k0;
+  const int rows_per_thread = (g.kn + g.kpar - 1) / g.kpar;
+  g.nb = (rows_per_thread + kGemvBatch - 1) / kGemvBatch;  // batches per thread
+  return g;
+}
+
+// Batch b of this thread: rows kr + (b * kGemvBatch + j) * kpar.
+__device__ __forceinline__ void gemv_load_batch(const u16* W, long ldb, const GemvShape& g, int k0, int b,
+                                                u32x4* dst) {
+  const int kr = min(g.kr, g.kpar - 1);
+#pragma unroll
+  for (int j = 0; j < kGemvBatch; ++j) {
+    const int k = min(kr + (b * kGemvBatch + j) * g.kpar, g.kn - 1);
+    dst[j] = *reinterpret_cast<const u32x4*>(W + (long)(k0 + k) * ldb);
+  }
+}
+
+__device__ __forceinline__ void gemv_prologue(const KArgs& a, const mk_instr& in, const mk_node& nd,
+                                              u32x4* b0, u32x4* b1) {
+  const GemvShape g = gemv_shape(in, nd);
+  const u16* W = buf<const u16>(a, nd.b) + g.gcol;
+  gemv_load_batch(W, nd.b.ld, g, in.k0, 0, b0);
+  gemv_load_batch(W, nd.b.ld, g, in.k0, 1, b1);
+}
+
 template <int DT, int MAXR>
-__device__ void gemv_tile(const KArgs& a, const mk_instr& in, const mk_node& nd, char* smem) {
-  constexpr int KB = 1024;  // K rows staged per pass
+__device__ __forceinline__ void gemv_fma_batch(const GemvShape& g, const u32x4* wb, int b, const float* xs,
+                                               int xstride, int rows, float (&acc)[MAXR][8]) {
+  if (!g.active) return;
+#pragma unroll
+  for (int j = 0; j < kGemvBatch; ++j) {
+    const int k = g.kr + (b * kGemvBatch + j) * g.kpar;
+    if (k < g.kn) {
+      float f[8];
+      unpack8<DT>(wb[j], f);
+#pragma unroll
+      for (int m = 0; m < MAXR; ++m) {
+        if (m < rows) {
+          const float x = xs[m * xstride + k];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[m][e] = fmaf(x, f[e], acc[m][e]);
+        }
+      }
+    }
+  }
+}
+
+// The body after the wait; b0 / b1 hold batches 0 and 1 (in flight).
+template <int DT, int MAXR>
+__device__ __forceinline__ void gemv_stream(const KArgs& a, const mk_instr& in, const mk_node& nd, char* smem,
+                                            u32x4* b0, u32x4* b1) {
   const int t = threadIdx.x;
   const int flags = in.flags;
   const bool silu = flags & MK_EP_SILU_MUL, rms = flags & MK_EP_RMSNORM_INPUT;
-  const int N = nd.N;
-  const int r0 = in.r0, rows = in.r1 - in.r0, c0 = in.c0, c1 = in.c1, k0 = in.k0, k1 = in.k1;
-  const int bw = c1 - c0;                       // output columns of this tile
-  const int wc = silu ? 2 * bw : bw;            // weight columns read
-  const int ncg = wc / 8;                       // 16-byte column groups
-  const int kpar = kThreads / ncg;              // K rows in flight at once
-  const int cg = t % ncg, kr = t / ncg;
-  const bool active = kr < kpar;
-  int gcol;
-  {
-    const int w = cg * 8;
-    gcol = (silu && w >= bw) ? N + c0 + (w - bw) : c0 + w;
+  const int N = nd.N, r0 = in.r0, rows = in.r1 - in.r0, c0 = in.c0, k0 = in.k0;
+  const GemvShape g = gemv_shape(in, nd);
+  const int bw = g.bw, wc = g.wc, kn = g.kn;
+  const u16* W = buf<const u16>(a, nd.b) + g.gcol;
+  const long ldb = nd.b.ld;
+  // LDS: activation chunk [MAXR][xstride] fp32, partial sums, reductions
+  const int xstride = (kn + 3) & ~3;
+  float* xs = reinterpret_cast<float*>(smem);
+  float* red = xs + MAXR * xstride;        // [kpar][MAXR][wc]
+  float* sum = red + 2048 * MAXR;          // [MAXR][wc], wc <= 512
+  float* misc = sum + 512 * MAXR;
+  // activation chunk, gamma-scaled under RMSNORM_INPUT; per-row sums of squares
+  float ssq[MAXR];
+#pragma unroll
+  for (int m = 0; m < MAXR; ++m) ssq[m] = 0.f;
+  const u16* A = buf<const u16>(a, nd.a) + (long)r0 * nd.a.ld + k0;
+  const u16* G = rms ? buf<const u16>(a, nd.gamma) + k0 : nullptr;
+  const int kc8 = kn / 8;
+  for (int i = t; i < rows * kc8; i += kThreads) {
+    const int m = i / kc8, kc = (i % kc8) * 8;
+    float f[8];
+    unpack8<DT>(*reinterpret_cast<const u32x4*>(A + (long)m * nd.a.ld + kc), f);
+    if (rms) {
+      float gm[8];
+      unpack8<DT>(*reinterpret_cast<const u32x4*>(G + kc), gm);
+      float sq = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        sq += f[e] * f[e];
+        f[e] *= gm[e];
+      }
+#pragma unroll
+      for (int mm = 0; mm < MAXR; ++mm)
+        if (mm == m) ssq[mm] += sq;
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) xs[m * xstride + kc + e] = f[e];
   }
-  const u16* A = buf<const u16>(a, nd.a) + (long)r0 * nd.a.ld;
-  const u16* G = rms ? buf<const u16>(a, nd.gamma) : nullptr;
-  const u16* W = buf<const u16>(a, nd.b) + gcol;
-  const long ldb = nd.b.ld, lda = nd.a.ld;
-
-  float* xs = reinterpret_cast<float*>(smem);          // [MAXR][KB] activation chunk
-  float* red = xs + 8 * KB;                            // [kpar][MAXR][wc] partial sums
-  float* misc = red + 8 * 8 * 256;                     // reductions
+  lds_barrier();
   float acc[MAXR][8];
 #pragma unroll
   for (int m = 0; m < MAXR; ++m)
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[m][e] = 0.f;
-  float ssq[MAXR];
-#pragma unroll
-  for (int m = 0; m < MAXR; ++m) ssq[m] = 0.f;
-
-  for (int kb = k0; kb < k1; kb += KB) {
-    const int kn = min(KB, k1 - kb);
-    const int kc8 = kn / 8;
-    __syncthreads();
-    for (int i = t; i < rows * kc8; i += kThreads) {
-      const int m = i / kc8, kc = (i % kc8) * 8;
-      float f[8];
-      unpack8<DT>(*reinterpret_cast<const u32x4*>(A + (long)m * lda + kb + kc), f);
-      if (rms) {
-        float gm[8];
-        unpack8<DT>(*reinterpret_cast<const u32x4*>(G + kb + kc), gm);
-        float s = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          s += f[e] * f[e];
-          f[e] *= gm[e];
-        }
-#pragma unroll
-        for (int mm = 0; mm < MAXR; ++mm)
-          if (mm == m) ssq[mm] += s;
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) xs[m * KB + kc + e] = f[e];
-    }
-    __syncthreads();
-    if (active) {
-      int k = kr;
-      for (; k + 7 * kpar < kn; k += 8 * kpar) {
-        u32x4 wv[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) wv[u] = *reinterpret_cast<const u32x4*>(W + (long)(kb + k + u * kpar) * ldb);
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          float f[8];
-          unpack8<DT>(wv[u], f);
-#pragma unroll
-          for (int m = 0; m < MAXR; ++m) {
-            if (m < rows) {
-              const float x = xs[m * KB + k + u * kpar];
-#pragma unroll
-              for (int e = 0; e < 8; ++e) acc[m][e] = fmaf(x, f[e], acc[m][e]);
-            }
-          }
-        }
-      }
-      for (; k < kn; k += kpar) {
-        float f[8];
-        unpack8<DT>(*reinterpret_cast<const u32x4*>(W + (long)(kb + k) * ldb), f);
-#pragma unroll
-        for (int m = 0; m < MAXR; ++m) {
-          if (m < rows) {
-            const float x = xs[m * KB + k];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) acc[m][e] = fmaf(x, f[e], acc[m][e]);
-          }
-        }
-      }
-    }
+  // stream: two batches in flight; batch b lives in b0 (even) or b1 (odd)
+  for (int b = 0; b < g.nb; b += 2) {
+    gemv_fma_batch<DT, MAXR>(g, b0, b, xs, xstride, rows, acc);
+    gemv_load_batch(W, ldb, g, k0, min(b + 2, g.nb - 1), b0);
+    if (b + 1 < g.nb) gemv_fma_batch<DT, MAXR>(g, b1, b + 1, xs, xstride, rows, acc);
+    gemv_load_batch(W, ldb, g, k0, min(b + 3, g.nb - 1), b1);
   }
-  __syncthreads();
-  if (active) {
+  if (g.active) {
 #pragma unroll
     for (int m = 0; m < MAXR; ++m)
       if (m < rows)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) red[(kr * MAXR + m) * wc + cg * 8 + e] = acc[m][e];
+        for (int e = 0; e < 8; ++e) red[(g.kr * MAXR + m) * wc + g.cg * 8 + e] = acc[m][e];
   }
-  __syncthreads();
-  // sum the kpar partial rows: sum[m][w] for m < rows, w < wc
-  float* sum = xs;  // reuse: [MAXR][wc]
+  lds_barrier();
   for (int i = t; i < rows * wc; i += kThreads) {
     const int m = i / wc, w = i % wc;
-    float s = 0.f;
-    for (int q = 0; q < kpar; ++q) s += red[(q * MAXR + m) * wc + w];
-    sum[m * wc + w] = s;
+    float sacc = 0.f;
+    for (int q = 0; q < g.kpar; ++q) sacc += red[(q * MAXR + m) * wc + w];
+    sum[m * wc + w] = sacc;
   }
-  // 1/rms per row when the instruction covers the whole K (no split)
   float* rinv = misc;
   if (rms && !(flags & MK_EP_PARTIAL)) {
 #pragma unroll
@@ -461,7 +502,7 @@ __device__ void gemv_tile(const KArgs& a, const mk_instr& in, const mk_node& nd,
       }
     }
   }
-  __syncthreads();
+  lds_barrier();
   if (flags & MK_EP_PARTIAL) {
     float* P = buf<float>(a, nd.part) + (long)in.split_idx * nd.part_plane;
     for (int i = t; i < rows * wc; i += kThreads) {
@@ -482,16 +523,28 @@ __device__ void gemv_tile(const KArgs& a, const mk_instr& in, const mk_node& nd,
   }
 }
 
+template <int DT>
+__device__ __forceinline__ void gemv_stream_rows(const KArgs& a, const mk_instr& in, const mk_node& nd,
+                                                 char* smem, u32x4* b0, u32x4* b1) {
+  if (in.r1 - in.r0 == 1) gemv_stream<DT, 1>(a, in, nd, smem, b0, b1);
+  else gemv_stream<DT, 8>(a, in, nd, smem, b0, b1);
+}
+
 // ---------------------------------------------------------------- REDUCE
 template <int DT>
-__device__ void reduce_tile(const KArgs& a, const mk_instr& in, const mk_node& nd, char* smem) {
+__device__ __forceinline__ void reduce_tile(const KArgs& a, const mk_instr& in, const mk_node& nd, char* smem) {
   const int t = threadIdx.x;
   const int flags = in.flags;
   const bool silu = flags & MK_EP_SILU_MUL, rms = flags & MK_EP_RMSNORM_INPUT;
   const int N = nd.N, S = nd.split, K = nd.K;
   const int r0 = in.r0, rows = in.r1 - in.r0, c0 = in.c0, bw = in.c1 - in.c0;
-  float* rinv = reinterpret_cast<float*>(smem);
+  const int wc = silu ? 2 * bw : bw;     // partial columns per row (gate | up)
+  const int ncg = wc / 8;
+  const int units = rows * ncg;          // 8-column partial units of the tile
+  float* rinv = reinterpret_cast<float*>(smem);   // [rows]
   float* scratch = rinv + 256;
+  float* psum = scratch + 64;                       // [threads][8]
+  float* sum = psum + kThreads * 8;                 // [rows][wc]
   if (rms) {
     const u16* X = buf<const u16>(a, nd.a);
     for (int m = 0; m < rows; ++m) {
@@ -505,35 +558,70 @@ __device__ void reduce_tile(const KArgs& a, const mk_instr& in, const mk_node& n
       s = block_sum(s, scratch);
       if (t == 0) rinv[m] = 1.0f / sqrtf(s / (float)K + nd.eps);
     }
-    __syncthreads();
   }
   const float* P = buf<const float>(a, nd.part);
   const long plane = nd.part_plane, ldp = nd.part.ld;
-  const int units = rows * (bw / 8);
-  for (int u = t; u < units; u += kThreads) {
-    const int m = u / (bw / 8), w = (u % (bw / 8)) * 8;
-    const int gr = r0 + m;
-    const float sc = rms ? rinv[m] : 1.0f;
-    epilogue8<DT>(a, nd, flags, gr, c0 + w, w, bw, [&](int ww, float* o) {
-      // weight-tile column ww: output column c0+ww (plain / gate) or the up
-      // column N + c0 + (ww - bw) under SILU_MUL
-      const int gc = (silu && ww >= bw) ? N + c0 + (ww - bw) : c0 + ww;
-      float s[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-      for (int p = 0; p < S; ++p) {
-        const float4* src = reinterpret_cast<const float4*>(P + p * plane + (long)gr * ldp + gc);
-        const float4 x0 = src[0], x1 = src[1];
-        s[0] += x0.x; s[1] += x0.y; s[2] += x0.z; s[3] += x0.w;
-        s[4] += x1.x; s[5] += x1.y; s[6] += x1.z; s[7] += x1.w;
-      }
+  // Each unit's S partial planes are split over tpu threads, each summing
+  // planes sub, sub + tpu, ... in order; the tpu sums are then added in
+  // thread order, so the result is the same on every run.
+  int tpu = 1;
+  while (tpu * 2 * units <= kThreads && tpu * 2 <= S) tpu *= 2;
+  for (int u0 = 0; u0 < units; u0 += kThreads / tpu) {
+    const int u = u0 + t / tpu, sub = t % tpu;
+    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (u < units) {
+      const int m = u / ncg, w = (u % ncg) * 8;
+      const int gc = (silu && w >= bw) ? N + c0 + (w - bw) : c0 + w;
+      const float* src = P + (long)(r0 + m) * ldp + gc;
+      int p = sub;
+      for (; p + 3 * tpu < S; p += 4 * tpu) {
+        float4 x[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) o[e] = s[e] * sc;
+        for (int q = 0; q < 4; ++q) {
+          x[2 * q] = *reinterpret_cast<const float4*>(src + (p + q * tpu) * plane);
+          x[2 * q + 1] = *reinterpret_cast<const float4*>(src + (p + q * tpu) * plane + 4);
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          acc[0] += x[2 * q].x; acc[1] += x[2 * q].y; acc[2] += x[2 * q].z; acc[3] += x[2 * q].w;
+          acc[4] += x[2 * q + 1].x; acc[5] += x[2 * q + 1].y; acc[6] += x[2 * q + 1].z; acc[7] += x[2 * q + 1].w;
+        }
+      }
+      for (; p < S; p += tpu) {
+        const float4 x0 = *reinterpret_cast<const float4*>(src + p * plane);
+        const float4 x1 = *reinterpret_cast<const float4*>(src + p * plane + 4);
+        acc[0] += x0.x; acc[1] += x0.y; acc[2] += x0.z; acc[3] += x0.w;
+        acc[4] += x1.x; acc[5] += x1.y; acc[6] += x1.z; acc[7] += x1.w;
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) psum[t * 8 + e] = acc[e];
+    __syncthreads();
+    if (sub == 0 && u < units) {
+      float tot[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+      for (int q = 0; q < tpu; ++q)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) tot[e] += psum[(t + q) * 8 + e];
+      const int m = u / ncg, w = (u % ncg) * 8;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sum[m * wc + w + e] = tot[e];
+    }
+    __syncthreads();
+  }
+  const int ounits = rows * (bw / 8);
+  for (int u = t; u < ounits; u += kThreads) {
+    const int m = u / (bw / 8), w = (u % (bw / 8)) * 8;
+    const float sc = rms ? rinv[m] : 1.0f;
+    epilogue8<DT>(a, nd, flags, r0 + m, c0 + w, w, bw, [&](int ww, float* o) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = sum[m * wc + ww + e] * sc;
     });
   }
 }
 
 // --------------------------------------------------------------- RMSNORM
 template <int DT>
-__device__ void rmsnorm_tile(const KArgs& a, const mk_instr& in, const mk_node& nd, char* smem) {
+__device__ __forceinline__ void rmsnorm_tile(const KArgs& a, const mk_instr& in, const mk_node& nd, char* smem) {
   const int t = threadIdx.x;
   const int H = nd.N;
   float* scratch = reinterpret_cast<float*>(smem);
@@ -567,7 +655,7 @@ __device__ void rmsnorm_tile(const KArgs& a, const mk_instr& in, const mk_node& 
 // S^T = K Q^T is computed so that each lane holds one query's scores, which
 // then feed the P V product as the B operand straight from registers.
 template <int DT>
-__device__ void attention_tile(const KArgs& a, const mk_instr& in, const mk_node& nd, char* smem) {
+__device__ __forceinline__ void attention_tile(const KArgs& a, const mk_instr& in, const mk_node& nd, char* smem) {
   constexpr int D = 128, KBLK = 64;
   constexpr int KS = D + kLdsPad;      // K tile row: 136 elements
   constexpr int VS = KBLK + kLdsPad;   // V^T tile row: 72 elements
@@ -704,7 +792,7 @@ __device__ void attention_tile(const KArgs& a, const mk_instr& in, const mk_node
 
 // ----------------------------------------------------------- elementwise
 template <int DT>
-__device__ void elementwise_tile(const KArgs& a, const mk_instr& in, const mk_node& nd) {
+__device__ __forceinline__ void elementwise_tile(const KArgs& a, const mk_instr& in, const mk_node& nd) {
   const int t = threadIdx.x;
   const bool add = in.opcode == MK_I_EW_ADD;
   const int wcols = in.c1 - in.c0, units = (in.r1 - in.r0) * (wcols / 8);
@@ -730,7 +818,7 @@ __device__ void elementwise_tile(const KArgs& a, const mk_instr& in, const mk_no
 
 // -------------------------------------------------------------- dispatch
 template <int DT>
-__device__ void run_body(const KArgs& a, const mk_instr& in, const mk_node& nd, char* smem) {
+__device__ __forceinline__ void run_body(const KArgs& a, const mk_instr& in, const mk_node& nd, char* smem) {
   switch (in.opcode) {
     case MK_I_GEMM:
       if (nd.tile_m == 128 && nd.tile_n == 128) gemm_tile<128, 128, DT>(a, in, nd, smem);
@@ -738,10 +826,12 @@ __device__ void run_body(const KArgs& a, const mk_instr& in, const mk_node& nd, 
       else if (nd.tile_m == 128 && nd.tile_n == 64) gemm_tile<128, 64, DT>(a, in, nd, smem);
       else gemm_tile<64, 64, DT>(a, in, nd, smem);
       break;
-    case MK_I_GEMV:
-      if (in.r1 - in.r0 == 1) gemv_tile<DT, 1>(a, in, nd, smem);
-      else gemv_tile<DT, 8>(a, in, nd, smem);
+    case MK_I_GEMV: {
+      u32x4 b0[kGemvBatch], b1[kGemvBatch];
+      gemv_prologue(a, in, nd, b0, b1);
+      gemv_stream_rows<DT>(a, in, nd, smem, b0, b1);
       break;
+    }
     case MK_I_REDUCE: reduce_tile<DT>(a, in, nd, smem); break;
     case MK_I_RMSNORM: rmsnorm_tile<DT>(a, in, nd, smem); break;
     case MK_I_ATTENTION: attention_tile<DT>(a, in, nd, smem); break;
@@ -763,7 +853,7 @@ __device__ __forceinline__ void copy_words(int* dst, const int* src) {
 
 // Thread 0 waits on every source counter; returns false (uniformly) if the
 // run was aborted.  `flag` is an LDS int.
-__device__ bool wait_sources(const KArgs& a, const mk_instr& in, int vcu, int gidx, int* flag) {
+__device__ __forceinline__ bool wait_sources(const KArgs& a, const mk_instr& in, int vcu, int gidx, int* flag) {
   if (threadIdx.x == 0) {
     int ok = 1;
     const long long t0 = wall_clock64();
@@ -808,29 +898,99 @@ __device__ __forceinline__ void release_dests(const KArgs& a, const mk_instr& in
 // One workgroup per CU; instruction `it * ncu + vcu` in iteration `it`.
 // Workgroups are dealt to the 8 XCDs round-robin, so the virtual CU index
 // groups each XCD's workgroups into one contiguous block of the placement.
-__global__ void __launch_bounds__(256, 1) mk_persistent(mkd::KArgs a) {
-  __shared__ mk_instr s_in;
-  __shared__ mk_node s_nd;
+// Records sit in three LDS slots and are loaded two iterations ahead, so
+// iteration it always sees its own record and the next one (the two-slot
+// instruction pipeline of MegaKittens Internals, section 09, one deeper);
+// node descriptors are cached in LDS.
+namespace mkd {
+
+struct Loop {
+  const KArgs& a;
+  mk_instr* slots;      // [3]
+  const mk_node* nodes;
+  int* flag;
+  char* smem;
+  int vcu;
+};
+
+__device__ __forceinline__ void stamp(const KArgs& a, int gidx, int k, unsigned long long v) {
+  a.trace[4 * (long)gidx + k] = v;
+}
+
+// Issue the load of record it + 2 (wave 0); returns its word for this lane.
+__device__ __forceinline__ int fetch_ahead(const Loop& L, int it) {
+  int w = 0;
+  if (threadIdx.x < 64 && it + 2 < L.a.n_iters)
+    w = reinterpret_cast<const int*>(L.a.instrs + (long)(it + 2) * L.a.ncu + L.vcu)[threadIdx.x];
+  return w;
+}
+__device__ __forceinline__ void store_ahead(const Loop& L, int it, int w) {
+  if (threadIdx.x < 64 && it + 2 < L.a.n_iters) reinterpret_cast<int*>(&L.slots[(it + 2) % 3])[threadIdx.x] = w;
+}
+
+// One generic iteration.  Returns false if the run was aborted.
+__device__ __forceinline__ bool generic_iter(const Loop& L, int it) {
+  const KArgs& a = L.a;
+  const int gidx = it * a.ncu + L.vcu;
+  const mk_instr& in = L.slots[it % 3];
+  const int w = fetch_ahead(L, it);
+  if (in.opcode != MK_I_NOOP) {
+    const mk_node& nd = L.nodes[in.node];
+    const bool tr = a.trace && threadIdx.x == 0;
+    if (tr) stamp(a, gidx, 0, wall_clock64());
+    if (in.opcode == MK_I_GEMV) {
+      // weights first: the first two batches load during the counter wait
+      u32x4 b0[kGemvBatch], b1[kGemvBatch];
+      gemv_prologue(a, in, nd, b0, b1);
+      if (!wait_sources(a, in, L.vcu, gidx, L.flag)) return false;
+      if (tr) stamp(a, gidx, 1, wall_clock64());
+      if (nd.dtype == MK_BF16) gemv_stream_rows<MK_BF16>(a, in, nd, L.smem, b0, b1);
+      else gemv_stream_rows<MK_F16>(a, in, nd, L.smem, b0, b1);
+    } else {
+      if (!wait_sources(a, in, L.vcu, gidx, L.flag)) return false;
+      if (tr) stamp(a, gidx, 1, wall_clock64());
+      run_instr(a, in, nd, L.smem);
+    }
+    if (tr) stamp(a, gidx, 2, wall_clock64());
+    release_dests(a, in);
+    if (tr) stamp(a, gidx, 3, wall_clock64());
+  } else {
+    __syncthreads();
+  }
+  store_ahead(L, it, w);
+  return true;
+}
+
+}  // namespace mkd
+
+__global__ void __launch_bounds__(256, 1) mk_persistent(mkd::KArgs args) {
+  // Read the arguments in place (kernarg segment, constant memory): the
+  // buffer table is indexed with runtime slots, which would otherwise force
+  // a private copy of the whole struct.
+  const mkd::KArgs& a = *(const mkd::KArgs*)__builtin_amdgcn_kernarg_segment_ptr();
+  (void)args;
+  __shared__ mk_instr s_in[3];
+  __shared__ mk_node s_nodes[mkd::kMaxNodes];
   __shared__ int s_flag;
   __shared__ __attribute__((aligned(16))) char smem[mkd::kSmemBytes];
+  const int t = threadIdx.x;
   const int b = blockIdx.x;
   const int vcu = (a.ncu % 8 == 0) ? (b % 8) * (a.ncu / 8) + b / 8 : b;
-  for (int it = 0; it < a.n_iters; ++it) {
-    const int gidx = it * a.ncu + vcu;
-    __syncthreads();
-    mkd::copy_words(reinterpret_cast<int*>(&s_in), reinterpret_cast<const int*>(a.instrs + gidx));
-    __syncthreads();
-    if (s_in.opcode == MK_I_NOOP) continue;
-    mkd::copy_words(reinterpret_cast<int*>(&s_nd), reinterpret_cast<const int*>(a.nodes + s_in.node));
-    if (!mkd::wait_sources(a, s_in, vcu, gidx, &s_flag)) return;  // includes a barrier
-    mkd::run_instr(a, s_in, s_nd, smem);
-    mkd::release_dests(a, s_in);
-  }
+  for (int i = t; i < a.n_nodes * 64; i += mkd::kThreads)
+    reinterpret_cast<int*>(s_nodes)[i] = reinterpret_cast<const int*>(a.nodes)[i];
+  for (int r = 0; r < 2 && r < a.n_iters; ++r)
+    mkd::copy_words(reinterpret_cast<int*>(&s_in[r]), reinterpret_cast<const int*>(a.instrs + (long)r * a.ncu + vcu));
+  __syncthreads();
+  const mkd::Loop L{a, s_in, s_nodes, &s_flag, smem, vcu};
+  for (int it = 0; it < a.n_iters; ++it)
+    if (!mkd::generic_iter(L, it)) return;
 }
 
 // Per-op baseline: one launch per node, one workgroup per instruction, no
 // counters (stream order carries the dependencies).
-__global__ void __launch_bounds__(256, 1) mk_node_kernel(mkd::KArgs a) {
+__global__ void __launch_bounds__(256, 1) mk_node_kernel(mkd::KArgs args) {
+  const mkd::KArgs& a = *(const mkd::KArgs*)__builtin_amdgcn_kernarg_segment_ptr();
+  (void)args;
   __shared__ mk_instr s_in;
   __shared__ mk_node s_nd;
   __shared__ __attribute__((aligned(16))) char smem[mkd::kSmemBytes];

@@ -174,6 +174,7 @@ mk_status fill_args(mk_plan* p, void* const* buffers, int n_buffers, mkd::KArgs&
   a.spin_ticks = p->dev->spin_ticks;
   a.n_iters = (int)p->stats.n_iters;
   a.ncu = p->opts.num_cus;
+  a.n_nodes = (int)p->node_descs.size();
   return MK_OK;
 }
 
@@ -181,12 +182,14 @@ mk_status fill_args(mk_plan* p, void* const* buffers, int n_buffers, mkd::KArgs&
 
 extern "C" {
 
-mk_status megakernel_run(mk_plan* p, void* const* buffers, int n_buffers, void* stream) {
+mk_status megakernel_run_traced(mk_plan* p, void* const* buffers, int n_buffers, void* stream,
+                                uint64_t* trace) {
   if (!p) { set_error("null plan"); return MK_E_INVALID; }
   mk_status st = ensure_device(p);
   if (st != MK_OK) return st;
   mkd::KArgs a;
   if ((st = fill_args(p, buffers, n_buffers, a)) != MK_OK) return st;
+  a.trace = reinterpret_cast<unsigned long long*>(trace);
   if (p->n_instr == 0) return MK_OK;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   // counters hold epoch * target; restart from zero well before int32 overflow
@@ -200,6 +203,10 @@ mk_status megakernel_run(mk_plan* p, void* const* buffers, int n_buffers, void* 
                                     dim3(mkd::kThreads), args, 0, s));
   p->epoch += 1;
   return MK_OK;
+}
+
+mk_status megakernel_run(mk_plan* p, void* const* buffers, int n_buffers, void* stream) {
+  return megakernel_run_traced(p, buffers, n_buffers, stream, nullptr);
 }
 
 mk_status megakernel_run_per_op(mk_plan* p, void* const* buffers, int n_buffers, void* stream) {
@@ -254,6 +261,15 @@ mk_status mk_plan_read_counters(mk_plan* p, int32_t* host, int64_t n, void* stre
   HIPCHK(hipStreamSynchronize(reinterpret_cast<hipStream_t>(stream)));
   if (!p->targets.empty())
     HIPCHK(hipMemcpy(host, p->dev->d_counters, p->targets.size() * sizeof(int32_t), hipMemcpyDeviceToHost));
+  return MK_OK;
+}
+
+mk_status mk_wall_clock_khz(int32_t* khz) {
+  if (!khz) { set_error("null argument"); return MK_E_INVALID; }
+  int dev = 0, rate = 0;
+  HIPCHK(hipGetDevice(&dev));
+  HIPCHK(hipDeviceGetAttribute(&rate, hipDeviceAttributeWallClockRate, dev));
+  *khz = rate;
   return MK_OK;
 }
 

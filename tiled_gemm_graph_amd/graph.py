@@ -230,6 +230,16 @@ class Plan:
         arr = self._ptrs(buffers)
         L.check(self._lib.megakernel_run(self._p, arr, len(arr), self._stream(stream)))
 
+    def run_traced(self, buffers, trace, stream=None) -> None:
+        """One forward that also records 4 wall-clock stamps per instruction
+        into ``trace`` (a device int64 tensor of 4 * n_iters * num_cus)."""
+        arr = self._ptrs(buffers)
+        st = self.stats()
+        if trace.numel() < 4 * st.n_iters * st.num_cus:
+            raise ValueError("trace buffer too small")
+        L.check(self._lib.megakernel_run_traced(self._p, arr, len(arr), self._stream(stream),
+                                                c_void_p(trace.data_ptr())))
+
     def run_per_op(self, buffers, stream=None) -> None:
         """Same graph with one launch per node (the per-op baseline)."""
         arr = self._ptrs(buffers)
