@@ -136,6 +136,15 @@ typedef struct {
   int32_t gemv_max_m;   /* 0 -> 8: GEMMs with M <= this use the GEMV body  */
   int64_t spin_limit_us;/* 0 -> 2000000: a counter wait longer than this
                            aborts the run with MK_E_DEADLOCK               */
+  int32_t cooperative;  /* 1: hipLaunchCooperativeKernel (residency of all
+                           num_cus workgroups guaranteed by the runtime);
+                           0: ordinary launch of num_cus workgroups, which
+                           the kernel's LDS use pins to one per CU.  An
+                           ordinary launch avoids a ~20 us gap between
+                           consecutive cooperative launches; should a
+                           workgroup not become resident, the bounded waits
+                           end the run with MK_E_DEADLOCK instead of a hang */
+  int32_t reserved;
 } mk_build_options;
 
 typedef struct {

@@ -152,3 +152,30 @@ def test_empty_rows_graph_runs():
     # zero-size tensors may have no address; pass any valid pointer
     plan.run([wt.data_ptr(), wt.data_ptr(), wt.data_ptr()])
     plan.check()
+
+
+def test_cooperative_launch_same_bytes():
+    d = workloads.small_dims("decode")
+    inp = workloads.generate("decode", d)
+    r0 = _run("decode", d, inp)
+    r1 = _run("decode", d, inp, cooperative=1)
+    assert torch.equal(r0.out, r1.out)
+
+
+@pytest.mark.parametrize("bn,split", [(64, 1), (128, 2), (256, 3), (512, 4)])
+def test_gemv_tile_shapes(bn, split):
+    # odd / even / single-batch weight streams and their hand-over between
+    # consecutive GEMV instructions
+    d = dict(m=1, hidden=1024, n_q=1024, n_kv=256, inter=1536)
+    inp = workloads.generate("decode", d)
+    t = dict(gemv=1, bn=bn, split=split)
+    tiles = [t, t, dict(t, bn=max(64, bn // 2)), t]   # gate_up reads 2 * bn columns
+    r = _run("decode", d, inp, tiles=tiles)
+    ref = OG.decode(inp, d)
+    rel = rel_fro(to_np(r.out), ref)
+    say(f"  bn={bn} split={split}: rel={rel:.3e}")
+    assert rel <= TOL["bf16"]
+    first = r.out.clone()
+    r.out.zero_()
+    r.forward_per_op(); torch.cuda.synchronize()
+    assert torch.equal(first, r.out)

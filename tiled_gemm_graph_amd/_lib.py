@@ -55,7 +55,8 @@ class OpAttrs(Structure):
 
 class BuildOptions(Structure):
     _fields_ = [("num_cus", c_int32), ("cluster_size", c_int32), ("reuse", c_int32),
-                ("gemv_max_m", c_int32), ("spin_limit_us", c_int64)]
+                ("gemv_max_m", c_int32), ("spin_limit_us", c_int64),
+                ("cooperative", c_int32), ("reserved", c_int32)]
 
 
 class PlanStats(Structure):

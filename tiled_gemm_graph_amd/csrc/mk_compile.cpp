@@ -124,7 +124,7 @@ struct Compiler {
       for (int bn : bns) {
         if (t.bn > 0 && bn != t.bn) continue;
         const I64 wc = (I64)bn * (silu ? 2 : 1);
-        if (wc > 512 || bn > std::max<I64>(N, 8)) continue;
+        if (wc > 1536 || bn > std::max<I64>(N, 8)) continue;
         const I64 tiles = cdiv(std::max<I64>(M, 1), t.bm) * cdiv(N, bn);
         for (I64 s = 1; s <= 128; ++s) {
           if (t.split > 0 && s != t.split) continue;
@@ -231,7 +231,7 @@ struct Compiler {
     if (gemv) {
       int wc = t.bn * (silu ? 2 : 1);
       if (t.bm > 8) unsup("GEMV body handles at most 8 rows per tile");
-      if (wc > 512 || wc % 8) unsup("GEMV weight tile must be <= 512 columns, multiple of 8");
+      if (wc > 1536 || wc % 8) unsup("GEMV weight tile must be <= 1536 columns, multiple of 8");
       if (K % 8) unsup("GEMV K must be a multiple of 8");
       {
         const I64 kc = std::min<I64>(K, cdiv(cdiv(K, S), 64) * 64);

@@ -37,6 +37,7 @@ constexpr int kLdsPad = 8;              // 16-bit elements of row padding
 constexpr int kSmemBytes = 140 * 1024;  // scratch per workgroup
 constexpr int kMaxNodes = 48;           // node descriptors cached in LDS
 constexpr int kGemvBatch = 8;           // 16-byte weight chunks per thread per batch
+constexpr int kGemvBufs = 4;            // weight batches in flight per thread
 
 struct KArgs {
   const mk_instr* instrs;   // [n_iters][ncu]
@@ -346,17 +347,21 @@ __device__ __forceinline__ void gemm_tile(const KArgs& a, const mk_instr& in, co
 }
 
 // ------------------------------------------------------------------ GEMV
-// Small-M GEMM (M <= 8 rows) that streams its weight tile from HBM.
-// Thread layout: ncg 16-byte column groups of the weight tile and kpar K
-// rows in flight; thread t owns group t % ncg and rows kr + j * kpar of the
-// K chunk.  The weights are loaded in batches of kGemvBatch chunks per thread
-// through two register buffers, so every thread always has two batches in
-// flight.  The first two batches are issued before the counter wait (weights
-// are graph inputs and need no producer); the activation chunk is loaded
-// after it.  All loads are unconditional (rows past the chunk re-read a valid
-// row and idle threads re-read a valid column) so the count of outstanding
-// loads is the same on every path and each wait leaves the younger batch in
-// flight.
+// Small-M GEMM (M <= 8 rows) that streams its weight tile from HBM, with two
+// wave roles.  Wave 0 is the controller: it waits on the counters, stages
+// the activation chunk in LDS, sums the partial products and stores and
+// releases the result.  Waves 1-3 stream the weights: thread tw owns 16-byte
+// column group tw % ncg of the weight tile and K rows kr, kr + kpar, ...
+// (kpar = 192 / ncg), and keeps two batches of kGemvBatch chunks in flight
+// in registers.  Their stream runs on across consecutive GEMV instructions:
+// the loads that follow the last batches of instruction i are batches 0 and
+// 1 of instruction i + 1, issued before that instruction's counters clear.
+// The vector-memory counter is per wave and retires in order, so the
+// controller's small dependent loads and its release never wait behind the
+// weight stream.  Weight loads are unconditional (rows past the chunk
+// re-read a valid row) so each wait can leave the younger batch in flight.
+constexpr int kWThreads = kThreads - 64;   // weight-streaming threads
+
 struct GemvShape {
   int bw, wc, ncg, kpar, cg, kr, gcol, kn, nb;
   bool active;
@@ -364,38 +369,43 @@ struct GemvShape {
 __device__ __forceinline__ GemvShape gemv_shape(const mk_instr& in, const mk_node& nd) {
   GemvShape g;
   const bool silu = in.flags & MK_EP_SILU_MUL;
+  const int tw = (int)threadIdx.x - 64;
   g.bw = in.c1 - in.c0;
   g.wc = silu ? 2 * g.bw : g.bw;
   g.ncg = g.wc / 8;
-  g.kpar = kThreads / g.ncg;
-  g.cg = threadIdx.x % g.ncg;
-  g.kr = threadIdx.x / g.ncg;
-  g.active = g.kr < g.kpar;
+  g.kpar = kWThreads / g.ncg;
+  g.cg = tw >= 0 ? tw % g.ncg : 0;
+  g.kr = tw >= 0 ? tw / g.ncg : g.kpar;
+  g.active = tw >= 0 && g.kr < g.kpar;
   const int w = g.cg * 8;
   g.gcol = (silu && w >= g.bw) ? nd.N + in.c0 + (w - g.bw) : in.c0 + w;
   g.kn = in.k1 - in.k0;
   const int rows_per_thread = (g.kn + g.kpar - 1) / g.kpar;
-  g.nb = (rows_per_thread + kGemvBatch - 1) / kGemvBatch;  // batches per thread
+  g.nb = (rows_per_thread + kGemvBatch - 1) / kGemvBatch;
   return g;
 }
 
-// Batch b of this thread: rows kr + (b * kGemvBatch + j) * kpar.
-__device__ __forceinline__ void gemv_load_batch(const u16* W, long ldb, const GemvShape& g, int k0, int b,
-                                                u32x4* dst) {
+// Batch b (clamped to the last one) of this weight thread.
+__device__ __forceinline__ void gemv_load_batch(const KArgs& a, const mk_instr& in, const mk_node& nd,
+                                                const GemvShape& g, int b, u32x4* dst) {
+  const u16* W = buf<const u16>(a, nd.b) + g.gcol;
+  const long ldb = nd.b.ld;
   const int kr = min(g.kr, g.kpar - 1);
+  b = min(b, g.nb - 1);
 #pragma unroll
   for (int j = 0; j < kGemvBatch; ++j) {
     const int k = min(kr + (b * kGemvBatch + j) * g.kpar, g.kn - 1);
-    dst[j] = *reinterpret_cast<const u32x4*>(W + (long)(k0 + k) * ldb);
+    dst[j] = *reinterpret_cast<const u32x4*>(W + (long)(in.k0 + k) * ldb);
   }
 }
 
+// Weight waves: batches 0 .. kGemvBufs-1 of `in` into B.
 __device__ __forceinline__ void gemv_prologue(const KArgs& a, const mk_instr& in, const mk_node& nd,
-                                              u32x4* b0, u32x4* b1) {
+                                              u32x4 (&B)[kGemvBufs][kGemvBatch]) {
+  if (threadIdx.x < 64) return;
   const GemvShape g = gemv_shape(in, nd);
-  const u16* W = buf<const u16>(a, nd.b) + g.gcol;
-  gemv_load_batch(W, nd.b.ld, g, in.k0, 0, b0);
-  gemv_load_batch(W, nd.b.ld, g, in.k0, 1, b1);
+#pragma unroll
+  for (int k = 0; k < kGemvBufs; ++k) gemv_load_batch(a, in, nd, g, k, B[k]);
 }
 
 template <int DT, int MAXR>
@@ -420,102 +430,119 @@ __device__ __forceinline__ void gemv_fma_batch(const GemvShape& g, const u32x4* 
   }
 }
 
-// The body after the wait; b0 / b1 hold batches 0 and 1 (in flight).
-template <int DT, int MAXR>
-__device__ __forceinline__ void gemv_stream(const KArgs& a, const mk_instr& in, const mk_node& nd, char* smem,
-                                            u32x4* b0, u32x4* b1) {
+// Body after the counter wait.  In the weight waves B[(k + S0) % kGemvBufs]
+// holds (in flight) batch k of `in`; on return B[(k + S0 + nb) % kGemvBufs]
+// holds batch k of `nx` (or redundant re-reads of `in` when nx is null).
+template <int DT, int MAXR, int S0>
+__device__ __forceinline__ void gemv_body(const KArgs& a, const mk_instr& in, const mk_node& nd, char* smem,
+                                          u32x4 (&B)[kGemvBufs][kGemvBatch], const mk_instr* nx,
+                                          const mk_node* nxd) {
   const int t = threadIdx.x;
   const int flags = in.flags;
   const bool silu = flags & MK_EP_SILU_MUL, rms = flags & MK_EP_RMSNORM_INPUT;
   const int N = nd.N, r0 = in.r0, rows = in.r1 - in.r0, c0 = in.c0, k0 = in.k0;
   const GemvShape g = gemv_shape(in, nd);
   const int bw = g.bw, wc = g.wc, kn = g.kn;
-  const u16* W = buf<const u16>(a, nd.b) + g.gcol;
-  const long ldb = nd.b.ld;
-  // LDS: activation chunk [MAXR][xstride] fp32, partial sums, reductions
   const int xstride = (kn + 3) & ~3;
-  float* xs = reinterpret_cast<float*>(smem);
-  float* red = xs + MAXR * xstride;        // [kpar][MAXR][wc]
-  float* sum = red + 2048 * MAXR;          // [MAXR][wc], wc <= 512
-  float* misc = sum + 512 * MAXR;
-  // activation chunk, gamma-scaled under RMSNORM_INPUT; per-row sums of squares
+  float* xs = reinterpret_cast<float*>(smem);   // [rows][xstride], rows * kn <= 8192
+  float* red = xs + rows * xstride;             // [kpar][MAXR][wc], kpar * wc <= 1536
+  float* sum = red + 1536 * MAXR;               // [MAXR][wc], wc <= 1536
   float ssq[MAXR];
 #pragma unroll
   for (int m = 0; m < MAXR; ++m) ssq[m] = 0.f;
-  const u16* A = buf<const u16>(a, nd.a) + (long)r0 * nd.a.ld + k0;
-  const u16* G = rms ? buf<const u16>(a, nd.gamma) + k0 : nullptr;
-  const int kc8 = kn / 8;
-  for (int i = t; i < rows * kc8; i += kThreads) {
-    const int m = i / kc8, kc = (i % kc8) * 8;
-    float f[8];
-    unpack8<DT>(*reinterpret_cast<const u32x4*>(A + (long)m * nd.a.ld + kc), f);
-    if (rms) {
-      float gm[8];
-      unpack8<DT>(*reinterpret_cast<const u32x4*>(G + kc), gm);
-      float sq = 0.f;
+  if (t < 64) {
+    // controller: activation chunk, gamma-scaled under RMSNORM_INPUT
+    const u16* A = buf<const u16>(a, nd.a) + (long)r0 * nd.a.ld + k0;
+    const u16* G = rms ? buf<const u16>(a, nd.gamma) + k0 : nullptr;
+    const int kc8 = kn / 8;
+    for (int i = t; i < rows * kc8; i += 64) {
+      const int m = i / kc8, kc = (i % kc8) * 8;
+      float f[8];
+      unpack8<DT>(*reinterpret_cast<const u32x4*>(A + (long)m * nd.a.ld + kc), f);
+      if (rms) {
+        float gm[8];
+        unpack8<DT>(*reinterpret_cast<const u32x4*>(G + kc), gm);
+        float sq = 0.f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        sq += f[e] * f[e];
-        f[e] *= gm[e];
+        for (int e = 0; e < 8; ++e) {
+          sq += f[e] * f[e];
+          f[e] *= gm[e];
+        }
+#pragma unroll
+        for (int mm = 0; mm < MAXR; ++mm)
+          if (mm == m) ssq[mm] += sq;
       }
 #pragma unroll
-      for (int mm = 0; mm < MAXR; ++mm)
-        if (mm == m) ssq[mm] += sq;
+      for (int e = 0; e < 8; ++e) xs[m * xstride + kc + e] = f[e];
     }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) xs[m * xstride + kc + e] = f[e];
   }
   lds_barrier();
-  float acc[MAXR][8];
-#pragma unroll
-  for (int m = 0; m < MAXR; ++m)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[m][e] = 0.f;
-  // stream: two batches in flight; batch b lives in b0 (even) or b1 (odd)
-  for (int b = 0; b < g.nb; b += 2) {
-    gemv_fma_batch<DT, MAXR>(g, b0, b, xs, xstride, rows, acc);
-    gemv_load_batch(W, ldb, g, k0, min(b + 2, g.nb - 1), b0);
-    if (b + 1 < g.nb) gemv_fma_batch<DT, MAXR>(g, b1, b + 1, xs, xstride, rows, acc);
-    gemv_load_batch(W, ldb, g, k0, min(b + 3, g.nb - 1), b1);
-  }
-  if (g.active) {
+  if (t >= 64) {
+    float acc[MAXR][8];
 #pragma unroll
     for (int m = 0; m < MAXR; ++m)
-      if (m < rows)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) red[(g.kr * MAXR + m) * wc + g.cg * 8 + e] = acc[m][e];
+      for (int e = 0; e < 8; ++e) acc[m][e] = 0.f;
+    // Loads target "virtual" batches: v < nb is batch v of this
+    // instruction, v >= nb batch v - nb of the next one (clamped to its last
+    // batch), or a redundant re-read of this tile when there is no next GEMV.
+    GemvShape gn = g;
+    if (nx) gn = gemv_shape(*nx, *nxd);
+    auto load_v = [&](int v, u32x4* dst) __attribute__((always_inline)) {
+      if (v < g.nb) gemv_load_batch(a, in, nd, g, v, dst);
+      else if (nx) gemv_load_batch(a, *nx, *nxd, gn, v - g.nb, dst);
+      else gemv_load_batch(a, in, nd, g, g.nb - 1, dst);
+    };
+    // Virtual batch v lives in B[(v + S0) % kGemvBufs].  Batch v is consumed,
+    // then its buffer receives batch v + kGemvBufs; steps past the end
+    // re-request the batch the buffer already holds, so the number of loads
+    // per step is fixed and each wait leaves the younger batches in flight.
+    for (int v0 = 0; v0 < g.nb; v0 += kGemvBufs) {
+#pragma unroll
+      for (int k = 0; k < kGemvBufs; ++k) {
+        const int v = v0 + k;
+        u32x4* buf_k = B[(k + S0) % kGemvBufs];
+        if (v < g.nb) gemv_fma_batch<DT, MAXR>(g, buf_k, v, xs, xstride, rows, acc);
+        load_v(v < g.nb ? v + kGemvBufs : v, buf_k);
+      }
+    }
+    if (g.active) {
+#pragma unroll
+      for (int m = 0; m < MAXR; ++m)
+        if (m < rows)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) red[(g.kr * MAXR + m) * wc + g.cg * 8 + e] = acc[m][e];
+    }
   }
   lds_barrier();
-  for (int i = t; i < rows * wc; i += kThreads) {
+  if (t >= 64) return;
+  // controller: reduce over the kpar row groups, then store
+  for (int i = t; i < rows * wc; i += 64) {
     const int m = i / wc, w = i % wc;
     float sacc = 0.f;
     for (int q = 0; q < g.kpar; ++q) sacc += red[(q * MAXR + m) * wc + w];
     sum[m * wc + w] = sacc;
   }
-  float* rinv = misc;
-  if (rms && !(flags & MK_EP_PARTIAL)) {
-#pragma unroll
-    for (int m = 0; m < MAXR; ++m) {
-      if (m < rows) {
-        const float tot = block_sum(ssq[m], misc + 8);
-        if (t == 0) rinv[m] = 1.0f / sqrtf(tot / (float)nd.K + nd.eps);
-      }
-    }
-  }
-  lds_barrier();
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // this wave's LDS writes are visible to its lanes
   if (flags & MK_EP_PARTIAL) {
     float* P = buf<float>(a, nd.part) + (long)in.split_idx * nd.part_plane;
-    for (int i = t; i < rows * wc; i += kThreads) {
+    for (int i = t; i < rows * wc; i += 64) {
       const int m = i / wc, w = i % wc;
       const int gc = (silu && w >= bw) ? N + c0 + (w - bw) : c0 + w;
       P[(long)(r0 + m) * nd.part.ld + gc] = sum[m * wc + w];
     }
     return;
   }
+  float rinv[MAXR];
+#pragma unroll
+  for (int m = 0; m < MAXR; ++m) rinv[m] = rms ? 1.0f / sqrtf(wave_sum(ssq[m]) / (float)nd.K + nd.eps) : 1.0f;
   const int units = rows * (bw / 8);
-  for (int u = t; u < units; u += kThreads) {
+  for (int u = t; u < units; u += 64) {
     const int m = u / (bw / 8), w = (u % (bw / 8)) * 8;
-    const float sc = rms ? rinv[m] : 1.0f;
+    float sc = 1.0f;
+#pragma unroll
+    for (int mm = 0; mm < MAXR; ++mm)
+      if (mm == m) sc = rinv[mm];
     epilogue8<DT>(a, nd, flags, r0 + m, c0 + w, w, bw, [&](int ww, float* o) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) o[e] = sum[m * wc + ww + e] * sc;
@@ -523,11 +550,27 @@ __device__ __forceinline__ void gemv_stream(const KArgs& a, const mk_instr& in, 
   }
 }
 
+template <int DT, int MAXR>
+__device__ __forceinline__ void gemv_body_s0(const KArgs& a, const mk_instr& in, const mk_node& nd, char* smem,
+                                             u32x4 (&B)[kGemvBufs][kGemvBatch], const mk_instr* nx,
+                                             const mk_node* nxd, int s0) {
+  switch (s0) {
+    case 0: gemv_body<DT, MAXR, 0>(a, in, nd, smem, B, nx, nxd); break;
+    case 1: gemv_body<DT, MAXR, 1>(a, in, nd, smem, B, nx, nxd); break;
+    case 2: gemv_body<DT, MAXR, 2>(a, in, nd, smem, B, nx, nxd); break;
+    default: gemv_body<DT, MAXR, 3>(a, in, nd, smem, B, nx, nxd); break;
+  }
+}
+
+// Runs `in` with its stream starting at buffer s0; returns the buffer where
+// the next instruction's stream starts.
 template <int DT>
-__device__ __forceinline__ void gemv_stream_rows(const KArgs& a, const mk_instr& in, const mk_node& nd,
-                                                 char* smem, u32x4* b0, u32x4* b1) {
-  if (in.r1 - in.r0 == 1) gemv_stream<DT, 1>(a, in, nd, smem, b0, b1);
-  else gemv_stream<DT, 8>(a, in, nd, smem, b0, b1);
+__device__ __forceinline__ int gemv_body_rows(const KArgs& a, const mk_instr& in, const mk_node& nd, char* smem,
+                                              u32x4 (&B)[kGemvBufs][kGemvBatch], const mk_instr* nx,
+                                              const mk_node* nxd, int s0) {
+  if (in.r1 - in.r0 == 1) gemv_body_s0<DT, 1>(a, in, nd, smem, B, nx, nxd, s0);
+  else gemv_body_s0<DT, 8>(a, in, nd, smem, B, nx, nxd, s0);
+  return (s0 + gemv_shape(in, nd).nb) % kGemvBufs;
 }
 
 // ---------------------------------------------------------------- REDUCE
@@ -827,9 +870,9 @@ __device__ __forceinline__ void run_body(const KArgs& a, const mk_instr& in, con
       else gemm_tile<64, 64, DT>(a, in, nd, smem);
       break;
     case MK_I_GEMV: {
-      u32x4 b0[kGemvBatch], b1[kGemvBatch];
-      gemv_prologue(a, in, nd, b0, b1);
-      gemv_stream_rows<DT>(a, in, nd, smem, b0, b1);
+      u32x4 B[kGemvBufs][kGemvBatch];
+      gemv_prologue(a, in, nd, B);
+      gemv_body_rows<DT>(a, in, nd, smem, B, nullptr, nullptr, 0);
       break;
     }
     case MK_I_REDUCE: reduce_tile<DT>(a, in, nd, smem); break;
@@ -938,19 +981,9 @@ __device__ __forceinline__ bool generic_iter(const Loop& L, int it) {
     const mk_node& nd = L.nodes[in.node];
     const bool tr = a.trace && threadIdx.x == 0;
     if (tr) stamp(a, gidx, 0, wall_clock64());
-    if (in.opcode == MK_I_GEMV) {
-      // weights first: the first two batches load during the counter wait
-      u32x4 b0[kGemvBatch], b1[kGemvBatch];
-      gemv_prologue(a, in, nd, b0, b1);
-      if (!wait_sources(a, in, L.vcu, gidx, L.flag)) return false;
-      if (tr) stamp(a, gidx, 1, wall_clock64());
-      if (nd.dtype == MK_BF16) gemv_stream_rows<MK_BF16>(a, in, nd, L.smem, b0, b1);
-      else gemv_stream_rows<MK_F16>(a, in, nd, L.smem, b0, b1);
-    } else {
-      if (!wait_sources(a, in, L.vcu, gidx, L.flag)) return false;
-      if (tr) stamp(a, gidx, 1, wall_clock64());
-      run_instr(a, in, nd, L.smem);
-    }
+    if (!wait_sources(a, in, L.vcu, gidx, L.flag)) return false;
+    if (tr) stamp(a, gidx, 1, wall_clock64());
+    run_instr(a, in, nd, L.smem);
     if (tr) stamp(a, gidx, 2, wall_clock64());
     release_dests(a, in);
     if (tr) stamp(a, gidx, 3, wall_clock64());
@@ -959,6 +992,56 @@ __device__ __forceinline__ bool generic_iter(const Loop& L, int it) {
   }
   store_ahead(L, it, w);
   return true;
+}
+
+// Release of a GEMV instruction: only the controller wave stored results.
+__device__ __forceinline__ void release_gemv(const KArgs& a, const mk_instr& in) {
+  if (threadIdx.x == 0 && in.n_dst) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    for (int k = 0; k < in.n_dst; ++k)
+      __hip_atomic_fetch_add(a.counters + in.dst_id[k], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// A run of GEMV instructions with the weight stream carried across them.
+// Returns -1 if the run was aborted.
+template <int DT>
+__device__ __forceinline__ int gemv_streak(const Loop& L, int& it) {
+  const KArgs& a = L.a;
+  u32x4 B[kGemvBufs][kGemvBatch];
+  int s0 = 0;
+  {
+    const mk_instr& in = L.slots[it % 3];
+    gemv_prologue(a, in, L.nodes[in.node], B);
+  }
+  for (;;) {
+    const int gidx = it * a.ncu + L.vcu;
+    const mk_instr& in = L.slots[it % 3];
+    const mk_node& nd = L.nodes[in.node];
+    const int w = fetch_ahead(L, it);
+    const bool tr = a.trace && threadIdx.x == 0;
+    if (tr) stamp(a, gidx, 0, wall_clock64());
+    if (!wait_sources(a, in, L.vcu, gidx, L.flag)) return -1;
+    if (tr) stamp(a, gidx, 1, wall_clock64());
+    // the next record became visible with the barrier in wait_sources
+    const mk_instr* nx = nullptr;
+    const mk_node* nxd = nullptr;
+    if (it + 1 < a.n_iters) {
+      const mk_instr& c = L.slots[(it + 1) % 3];
+      if (c.opcode == MK_I_GEMV && L.nodes[c.node].dtype == nd.dtype) {
+        nx = &c;
+        nxd = &L.nodes[c.node];
+      }
+    }
+    s0 = gemv_body_rows<DT>(a, in, nd, L.smem, B, nx, nxd, s0);
+    if (tr) stamp(a, gidx, 2, wall_clock64());
+    release_gemv(a, in);
+    if (tr) stamp(a, gidx, 3, wall_clock64());
+    store_ahead(L, it, w);
+    ++it;
+    if (!nx) return 0;
+  }
 }
 
 }  // namespace mkd
@@ -982,8 +1065,18 @@ __global__ void __launch_bounds__(256, 1) mk_persistent(mkd::KArgs args) {
     mkd::copy_words(reinterpret_cast<int*>(&s_in[r]), reinterpret_cast<const int*>(a.instrs + (long)r * a.ncu + vcu));
   __syncthreads();
   const mkd::Loop L{a, s_in, s_nodes, &s_flag, smem, vcu};
-  for (int it = 0; it < a.n_iters; ++it)
+  int it = 0;
+  while (it < a.n_iters) {
+    const mk_instr& in = s_in[it % 3];
+    if (in.opcode == MK_I_GEMV) {
+      const int st = s_nodes[in.node].dtype == MK_BF16 ? mkd::gemv_streak<MK_BF16>(L, it)
+                                                      : mkd::gemv_streak<MK_F16>(L, it);
+      if (st < 0) return;
+      continue;
+    }
     if (!mkd::generic_iter(L, it)) return;
+    ++it;
+  }
 }
 
 // Per-op baseline: one launch per node, one workgroup per instruction, no

@@ -198,9 +198,14 @@ mk_status megakernel_run_traced(mk_plan* p, void* const* buffers, int n_buffers,
     p->epoch = 0;
   }
   a.epoch = (int)(p->epoch + 1);
-  void* args[] = {&a};
-  HIPCHK(hipLaunchCooperativeKernel(reinterpret_cast<const void*>(mk_persistent), dim3(p->opts.num_cus),
-                                    dim3(mkd::kThreads), args, 0, s));
+  if (p->opts.cooperative) {
+    void* args[] = {&a};
+    HIPCHK(hipLaunchCooperativeKernel(reinterpret_cast<const void*>(mk_persistent), dim3(p->opts.num_cus),
+                                      dim3(mkd::kThreads), args, 0, s));
+  } else {
+    hipLaunchKernelGGL(mk_persistent, dim3(p->opts.num_cus), dim3(mkd::kThreads), 0, s, a);
+    HIPCHK(hipGetLastError());
+  }
   p->epoch += 1;
   return MK_OK;
 }
