@@ -35,6 +35,45 @@ DESCR = {
              "attention, RMSNorm, rotary, SiLU*mul MLP inter 14336, bf16",
 }
 BOUND = dict(mlp3="mfma", decode="hbm", prefill="mfma", decode_gemm="hbm", layer="mfma")
+KERNEL = "mk_persistent"
+CSRC = os.path.join(ROOT, "tiled_gemm_graph_amd", "csrc")
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def kernel_source_hash():
+    """sha256 over the device sources the persistent kernel is built from."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        if name.endswith((".h", ".hip")):
+            with open(os.path.join(CSRC, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    with open(os.path.join(ROOT, "include", "mk.h"), "rb") as f:
+        h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload):
+    """HBM bytes per launch of the persistent kernel from the committed
+    rocprofv3 counter summary: FETCH_SIZE and WRITE_SIZE (KiB per dispatch)
+    scaled by what the same counters read for a plain copy of known size.
+    None when there is no summary or the kernel sources changed since."""
+    path = os.path.join(PROFILES, f"{KERNEL}_{workload}_hbm_counters.md")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for ln in f:
+            if ln.startswith("- ") and ": " in ln:
+                k, v = ln[2:].split(": ", 1)
+                kv[k.strip()] = v.strip().strip("`")
+    try:
+        if kv["kernel_source_sha256"] != kernel_source_hash():
+            return None
+        return (float(kv["fetch_kib_per_dispatch"]) * float(kv["fetch_scale"])
+                + float(kv["write_kib_per_dispatch"]) * float(kv["write_scale"])) * 1024.0
+    except (KeyError, ValueError):
+        return None
 
 
 def log(*a):
@@ -128,12 +167,13 @@ def bench_one(workload, steps, warmup, cpu_budget, do_check=True):
     gbs = st.bytes / (us * 1e-6) / 1e9
     tfl = st.flops / (us * 1e-6) / 1e12
     bound = BOUND[workload]
+    traffic = measured_traffic(workload)
     if bound == "hbm":
         roof = {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": gbs / PEAK_HBM_GBS, "traffic": None}
+                "frac": gbs / PEAK_HBM_GBS, "traffic": traffic}
     else:
         roof = {"bound": "mfma", "achieved": tfl, "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s",
-                "frac": tfl / PEAK_MFMA_TFLOPS, "traffic": None}
+                "frac": tfl / PEAK_MFMA_TFLOPS, "traffic": traffic}
     line = {
         "metric": METRIC,
         "value": us,
@@ -167,6 +207,20 @@ def bench_one(workload, steps, warmup, cpu_budget, do_check=True):
     return line
 
 
+def copy_calibration(mib, steps):
+    """A plain device copy of known size: reads and writes ``mib`` MiB per
+    launch.  Profiling it with the HBM counters gives the scale that turns
+    FETCH_SIZE / WRITE_SIZE into bytes."""
+    import torch
+    n = mib << 20
+    src = torch.randint(0, 255, (n,), dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    ms = time_forwards(lambda: dst.copy_(src), steps, 2)
+    assert torch.equal(dst, src)
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "ms": ms,
+                      "gbps": 2 * n / (ms * 1e-3) / 1e9}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -177,7 +231,14 @@ def main():
     ap.add_argument("--all", action="store_true", help="one JSON line per workload")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-check", action="store_true")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="only time a plain copy of this many MiB (counter calibration)")
+    ap.add_argument("--source-hash", action="store_true",
+                    help="print the hash of the kernel sources and exit")
     args = ap.parse_args()
+    if args.source_hash:
+        print(kernel_source_hash())
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the tile-graph "
               "megakernel is a single-GPU path", file=sys.stderr)
@@ -186,6 +247,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+    if args.copy_mib:
+        copy_calibration(args.copy_mib, args.steps)
+        return
     wls = ["decode", "mlp3", "prefill", "decode_gemm", "layer"] if args.all else [args.workload]
     for wl in wls:
         line = bench_one(wl, args.steps, args.warmup, args.cpu_seconds, not args.no_check)

@@ -104,7 +104,11 @@ enum {
  * GEMM: bm x bn output tile (bn counts output columns, so a SILU_MUL tile
  * reads 2*bn weight columns), split = K chunks (> 1 adds a REDUCE node over
  * rbm x rbn tiles), dup = copies of each tile (cluster duplicate, host
- * profile only), gemv = 1 selects the small-M streaming body.
+ * profile only).  gemv selects the small-M streaming body: 1 = tiles of
+ * bn columns of the row-major [K, N] weight with K split `split` ways;
+ * 2 = packed column tiles: each instruction computes bn output columns
+ * over the whole K from a weight tile stored contiguously in the packed
+ * layout of mk_plan_weight_layout (no K split, no REDUCE node).
  * RMSNORM: rows per instruction.  ATTENTION: bq query rows per instruction.
  * ADD / RELU: er x ec tiles. */
 typedef struct {
@@ -144,7 +148,11 @@ typedef struct {
                            consecutive cooperative launches; should a
                            workgroup not become resident, the bounded waits
                            end the run with MK_E_DEADLOCK instead of a hang */
-  int32_t reserved;
+  int32_t gemv_pack;    /* 0: GEMVs whose weight is a whole weight tensor
+                           read by no other op, with at least num_cus
+                           8-column tiles, use packed column tiles
+                           (tile.gemv = 2); 1: never; 2: whenever the
+                           weight qualifies, however narrow N is            */
 } mk_build_options;
 
 typedef struct {
@@ -200,7 +208,9 @@ typedef struct {
   mk_operand a, b, out, bias, res, gamma, part, aux;
   int64_t part_plane;        /* elements between split-K planes of part     */
   int32_t tile_m, tile_n;    /* GEMM kernel tile: rows x weight columns     */
-  int32_t reserved[MK_NODE_WORDS - 20 - 8 * 4 - 2 - 2];
+  int32_t layout;            /* GEMV weight: 0 row-major [K, Nb]; 1 packed
+                                column tiles [tiles][K][tile_n]            */
+  int32_t reserved[MK_NODE_WORDS - 20 - 8 * 4 - 2 - 2 - 1];
 } mk_node;
 
 typedef struct mk_graph mk_graph;
@@ -241,7 +251,8 @@ void mk_plan_destroy(mk_plan *p);
 /* One forward as one persistent cooperative launch on `stream` (a
  * hipStream_t; 0 = null stream).  buffers[i] is the device pointer of tensor
  * id i for every caller-owned tensor (inputs, weights, outputs); entries of
- * views and intermediates are ignored.  Asynchronous: call mk_plan_check to
+ * views and intermediates are ignored.  A weight the plan packs
+ * (mk_plan_weight_layout) is passed as its packed buffer.  Asynchronous: call mk_plan_check to
  * learn whether a counter wait gave up. */
 mk_status megakernel_run(mk_plan *p, void *const *buffers, int n_buffers, void *stream);
 /* megakernel_run that also writes four wall-clock stamps per executed
@@ -274,6 +285,31 @@ mk_status mk_plan_barriers(const mk_plan *p, const int32_t **targets, int64_t *n
 mk_status mk_plan_slots(const mk_plan *p, const int32_t **slot_of_tensor, int64_t *n);
 /* Tile parameters the compiler chose for graph op `op`. */
 mk_status mk_plan_op_tile(const mk_plan *p, int32_t op, mk_tile *out);
+/* Layout in which the plan reads weight tensor `tensor`.  *packed = 0: the
+ * caller's row-major tensor as declared.  *packed = 1: a GEMV reads it as
+ * packed column tiles and every run takes, in buffers[tensor], a device
+ * buffer of *bytes bytes filled by mk_plan_pack_weight.
+ *
+ * Packed layout (bn = the op's tile.bn output columns per tile, T =
+ * ceil(N / bn) tiles, w = bn, or 2 * bn under SILU_MUL): element
+ * [t][k][j] of a [T][K][w] array holds W[k][col(t * bn + j)] for j < bn
+ * and, under SILU_MUL, W[k][N + col(t * bn + j - bn)] for j >= bn; entries
+ * whose position t * bn + j (mod bn under SILU_MUL) reaches N are zero.
+ * col() is the identity except under ROPE, where output positions
+ * [0, rope_cols) are interleaved in rotation pairs: position p of head
+ * h = p / head_dim, i = (p % head_dim) / 2 maps to column
+ * h * head_dim + i + (p % 2) * head_dim / 2, so each tile holds both
+ * columns of every rotation pair it touches.  The layout is this
+ * library's own: it makes each instruction's weight tile one contiguous
+ * stream, which a row-major weight cut into narrow column tiles is not. */
+mk_status mk_plan_weight_layout(const mk_plan *p, int32_t tensor, int32_t *packed,
+                                int64_t *bytes);
+/* Fill the packed buffer dst (device, mk_plan_weight_layout bytes) from the
+ * row-major weight src (device) on `stream`.  Call once per weight value;
+ * runs read dst, not src.  Fails with MK_E_INVALID for a tensor the plan
+ * does not pack. */
+mk_status mk_plan_pack_weight(mk_plan *p, int32_t tensor, const void *src, void *dst,
+                              void *stream);
 /* Copy the counters to host memory after a run (synchronises `stream`).
  * After e runs every counter equals e * its target. */
 mk_status mk_plan_read_counters(mk_plan *p, int32_t *host, int64_t n, void *stream);

@@ -40,6 +40,15 @@ Lowering and tiling spec (the compiler implements the same rules):
   rows x cols (S == 1 only).  REDUCE reads P [0, S) x rows x cols (and N +
   cols), bias / residual rows x cols, and under RMSNORM_INPUT the A rows
   over the full K (for the row's sum of squares).
+  gemv == 2 (packed column tiles): one GEMV node, no split, no REDUCE;
+  tiles (tm, tn) row-major over bm rows x bn output *positions*; each
+  instruction covers the whole K.  Position p is output column p, except
+  under ROPE for p < rope_cols (default N), where p of head h = p // hd,
+  i = (p % hd) // 2 is column h * hd + i + (p % 2) * hd / 2 (the two
+  columns of a rotation pair are neighbours in position order).  Reads: A
+  rows x [0, K); B [0, K) x the tile's columns (and x N + those columns
+  under SILU_MUL); gamma [0, K); bias / residual rows x the columns; writes
+  out rows x the columns.
 ``rmsnorm`` op, tile param rows R: row blocks of R rows; reads x rows x all
   columns and gamma; writes rows x all columns.
 ``attention`` op, tile param bq: q blocks of bq rows; order: q block
@@ -231,7 +240,61 @@ def lower(g: Graph) -> List[Node]:
     return nodes
 
 
+def _position_column(p: int, hd: int, rope_cols: int) -> int:
+    """Output column of packed-tile position p."""
+    if hd and p < rope_cols:
+        h, w = divmod(p, hd)
+        return h * hd + w // 2 + (w % 2) * (hd // 2)
+    return p
+
+
+def _column_runs(p0: int, p1: int, hd: int, rope_cols: int) -> List[Tuple[int, int]]:
+    """Columns of positions [p0, p1), merged into maximal [c0, c1) runs."""
+    cols = sorted(_position_column(p, hd, rope_cols) for p in range(p0, p1))
+    runs: List[List[int]] = []
+    for c in cols:
+        if runs and runs[-1][1] == c:
+            runs[-1][1] = c + 1
+        else:
+            runs.append([c, c + 1])
+    return [(a, b) for a, b in runs]
+
+
+def _lower_packed_gemv(g: Graph, oi: int, op: Op) -> List[Node]:
+    A, B = op.ins["a"], op.ins["b"]
+    M, K = A.rows, A.cols
+    fl = op.flags
+    N = g.tensors[op.out].padded[3]
+    t = op.tile
+    bm, bn = t["bm"], t["bn"]
+    hd = int(op.attrs.get("head_dim", 0)) if fl & ROPE else 0
+    rope_cols = int(op.attrs.get("rope_cols", 0) or N) if fl & ROPE else 0
+    out = g.full(op.out)
+    gamma, bias, res = op.ins.get("gamma"), op.ins.get("bias"), op.ins.get("residual")
+    ins = []
+    for tm in range(_cdiv(M, bm)):
+        for tn in range(_cdiv(N, bn)):
+            r0, r1 = tm * bm, min(M, tm * bm + bm)
+            runs = _column_runs(tn * bn, min(N, tn * bn + bn), hd, rope_cols)
+            reads = [(A.tensor, A.box(r0, r1, 0, K))]
+            reads += [(B.tensor, B.box(0, K, c0, c1)) for c0, c1 in runs]
+            if fl & SILU_MUL:
+                reads += [(B.tensor, B.box(0, K, N + c0, N + c1)) for c0, c1 in runs]
+            if fl & RMSNORM_INPUT:
+                reads.append((gamma.tensor, gamma.box(0, 1, 0, K)))
+            if fl & BIAS:
+                reads += [(bias.tensor, bias.box(r0, r1, c0, c1)) for c0, c1 in runs]
+            if fl & RESIDUAL:
+                reads += [(res.tensor, res.box(r0, r1, c0, c1)) for c0, c1 in runs]
+            writes = [(op.out, out.box(r0, r1, c0, c1)) for c0, c1 in runs]
+            ins.append(Instr((tm, tn, 0, 0), reads, writes))
+    edges = [A, B] + [e for e in (gamma, bias, res) if e is not None]
+    return [Node(oi, GEMV, fl, op.out, edges, ins)]
+
+
 def _lower_gemm(g: Graph, oi: int, op: Op) -> List[Node]:
+    if op.tile.get("gemv", 0) == 2:
+        return _lower_packed_gemv(g, oi, op)
     A, B = op.ins["a"], op.ins["b"]
     M, K = A.rows, A.cols
     fl = op.flags

@@ -56,7 +56,7 @@ class OpAttrs(Structure):
 class BuildOptions(Structure):
     _fields_ = [("num_cus", c_int32), ("cluster_size", c_int32), ("reuse", c_int32),
                 ("gemv_max_m", c_int32), ("spin_limit_us", c_int64),
-                ("cooperative", c_int32), ("reserved", c_int32)]
+                ("cooperative", c_int32), ("gemv_pack", c_int32)]
 
 
 class PlanStats(Structure):
@@ -77,7 +77,8 @@ EXPORTS = [
     "megakernel_run_per_op",
     "mk_plan_check", "mk_plan_stats_get", "mk_plan_instructions", "mk_plan_nodes",
     "mk_plan_barriers", "mk_plan_slots", "mk_plan_op_tile", "mk_plan_read_counters",
-    "mk_plan_epoch", "mk_wall_clock_khz", "mk_last_error", "mk_abi_version",
+    "mk_plan_epoch", "mk_plan_weight_layout", "mk_plan_pack_weight", "mk_wall_clock_khz",
+    "mk_last_error", "mk_abi_version",
 ]
 
 _lib = None
@@ -112,6 +113,8 @@ def load() -> ctypes.CDLL:
         "mk_plan_op_tile": ([vp, c_int32, POINTER(Tile)], c_int),
         "mk_plan_read_counters": ([vp, i32p, c_int64, vp], c_int),
         "mk_plan_epoch": ([vp, i64p], c_int),
+        "mk_plan_weight_layout": ([vp, c_int32, i32p, i64p], c_int),
+        "mk_plan_pack_weight": ([vp, c_int32, vp, vp, vp], c_int),
         "mk_wall_clock_khz": ([i32p], c_int),
         "mk_last_error": ([], c_char_p),
         "mk_abi_version": ([], c_int32),

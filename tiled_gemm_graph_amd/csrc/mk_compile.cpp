@@ -78,6 +78,30 @@ bool chunks_ok(I64 K, I64 S) {
   return (S - 1) * kc < K;
 }
 
+// Largest activation chunk (rows x K elements) a GEMV instruction stages in
+// LDS as fp32: one row may take up to 16384 elements, more rows 8192 in all.
+I64 gemv_x_limit(I64 rows) { return rows <= 1 ? 16384 : 8192; }
+
+// Output columns of packed-tile positions [c0, c1) as contiguous runs.
+// With hd > 0, positions [0, rope_cols) interleave each head's rotation
+// pairs: position p of head h = p / hd, i = (p % hd) / 2, is column
+// h * hd + i + (p % 2) * hd / 2.  c0 and every head boundary are even.
+std::vector<std::pair<I64, I64>> pos_runs(I64 c0, I64 c1, I64 hd, I64 rope_cols) {
+  std::vector<std::pair<I64, I64>> r;
+  I64 p = c0;
+  if (hd > 0) {
+    while (p < c1 && p < rope_cols) {
+      const I64 h = p / hd, pe = std::min(std::min(c1, (h + 1) * hd), rope_cols);
+      const I64 i0 = (p - h * hd) / 2, i1 = (pe - h * hd + 1) / 2;
+      r.push_back({h * hd + i0, h * hd + i1});
+      r.push_back({h * hd + hd / 2 + i0, h * hd + hd / 2 + i1});
+      p = pe;
+    }
+  }
+  if (p < c1) r.push_back({p, c1});
+  return r;
+}
+
 struct Compiler {
   const mk_graph& g;
   mk_plan& p;
@@ -102,25 +126,48 @@ struct Compiler {
   }
 
   // ---------------------------------------------------------------- tiles
-  mk_tile choose_gemm_tile(const OpRec& op, I64 M, I64 N, I64 K, bool silu, int dt) {
+  mk_tile choose_gemm_tile(const OpRec& op, I64 M, I64 N, I64 K, bool silu, int dt,
+                           bool packable) {
     mk_tile t = op.attrs.tile;
     if (t.dup <= 0) t.dup = 1;
     if (t.gemv < 0) t.gemv = 0;
     bool explicit_gemv = op.attrs.tile.gemv != 0 || op.attrs.tile.bm != 0;
-    if (!explicit_gemv && M <= p.opts.gemv_max_m) t.gemv = 1;
+    if (!explicit_gemv && M <= p.opts.gemv_max_m) {
+      t.gemv = 1;
+      // Packed column tiles need no K split and no REDUCE node; they pay
+      // when there are enough 8-column tiles to give every CU one.
+      const bool wide = cdiv(N, 8) >= ncu;
+      if (packable && t.split <= 1 && (p.opts.gemv_pack == 2 || (p.opts.gemv_pack == 0 && wide)))
+        t.gemv = 2;
+    }
+    if (t.gemv == 2) {
+      if (!packable)
+        fail(MK_E_INVALID, "packed GEMV tiles need a whole 2-D weight tensor read by no other op");
+      if (t.split > 1) fail(MK_E_INVALID, "packed GEMV tiles take no K split");
+      if (t.bm <= 0) t.bm = (int)std::max<I64>(M, 1);
+      if (t.bn <= 0) t.bn = (int)std::max<I64>(8, cdiv(cdiv(N, ncu), 8) * 8);
+      t.split = 1;
+      if (t.rbm <= 0) t.rbm = t.bm;
+      if (t.rbn <= 0) t.rbn = t.bn;
+      return t;
+    }
     if (t.gemv) {
       if (t.bm <= 0) t.bm = (int)std::max<I64>(M, 1);
       const I64 rows = std::min<I64>(std::max<I64>(M, 1), t.bm);
       // Streaming GEMV: pick the weight-tile width and the K split that
       // minimise a makespan estimate: waves of CUs times (per-instruction
-      // overhead + bytes / per-CU bandwidth), with 32-512 KB of weights per
-      // instruction and the activation chunk small enough for LDS.
+      // overhead + bytes loaded / per-CU bandwidth), with 32-512 KB of
+      // weights per instruction and the activation chunk small enough for
+      // LDS.  192 threads stream the tile, 8 columns each, so the per-CU
+      // bandwidth scales with the fraction of them a width keeps busy, and
+      // the bytes loaded include the rounding of each thread's rows up to
+      // whole 8-row batches.
       const double bw_cu = 22e3;   // bytes per microsecond per CU
       const double ovh = 2.5;      // microseconds per instruction
       const int eb = dtype_bytes((mk_dtype)dt);
       double best = 1e300;
       int best_bn = t.bn > 0 ? t.bn : (silu ? 128 : 256), best_s = t.split > 0 ? t.split : 1;
-      const int bns[] = {512, 448, 384, 320, 256, 224, 192, 128, 64};  // wide rows first on ties
+      const int bns[] = {768, 512, 448, 384, 320, 256, 224, 192, 128, 96, 64};  // wide first on ties
       for (int bn : bns) {
         if (t.bn > 0 && bn != t.bn) continue;
         const I64 wc = (I64)bn * (silu ? 2 : 1);
@@ -130,10 +177,14 @@ struct Compiler {
           if (t.split > 0 && s != t.split) continue;
           if (!chunks_ok(K, s)) continue;
           const I64 kc = std::min<I64>(K, cdiv(cdiv(K, s), 64) * 64);
-          if (kc * rows > 8192) continue;
+          if (kc * rows > gemv_x_limit(rows)) continue;
           const double bytes = (double)kc * wc * eb;
           if (bytes > 512 * 1024.0 || (bytes < 32 * 1024.0 && s > 1)) continue;
-          const double cost = (double)cdiv(tiles * s, ncu) * (ovh + bytes / bw_cu);
+          const I64 ncg = wc / 8, kpar = 192 / ncg;
+          const I64 loaded_rows = kpar * cdiv(cdiv(kc, kpar), 8) * 8;
+          const double active = (double)(kpar * ncg) / 192.0;
+          const double loaded = (double)loaded_rows * wc * eb;
+          const double cost = (double)cdiv(tiles * s, ncu) * (ovh + loaded / (bw_cu * active));
           if (cost < best * (1 - 1e-9)) {
             best = cost;
             best_bn = bn;
@@ -173,7 +224,12 @@ struct Compiler {
   }
 
   // ------------------------------------------------------------- lowering
+  std::vector<int> uses;  // op inputs naming each root tensor
+
   void lower() {
+    uses.assign(p.tensors.size(), 0);
+    for (const OpRec& op : g.ops)
+      for (int i : op.in) uses[edge_of(p.tensors, i).tensor]++;
     for (size_t oi = 0; oi < g.ops.size(); ++oi) {
       const OpRec& op = g.ops[oi];
       mk_tile tile{};
@@ -218,12 +274,16 @@ struct Compiler {
     mk_dtype dt = T[A.tensor].dt;
     if (T[B.tensor].dt != dt || O.dt != dt) fail(MK_E_INVALID, "GEMM dtypes differ");
     if (K < 1) fail(MK_E_INVALID, "GEMM needs K >= 1");
-    mk_tile t = choose_gemm_tile(op, M, N, K, silu, dt);
+    // A weight may be packed when the op reads it whole and alone.
+    bool packable = !T[op.in[1]].is_view && T[B.tensor].role == MK_WEIGHT && uses[B.tensor] == 1 &&
+                    (dt == MK_F16 || dt == MK_BF16) && K % 8 == 0 && N % 8 == 0;
+    mk_tile t = choose_gemm_tile(op, M, N, K, silu, dt, packable);
     if (t.bm <= 0 || t.bn <= 0 || t.split <= 0 || t.dup <= 0)
       fail(MK_E_INVALID, "bad GEMM tile");
     int S = t.split;
     auto chunks = k_chunks(std::max<I64>(K, 1), S);
     bool gemv = t.gemv != 0;
+    const bool packed = t.gemv == 2;
     int opcode = gemv ? MK_I_GEMV : MK_I_GEMM;
     // kernel support
     if (dt != MK_F16 && dt != MK_BF16) unsup("GEMM dtype must be fp16 or bf16");
@@ -235,9 +295,11 @@ struct Compiler {
       if (K % 8) unsup("GEMV K must be a multiple of 8");
       {
         const I64 kc = std::min<I64>(K, cdiv(cdiv(K, S), 64) * 64);
-        if (kc * std::min<I64>(std::max<I64>(M, 1), t.bm) > 8192)
-          unsup("GEMV activation chunk (rows x K chunk) exceeds 8192 elements");
+        const I64 rows = std::min<I64>(std::max<I64>(M, 1), t.bm);
+        if (kc * rows > gemv_x_limit(rows))
+          unsup("GEMV activation chunk exceeds 16384 elements (one row) or 8192 (more rows)");
       }
+      if (packed && (t.bn % 8 || t.dup != 1)) unsup("packed GEMV tiles are multiples of 8 columns");
     } else {
       int bnk = t.bn * (silu ? 2 : 1);
       if (!((t.bm == 64 || t.bm == 128) && (bnk == 64 || bnk == 128)))
@@ -252,11 +314,11 @@ struct Compiler {
       if (hd <= 0 || hd % 2 || hd > 256) fail(MK_E_INVALID, "ROPE needs an even head_dim <= 256");
       if (rc % hd || rc > N) fail(MK_E_INVALID, "rope_cols must be a multiple of head_dim <= N");
       int tbn = S > 1 ? t.rbn : t.bn;
-      if (tbn % hd) unsup("ROPE tiles must hold whole heads");
+      if (!packed && tbn % hd) unsup("ROPE tiles must hold whole heads");
       if (hd % 16) unsup("ROPE head_dim must be a multiple of 16");
       if (silu) fail(MK_E_INVALID, "ROPE and SILU_MUL cannot be combined");
     }
-    if (t.gemv && S == 1 && (fl & MK_EP_ROPE)) unsup("ROPE on the GEMV body needs a split");
+    if (t.gemv == 1 && S == 1 && (fl & MK_EP_ROPE)) unsup("ROPE on the row-major GEMV body needs a split");
     int pt = -1;
     if (S > 1) pt = add_internal(MK_F32, {1, S, M, Nb});
     int rope_t = -1;
@@ -280,6 +342,7 @@ struct Compiler {
     }
     Edge P;
     if (S > 1) P = edge_of(p.tensors, pt);
+    const I64 rope_cols = (fl & MK_EP_ROPE) ? (op.attrs.rope_cols ? op.attrs.rope_cols : N) : 0;
     for (I64 tm = 0; tm < cdiv(M, t.bm); ++tm)
       for (I64 tn = 0; tn < cdiv(N, t.bn); ++tn) {
         I64 r0 = tm * t.bm, r1 = std::min(M, r0 + t.bm);
@@ -293,6 +356,22 @@ struct Compiler {
           in.r0 = (int32_t)r0; in.r1 = (int32_t)r1; in.c0 = (int32_t)c0; in.c1 = (int32_t)c1;
           in.k0 = (int32_t)k0; in.k1 = (int32_t)k1; in.s = s;
           in.reads.push_back({A.tensor, box2(A, r0, r1, k0, k1)});
+          if (packed) {
+            // positions [c0, c1) cover the columns of pos_runs
+            const auto runs = pos_runs(c0, c1, (fl & MK_EP_ROPE) ? op.attrs.head_dim : 0, rope_cols);
+            for (const auto& rc : runs) in.reads.push_back({B.tensor, box2(B, 0, K, rc.first, rc.second)});
+            if (silu)
+              for (const auto& rc : runs)
+                in.reads.push_back({B.tensor, box2(B, 0, K, N + rc.first, N + rc.second)});
+            if (fl & MK_EP_RMSNORM_INPUT) in.reads.push_back({gamma.tensor, box2(gamma, 0, 1, 0, K)});
+            for (const auto& rc : runs) {
+              if (fl & MK_EP_BIAS) in.reads.push_back({bias.tensor, box2(bias, r0, r1, rc.first, rc.second)});
+              if (fl & MK_EP_RESIDUAL) in.reads.push_back({res.tensor, box2(res, r0, r1, rc.first, rc.second)});
+            }
+            for (const auto& rc : runs) in.writes.push_back({op.out, box2(out, r0, r1, rc.first, rc.second)});
+            n.ins.push_back(in);
+            continue;
+          }
           in.reads.push_back({B.tensor, box2(B, k0, k1, c0, c1)});
           if (silu) in.reads.push_back({B.tensor, box2(B, k0, k1, N + c0, N + c1)});
           if (fl & MK_EP_RMSNORM_INPUT) in.reads.push_back({gamma.tensor, box2(gamma, 0, 1, k0, k1)});
@@ -325,6 +404,22 @@ struct Compiler {
     d.part_plane = M * Nb;
     d.tile_m = t.bm;
     d.tile_n = t.bn * (silu ? 2 : 1);
+    d.layout = packed ? 1 : 0;
+    if (packed) {
+      PackInfo pk;
+      pk.tensor = B.tensor;
+      pk.K = K;
+      pk.N = N;
+      pk.bn = t.bn;
+      pk.wc = d.tile_n;
+      pk.tiles = cdiv(N, t.bn);
+      pk.silu = silu;
+      pk.head_dim = (fl & MK_EP_ROPE) ? op.attrs.head_dim : 0;
+      pk.rope_cols = rope_cols;
+      pk.dt = dt;
+      pk.bytes = pk.tiles * K * pk.wc * dtype_bytes(dt);
+      p.packs.push_back(pk);
+    }
     p.nodes.push_back(n);
     node_edges.push_back({{"a", A}, {"b", B}, {"gamma", gamma},
                           {"bias", S == 1 ? bias : Edge{}}, {"res", S == 1 ? res : Edge{}},
@@ -983,6 +1078,7 @@ mk_status megakernel_build(const mk_graph* g, const mk_build_options* opts, mk_p
   if (p->opts.gemv_max_m <= 0) p->opts.gemv_max_m = 8;
   if (p->opts.spin_limit_us <= 0) p->opts.spin_limit_us = 2000000;
   if (p->opts.reuse < 0 || p->opts.reuse > 2) { delete p; set_error("reuse must be 0, 1 or 2"); return MK_E_INVALID; }
+  if (p->opts.gemv_pack < 0 || p->opts.gemv_pack > 2) { delete p; set_error("gemv_pack must be 0, 1 or 2"); return MK_E_INVALID; }
   bool has_out = false;
   for (const OpRec& op : g->ops) has_out |= g->t[op.out].role == MK_OUTPUT;
   if (!g->ops.empty() && !has_out) { delete p; set_error("graph has no OUTPUT tensor"); return MK_E_INVALID; }
@@ -1044,6 +1140,19 @@ mk_status mk_plan_op_tile(const mk_plan* p, int32_t op, mk_tile* out) {
   if (!p || !out) { set_error("null argument"); return MK_E_INVALID; }
   if (op < 0 || op >= (int)p->op_tiles.size()) { set_error("bad op index"); return MK_E_INVALID; }
   *out = p->op_tiles[op];
+  return MK_OK;
+}
+
+mk_status mk_plan_weight_layout(const mk_plan* p, int32_t tensor, int32_t* packed, int64_t* bytes) {
+  if (!p || !packed || !bytes) { set_error("null argument"); return MK_E_INVALID; }
+  if (tensor < 0 || tensor >= p->n_graph_tensors) { set_error("bad tensor id"); return MK_E_INVALID; }
+  *packed = 0;
+  *bytes = 0;
+  for (const PackInfo& pk : p->packs)
+    if (pk.tensor == tensor) {
+      *packed = 1;
+      *bytes = pk.bytes;
+    }
   return MK_OK;
 }
 

@@ -74,6 +74,20 @@ struct Node {
   mk_node desc{};
 };
 
+// A weight tensor that a GEMV reads as packed column tiles.
+struct PackInfo {
+  int tensor = -1;
+  I64 K = 0, N = 0;
+  int bn = 0;        // output positions per tile
+  int wc = 0;        // packed row width: bn, or 2 * bn under SILU_MUL
+  I64 tiles = 0;
+  bool silu = false;
+  int head_dim = 0;  // > 0: positions [0, rope_cols) interleave rotation pairs
+  I64 rope_cols = 0;
+  mk_dtype dt = MK_F16;
+  I64 bytes = 0;
+};
+
 }  // namespace mk
 
 struct mk_graph {
@@ -96,6 +110,7 @@ struct mk_plan {
   std::vector<int32_t> slot_of_tensor;   // by tensor id (graph + internal)
   std::vector<int32_t> slot_owner;       // slot -> representative tensor id
   std::vector<mk::I64> slot_bytes;
+  std::vector<mk::PackInfo> packs;   // weights read in the packed layout
   mk_plan_stats stats{};
   int64_t n_instr = 0;
   int64_t epoch = 0;

@@ -135,6 +135,12 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_s_barrier();
 }
 
+// Wave index as a scalar: branches on it are taken per wave (no exec
+// masking), so waits inside a branch are executed only by the waves that
+// take it.  Each wave's vector-memory counter is its own; a wait emitted in
+// code that every wave runs would also drain the other waves' streams.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6); }
+
 template <typename T>
 __device__ __forceinline__ T* buf(const KArgs& a, const mk_operand& o) {
   return reinterpret_cast<T*>(a.bufs[o.slot]) + o.off;
@@ -144,40 +150,45 @@ __device__ __forceinline__ T* buf(const KArgs& a, const mk_operand& o) {
 // Applies the non-partial epilogue to 8 consecutive output columns of one
 // row and stores them.  raw(w) returns the 8 fp32 product values at
 // weight-tile column w (w = output column for plain tiles; gate at w and up
-// at w + half for SILU_MUL).  gr, gc: global row / output column.
+// at w + half for SILU_MUL).  gr, gc: global row / output column.  ROPE
+// rotates the values after BIAS and RESIDUAL, so the partner columns (half
+// a head away) take the same steps first.
 template <int DT, typename Raw>
 __device__ __forceinline__ void epilogue8(const KArgs& a, const mk_node& nd, int flags, int gr,
                                           int gc, int w, int half, Raw raw) {
+  auto pre = [&](int ww, int cc, float* v) __attribute__((always_inline)) {
+    if (flags & MK_EP_SILU_MUL) {
+      float g[8], u[8];
+      raw(ww, g);
+      raw(ww + half, u);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = silu(g[e]) * u[e];
+    } else {
+      raw(ww, v);
+    }
+    if (flags & MK_EP_BIAS) {
+      const u32x4 b = *reinterpret_cast<const u32x4*>(buf<u16>(a, nd.bias) + (long)gr * nd.bias.ld + cc);
+      float f[8];
+      unpack8<DT>(b, f);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] += f[e];
+    }
+    if (flags & MK_EP_RESIDUAL) {
+      const u32x4 b = *reinterpret_cast<const u32x4*>(buf<u16>(a, nd.res) + (long)gr * nd.res.ld + cc);
+      float f[8];
+      unpack8<DT>(b, f);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] += f[e];
+    }
+  };
   float v[8];
-  if (flags & MK_EP_SILU_MUL) {
-    float g[8], u[8];
-    raw(w, g);
-    raw(w + half, u);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = silu(g[e]) * u[e];
-  } else {
-    raw(w, v);
-  }
-  if (flags & MK_EP_BIAS) {
-    const u32x4 b = *reinterpret_cast<const u32x4*>(buf<u16>(a, nd.bias) + (long)gr * nd.bias.ld + gc);
-    float f[8];
-    unpack8<DT>(b, f);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] += f[e];
-  }
-  if (flags & MK_EP_RESIDUAL) {
-    const u32x4 b = *reinterpret_cast<const u32x4*>(buf<u16>(a, nd.res) + (long)gr * nd.res.ld + gc);
-    float f[8];
-    unpack8<DT>(b, f);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] += f[e];
-  }
+  pre(w, gc, v);
   if ((flags & MK_EP_ROPE) && gc < nd.rope_cols) {
     const int hd = nd.head_dim, hh = hd >> 1;
     const int i0 = gc % hd;  // 8 columns never straddle the half (hd % 16 == 0)
     const bool lo = i0 < hh;
     float p[8];
-    raw(lo ? w + hh : w - hh, p);
+    pre(lo ? w + hh : w - hh, lo ? gc + hh : gc - hh, p);
     const float* tab = buf<float>(a, nd.aux) + (long)gr * hd;  // [cos(half) | sin(half)]
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -363,7 +374,8 @@ __device__ __forceinline__ void gemm_tile(const KArgs& a, const mk_instr& in, co
 constexpr int kWThreads = kThreads - 64;   // weight-streaming threads
 
 struct GemvShape {
-  int bw, wc, ncg, kpar, cg, kr, gcol, kn, nb;
+  int bw, wc, ncg, kpar, cg, kr, kn, nb, ldb;
+  long wbase;   // element offset of this thread's first weight column
   bool active;
 };
 __device__ __forceinline__ GemvShape gemv_shape(const mk_instr& in, const mk_node& nd) {
@@ -378,7 +390,15 @@ __device__ __forceinline__ GemvShape gemv_shape(const mk_instr& in, const mk_nod
   g.kr = tw >= 0 ? tw / g.ncg : g.kpar;
   g.active = tw >= 0 && g.kr < g.kpar;
   const int w = g.cg * 8;
-  g.gcol = (silu && w >= g.bw) ? nd.N + in.c0 + (w - g.bw) : in.c0 + w;
+  if (nd.layout) {
+    // packed tile coord[1]: [K][tile_n] rows of (gate | up) positions
+    const int pc = (silu && w >= g.bw) ? (nd.tile_n >> 1) + (w - g.bw) : w;
+    g.ldb = nd.tile_n;
+    g.wbase = (long)in.coord[1] * nd.K * nd.tile_n + pc;
+  } else {
+    g.ldb = nd.b.ld;
+    g.wbase = (silu && w >= g.bw) ? nd.N + in.c0 + (w - g.bw) : in.c0 + w;
+  }
   g.kn = in.k1 - in.k0;
   const int rows_per_thread = (g.kn + g.kpar - 1) / g.kpar;
   g.nb = (rows_per_thread + kGemvBatch - 1) / kGemvBatch;
@@ -388,8 +408,8 @@ __device__ __forceinline__ GemvShape gemv_shape(const mk_instr& in, const mk_nod
 // Batch b (clamped to the last one) of this weight thread.
 __device__ __forceinline__ void gemv_load_batch(const KArgs& a, const mk_instr& in, const mk_node& nd,
                                                 const GemvShape& g, int b, u32x4* dst) {
-  const u16* W = buf<const u16>(a, nd.b) + g.gcol;
-  const long ldb = nd.b.ld;
+  const u16* W = buf<const u16>(a, nd.b) + g.wbase;
+  const long ldb = g.ldb;
   const int kr = min(g.kr, g.kpar - 1);
   b = min(b, g.nb - 1);
 #pragma unroll
@@ -402,7 +422,7 @@ __device__ __forceinline__ void gemv_load_batch(const KArgs& a, const mk_instr& 
 // Weight waves: batches 0 .. kGemvBufs-1 of `in` into B.
 __device__ __forceinline__ void gemv_prologue(const KArgs& a, const mk_instr& in, const mk_node& nd,
                                               u32x4 (&B)[kGemvBufs][kGemvBatch]) {
-  if (threadIdx.x < 64) return;
+  if (wave_id() == 0) return;
   const GemvShape g = gemv_shape(in, nd);
 #pragma unroll
   for (int k = 0; k < kGemvBufs; ++k) gemv_load_batch(a, in, nd, g, k, B[k]);
@@ -430,6 +450,60 @@ __device__ __forceinline__ void gemv_fma_batch(const GemvShape& g, const u32x4* 
   }
 }
 
+// Epilogue of a packed column tile (controller wave).  Positions
+// [c0, c0 + bw) map to output columns; under ROPE, positions below
+// rope_cols come in rotation pairs (column d and d + head_dim / 2 of one
+// head), so both partners of a pair are in this tile.  Order: SILU_MUL
+// (of the rms-scaled gate and up), BIAS, RESIDUAL, ROPE, RELU, cast.
+template <int DT, int MAXR>
+__device__ __forceinline__ void gemv_store_packed(const KArgs& a, const mk_node& nd, int flags, int r0,
+                                                  int c0, int rows, int bw, int wc, const float* sum,
+                                                  const float (&rinv)[MAXR]) {
+  const bool silu_mul = flags & MK_EP_SILU_MUL, rope = flags & MK_EP_ROPE;
+  const int hd = nd.head_dim, hh = hd >> 1;
+  const int npair = bw >> 1;
+  u16* O = buf<u16>(a, nd.out);
+  for (int u = threadIdx.x; u < rows * npair; u += 64) {
+    const int m = u / npair, q = (u - m * npair) * 2;
+    const int gr = r0 + m;
+    float sc = 1.0f;
+#pragma unroll
+    for (int mm = 0; mm < MAXR; ++mm)
+      if (mm == m) sc = rinv[mm];
+    const bool rot = rope && c0 + q < nd.rope_cols;
+    float v[2];
+    int col[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int pos = c0 + q + e;
+      int c = pos;
+      if (rot) {
+        const int h = pos / hd, w = pos - h * hd;
+        c = h * hd + (w >> 1) + (w & 1) * hh;
+      }
+      col[e] = c;
+      float x = sum[m * wc + q + e] * sc;
+      if (silu_mul) x = silu(x) * (sum[m * wc + bw + q + e] * sc);
+      if (flags & MK_EP_BIAS) x += to_f<DT>(buf<const u16>(a, nd.bias)[(long)gr * nd.bias.ld + c]);
+      if (flags & MK_EP_RESIDUAL) x += to_f<DT>(buf<const u16>(a, nd.res)[(long)gr * nd.res.ld + c]);
+      v[e] = x;
+    }
+    if (rot) {
+      const float* tab = buf<float>(a, nd.aux) + (long)gr * hd;  // [cos(half) | sin(half)]
+      const int i = col[0] - (col[0] / hd) * hd;
+      const float cs = tab[i], sn = tab[hh + i];
+      const float x1 = v[0], x2 = v[1];
+      v[0] = x1 * cs - x2 * sn;
+      v[1] = x2 * cs + x1 * sn;
+    }
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const float y = (flags & MK_EP_RELU) ? fmaxf(v[e], 0.0f) : v[e];
+      O[(long)gr * nd.out.ld + col[e]] = from_f<DT>(y);
+    }
+  }
+}
+
 // Body after the counter wait.  In the weight waves B[(k + S0) % kGemvBufs]
 // holds (in flight) batch k of `in`; on return B[(k + S0 + nb) % kGemvBufs]
 // holds batch k of `nx` (or redundant re-reads of `in` when nx is null).
@@ -444,40 +518,61 @@ __device__ __forceinline__ void gemv_body(const KArgs& a, const mk_instr& in, co
   const GemvShape g = gemv_shape(in, nd);
   const int bw = g.bw, wc = g.wc, kn = g.kn;
   const int xstride = (kn + 3) & ~3;
-  float* xs = reinterpret_cast<float*>(smem);   // [rows][xstride], rows * kn <= 8192
+  float* xs = reinterpret_cast<float*>(smem);   // [rows][xstride], rows * kn <= 16384 (8192 if rows > 1)
   float* red = xs + rows * xstride;             // [kpar][MAXR][wc], kpar * wc <= 1536
   float* sum = red + 1536 * MAXR;               // [MAXR][wc], wc <= 1536
-  float ssq[MAXR];
-#pragma unroll
-  for (int m = 0; m < MAXR; ++m) ssq[m] = 0.f;
-  if (t < 64) {
-    // controller: activation chunk, gamma-scaled under RMSNORM_INPUT
+  float* sq = sum + 1536 * MAXR;                // [4 waves][MAXR] sums of squares
+  {
+    // All four waves stage the activation chunk (gamma-scaled under
+    // RMSNORM_INPUT) with every load of a thread in flight at once (at most
+    // 8: rows * kn / 8 <= 2048 chunks); each wave adds up its squares.
     const u16* A = buf<const u16>(a, nd.a) + (long)r0 * nd.a.ld + k0;
-    const u16* G = rms ? buf<const u16>(a, nd.gamma) + k0 : nullptr;
-    const int kc8 = kn / 8;
-    for (int i = t; i < rows * kc8; i += 64) {
-      const int m = i / kc8, kc = (i % kc8) * 8;
-      float f[8];
-      unpack8<DT>(*reinterpret_cast<const u32x4*>(A + (long)m * nd.a.ld + kc), f);
-      if (rms) {
-        float gm[8];
-        unpack8<DT>(*reinterpret_cast<const u32x4*>(G + kc), gm);
-        float sq = 0.f;
+    const int kc8 = kn / 8, nch = rows * kc8;
+    u32x4 xv[8], gv[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          sq += f[e] * f[e];
-          f[e] *= gm[e];
+    for (int j = 0; j < 8; ++j) {
+      const int i = min(t + j * kThreads, nch - 1);
+      const int m = i / kc8, kc = (i - m * kc8) * 8;
+      xv[j] = *reinterpret_cast<const u32x4*>(A + (long)m * nd.a.ld + kc);
+      if (rms) gv[j] = *reinterpret_cast<const u32x4*>(buf<const u16>(a, nd.gamma) + k0 + kc);
+    }
+    float sqt[MAXR];
+#pragma unroll
+    for (int m = 0; m < MAXR; ++m) sqt[m] = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int i = t + j * kThreads;
+      if (i < nch) {
+        const int m = i / kc8, kc = (i - m * kc8) * 8;
+        float f[8];
+        unpack8<DT>(xv[j], f);
+        if (rms) {
+          float gm[8];
+          unpack8<DT>(gv[j], gm);
+          float q = 0.f;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            q += f[e] * f[e];
+            f[e] *= gm[e];
+          }
+#pragma unroll
+          for (int mm = 0; mm < MAXR; ++mm)
+            if (mm == m) sqt[mm] += q;
         }
 #pragma unroll
-        for (int mm = 0; mm < MAXR; ++mm)
-          if (mm == m) ssq[mm] += sq;
+        for (int e = 0; e < 8; ++e) xs[m * xstride + kc + e] = f[e];
       }
+    }
+    if (rms) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) xs[m * xstride + kc + e] = f[e];
+      for (int m = 0; m < MAXR; ++m) {
+        const float v = wave_sum(sqt[m]);
+        if ((t & 63) == 0) sq[wave_id() * MAXR + m] = v;
+      }
     }
   }
   lds_barrier();
-  if (t >= 64) {
+  if (wave_id() != 0) {
     float acc[MAXR][8];
 #pragma unroll
     for (int m = 0; m < MAXR; ++m)
@@ -515,15 +610,26 @@ __device__ __forceinline__ void gemv_body(const KArgs& a, const mk_instr& in, co
     }
   }
   lds_barrier();
-  if (t >= 64) return;
-  // controller: reduce over the kpar row groups, then store
-  for (int i = t; i < rows * wc; i += 64) {
-    const int m = i / wc, w = i % wc;
-    float sacc = 0.f;
-    for (int q = 0; q < g.kpar; ++q) sacc += red[(q * MAXR + m) * wc + w];
-    sum[m * wc + w] = sacc;
+  {
+    // All waves sum the kpar row groups: tpu consecutive lanes per output,
+    // each adding groups sub, sub + tpu, ..., then a butterfly over the tpu
+    // lanes (a fixed order, so every run gives the same bits).
+    const int nout = rows * wc;
+    int tpu = 1;
+    while (tpu < 16 && tpu * 2 * nout <= kThreads) tpu *= 2;
+    for (int o0 = 0; o0 < nout; o0 += kThreads / tpu) {
+      const int o = o0 + t / tpu, sub = t % tpu;
+      float v = 0.f;
+      if (o < nout) {
+        const int m = o / wc, w = o - m * wc;
+        for (int q = sub; q < g.kpar; q += tpu) v += red[(q * MAXR + m) * wc + w];
+      }
+      for (int off = tpu >> 1; off > 0; off >>= 1) v += __shfl_xor(v, off);
+      if (sub == 0 && o < nout) sum[o] = v;
+    }
   }
-  __builtin_amdgcn_s_waitcnt(0xc07f);  // this wave's LDS writes are visible to its lanes
+  lds_barrier();
+  if (wave_id() != 0) return;
   if (flags & MK_EP_PARTIAL) {
     float* P = buf<float>(a, nd.part) + (long)in.split_idx * nd.part_plane;
     for (int i = t; i < rows * wc; i += 64) {
@@ -535,7 +641,13 @@ __device__ __forceinline__ void gemv_body(const KArgs& a, const mk_instr& in, co
   }
   float rinv[MAXR];
 #pragma unroll
-  for (int m = 0; m < MAXR; ++m) rinv[m] = rms ? 1.0f / sqrtf(wave_sum(ssq[m]) / (float)nd.K + nd.eps) : 1.0f;
+  for (int m = 0; m < MAXR; ++m)
+    rinv[m] = rms ? 1.0f / sqrtf((sq[m] + sq[MAXR + m] + sq[2 * MAXR + m] + sq[3 * MAXR + m]) / (float)nd.K + nd.eps)
+                  : 1.0f;
+  if (nd.layout) {
+    gemv_store_packed<DT, MAXR>(a, nd, flags, r0, c0, rows, bw, wc, sum, rinv);
+    return;
+  }
   const int units = rows * (bw / 8);
   for (int u = t; u < units; u += 64) {
     const int m = u / (bw / 8), w = (u % (bw / 8)) * 8;
@@ -894,36 +1006,6 @@ __device__ __forceinline__ void copy_words(int* dst, const int* src) {
   if (threadIdx.x < 64) dst[threadIdx.x] = src[threadIdx.x];
 }
 
-// Thread 0 waits on every source counter; returns false (uniformly) if the
-// run was aborted.  `flag` is an LDS int.
-__device__ __forceinline__ bool wait_sources(const KArgs& a, const mk_instr& in, int vcu, int gidx, int* flag) {
-  if (threadIdx.x == 0) {
-    int ok = 1;
-    const long long t0 = wall_clock64();
-    for (int k = 0; k < in.n_src && ok; ++k) {
-      const int id = in.src_id[k];
-      const int need = a.epoch * in.src_target[k];
-      int v;
-      while ((v = __hip_atomic_load(a.counters + id, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) < need) {
-        if (__hip_atomic_load(a.err + 6, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) { ok = 0; break; }
-        if (wall_clock64() - t0 > a.spin_ticks) {
-          if (atomicCAS(a.err, 0, (int)MK_E_DEADLOCK) == 0) {
-            a.err[1] = vcu; a.err[2] = gidx; a.err[3] = id; a.err[4] = v; a.err[5] = need;
-          }
-          __hip_atomic_store(a.err + 6, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          ok = 0;
-          break;
-        }
-        __builtin_amdgcn_s_sleep(1);
-      }
-    }
-    if (ok && in.n_src) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    *flag = ok;
-  }
-  __syncthreads();
-  return *flag != 0;
-}
-
 __device__ __forceinline__ void release_dests(const KArgs& a, const mk_instr& in) {
   // every wave: its stores have completed; then one lane makes them visible
   // at agent scope and arrives on each destination counter
@@ -960,35 +1042,74 @@ __device__ __forceinline__ void stamp(const KArgs& a, int gidx, int k, unsigned 
   a.trace[4 * (long)gidx + k] = v;
 }
 
-// Issue the load of record it + 2 (wave 0); returns its word for this lane.
+// Wave 0: this lane's word of record it + 2 (clamped to the last iteration so
+// the load is unconditional).
 __device__ __forceinline__ int fetch_ahead(const Loop& L, int it) {
-  int w = 0;
-  if (threadIdx.x < 64 && it + 2 < L.a.n_iters)
-    w = reinterpret_cast<const int*>(L.a.instrs + (long)(it + 2) * L.a.ncu + L.vcu)[threadIdx.x];
-  return w;
+  const long r = min(it + 2, L.a.n_iters - 1);
+  return reinterpret_cast<const int*>(L.a.instrs + r * L.a.ncu + L.vcu)[threadIdx.x & 63];
 }
+
+// Start of iteration it.  Wave 0 issues the load of record it + 2 (used at
+// the end of the iteration) while its lane 0 waits on every source counter
+// (relaxed agent-scope polls, then one acquire); all waves then meet at an
+// LDS-only barrier, so the weight waves keep their loads in flight.
+// Returns false (uniformly) if the run was aborted.
+__device__ __forceinline__ bool wait_sources(const Loop& L, const mk_instr& in, int it, int gidx, int& w) {
+  const KArgs& a = L.a;
+  if (wave_id() == 0) {
+    w = fetch_ahead(L, it);
+    if (threadIdx.x == 0) {
+      int ok = 1;
+      const long long t0 = wall_clock64();
+      for (int k = 0; k < in.n_src && ok; ++k) {
+        const int id = in.src_id[k];
+        const int need = a.epoch * in.src_target[k];
+        int v;
+        while ((v = __hip_atomic_load(a.counters + id, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) < need) {
+          if (__hip_atomic_load(a.err + 6, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) { ok = 0; break; }
+          if (wall_clock64() - t0 > a.spin_ticks) {
+            if (atomicCAS(a.err, 0, (int)MK_E_DEADLOCK) == 0) {
+              a.err[1] = L.vcu; a.err[2] = gidx; a.err[3] = id; a.err[4] = v; a.err[5] = need;
+            }
+            __hip_atomic_store(a.err + 6, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            ok = 0;
+            break;
+          }
+          __builtin_amdgcn_s_sleep(1);
+        }
+      }
+      if (ok && in.n_src) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      *L.flag = ok;
+    }
+  }
+  lds_barrier();
+  return *L.flag != 0;
+}
+
+// End of iteration it (wave 0): park record it + 2 in slot (it + 2) % 3.
+// Every wave has passed this iteration's barriers, so none still reads the
+// record of iteration it - 1 that the slot held; the next iteration's
+// barrier publishes it.
 __device__ __forceinline__ void store_ahead(const Loop& L, int it, int w) {
-  if (threadIdx.x < 64 && it + 2 < L.a.n_iters) reinterpret_cast<int*>(&L.slots[(it + 2) % 3])[threadIdx.x] = w;
+  if (wave_id() == 0 && it + 2 < L.a.n_iters)
+    reinterpret_cast<int*>(&L.slots[(it + 2) % 3])[threadIdx.x & 63] = w;
 }
 
 // One generic iteration.  Returns false if the run was aborted.
-__device__ __forceinline__ bool generic_iter(const Loop& L, int it) {
+__device__ __forceinline__ bool generic_iter(const Loop& L, int it, int& w) {
   const KArgs& a = L.a;
   const int gidx = it * a.ncu + L.vcu;
   const mk_instr& in = L.slots[it % 3];
-  const int w = fetch_ahead(L, it);
+  const bool tr = a.trace && threadIdx.x == 0 && in.opcode != MK_I_NOOP;
+  if (tr) stamp(a, gidx, 0, wall_clock64());
+  if (!wait_sources(L, in, it, gidx, w)) return false;
   if (in.opcode != MK_I_NOOP) {
     const mk_node& nd = L.nodes[in.node];
-    const bool tr = a.trace && threadIdx.x == 0;
-    if (tr) stamp(a, gidx, 0, wall_clock64());
-    if (!wait_sources(a, in, L.vcu, gidx, L.flag)) return false;
     if (tr) stamp(a, gidx, 1, wall_clock64());
     run_instr(a, in, nd, L.smem);
     if (tr) stamp(a, gidx, 2, wall_clock64());
     release_dests(a, in);
     if (tr) stamp(a, gidx, 3, wall_clock64());
-  } else {
-    __syncthreads();
   }
   store_ahead(L, it, w);
   return true;
@@ -996,8 +1117,9 @@ __device__ __forceinline__ bool generic_iter(const Loop& L, int it) {
 
 // Release of a GEMV instruction: only the controller wave stored results.
 __device__ __forceinline__ void release_gemv(const KArgs& a, const mk_instr& in) {
+  if (wave_id() != 0) return;
+  __builtin_amdgcn_s_waitcnt(0);  // wave 0's stores have completed
   if (threadIdx.x == 0 && in.n_dst) {
-    __builtin_amdgcn_s_waitcnt(0);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     for (int k = 0; k < in.n_dst; ++k)
       __hip_atomic_fetch_add(a.counters + in.dst_id[k], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1007,7 +1129,7 @@ __device__ __forceinline__ void release_gemv(const KArgs& a, const mk_instr& in)
 // A run of GEMV instructions with the weight stream carried across them.
 // Returns -1 if the run was aborted.
 template <int DT>
-__device__ __forceinline__ int gemv_streak(const Loop& L, int& it) {
+__device__ __forceinline__ int gemv_streak(const Loop& L, int& it, int& w) {
   const KArgs& a = L.a;
   u32x4 B[kGemvBufs][kGemvBatch];
   int s0 = 0;
@@ -1019,10 +1141,9 @@ __device__ __forceinline__ int gemv_streak(const Loop& L, int& it) {
     const int gidx = it * a.ncu + L.vcu;
     const mk_instr& in = L.slots[it % 3];
     const mk_node& nd = L.nodes[in.node];
-    const int w = fetch_ahead(L, it);
     const bool tr = a.trace && threadIdx.x == 0;
     if (tr) stamp(a, gidx, 0, wall_clock64());
-    if (!wait_sources(a, in, L.vcu, gidx, L.flag)) return -1;
+    if (!wait_sources(L, in, it, gidx, w)) return -1;
     if (tr) stamp(a, gidx, 1, wall_clock64());
     // the next record became visible with the barrier in wait_sources
     const mk_instr* nx = nullptr;
@@ -1065,16 +1186,16 @@ __global__ void __launch_bounds__(256, 1) mk_persistent(mkd::KArgs args) {
     mkd::copy_words(reinterpret_cast<int*>(&s_in[r]), reinterpret_cast<const int*>(a.instrs + (long)r * a.ncu + vcu));
   __syncthreads();
   const mkd::Loop L{a, s_in, s_nodes, &s_flag, smem, vcu};
-  int it = 0;
+  int it = 0, w = 0;
   while (it < a.n_iters) {
     const mk_instr& in = s_in[it % 3];
     if (in.opcode == MK_I_GEMV) {
-      const int st = s_nodes[in.node].dtype == MK_BF16 ? mkd::gemv_streak<MK_BF16>(L, it)
-                                                      : mkd::gemv_streak<MK_F16>(L, it);
+      const int st = s_nodes[in.node].dtype == MK_BF16 ? mkd::gemv_streak<MK_BF16>(L, it, w)
+                                                      : mkd::gemv_streak<MK_F16>(L, it, w);
       if (st < 0) return;
       continue;
     }
-    if (!mkd::generic_iter(L, it)) return;
+    if (!mkd::generic_iter(L, it, w)) return;
     ++it;
   }
 }

@@ -29,6 +29,38 @@ struct mk_plan_device {
   int max_target = 1;
 };
 
+// Packed column tiles of a row-major weight src [K][ld] (the layout of
+// mk_plan_weight_layout): element e of dst [tiles][K][wc] takes src at row k
+// and the column of tile position t * bn + j (gate) or N + that column (up,
+// j >= bn under SILU_MUL); positions at or past N are zero.
+__global__ void mk_pack_kernel(const unsigned short* __restrict__ src, unsigned short* __restrict__ dst,
+                               long K, long N, long ld, int bn, int wc, long tiles, int silu, int hd,
+                               long rope_cols) {
+  const long total = tiles * K * wc;
+  for (long e = (long)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += (long)gridDim.x * blockDim.x) {
+    const int j = (int)(e % wc);
+    const long k = (e / wc) % K;
+    const long t = e / ((long)wc * K);
+    int pj = j;
+    long up = 0;
+    if (silu && j >= bn) {
+      pj = j - bn;
+      up = N;
+    }
+    const long pos = t * bn + pj;
+    unsigned short v = 0;
+    if (pos < N) {
+      long col = pos;
+      if (hd > 0 && pos < rope_cols) {
+        const long h = pos / hd, w = pos - h * hd;
+        col = h * hd + (w >> 1) + (w & 1) * (hd >> 1);
+      }
+      v = src[k * ld + up + col];
+    }
+    dst[e] = v;
+  }
+}
+
 namespace {
 
 using mk::set_error;
@@ -266,6 +298,24 @@ mk_status mk_plan_read_counters(mk_plan* p, int32_t* host, int64_t n, void* stre
   HIPCHK(hipStreamSynchronize(reinterpret_cast<hipStream_t>(stream)));
   if (!p->targets.empty())
     HIPCHK(hipMemcpy(host, p->dev->d_counters, p->targets.size() * sizeof(int32_t), hipMemcpyDeviceToHost));
+  return MK_OK;
+}
+
+mk_status mk_plan_pack_weight(mk_plan* p, int32_t tensor, const void* src, void* dst, void* stream) {
+  if (!p || !src || !dst) { set_error("null argument"); return MK_E_INVALID; }
+  const mk::PackInfo* pk = nullptr;
+  for (const mk::PackInfo& q : p->packs)
+    if (q.tensor == tensor) pk = &q;
+  if (!pk) { set_error("tensor " + std::to_string(tensor) + " is not packed by this plan"); return MK_E_INVALID; }
+  const long total = pk->tiles * pk->K * pk->wc;
+  if (total == 0) return MK_OK;
+  const long ld = p->tensors[tensor].shape[3];
+  const int blocks = (int)std::min<long>((total + 255) / 256, 8192);
+  hipLaunchKernelGGL(mk_pack_kernel, dim3(blocks), dim3(256), 0, reinterpret_cast<hipStream_t>(stream),
+                     static_cast<const unsigned short*>(src), static_cast<unsigned short*>(dst), (long)pk->K,
+                     (long)pk->N, ld, pk->bn, pk->wc, (long)pk->tiles, pk->silu ? 1 : 0, pk->head_dim,
+                     (long)pk->rope_cols);
+  HIPCHK(hipGetLastError());
   return MK_OK;
 }
 

@@ -119,10 +119,11 @@ class Graph:
 
     # compile -----------------------------------------------------------
     def build(self, num_cus: int = 0, cluster_size: int = 0, reuse: int = 0,
-              gemv_max_m: int = 0, spin_limit_us: int = 0, cooperative: int = 0) -> "Plan":
+              gemv_max_m: int = 0, spin_limit_us: int = 0, cooperative: int = 0,
+              gemv_pack: int = 0) -> "Plan":
         opts = L.BuildOptions(num_cus=num_cus, cluster_size=cluster_size, reuse=reuse,
                               gemv_max_m=gemv_max_m, spin_limit_us=spin_limit_us,
-                              cooperative=cooperative)
+                              cooperative=cooperative, gemv_pack=gemv_pack)
         p = c_void_p()
         L.check(self._lib.megakernel_build(self._g, byref(opts), byref(p)))
         return Plan(p, self)
@@ -183,6 +184,27 @@ class Plan:
 
     def op_tiles(self) -> List[Dict[str, int]]:
         return [self.op_tile(i) for i in range(self.n_ops)]
+
+    def weight_layout(self, tensor: Union[int, str]):
+        """(packed, bytes): whether runs read this weight as packed column
+        tiles, and the size of the packed buffer."""
+        tid = self.ids[tensor] if isinstance(tensor, str) else tensor
+        pk, nb = c_int32(), c_int64()
+        L.check(self._lib.mk_plan_weight_layout(self._p, tid, byref(pk), byref(nb)))
+        return bool(pk.value), nb.value
+
+    def packed_weights(self) -> List[str]:
+        return [n for n, i in self.ids.items()
+                if self.roles.get(i) == "weight" and self.weight_layout(i)[0]]
+
+    def pack_weight(self, tensor: Union[int, str], src, dst, stream=None) -> None:
+        """Fill device buffer ``dst`` with the packed layout of row-major
+        weight ``src`` (both device tensors or pointers)."""
+        tid = self.ids[tensor] if isinstance(tensor, str) else tensor
+        sp = src if isinstance(src, int) else src.data_ptr()
+        dp = dst if isinstance(dst, int) else dst.data_ptr()
+        L.check(self._lib.mk_plan_pack_weight(self._p, tid, c_void_p(sp), c_void_p(dp),
+                                              self._stream(stream)))
 
     @property
     def epoch(self) -> int:

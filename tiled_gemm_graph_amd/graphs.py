@@ -164,16 +164,26 @@ class Runner:
         self.graph = build(workload, dims, tiles)
         self.plan: Plan = self.graph.build(**opts)
         self.bufs = {k: v.to(device).contiguous() for k, v in inputs.items()}
+        # weights the plan reads as packed column tiles: pack once, run on the copy
+        self.packed = {}
+        for name in self.plan.packed_weights():
+            nbytes = self.plan.weight_layout(name)[1]
+            dst = torch.empty(nbytes // 2, dtype=self.bufs[name].dtype, device=device)
+            self.plan.pack_weight(name, self.bufs[name], dst)
+            self.packed[name] = dst
+        self.run_bufs = dict(self.bufs)
+        self.run_bufs.update(self.packed)
         self.out_name = output_name(workload, dims)
         oid = self.graph.ids[self.out_name]
         tdt = torch.float16 if DTYPE[workload] == "f16" else torch.bfloat16
         self.out = torch.empty(self.graph.shapes[oid], dtype=tdt, device=device)
         self.bufs[self.out_name] = self.out
+        self.run_bufs[self.out_name] = self.out
 
     def forward(self, stream=None):
-        self.plan.run(self.bufs, stream)
+        self.plan.run(self.run_bufs, stream)
         return self.out
 
     def forward_per_op(self, stream=None):
-        self.plan.run_per_op(self.bufs, stream)
+        self.plan.run_per_op(self.run_bufs, stream)
         return self.out

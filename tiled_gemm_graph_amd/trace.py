@@ -33,7 +33,7 @@ def capture(runner) -> np.ndarray:
     st = runner.plan.stats()
     n = 4 * st.n_iters * st.num_cus
     buf = torch.zeros(n, dtype=torch.int64, device=runner.out.device)
-    runner.plan.run_traced(runner.bufs, buf)
+    runner.plan.run_traced(runner.run_bufs, buf)
     runner.plan.check()
     torch.cuda.synchronize()
     return buf.view(-1, 4).cpu().numpy()[: st.n_instr]
