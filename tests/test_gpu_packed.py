@@ -137,3 +137,23 @@ def test_rope_bias_residual_epilogue(mode):
     assert rel <= TOL["bf16"]
     zref = ops.gemm(got[:, :128], f(W2), dt=np.float64)
     assert rel_fro(to_np(z), zref) <= TOL["bf16"]
+
+
+def test_full_decode_repeated_runs_identical():
+    # packed tiles publish their outputs with write-through stores and no L2
+    # write-back: repeated runs must give the same bytes every time
+    d = workloads.default_dims("decode")
+    inp = workloads.generate("decode", d)
+    say(f"[gpu] full decode x40 dims={d}")
+    r = G.Runner("decode", d, inp)
+    r.forward(); r.plan.check(); torch.cuda.synchronize()
+    first = r.out.clone()
+    outs = []
+    for _ in range(40):
+        r.forward()
+        outs.append(r.out.clone())
+    r.plan.check(); torch.cuda.synchronize()
+    for o in outs:
+        assert torch.equal(o, first)
+    c = r.plan.read_counters()
+    assert np.array_equal(c, 41 * r.plan.barriers().astype(np.int64))

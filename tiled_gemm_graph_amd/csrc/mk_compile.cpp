@@ -161,7 +161,7 @@ struct Compiler {
       // LDS.  192 threads stream the tile, 8 columns each, so the per-CU
       // bandwidth scales with the fraction of them a width keeps busy, and
       // the bytes loaded include the rounding of each thread's rows up to
-      // whole 8-row batches.
+      // whole 4-row batches.
       const double bw_cu = 22e3;   // bytes per microsecond per CU
       const double ovh = 2.5;      // microseconds per instruction
       const int eb = dtype_bytes((mk_dtype)dt);
@@ -181,7 +181,7 @@ struct Compiler {
           const double bytes = (double)kc * wc * eb;
           if (bytes > 512 * 1024.0 || (bytes < 32 * 1024.0 && s > 1)) continue;
           const I64 ncg = wc / 8, kpar = 192 / ncg;
-          const I64 loaded_rows = kpar * cdiv(cdiv(kc, kpar), 8) * 8;
+          const I64 loaded_rows = kpar * cdiv(cdiv(kc, kpar), 4) * 4;   // 4-row batches
           const double active = (double)(kpar * ncg) / 192.0;
           const double loaded = (double)loaded_rows * wc * eb;
           const double cost = (double)cdiv(tiles * s, ncu) * (ovh + loaded / (bw_cu * active));

@@ -36,8 +36,8 @@ constexpr int kBK = 64;                 // GEMM K step
 constexpr int kLdsPad = 8;              // 16-bit elements of row padding
 constexpr int kSmemBytes = 140 * 1024;  // scratch per workgroup
 constexpr int kMaxNodes = 48;           // node descriptors cached in LDS
-constexpr int kGemvBatch = 8;           // 16-byte weight chunks per thread per batch
-constexpr int kGemvBufs = 4;            // weight batches in flight per thread
+constexpr int kGemvBatch = 4;           // 16-byte weight chunks per thread per batch
+constexpr int kGemvBufs = 3;            // weight batches in flight per thread
 
 struct KArgs {
   const mk_instr* instrs;   // [n_iters][ncu]
@@ -496,10 +496,13 @@ __device__ __forceinline__ void gemv_store_packed(const KArgs& a, const mk_node&
       v[0] = x1 * cs - x2 * sn;
       v[1] = x2 * cs + x1 * sn;
     }
+    // Agent-scope stores write through to the device-coherent level, so the
+    // release needs no L2 write-back (release_gemv).
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
       const float y = (flags & MK_EP_RELU) ? fmaxf(v[e], 0.0f) : v[e];
-      O[(long)gr * nd.out.ld + col[e]] = from_f<DT>(y);
+      __hip_atomic_store(O + (long)gr * nd.out.ld + col[e], from_f<DT>(y), __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 }
@@ -1050,36 +1053,40 @@ __device__ __forceinline__ int fetch_ahead(const Loop& L, int it) {
 }
 
 // Start of iteration it.  Wave 0 issues the load of record it + 2 (used at
-// the end of the iteration) while its lane 0 waits on every source counter
-// (relaxed agent-scope polls, then one acquire); all waves then meet at an
-// LDS-only barrier, so the weight waves keep their loads in flight.
+// the end of the iteration) while its lanes wait on the source counters,
+// one counter per lane (relaxed agent-scope polls, then one acquire); all
+// waves then meet at an LDS-only barrier, so the weight waves keep their
+// loads in flight.
 // Returns false (uniformly) if the run was aborted.
 __device__ __forceinline__ bool wait_sources(const Loop& L, const mk_instr& in, int it, int gidx, int& w) {
   const KArgs& a = L.a;
   if (wave_id() == 0) {
     w = fetch_ahead(L, it);
-    if (threadIdx.x == 0) {
-      int ok = 1;
+    // lane k polls source counter k, so the waits overlap
+    const int lane = threadIdx.x;
+    int ok = 1;
+    if (lane < in.n_src) {
+      const int id = in.src_id[lane];
+      const int need = a.epoch * in.src_target[lane];
       const long long t0 = wall_clock64();
-      for (int k = 0; k < in.n_src && ok; ++k) {
-        const int id = in.src_id[k];
-        const int need = a.epoch * in.src_target[k];
-        int v;
-        while ((v = __hip_atomic_load(a.counters + id, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) < need) {
-          if (__hip_atomic_load(a.err + 6, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) { ok = 0; break; }
-          if (wall_clock64() - t0 > a.spin_ticks) {
-            if (atomicCAS(a.err, 0, (int)MK_E_DEADLOCK) == 0) {
-              a.err[1] = L.vcu; a.err[2] = gidx; a.err[3] = id; a.err[4] = v; a.err[5] = need;
-            }
-            __hip_atomic_store(a.err + 6, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            ok = 0;
-            break;
+      int v;
+      while ((v = __hip_atomic_load(a.counters + id, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) < need) {
+        if (__hip_atomic_load(a.err + 6, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) { ok = 0; break; }
+        if (wall_clock64() - t0 > a.spin_ticks) {
+          if (atomicCAS(a.err, 0, (int)MK_E_DEADLOCK) == 0) {
+            a.err[1] = L.vcu; a.err[2] = gidx; a.err[3] = id; a.err[4] = v; a.err[5] = need;
           }
-          __builtin_amdgcn_s_sleep(1);
+          __hip_atomic_store(a.err + 6, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          ok = 0;
+          break;
         }
+        __builtin_amdgcn_s_sleep(1);
       }
-      if (ok && in.n_src) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-      *L.flag = ok;
+    }
+    const int all_ok = __all(ok);
+    if (lane == 0) {
+      if (all_ok && in.n_src) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      *L.flag = all_ok;
     }
   }
   lds_barrier();
@@ -1116,11 +1123,16 @@ __device__ __forceinline__ bool generic_iter(const Loop& L, int it, int& w) {
 }
 
 // Release of a GEMV instruction: only the controller wave stored results.
-__device__ __forceinline__ void release_gemv(const KArgs& a, const mk_instr& in) {
+// A packed tile stored them with agent-scope (write-through) stores, so
+// their completion is enough and the L2 write-back of an agent-scope
+// release fence (about 1.7 us) is skipped; other tiles take the fence.
+__device__ __forceinline__ void release_gemv(const KArgs& a, const mk_instr& in, const mk_node& nd) {
   if (wave_id() != 0) return;
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
   __builtin_amdgcn_s_waitcnt(0);  // wave 0's stores have completed
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
   if (threadIdx.x == 0 && in.n_dst) {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    if (!nd.layout) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     for (int k = 0; k < in.n_dst; ++k)
       __hip_atomic_fetch_add(a.counters + in.dst_id[k], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
@@ -1157,7 +1169,7 @@ __device__ __forceinline__ int gemv_streak(const Loop& L, int& it, int& w) {
     }
     s0 = gemv_body_rows<DT>(a, in, nd, L.smem, B, nx, nxd, s0);
     if (tr) stamp(a, gidx, 2, wall_clock64());
-    release_gemv(a, in);
+    release_gemv(a, in, nd);
     if (tr) stamp(a, gidx, 3, wall_clock64());
     store_ahead(L, it, w);
     ++it;
