@@ -104,11 +104,13 @@ enum {
  * GEMM: bm x bn output tile (bn counts output columns, so a SILU_MUL tile
  * reads 2*bn weight columns), split = K chunks (> 1 adds a REDUCE node over
  * rbm x rbn tiles), dup = copies of each tile (cluster duplicate, host
- * profile only).  gemv selects the small-M streaming body: 1 = tiles of
- * bn columns of the row-major [K, N] weight with K split `split` ways;
- * 2 = packed column tiles: each instruction computes bn output columns
- * over the whole K from a weight tile stored contiguously in the packed
- * layout of mk_plan_weight_layout (no K split, no REDUCE node).
+ * profile only).  gemv = 1 selects the small-M streaming body.  layout
+ * selects how the weight is read: 0 = the compiler's choice, 1 = the
+ * row-major [K, N] tensor, 2 = the packed layout of mk_plan_weight_layout
+ * (GEMV: column tiles of bn outputs over the whole K, no split, no REDUCE
+ * node; GEMM: bm x w tiles of 256 x 128, 128 x 256 or 128 x 128, w = the
+ * tile's weight columns, bn or 2 * bn under SILU_MUL; a K split is
+ * allowed).
  * RMSNORM: rows per instruction.  ATTENTION: bq query rows per instruction.
  * ADD / RELU: er x ec tiles. */
 typedef struct {
@@ -117,6 +119,7 @@ typedef struct {
   int32_t rows;
   int32_t bq;
   int32_t er, ec;
+  int32_t layout;
 } mk_tile;
 
 typedef struct {
@@ -148,11 +151,12 @@ typedef struct {
                            consecutive cooperative launches; should a
                            workgroup not become resident, the bounded waits
                            end the run with MK_E_DEADLOCK instead of a hang */
-  int32_t gemv_pack;    /* 0: GEMVs whose weight is a whole weight tensor
-                           read by no other op, with at least num_cus
-                           8-column tiles, use packed column tiles
-                           (tile.gemv = 2); 1: never; 2: whenever the
-                           weight qualifies, however narrow N is            */
+  int32_t pack;         /* weights read in the packed layout (tile.layout
+                           0 = compiler's choice): a weight qualifies when
+                           it is a whole 2-D weight tensor read by no other
+                           op.  0: GEMMs whenever it qualifies, GEMVs when
+                           it also has at least num_cus 8-column tiles;
+                           1: never; 2: whenever it qualifies               */
 } mk_build_options;
 
 typedef struct {
@@ -208,8 +212,9 @@ typedef struct {
   mk_operand a, b, out, bias, res, gamma, part, aux;
   int64_t part_plane;        /* elements between split-K planes of part     */
   int32_t tile_m, tile_n;    /* GEMM kernel tile: rows x weight columns     */
-  int32_t layout;            /* GEMV weight: 0 row-major [K, Nb]; 1 packed
-                                column tiles [tiles][K][tile_n]            */
+  int32_t layout;            /* weight: 0 row-major [K, Nb]; 1 packed GEMV
+                                column tiles [tiles][K][tile_n]; 2 packed
+                                GEMM tiles [tiles][K/64][tile_n][64]       */
   int32_t reserved[MK_NODE_WORDS - 20 - 8 * 4 - 2 - 2 - 1];
 } mk_node;
 
@@ -290,7 +295,7 @@ mk_status mk_plan_op_tile(const mk_plan *p, int32_t op, mk_tile *out);
  * packed column tiles and every run takes, in buffers[tensor], a device
  * buffer of *bytes bytes filled by mk_plan_pack_weight.
  *
- * Packed layout (bn = the op's tile.bn output columns per tile, T =
+ * GEMV packed layout (bn = the op's tile.bn output columns per tile, T =
  * ceil(N / bn) tiles, w = bn, or 2 * bn under SILU_MUL): element
  * [t][k][j] of a [T][K][w] array holds W[k][col(t * bn + j)] for j < bn
  * and, under SILU_MUL, W[k][N + col(t * bn + j - bn)] for j >= bn; entries
@@ -299,9 +304,19 @@ mk_status mk_plan_op_tile(const mk_plan *p, int32_t op, mk_tile *out);
  * [0, rope_cols) are interleaved in rotation pairs: position p of head
  * h = p / head_dim, i = (p % head_dim) / 2 maps to column
  * h * head_dim + i + (p % 2) * head_dim / 2, so each tile holds both
- * columns of every rotation pair it touches.  The layout is this
- * library's own: it makes each instruction's weight tile one contiguous
- * stream, which a row-major weight cut into narrow column tiles is not. */
+ * columns of every rotation pair it touches.
+ *
+ * GEMM packed layout (w = weight columns per tile = tile.bn, or 2 * tile.bn
+ * under SILU_MUL; T = ceil(N / tile.bn) tiles): element [t][kt][j][kk] of
+ * a [T][K/64][w][64] array holds W[64 kt + kk][col], col = t * w + j;
+ * under SILU_MUL each half of a tile (h = j / (w/2), q = j % (w/2)) holds
+ * the gate columns, then the up columns, of the same w/4 outputs
+ * o = t * w/2 + h * w/4 + q % (w/4): col = o for q < w/4, else N + o.
+ * Columns whose output reaches N are zero.
+ *
+ * Both layouts are this library's own: they make each instruction's
+ * weight tile (per K step for GEMM) one contiguous stream with every
+ * weight column's K values together. */
 mk_status mk_plan_weight_layout(const mk_plan *p, int32_t tensor, int32_t *packed,
                                 int64_t *bytes);
 /* Fill the packed buffer dst (device, mk_plan_weight_layout bytes) from the

@@ -29,8 +29,16 @@ Lowering and tiling spec (the compiler implements the same rules):
   out [M, N]; A view [M, K]; B view [K, Nb] with Nb = 2N under SILU_MUL
   (gate columns first) else N.  K is cut into S chunks of
   Kc = roundup(ceil(K/S), 64) rows (every chunk must be non-empty).
-  Tiles run row-major over (tm, tn), chunk index s fastest, each tile
-  repeated ``dup`` times (the CTA-pair duplicate of section 04).
+  Tiles run in groups, chunk index s fastest, each tile repeated ``dup``
+  times (the CTA-pair duplicate of section 04).  GEMM-body nodes cut the
+  TM x TN tile grid into groups of gm = min(TM, 4) rows by
+  gn = min(TN, max(1, B // (gm * S))) columns, B = ncu // 8 when ncu is a
+  multiple of 8, else 32; groups are taken row by row and the tiles of a
+  group row by row (one group is one XCD's share of a wave: the persistent
+  kernel deals its workgroups to the 8 XCDs in blocks of B).  GEMV-body
+  nodes run row-major over (tm, tn).  Placement: a GEMM-body node with at
+  least ncu instructions starts on a multiple of ncu // 8 (when ncu is a
+  multiple of 8), the gap before it being Noops.
   S == 1: one node (opcode GEMV if gemv else GEMM) with the op's flags.
   S > 1: a partial node (opcode GEMV/GEMM, flags PARTIAL | the op's
   SILU_MUL and RMSNORM_INPUT bits) writing fp32 partials P [S, M, Nb],
@@ -40,7 +48,8 @@ Lowering and tiling spec (the compiler implements the same rules):
   rows x cols (S == 1 only).  REDUCE reads P [0, S) x rows x cols (and N +
   cols), bias / residual rows x cols, and under RMSNORM_INPUT the A rows
   over the full K (for the row's sum of squares).
-  gemv == 2 (packed column tiles): one GEMV node, no split, no REDUCE;
+  gemv == 1 with layout == 2 (packed column tiles): one GEMV node, no
+  split, no REDUCE;
   tiles (tm, tn) row-major over bm rows x bn output *positions*; each
   instruction covers the whole K.  Position p is output column p, except
   under ROPE for p < rope_cols (default N), where p of head h = p // hd,
@@ -181,13 +190,13 @@ def _chunks(K: int, S: int) -> List[Tuple[int, int]]:
     return ch
 
 
-def lower(g: Graph) -> List[Node]:
+def lower(g: Graph, ncu: int = 256) -> List[Node]:
     """Lower graph ops to nodes with their instruction boxes (tiling spec in
     the module docstring).  May append partial-sum tensors to ``g``."""
     nodes: List[Node] = []
     for oi, op in enumerate(g.ops):
         if op.kind == "gemm":
-            nodes.extend(_lower_gemm(g, oi, op))
+            nodes.extend(_lower_gemm(g, oi, op, ncu))
         elif op.kind == "rmsnorm":
             x, gm = op.ins["x"], op.ins["gamma"]
             M, H = x.rows, x.cols
@@ -292,8 +301,25 @@ def _lower_packed_gemv(g: Graph, oi: int, op: Op) -> List[Node]:
     return [Node(oi, GEMV, fl, op.out, edges, ins)]
 
 
-def _lower_gemm(g: Graph, oi: int, op: Op) -> List[Node]:
-    if op.tile.get("gemv", 0) == 2:
+def _grouped_tiles(TM: int, TN: int, S: int, ncu: int) -> List[Tuple[int, int]]:
+    """GEMM tile order: the tile grid cut into gm x gn groups, groups taken
+    row by row, tiles row by row inside each group."""
+    if TM == 0 or TN == 0:
+        return []
+    B = ncu // 8 if ncu % 8 == 0 else 32
+    gm = min(TM, 4)
+    gn = min(TN, max(1, B // (gm * S)))
+    order = []
+    for gi in range(_cdiv(TM, gm)):
+        for gj in range(_cdiv(TN, gn)):
+            rows = [tm for tm in range(TM) if tm // gm == gi]
+            cols = [tn for tn in range(TN) if tn // gn == gj]
+            order += [(tm, tn) for tm in rows for tn in cols]
+    return order
+
+
+def _lower_gemm(g: Graph, oi: int, op: Op, ncu: int = 256) -> List[Node]:
+    if op.tile.get("gemv", 0) and op.tile.get("layout", 0) == 2:
         return _lower_packed_gemv(g, oi, op)
     A, B = op.ins["a"], op.ins["b"]
     M, K = A.rows, A.cols
@@ -315,8 +341,13 @@ def _lower_gemm(g: Graph, oi: int, op: Op) -> List[Node]:
                       "intermediate")
         P = g.full(pt)
     ins = []
-    for tm in range(_cdiv(M, bm)):
-        for tn in range(_cdiv(N, bn)):
+    TM, TN = _cdiv(M, bm), _cdiv(N, bn)
+    if opcode == GEMM:
+        tiles = _grouped_tiles(TM, TN, S, ncu)
+    else:
+        tiles = [(tm, tn) for tm in range(TM) for tn in range(TN)]
+    for tm, tn in tiles:
+        if True:
             r0, r1 = tm * bm, min(M, tm * bm + bm)
             c0, c1 = tn * bn, min(N, tn * bn + bn)
             for s, (k0, k1) in enumerate(chunks):
@@ -400,10 +431,12 @@ def schedule(g: Graph, ncu: int, cluster_size: int = 1, reuse: int = 0) -> Sched
     """Derive the full schedule.  ``reuse``: 0 = no pooling, 1 = pool
     intermediates, 2 = pool intermediates and let graph outputs take pooled
     slots (the dispatcher-owned outputs of MegaKittens Internals, sec. 07)."""
-    nodes = lower(g)
+    nodes = lower(g, ncu)
     # phase 1: count and place
     pos = 0
     for n in nodes:
+        if n.opcode == GEMM and ncu % 8 == 0 and len(n.instrs) >= ncu:
+            pos = _cdiv(pos, ncu // 8) * (ncu // 8)
         n.start = pos
         pos += _cdiv(len(n.instrs), cluster_size) * cluster_size
         n.end = pos

@@ -41,7 +41,7 @@ def test_pack_kernel_matches_layout():
     inp = workloads.generate("decode", d)
     say(f"[gpu] pack layout decode dims={d}")
     g = G.build("decode", d)
-    plan = g.build(gemv_pack=2)
+    plan = g.build(pack=2)
     for name in ("Wqkv", "Wgu", "Wd"):
         oi = {"Wqkv": 0, "Wo": 1, "Wgu": 2, "Wd": 3}[name]
         t = plan.op_tile(oi)
@@ -63,8 +63,8 @@ def test_pack_kernel_matches_layout():
 def test_forced_packed_decode_parity(dims):
     inp = workloads.generate("decode", dims)
     say(f"[gpu] packed decode dims={dims}")
-    r = G.Runner("decode", dims, inp, gemv_pack=2)
-    assert [t["gemv"] for t in r.plan.op_tiles()] == [2, 2, 2, 2]
+    r = G.Runner("decode", dims, inp, pack=2)
+    assert [t["layout"] for t in r.plan.op_tiles()] == [2, 2, 2, 2]
     r.forward(); r.forward(); r.plan.check(); torch.cuda.synchronize()
     ref = OG.decode(inp, dims)
     got = to_np(r.out)
@@ -84,8 +84,8 @@ def test_full_decode_packed_matches_row_major_path():
     inp = workloads.generate("decode", d)
     say(f"[gpu] full decode packed vs row-major split-K dims={d}")
     rp = G.Runner("decode", d, inp)
-    assert [t["gemv"] for t in rp.plan.op_tiles()] == [2, 2, 2, 2]
-    rr = G.Runner("decode", d, inp, gemv_pack=1)
+    assert [t["layout"] for t in rp.plan.op_tiles()] == [2, 2, 2, 2]
+    rr = G.Runner("decode", d, inp, pack=1)
     rp.forward(); rp.plan.check()
     rr.forward(); rr.plan.check()
     torch.cuda.synchronize()
@@ -109,7 +109,7 @@ def _rope_reference(x, W, b, res, hd, rope_cols):
 def test_rope_bias_residual_epilogue(mode):
     M = 64 if mode == "gemm" else 3
     K, N, hd, rc = 256, 384, 64, 256
-    tile = {"packed": dict(gemv=2), "split": dict(gemv=1, bn=128, split=2, rbn=128),
+    tile = {"packed": dict(gemv=1, layout=2), "split": dict(gemv=1, bn=128, split=2, rbn=128),
             "gemm": dict(gemv=0, bm=64, bn=128)}[mode]
     say(f"[gpu] rope+bias+residual mode={mode} M={M} K={K} N={N} hd={hd} rope_cols={rc}")
     g, _, _ = rope_graph(M, K, N, hd, rc, tile=tile)

@@ -14,7 +14,7 @@ def test_decode_weights_are_packed_with_documented_sizes():
     d = workloads.default_dims("decode")
     plan = G.build("decode", d).build()
     tiles = plan.op_tiles()
-    assert [t["gemv"] for t in tiles] == [2, 2, 2, 2]
+    assert [(t["gemv"], t["layout"]) for t in tiles] == [(1, 2)] * 4
     H, nqkv, I = d["hidden"], d["n_q"] + 2 * d["n_kv"], d["inter"]
     # [tiles][K][w] elements of 2 bytes; w = bn, or 2 * bn with SILU_MUL
     expect = {"Wqkv": (H, nqkv, tiles[0]["bn"], 1), "Wo": (d["n_q"], H, tiles[1]["bn"], 1),
@@ -33,14 +33,14 @@ def test_decode_weights_are_packed_with_documented_sizes():
 
 def test_gemv_pack_option():
     d = workloads.default_dims("decode")
-    plan = G.build("decode", d).build(gemv_pack=1)
-    assert [t["gemv"] for t in plan.op_tiles()] == [1, 1, 1, 1]
+    plan = G.build("decode", d).build(pack=1)
+    assert [(t["gemv"], t["layout"]) for t in plan.op_tiles()] == [(1, 1)] * 4
     assert plan.packed_weights() == []
     small = workloads.small_dims("decode")
-    assert [t["gemv"] for t in G.build("decode", small).build().op_tiles()] == [1, 1, 1, 1]
-    assert [t["gemv"] for t in G.build("decode", small).build(gemv_pack=2).op_tiles()] == [2] * 4
+    assert [t["layout"] for t in G.build("decode", small).build().op_tiles()] == [1] * 4
+    assert [t["layout"] for t in G.build("decode", small).build(pack=2).op_tiles()] == [2] * 4
     with pytest.raises(L.MkError):
-        G.build("decode", small).build(gemv_pack=3)
+        G.build("decode", small).build(pack=3)
 
 
 def test_packed_rejects_views_and_shared_weights():
@@ -48,7 +48,7 @@ def test_packed_rejects_views_and_shared_weights():
     x = g.tensor("x", "bf16", (1, 64), "input")
     w = g.tensor("w", "bf16", (64, 128), "weight")
     y = g.tensor("y", "bf16", (1, 64), "output")
-    g.gemm(x, g.cols(w, 0, 64), y, tile=dict(gemv=2))
+    g.gemm(x, g.cols(w, 0, 64), y, tile=dict(gemv=1, layout=2))
     with pytest.raises(L.MkError):
         g.build()
     g = Graph()
@@ -58,8 +58,8 @@ def test_packed_rejects_views_and_shared_weights():
     z = g.tensor("z", "bf16", (1, 64), "output")
     g.gemm(x, w, y)
     g.gemm(y, w, z)
-    plan = g.build(gemv_pack=2)
-    assert [t["gemv"] for t in plan.op_tiles()] == [1, 1]   # w is read by two ops
+    plan = g.build(pack=2)
+    assert [t["layout"] for t in plan.op_tiles()] == [1, 1]   # w is read by two ops
 
 
 def _compare(wl, dims, ncu, **opts):
@@ -77,7 +77,7 @@ def _compare(wl, dims, ncu, **opts):
 
 @pytest.mark.parametrize("ncu", [16, 256])
 def test_forced_packed_decode_lists_match_oracle(ncu):
-    _compare("decode", workloads.small_dims("decode"), ncu, gemv_pack=2)
+    _compare("decode", workloads.small_dims("decode"), ncu, pack=2)
 
 
 def rope_graph(M, K, N, hd, rope_cols, tile=None):
@@ -110,9 +110,9 @@ def rope_graph(M, K, N, hd, rope_cols, tile=None):
 def test_packed_rope_lists_match_oracle(ncu):
     M, K, N, hd, rc = 2, 256, 384, 64, 256
     g, og, (ox, oW, ob, orr, oW2, oy, oz) = rope_graph(M, K, N, hd, rc)
-    plan = g.build(num_cus=ncu, gemv_pack=2)
+    plan = g.build(num_cus=ncu, pack=2)
     t0, t1 = _oracle_tiles(plan.op_tiles())
-    assert t0["gemv"] == 2 and t0["bn"] % hd != 0     # tiles cut across heads
+    assert t0["layout"] == 2 and t0["bn"] % hd != 0     # tiles cut across heads
     og.ops.append(S.Op("gemm", dict(a=og.full(ox), b=og.full(oW), bias=og.full(ob),
                                     residual=og.full(orr)), oy,
                        S.BIAS | S.RESIDUAL | S.ROPE, t0, dict(head_dim=hd, rope_cols=rc)))

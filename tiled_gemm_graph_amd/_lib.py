@@ -41,7 +41,8 @@ class MkError(RuntimeError):
 
 class Tile(Structure):
     _fields_ = [(n, c_int32) for n in
-                ("bm", "bn", "split", "dup", "gemv", "rbm", "rbn", "rows", "bq", "er", "ec")]
+                ("bm", "bn", "split", "dup", "gemv", "rbm", "rbn", "rows", "bq", "er", "ec",
+                 "layout")]
 
     def as_dict(self):
         return {n: getattr(self, n) for n, _ in self._fields_}
@@ -56,7 +57,7 @@ class OpAttrs(Structure):
 class BuildOptions(Structure):
     _fields_ = [("num_cus", c_int32), ("cluster_size", c_int32), ("reuse", c_int32),
                 ("gemv_max_m", c_int32), ("spin_limit_us", c_int64),
-                ("cooperative", c_int32), ("gemv_pack", c_int32)]
+                ("cooperative", c_int32), ("pack", c_int32)]
 
 
 class PlanStats(Structure):

@@ -130,28 +130,30 @@ struct Compiler {
                            bool packable) {
     mk_tile t = op.attrs.tile;
     if (t.dup <= 0) t.dup = 1;
-    if (t.gemv < 0) t.gemv = 0;
-    bool explicit_gemv = op.attrs.tile.gemv != 0 || op.attrs.tile.bm != 0;
-    if (!explicit_gemv && M <= p.opts.gemv_max_m) {
-      t.gemv = 1;
-      // Packed column tiles need no K split and no REDUCE node; they pay
-      // when there are enough 8-column tiles to give every CU one.
-      const bool wide = cdiv(N, 8) >= ncu;
-      if (packable && t.split <= 1 && (p.opts.gemv_pack == 2 || (p.opts.gemv_pack == 0 && wide)))
-        t.gemv = 2;
-    }
-    if (t.gemv == 2) {
-      if (!packable)
-        fail(MK_E_INVALID, "packed GEMV tiles need a whole 2-D weight tensor read by no other op");
-      if (t.split > 1) fail(MK_E_INVALID, "packed GEMV tiles take no K split");
-      if (t.bm <= 0) t.bm = (int)std::max<I64>(M, 1);
-      if (t.bn <= 0) t.bn = (int)std::max<I64>(8, cdiv(cdiv(N, ncu), 8) * 8);
-      t.split = 1;
-      if (t.rbm <= 0) t.rbm = t.bm;
-      if (t.rbn <= 0) t.rbn = t.bn;
-      return t;
-    }
+    if (t.gemv < 0 || t.gemv > 1) fail(MK_E_INVALID, "tile.gemv must be 0 or 1");
+    if (t.layout < 0 || t.layout > 2) fail(MK_E_INVALID, "tile.layout must be 0, 1 or 2");
+    if (t.layout == 2 && !packable)
+      fail(MK_E_INVALID, "a packed weight must be a whole 2-D weight tensor read by no other op");
+    const bool explicit_gemv = op.attrs.tile.gemv != 0 || op.attrs.tile.bm != 0;
+    if (!explicit_gemv && M <= p.opts.gemv_max_m) t.gemv = 1;
+    const bool rope = op.attrs.epilogue & MK_EP_ROPE;
+    const I64 hd = op.attrs.head_dim > 0 ? op.attrs.head_dim : 1;
     if (t.gemv) {
+      if (t.layout == 0) {
+        // Packed column tiles need no K split and no REDUCE node; they pay
+        // when there are enough 8-column tiles to give every CU one.
+        const bool wide = cdiv(N, 8) >= ncu;
+        t.layout = (packable && t.split <= 1 && (p.opts.pack == 2 || (p.opts.pack == 0 && wide))) ? 2 : 1;
+      }
+      if (t.layout == 2) {
+        if (t.split > 1) fail(MK_E_INVALID, "packed GEMV tiles take no K split");
+        if (t.bm <= 0) t.bm = (int)std::max<I64>(M, 1);
+        if (t.bn <= 0) t.bn = (int)std::max<I64>(8, cdiv(cdiv(N, ncu), 8) * 8);
+        t.split = 1;
+        if (t.rbm <= 0) t.rbm = t.bm;
+        if (t.rbn <= 0) t.rbn = t.bn;
+        return t;
+      }
       if (t.bm <= 0) t.bm = (int)std::max<I64>(M, 1);
       const I64 rows = std::min<I64>(std::max<I64>(M, 1), t.bm);
       // Streaming GEMV: pick the weight-tile width and the K split that
@@ -196,30 +198,77 @@ struct Compiler {
       if (t.split <= 0) t.split = best_s;
       if (t.rbm <= 0) t.rbm = t.bm;
       if (t.rbn <= 0) t.rbn = 256;
-    } else {
-      if (t.bm <= 0 || t.bn <= 0) {
-        // Largest kernel tile that still fills one wave of CUs.
-        // Rotary tiles must hold whole heads.
-        const int cand[3][2] = {{128, 128}, {64, 128}, {64, 64}};
-        const bool rope = op.attrs.epilogue & MK_EP_ROPE;
-        const int hd = op.attrs.head_dim > 0 ? op.attrs.head_dim : 1;
-        int pick = rope ? 1 : 2;
-        for (int c = 0; c < 3; ++c) {
-          int bnk = cand[c][1];
-          int bn = silu ? bnk / 2 : bnk;
-          if (rope && bn % hd) continue;
-          if (cdiv(M, cand[c][0]) * cdiv(N, bn) >= ncu) {
-            pick = c;
-            break;
+      return t;
+    }
+    // GEMM body.  Packed weights take the LDS-streamed body with 128/256
+    // tiles; the row-major body keeps 64/128 tiles.
+    if (t.layout == 0) {
+      const int wbn = t.bn * (silu ? 2 : 1);
+      const bool shape_ok = (t.bm == 0 || t.bm == 128 || t.bm == 256) && (t.bn == 0 || wbn == 128 || wbn == 256);
+      t.layout = (packable && p.opts.pack != 1 && shape_ok && K % 64 == 0 && (!rope || hd == 64 || hd == 128))
+                     ? 2 : 1;
+    }
+    if (t.layout == 2) {
+      // Makespan estimate over tile shapes and K splits: waves of CUs times
+      // the tile's MFMA time at an efficiency that grows with the tile (its
+      // flops per byte staged), plus a per-instruction overhead, plus the
+      // fp32 partial traffic and the REDUCE hop of a split.
+      struct Cand { int bm, bn; double eff; };
+      // (256 x 256 would need all 256 accumulator registers of a wave, more
+      // than the persistent kernel can spare beside its other bodies.)
+      const Cand cands[] = {{256, 128, 0.62}, {128, 256, 0.62}, {128, 128, 0.45}};
+      const double peak_cu = 2.5e15 / 256.0 / 1e6;   // flops per microsecond per CU
+      double best = 1e300;
+      int bbm = 0, bbn = 0, bs = 1;
+      for (const Cand& c : cands) {
+        if (t.bm > 0 && c.bm != t.bm) continue;
+        if (t.bn > 0 && c.bn != t.bn * (silu ? 2 : 1)) continue;
+        if (rope && (c.bn / 2) % hd) continue;
+        const I64 bn_out = silu ? c.bn / 2 : c.bn;
+        const I64 tiles = cdiv(std::max<I64>(M, 1), c.bm) * cdiv(N, bn_out);
+        for (I64 sp = 1; sp <= 16; ++sp) {
+          if (t.split > 0 && sp != t.split) continue;
+          if (!chunks_ok(K, sp)) continue;
+          const I64 kc = std::min<I64>(K, cdiv(cdiv(K, sp), 64) * 64);
+          const double t_inst = 2.0 * c.bm * c.bn * kc / (peak_cu * c.eff) + 2.0;
+          double cost = (double)cdiv(tiles * sp, ncu) * t_inst;
+          if (sp > 1) cost += 8.0 * sp * M * (silu ? 2 * N : N) / 5e6 + 6.0;
+          if (cost < best * (1 - 1e-9)) {
+            best = cost;
+            bbm = c.bm;
+            bbn = c.bn;
+            bs = (int)sp;
           }
         }
-        if (t.bm <= 0) t.bm = cand[pick][0];
-        if (t.bn <= 0) t.bn = silu ? cand[pick][1] / 2 : cand[pick][1];
       }
-      if (t.split <= 0) t.split = 1;
+      if (bbm == 0) fail(MK_E_INVALID, "no packed GEMM tile fits these tile parameters");
+      t.bm = bbm;
+      t.bn = silu ? bbn / 2 : bbn;   // tile.bn counts output columns
+      t.split = bs;
       if (t.rbm <= 0) t.rbm = t.bm;
       if (t.rbn <= 0) t.rbn = t.bn;
+      return t;
     }
+    if (t.bm <= 0 || t.bn <= 0) {
+      // Largest kernel tile that still fills one wave of CUs.
+      // Rotary tiles must hold whole heads.
+      const int cand[3][2] = {{128, 128}, {64, 128}, {64, 64}};
+      int pick = rope ? 1 : 2;
+      for (int c = 0; c < 3; ++c) {
+        int bnk = cand[c][1];
+        int bn = silu ? bnk / 2 : bnk;
+        if (rope && bn % hd) continue;
+        if (cdiv(M, cand[c][0]) * cdiv(N, bn) >= ncu) {
+          pick = c;
+          break;
+        }
+      }
+      if (t.bm <= 0) t.bm = cand[pick][0];
+      if (t.bn <= 0) t.bn = silu ? cand[pick][1] / 2 : cand[pick][1];
+    }
+    if (t.split <= 0) t.split = 1;
+    if (t.rbm <= 0) t.rbm = t.bm;
+    if (t.rbn <= 0) t.rbn = t.bn;
     return t;
   }
 
@@ -283,7 +332,8 @@ struct Compiler {
     int S = t.split;
     auto chunks = k_chunks(std::max<I64>(K, 1), S);
     bool gemv = t.gemv != 0;
-    const bool packed = t.gemv == 2;
+    const bool packed = gemv && t.layout == 2;       // GEMV column tiles
+    const bool packed_gemm = !gemv && t.layout == 2;  // GEMM K tiles
     int opcode = gemv ? MK_I_GEMV : MK_I_GEMM;
     // kernel support
     if (dt != MK_F16 && dt != MK_BF16) unsup("GEMM dtype must be fp16 or bf16");
@@ -300,6 +350,19 @@ struct Compiler {
           unsup("GEMV activation chunk exceeds 16384 elements (one row) or 8192 (more rows)");
       }
       if (packed && (t.bn % 8 || t.dup != 1)) unsup("packed GEMV tiles are multiples of 8 columns");
+    } else if (packed_gemm) {
+      int bnk = t.bn * (silu ? 2 : 1);
+      if (!((t.bm == 128 || t.bm == 256) && (bnk == 128 || bnk == 256)) || (t.bm == 256 && bnk == 256))
+        unsup("packed GEMM tiles are 256 x 128, 128 x 256 or 128 x 128 (rows x weight columns)");
+      if (K % 64) unsup("GEMM K must be a multiple of 64");
+      if (A.lo[3] % 8 || T[A.tensor].shape[3] % 8) unsup("packed GEMM A rows must be 16-byte aligned");
+      if (fl & MK_EP_RMSNORM_INPUT) unsup("RMSNORM_INPUT needs the GEMV body");
+      if (t.dup != 1) unsup("duplicated tiles are a host profile only");
+      if ((fl & MK_EP_ROPE) && S == 1) {
+        const int hd = op.attrs.head_dim;
+        if ((hd != 64 && hd != 128) || (bnk / 2) % hd)
+          unsup("ROPE on a packed GEMM tile needs head_dim 64 or 128 within half a tile");
+      }
     } else {
       int bnk = t.bn * (silu ? 2 : 1);
       if (!((t.bm == 64 || t.bm == 128) && (bnk == 64 || bnk == 128)))
@@ -314,11 +377,11 @@ struct Compiler {
       if (hd <= 0 || hd % 2 || hd > 256) fail(MK_E_INVALID, "ROPE needs an even head_dim <= 256");
       if (rc % hd || rc > N) fail(MK_E_INVALID, "rope_cols must be a multiple of head_dim <= N");
       int tbn = S > 1 ? t.rbn : t.bn;
-      if (!packed && tbn % hd) unsup("ROPE tiles must hold whole heads");
+      if (!packed && !(packed_gemm && S == 1) && tbn % hd) unsup("ROPE tiles must hold whole heads");
       if (hd % 16) unsup("ROPE head_dim must be a multiple of 16");
       if (silu) fail(MK_E_INVALID, "ROPE and SILU_MUL cannot be combined");
     }
-    if (t.gemv == 1 && S == 1 && (fl & MK_EP_ROPE)) unsup("ROPE on the row-major GEMV body needs a split");
+    if (gemv && !packed && S == 1 && (fl & MK_EP_ROPE)) unsup("ROPE on the row-major GEMV body needs a split");
     int pt = -1;
     if (S > 1) pt = add_internal(MK_F32, {1, S, M, Nb});
     int rope_t = -1;
@@ -343,8 +406,9 @@ struct Compiler {
     Edge P;
     if (S > 1) P = edge_of(p.tensors, pt);
     const I64 rope_cols = (fl & MK_EP_ROPE) ? (op.attrs.rope_cols ? op.attrs.rope_cols : N) : 0;
-    for (I64 tm = 0; tm < cdiv(M, t.bm); ++tm)
-      for (I64 tn = 0; tn < cdiv(N, t.bn); ++tn) {
+    for (const auto& tile_rc : tile_order(cdiv(M, t.bm), cdiv(N, t.bn), S, !gemv)) {
+      {
+        const I64 tm = tile_rc.first, tn = tile_rc.second;
         I64 r0 = tm * t.bm, r1 = std::min(M, r0 + t.bm);
         I64 c0 = tn * t.bn, c1 = std::min(N, c0 + t.bn);
         for (int s = 0; s < S; ++s) {
@@ -391,6 +455,7 @@ struct Compiler {
           }
         }
       }
+    }
     // node descriptor (slots filled later)
     mk_node& d = n.desc;
     d.opcode = opcode;
@@ -404,7 +469,21 @@ struct Compiler {
     d.part_plane = M * Nb;
     d.tile_m = t.bm;
     d.tile_n = t.bn * (silu ? 2 : 1);
-    d.layout = packed ? 1 : 0;
+    d.layout = packed ? 1 : packed_gemm ? 2 : 0;
+    if (packed_gemm) {
+      PackInfo pk;
+      pk.kind = 2;
+      pk.tensor = B.tensor;
+      pk.K = K;
+      pk.N = N;
+      pk.bn = d.tile_n;
+      pk.wc = d.tile_n;
+      pk.tiles = cdiv(N, t.bn);
+      pk.silu = silu;
+      pk.dt = dt;
+      pk.bytes = pk.tiles * K * pk.wc * dtype_bytes(dt);
+      p.packs.push_back(pk);
+    }
     if (packed) {
       PackInfo pk;
       pk.tensor = B.tensor;
@@ -462,6 +541,32 @@ struct Compiler {
                             {"aux", rope_t >= 0 ? edge_of(p.tensors, rope_t) : Edge{}}});
     }
     return t;
+  }
+
+  // Tile order of a GEMM node: groups of gm x gn tiles (gm = min(TM, 4),
+  // gn = min(TN, max(1, B / (gm * S))), B = num_cus / 8 when num_cus is a
+  // multiple of 8, else 32), groups row-major over the group grid, tiles
+  // row-major inside a group.  With workgroups dealt to the 8 XCDs in blocks
+  // of B consecutive instructions, one group is one XCD's share of a wave,
+  // and its A row panels and B column panels are shared in that XCD's L2.
+  // Other nodes (grouped = false) run row-major.
+  std::vector<std::pair<I64, I64>> tile_order(I64 TM, I64 TN, I64 S, bool grouped) const {
+    std::vector<std::pair<I64, I64>> v;
+    if (TM <= 0 || TN <= 0) return v;
+    v.reserve(TM * TN);
+    if (!grouped) {
+      for (I64 tm = 0; tm < TM; ++tm)
+        for (I64 tn = 0; tn < TN; ++tn) v.push_back({tm, tn});
+      return v;
+    }
+    const I64 B = ncu % 8 == 0 ? ncu / 8 : 32;
+    const I64 gm = std::min<I64>(TM, 4);
+    const I64 gn = std::min<I64>(TN, std::max<I64>(1, B / (gm * S)));
+    for (I64 g0 = 0; g0 < TM; g0 += gm)
+      for (I64 h0 = 0; h0 < TN; h0 += gn)
+        for (I64 tm = g0; tm < std::min(TM, g0 + gm); ++tm)
+          for (I64 tn = h0; tn < std::min(TN, h0 + gn); ++tn) v.push_back({tm, tn});
+    return v;
   }
 
   mk_tile lower_rmsnorm(int oi, const OpRec& op) {
@@ -606,6 +711,11 @@ struct Compiler {
     int cs = p.opts.cluster_size;
     I64 pos = 0;
     for (auto& n : p.nodes) {
+      // a GEMM node of at least num_cus instructions starts on an XCD block
+      // boundary (num_cus / 8 instructions), so its tile groups line up with
+      // the XCDs; the gap is Noops
+      if (n.opcode == MK_I_GEMM && ncu % 8 == 0 && (I64)n.ins.size() >= ncu)
+        pos = cdiv(pos, ncu / 8) * (ncu / 8);
       n.start = (int)pos;
       pos += cdiv((I64)n.ins.size(), cs) * cs;
       n.end = (int)pos;
@@ -1078,7 +1188,7 @@ mk_status megakernel_build(const mk_graph* g, const mk_build_options* opts, mk_p
   if (p->opts.gemv_max_m <= 0) p->opts.gemv_max_m = 8;
   if (p->opts.spin_limit_us <= 0) p->opts.spin_limit_us = 2000000;
   if (p->opts.reuse < 0 || p->opts.reuse > 2) { delete p; set_error("reuse must be 0, 1 or 2"); return MK_E_INVALID; }
-  if (p->opts.gemv_pack < 0 || p->opts.gemv_pack > 2) { delete p; set_error("gemv_pack must be 0, 1 or 2"); return MK_E_INVALID; }
+  if (p->opts.pack < 0 || p->opts.pack > 2) { delete p; set_error("pack must be 0, 1 or 2"); return MK_E_INVALID; }
   bool has_out = false;
   for (const OpRec& op : g->ops) has_out |= g->t[op.out].role == MK_OUTPUT;
   if (!g->ops.empty() && !has_out) { delete p; set_error("graph has no OUTPUT tensor"); return MK_E_INVALID; }

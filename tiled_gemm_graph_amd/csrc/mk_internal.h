@@ -76,10 +76,11 @@ struct Node {
 
 // A weight tensor that a GEMV reads as packed column tiles.
 struct PackInfo {
+  int kind = 1;      // 1: GEMV column tiles [T][K][wc]; 2: GEMM tiles [T][K/64][bn][64]
   int tensor = -1;
   I64 K = 0, N = 0;
-  int bn = 0;        // output positions per tile
-  int wc = 0;        // packed row width: bn, or 2 * bn under SILU_MUL
+  int bn = 0;        // GEMV: output positions per tile; GEMM: weight columns per tile
+  int wc = 0;        // GEMV: packed row width (bn, or 2 * bn under SILU_MUL); GEMM: bn
   I64 tiles = 0;
   bool silu = false;
   int head_dim = 0;  // > 0: positions [0, rope_cols) interleave rotation pairs

@@ -34,7 +34,7 @@ namespace mkd {
 constexpr int kThreads = 256;
 constexpr int kBK = 64;                 // GEMM K step
 constexpr int kLdsPad = 8;              // 16-bit elements of row padding
-constexpr int kSmemBytes = 140 * 1024;  // scratch per workgroup
+constexpr int kSmemBytes = 144 * 1024;   // dynamic tile arena (LDS); 160 KB per CU in all
 constexpr int kMaxNodes = 48;           // node descriptors cached in LDS
 constexpr int kGemvBatch = 4;           // 16-byte weight chunks per thread per batch
 constexpr int kGemvBufs = 3;            // weight batches in flight per thread
@@ -354,6 +354,256 @@ __device__ __forceinline__ void gemm_tile(const KArgs& a, const mk_instr& in, co
 #pragma unroll
       for (int e = 0; e < 8; ++e) o[e] = s[e];
     });
+  }
+}
+
+// ----------------------------------------------------- GEMM, packed weight
+// C[BM x BN] = A[r0:r0+BM, k0:k1] @ B-tile, with B read from the packed
+// layout [T][K/64][BN][64]: for every 64-deep K step, each of the tile's BN
+// weight columns holds its 64 k values contiguously, so A rows and B
+// columns load the same way.  Both stream into LDS with direct
+// global-to-LDS 16-byte loads (no registers), in a ring of ST stages of
+// 64-deep K slices (as many as the arena holds, at most 4), so the loads of
+// a K step are issued ST - 1 steps before it is used.  An LDS row is 128 bytes (8 chunks of 8 k values); chunk c of row
+// r sits at c ^ ((r >> 1) & 7), so the 32 rows an MFMA operand read touches
+// spread over all banks.  The swizzle is applied on the global side: lane L
+// of a load fills LDS byte L * 16 of its 1 KB block and fetches the chunk
+// that belongs there.
+//
+// Four waves in 2 x 2, each WM x WN = BM/2 x BN/2 of v_mfma_f32_32x32x16
+// tiles.  The epilogue runs from the accumulators: the packing puts the
+// gate and up columns of one output (SILU_MUL) WN/2 columns apart inside a
+// wave's half, and a rotary partner is head_dim/2 columns away in the same
+// wave, so both partners of every pair are in the same lane.
+// s_waitcnt with vmcnt(N) only (expcnt and lgkmcnt left alone).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N <= 63, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0f70);
+}
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef const __attribute__((address_space(1))) void gbl_void_t;
+
+__device__ __forceinline__ void g2lds16(const void* src, void* lds) {
+  __builtin_amdgcn_global_load_lds((gbl_void_t*)src, (lds_void_t*)lds, 16, 0, 0);
+}
+
+// The same load written out, for the GEMM K loop: the compiler cannot tell
+// that the loop's LDS operand reads never touch a stage still being filled,
+// and before every such read it would wait for all loads in flight.  Here
+// the caller orders the loads itself (wait_vmcnt before the barrier that
+// precedes a stage's use).  dst is the wave-uniform LDS byte address of the
+// 1 KB block (lane L writes byte L * 16 of it); it travels in M0, which is
+// restored, so the compiler's own use of M0 is undisturbed.
+__device__ __forceinline__ void g2lds16_asm(const void* src, unsigned dst) {
+  unsigned saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %2, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(dst), "v"(src)
+      : "memory");
+}
+
+// One K step of the packed GEMM: issue the direct-to-LDS loads of a later
+// stage into `nxt` (when issue is set) and run this stage's MFMAs from
+// `cur`.  The two stage buffers are distinct restrict pointers so the
+// waitcnt pass knows the operand reads cannot alias the loads in flight and
+// does not drain them; completion is awaited explicitly (wait_vmcnt) before
+// the barrier that precedes a stage's use.
+template <int BM, int BN, int DT>
+struct PackedGemmStep {
+  static constexpr int ROWB = 128, A_BYTES = BM * ROWB;
+  static constexpr int WM = BM / 2, WN = BN / 2, FM = WM / 32, FN = WN / 32;
+  static constexpr int A_LOADS = BM / 32, B_LOADS = BN / 32;
+  // nxt_lds: LDS byte address of the stage being filled; wave_s: the wave
+  // index as a scalar.
+  __device__ __forceinline__ static void run(const char* __restrict__ cur, unsigned nxt_lds, bool issue,
+                                             const u16* a_lane, const int (&a_off)[A_LOADS], int a_koff,
+                                             const u16* bk, const int (&b_off)[B_LOADS], int wave_s, int lane,
+                                             int wm, int wn, f32x16 (&acc)[FM][FN]) {
+    if (issue) {
+#pragma unroll
+      for (int i = 0; i < A_LOADS; ++i)
+        g2lds16_asm(a_lane + a_off[i] + a_koff, nxt_lds + (8 * (wave_s + 4 * i)) * ROWB);
+#pragma unroll
+      for (int i = 0; i < B_LOADS; ++i)
+        g2lds16_asm(bk + b_off[i], nxt_lds + A_BYTES + (8 * (wave_s + 4 * i)) * ROWB);
+    }
+    const char* as = cur;
+    const char* bs = cur + A_BYTES;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const int c = kk * 2 + (lane >> 5);
+      u32x4 af[FM], bf[FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const int row = wm * WM + i * 32 + (lane & 31);
+        af[i] = *reinterpret_cast<const u32x4*>(as + row * ROWB + ((c ^ ((row >> 1) & 7)) << 4));
+      }
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int row = wn * WN + j * 32 + (lane & 31);
+        bf[j] = *reinterpret_cast<const u32x4*>(bs + row * ROWB + ((c ^ ((row >> 1) & 7)) << 4));
+      }
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = mfma32<DT>(af[i], bf[j], acc[i][j]);
+    }
+  }
+};
+
+// Workgroup barrier with no memory fence: the caller has already waited
+// for the operations the barrier publishes (LDS is coherent within the CU);
+// the signal fences keep the compiler from moving memory accesses across it.
+__device__ __forceinline__ void bare_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+template <int BM, int BN, int DT>
+__device__ __forceinline__ void gemm_packed_tile(const KArgs& a, const mk_instr& in, const mk_node& nd,
+                                                 char* smem) {
+  constexpr int ROWB = 128;                         // bytes per LDS row: 64 k values
+  constexpr int A_BYTES = BM * ROWB, STAGE = (BM + BN) * ROWB;
+  constexpr int WM = BM / 2, WN = BN / 2, FM = WM / 32, FN = WN / 32;
+  constexpr int A_LOADS = BM / 32, B_LOADS = BN / 32;  // 16-byte loads per thread per stage
+  constexpr int ST = (kSmemBytes / STAGE) < 4 ? (kSmemBytes / STAGE) : 4;
+  static_assert(ST >= 2, "two stages must fit in LDS");
+  constexpr int L = A_LOADS + B_LOADS;                 // loads per thread per stage
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int flags = in.flags;
+  const int M = nd.M, N = nd.N, K = nd.K;
+  const int r0 = in.r0, c0 = in.c0, k0 = in.k0, k1 = in.k1;
+  const u16* A = buf<const u16>(a, nd.a);
+  const long lda = nd.a.ld;
+
+  // Load instruction i of this wave fills rows 8 * (wave + 4 * i) .. + 8 of
+  // its operand: lane -> row (lane >> 3), physical chunk (lane & 7).  The
+  // rows of one lane are 32 apart, so they share the swizzle chunk; their
+  // element offsets fit in 32 bits (A has fewer than 2^31 elements).
+  const int row0 = 8 * wave + (lane >> 3);
+  const u16* a_lane = A + k0 + (((lane & 7) ^ ((row0 >> 1) & 7)) << 3);
+  int a_off[A_LOADS];
+#pragma unroll
+  for (int i = 0; i < A_LOADS; ++i) a_off[i] = min(r0 + row0 + 32 * i, M - 1) * (int)lda;
+  const long nkt = K / 64;
+  const u16* b_base = buf<const u16>(a, nd.b) + ((long)in.coord[1] * nkt + k0 / 64) * (long)BN * 64;
+  int b_off[B_LOADS];
+#pragma unroll
+  for (int i = 0; i < B_LOADS; ++i) {
+    const int row = 8 * (wave + 4 * i) + (lane >> 3);
+    const int c = (lane & 7) ^ ((row >> 1) & 7);
+    b_off[i] = row * 64 + c * 8;
+  }
+  // LDS byte address of the arena (a generic pointer to LDS keeps the LDS
+  // offset in its low 32 bits) and the wave index, both as scalars
+  const unsigned smem_lds = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)smem);
+  const int wave_s = wave_id();
+  auto issue = [&](int kt, int st) __attribute__((always_inline)) {
+    const unsigned as = smem_lds + st * STAGE;
+#pragma unroll
+    for (int i = 0; i < A_LOADS; ++i) g2lds16_asm(a_lane + a_off[i] + kt * 64, as + (8 * (wave_s + 4 * i)) * ROWB);
+    const u16* bk = b_base + (long)kt * BN * 64;
+#pragma unroll
+    for (int i = 0; i < B_LOADS; ++i) g2lds16_asm(bk + b_off[i], as + A_BYTES + (8 * (wave_s + 4 * i)) * ROWB);
+  };
+
+  f32x16 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+  const int nk = (k1 - k0) / 64;
+#pragma unroll
+  for (int s = 0; s < ST - 1; ++s)
+    if (s < nk) issue(s, s);
+  for (int kt = 0; kt < nk; ++kt) {
+    // stage kt has landed once at most min(ST - 2, nk - 1 - kt) younger
+    // stages of this wave are still in flight; then every wave's part is
+    // visible after the barrier, and the buffer of stage kt - 1 is free
+    const int younger = min(ST - 2, nk - 1 - kt);
+    if (younger >= 2 && ST >= 4) wait_vmcnt<2 * L>();
+    else if (younger >= 1) wait_vmcnt<L>();
+    else wait_vmcnt<0>();
+    bare_barrier();
+    const int kn = kt + ST - 1;
+    PackedGemmStep<BM, BN, DT>::run(smem + (kt % ST) * STAGE, smem_lds + (kn % ST) * STAGE, kn < nk, a_lane, a_off,
+                                    kn * 64, b_base + (long)kn * BN * 64, b_off, wave_s, lane, wm, wn, acc);
+  }
+
+  // ---- epilogue, one 32-row strip of each wave row at a time: the
+  // accumulators go to an fp32 LDS strip Cs[64][BN + 4] (LDS row sr holds
+  // tile row (sr / 32) * WM + i * 32 + sr % 32), then 8-column units run
+  // the epilogue.  acc[i][j][e] is tile row wm*WM + i*32 + 8*(e>>2) +
+  // 4*(lane>>5) + (e&3), weight column wn*WN + j*32 + (lane&31).
+  constexpr int CS = BN + 4;
+  float* Cs = reinterpret_cast<float*>(smem);
+  const int r1 = in.r1, c1 = in.c1;
+  const bool silu_mul = flags & MK_EP_SILU_MUL;
+  constexpr int UNITS = 64 * BN / 8;   // 8-column units of a strip (weight columns)
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+    __syncthreads();   // the previous strip (or the last K stage) is consumed
+#pragma unroll
+    for (int jj = 0; jj < FN; ++jj)
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        Cs[(wm * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3)) * CS + wn * WN + jj * 32 + (lane & 31)] =
+            acc[i][jj][e];
+    __syncthreads();
+    for (int u = t; u < UNITS; u += kThreads) {
+      const int sr = u / (BN / 8), w = (u % (BN / 8)) * 8;   // strip row, weight column
+      const int gr = r0 + (sr >> 5) * WM + i * 32 + (sr & 31);
+      if (gr >= r1) continue;
+      const float* src = Cs + sr * CS;
+      if (flags & MK_EP_PARTIAL) {
+        // weight column w -> partial column (gate o, up N + o) or output column
+        int pc;
+        if (silu_mul) {
+          const int h = w / WN, q = w % WN;
+          const int o = c0 + h * (WN / 2) + q % (WN / 2);
+          if (o >= c1) continue;
+          pc = q < WN / 2 ? o : N + o;
+        } else {
+          pc = c0 + w;
+          if (pc >= c1) continue;
+        }
+        float4* dst = reinterpret_cast<float4*>(buf<float>(a, nd.part) + (long)in.split_idx * nd.part_plane +
+                                                (long)gr * nd.part.ld + pc);
+        dst[0] = make_float4(src[w], src[w + 1], src[w + 2], src[w + 3]);
+        dst[1] = make_float4(src[w + 4], src[w + 5], src[w + 6], src[w + 7]);
+        continue;
+      }
+      int gc, ww, half;
+      if (silu_mul) {
+        // one unit per 8 gate columns: up is WN / 2 columns further
+        const int h = w / WN, q = w % WN;
+        if (q >= WN / 2) continue;
+        gc = c0 + h * (WN / 2) + q;
+        ww = w;
+        half = WN / 2;
+      } else {
+        gc = c0 + w;
+        ww = w;
+        half = BN;
+      }
+      if (gc >= c1) continue;
+      epilogue8<DT>(a, nd, flags, gr, gc, ww, half, [&](int x, float* o) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = src[x + e];
+      });
+    }
   }
 }
 
@@ -979,7 +1229,11 @@ template <int DT>
 __device__ __forceinline__ void run_body(const KArgs& a, const mk_instr& in, const mk_node& nd, char* smem) {
   switch (in.opcode) {
     case MK_I_GEMM:
-      if (nd.tile_m == 128 && nd.tile_n == 128) gemm_tile<128, 128, DT>(a, in, nd, smem);
+      if (nd.layout == 2) {
+        if (nd.tile_m == 256 && nd.tile_n == 128) gemm_packed_tile<256, 128, DT>(a, in, nd, smem);
+        else if (nd.tile_m == 128 && nd.tile_n == 256) gemm_packed_tile<128, 256, DT>(a, in, nd, smem);
+        else gemm_packed_tile<128, 128, DT>(a, in, nd, smem);
+      } else if (nd.tile_m == 128 && nd.tile_n == 128) gemm_tile<128, 128, DT>(a, in, nd, smem);
       else if (nd.tile_m == 64 && nd.tile_n == 128) gemm_tile<64, 128, DT>(a, in, nd, smem);
       else if (nd.tile_m == 128 && nd.tile_n == 64) gemm_tile<128, 64, DT>(a, in, nd, smem);
       else gemm_tile<64, 64, DT>(a, in, nd, smem);

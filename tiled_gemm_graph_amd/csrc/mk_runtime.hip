@@ -61,6 +61,34 @@ __global__ void mk_pack_kernel(const unsigned short* __restrict__ src, unsigned 
   }
 }
 
+// GEMM tiles of a row-major weight src [K][ld] (mk_plan_weight_layout):
+// element e of dst [tiles][K/64][bn][64] is src[kt * 64 + kk][col] for
+// weight column j of tile t.  Plain: col = t * bn + j.  SILU_MUL: each half
+// of the tile (wn = bn / 2 columns) holds gate columns then up columns of
+// the same wn / 2 outputs o = t * bn / 2 + (j / wn) * wn / 2 + (j % wn) % (wn / 2),
+// col = o (gate) or N + o (up).  Outputs at or past N are zero.
+__global__ void mk_pack_gemm_kernel(const unsigned short* __restrict__ src, unsigned short* __restrict__ dst,
+                                    long K, long N, long ld, int bn, long tiles, int silu) {
+  const long nkt = K / 64;
+  const long total = tiles * K * bn;
+  for (long e = (long)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += (long)gridDim.x * blockDim.x) {
+    const long kk = e % 64;
+    const long j = (e / 64) % bn;
+    const long kt = (e / (64L * bn)) % nkt;
+    const long t = e / (64L * bn * nkt);
+    long o, col;
+    if (silu) {
+      const long wn = bn / 2, q = j % wn;
+      o = t * (bn / 2) + (j / wn) * (wn / 2) + q % (wn / 2);
+      col = q < wn / 2 ? o : N + o;
+    } else {
+      o = t * bn + j;
+      col = o;
+    }
+    dst[e] = o < N ? src[(kt * 64 + kk) * ld + col] : (unsigned short)0;
+  }
+}
+
 namespace {
 
 using mk::set_error;
@@ -311,6 +339,13 @@ mk_status mk_plan_pack_weight(mk_plan* p, int32_t tensor, const void* src, void*
   if (total == 0) return MK_OK;
   const long ld = p->tensors[tensor].shape[3];
   const int blocks = (int)std::min<long>((total + 255) / 256, 8192);
+  if (pk->kind == 2) {
+    hipLaunchKernelGGL(mk_pack_gemm_kernel, dim3(blocks), dim3(256), 0, reinterpret_cast<hipStream_t>(stream),
+                       static_cast<const unsigned short*>(src), static_cast<unsigned short*>(dst), (long)pk->K,
+                       (long)pk->N, ld, pk->bn, (long)pk->tiles, pk->silu ? 1 : 0);
+    HIPCHK(hipGetLastError());
+    return MK_OK;
+  }
   hipLaunchKernelGGL(mk_pack_kernel, dim3(blocks), dim3(256), 0, reinterpret_cast<hipStream_t>(stream),
                      static_cast<const unsigned short*>(src), static_cast<unsigned short*>(dst), (long)pk->K,
                      (long)pk->N, ld, pk->bn, pk->wc, (long)pk->tiles, pk->silu ? 1 : 0, pk->head_dim,
