@@ -436,24 +436,30 @@ struct PackedGemmStep {
     }
     const char* as = cur;
     const char* bs = cur + A_BYTES;
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
+    // operand fragments of the four 16-deep sub-steps, double-buffered so
+    // the LDS reads of sub-step kk + 1 are in flight during kk's MFMAs
+    u32x4 af[2][FM], bf[2][FN];
+    auto load = [&](int kk, int b) __attribute__((always_inline)) {
       const int c = kk * 2 + (lane >> 5);
-      u32x4 af[FM], bf[FN];
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
         const int row = wm * WM + i * 32 + (lane & 31);
-        af[i] = *reinterpret_cast<const u32x4*>(as + row * ROWB + ((c ^ ((row >> 1) & 7)) << 4));
+        af[b][i] = *reinterpret_cast<const u32x4*>(as + row * ROWB + ((c ^ ((row >> 1) & 7)) << 4));
       }
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
         const int row = wn * WN + j * 32 + (lane & 31);
-        bf[j] = *reinterpret_cast<const u32x4*>(bs + row * ROWB + ((c ^ ((row >> 1) & 7)) << 4));
+        bf[b][j] = *reinterpret_cast<const u32x4*>(bs + row * ROWB + ((c ^ ((row >> 1) & 7)) << 4));
       }
+    };
+    load(0, 0);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      if (kk + 1 < 4) load(kk + 1, (kk + 1) & 1);
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < FN; ++j) acc[i][j] = mfma32<DT>(af[i], bf[j], acc[i][j]);
+        for (int j = 0; j < FN; ++j) acc[i][j] = mfma32<DT>(af[kk & 1][i], bf[kk & 1][j], acc[i][j]);
     }
   }
 };
@@ -655,17 +661,36 @@ __device__ __forceinline__ GemvShape gemv_shape(const mk_instr& in, const mk_nod
   return g;
 }
 
-// Batch b (clamped to the last one) of this weight thread.
-__device__ __forceinline__ void gemv_load_batch(const KArgs& a, const mk_instr& in, const mk_node& nd,
-                                                const GemvShape& g, int b, u32x4* dst) {
-  const u16* W = buf<const u16>(a, nd.b) + g.wbase;
-  const long ldb = g.ldb;
-  const int kr = min(g.kr, g.kpar - 1);
-  b = min(b, g.nb - 1);
+// A weight thread's rows of one GEMV instruction, resolved once: row r of
+// the thread (chunk row kr + r * kpar) sits at p + r * step.  rv rows are
+// valid; loads clamp to row nrows - 1 (nrows >= 1, a valid row even for an
+// idle thread), so every load is issued and each wait can leave the younger
+// batches in flight.
+struct GemvStream {
+  const u16* p;
+  long step;
+  int nrows, rv, nb;
+};
+__device__ __forceinline__ GemvStream gemv_stream(const KArgs& a, const mk_instr& in, const mk_node& nd,
+                                                  const GemvShape& g) {
+  GemvStream st;
+  const bool has = g.active && g.kr < g.kn;
+  const int kr = has ? g.kr : 0;
+  st.p = buf<const u16>(a, nd.b) + g.wbase + (long)(in.k0 + kr) * g.ldb;
+  st.step = (long)g.kpar * g.ldb;
+  st.rv = has ? (g.kn - g.kr + g.kpar - 1) / g.kpar : 0;
+  st.nrows = st.rv > 0 ? st.rv : 1;
+  st.nb = g.nb;
+  return st;
+}
+
+// Batch b (clamped to the last one) of a stream.
+__device__ __forceinline__ void gemv_load(const GemvStream& st, int b, u32x4* dst) {
+  b = min(b, st.nb - 1);
 #pragma unroll
   for (int j = 0; j < kGemvBatch; ++j) {
-    const int k = min(kr + (b * kGemvBatch + j) * g.kpar, g.kn - 1);
-    dst[j] = *reinterpret_cast<const u32x4*>(W + (long)(in.k0 + k) * ldb);
+    const int r = min(b * kGemvBatch + j, st.nrows - 1);
+    dst[j] = *reinterpret_cast<const u32x4*>(st.p + (long)r * st.step);
   }
 }
 
@@ -673,25 +698,25 @@ __device__ __forceinline__ void gemv_load_batch(const KArgs& a, const mk_instr& 
 __device__ __forceinline__ void gemv_prologue(const KArgs& a, const mk_instr& in, const mk_node& nd,
                                               u32x4 (&B)[kGemvBufs][kGemvBatch]) {
   if (wave_id() == 0) return;
-  const GemvShape g = gemv_shape(in, nd);
+  const GemvStream st = gemv_stream(a, in, nd, gemv_shape(in, nd));
 #pragma unroll
-  for (int k = 0; k < kGemvBufs; ++k) gemv_load_batch(a, in, nd, g, k, B[k]);
+  for (int k = 0; k < kGemvBufs; ++k) gemv_load(st, k, B[k]);
 }
 
+// xk = this thread's first activation (xs + kr); rows r < rv of batch b.
 template <int DT, int MAXR>
-__device__ __forceinline__ void gemv_fma_batch(const GemvShape& g, const u32x4* wb, int b, const float* xs,
+__device__ __forceinline__ void gemv_fma_batch(const u32x4* wb, int b, const float* xk, int kpar, int rv,
                                                int xstride, int rows, float (&acc)[MAXR][8]) {
-  if (!g.active) return;
 #pragma unroll
   for (int j = 0; j < kGemvBatch; ++j) {
-    const int k = g.kr + (b * kGemvBatch + j) * g.kpar;
-    if (k < g.kn) {
+    const int r = b * kGemvBatch + j;
+    if (r < rv) {
       float f[8];
       unpack8<DT>(wb[j], f);
 #pragma unroll
       for (int m = 0; m < MAXR; ++m) {
         if (m < rows) {
-          const float x = xs[m * xstride + k];
+          const float x = xk[m * xstride + r * kpar];
 #pragma unroll
           for (int e = 0; e < 8; ++e) acc[m][e] = fmaf(x, f[e], acc[m][e]);
         }
@@ -705,10 +730,35 @@ __device__ __forceinline__ void gemv_fma_batch(const GemvShape& g, const u32x4* 
 // rope_cols come in rotation pairs (column d and d + head_dim / 2 of one
 // head), so both partners of a pair are in this tile.  Order: SILU_MUL
 // (of the rms-scaled gate and up), BIAS, RESIDUAL, ROPE, RELU, cast.
+// Output column of packed-tile position pos (rotation pairs interleaved
+// below rope_cols under ROPE).
+__device__ __forceinline__ int packed_col(const mk_node& nd, bool rot, int pos) {
+  if (!rot) return pos;
+  const int hd = nd.head_dim, h = pos / hd, w = pos - h * hd;
+  return h * hd + (w >> 1) + (w & 1) * (hd >> 1);
+}
+
+// Bias and residual of the pair a controller lane stores first (unit u =
+// lane), loaded while the weight stream runs: [bias0, bias1, res0, res1].
+template <int DT>
+__device__ __forceinline__ void gemv_packed_prefetch(const KArgs& a, const mk_node& nd, int flags, int r0,
+                                                     int c0, int rows, int bw, float (&pf)[4]) {
+  const int npair = bw >> 1, u = threadIdx.x & 63;
+  if (!(flags & (MK_EP_BIAS | MK_EP_RESIDUAL)) || u >= rows * npair) return;
+  const int m = u / npair, q = (u - m * npair) * 2, gr = r0 + m;
+  const bool rot = (flags & MK_EP_ROPE) && c0 + q < nd.rope_cols;
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const int c = packed_col(nd, rot, c0 + q + e);
+    if (flags & MK_EP_BIAS) pf[e] = to_f<DT>(buf<const u16>(a, nd.bias)[(long)gr * nd.bias.ld + c]);
+    if (flags & MK_EP_RESIDUAL) pf[2 + e] = to_f<DT>(buf<const u16>(a, nd.res)[(long)gr * nd.res.ld + c]);
+  }
+}
+
 template <int DT, int MAXR>
 __device__ __forceinline__ void gemv_store_packed(const KArgs& a, const mk_node& nd, int flags, int r0,
                                                   int c0, int rows, int bw, int wc, const float* sum,
-                                                  const float (&rinv)[MAXR]) {
+                                                  const float (&rinv)[MAXR], const float (&pf)[4]) {
   const bool silu_mul = flags & MK_EP_SILU_MUL, rope = flags & MK_EP_ROPE;
   const int hd = nd.head_dim, hh = hd >> 1;
   const int npair = bw >> 1;
@@ -721,21 +771,19 @@ __device__ __forceinline__ void gemv_store_packed(const KArgs& a, const mk_node&
     for (int mm = 0; mm < MAXR; ++mm)
       if (mm == m) sc = rinv[mm];
     const bool rot = rope && c0 + q < nd.rope_cols;
+    const bool first = u == (int)threadIdx.x;   // operands prefetched during the stream
     float v[2];
     int col[2];
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
-      const int pos = c0 + q + e;
-      int c = pos;
-      if (rot) {
-        const int h = pos / hd, w = pos - h * hd;
-        c = h * hd + (w >> 1) + (w & 1) * hh;
-      }
+      const int c = packed_col(nd, rot, c0 + q + e);
       col[e] = c;
       float x = sum[m * wc + q + e] * sc;
       if (silu_mul) x = silu(x) * (sum[m * wc + bw + q + e] * sc);
-      if (flags & MK_EP_BIAS) x += to_f<DT>(buf<const u16>(a, nd.bias)[(long)gr * nd.bias.ld + c]);
-      if (flags & MK_EP_RESIDUAL) x += to_f<DT>(buf<const u16>(a, nd.res)[(long)gr * nd.res.ld + c]);
+      if (flags & MK_EP_BIAS)
+        x += first ? pf[e] : to_f<DT>(buf<const u16>(a, nd.bias)[(long)gr * nd.bias.ld + c]);
+      if (flags & MK_EP_RESIDUAL)
+        x += first ? pf[2 + e] : to_f<DT>(buf<const u16>(a, nd.res)[(long)gr * nd.res.ld + c]);
       v[e] = x;
     }
     if (rot) {
@@ -825,6 +873,8 @@ __device__ __forceinline__ void gemv_body(const KArgs& a, const mk_instr& in, co
     }
   }
   lds_barrier();
+  float pf[4] = {0.f, 0.f, 0.f, 0.f};
+  if (nd.layout == 1 && wave_id() == 0) gemv_packed_prefetch<DT>(a, nd, flags, r0, c0, rows, bw, pf);
   if (wave_id() != 0) {
     float acc[MAXR][8];
 #pragma unroll
@@ -834,12 +884,18 @@ __device__ __forceinline__ void gemv_body(const KArgs& a, const mk_instr& in, co
     // Loads target "virtual" batches: v < nb is batch v of this
     // instruction, v >= nb batch v - nb of the next one (clamped to its last
     // batch), or a redundant re-read of this tile when there is no next GEMV.
-    GemvShape gn = g;
-    if (nx) gn = gemv_shape(*nx, *nxd);
+    const GemvStream sc = gemv_stream(a, in, nd, g);
+    const GemvStream sn = nx ? gemv_stream(a, *nx, *nxd, gemv_shape(*nx, *nxd)) : sc;
+    const int nshift = nx ? g.nb : 0;
+    const float* xk = xs + (g.active && g.kr < g.kn ? g.kr : 0);
     auto load_v = [&](int v, u32x4* dst) __attribute__((always_inline)) {
-      if (v < g.nb) gemv_load_batch(a, in, nd, g, v, dst);
-      else if (nx) gemv_load_batch(a, *nx, *nxd, gn, v - g.nb, dst);
-      else gemv_load_batch(a, in, nd, g, g.nb - 1, dst);
+      const bool nxt = v >= g.nb;
+      GemvStream st;
+      st.p = nxt ? sn.p : sc.p;
+      st.step = nxt ? sn.step : sc.step;
+      st.nrows = nxt ? sn.nrows : sc.nrows;
+      st.nb = nxt ? sn.nb : sc.nb;
+      gemv_load(st, nxt ? v - nshift : v, dst);
     };
     // Virtual batch v lives in B[(v + S0) % kGemvBufs].  Batch v is consumed,
     // then its buffer receives batch v + kGemvBufs; steps past the end
@@ -850,7 +906,7 @@ __device__ __forceinline__ void gemv_body(const KArgs& a, const mk_instr& in, co
       for (int k = 0; k < kGemvBufs; ++k) {
         const int v = v0 + k;
         u32x4* buf_k = B[(k + S0) % kGemvBufs];
-        if (v < g.nb) gemv_fma_batch<DT, MAXR>(g, buf_k, v, xs, xstride, rows, acc);
+        if (v < g.nb) gemv_fma_batch<DT, MAXR>(buf_k, v, xk, g.kpar, sc.rv, xstride, rows, acc);
         load_v(v < g.nb ? v + kGemvBufs : v, buf_k);
       }
     }
@@ -898,7 +954,7 @@ __device__ __forceinline__ void gemv_body(const KArgs& a, const mk_instr& in, co
     rinv[m] = rms ? 1.0f / sqrtf((sq[m] + sq[MAXR + m] + sq[2 * MAXR + m] + sq[3 * MAXR + m]) / (float)nd.K + nd.eps)
                   : 1.0f;
   if (nd.layout) {
-    gemv_store_packed<DT, MAXR>(a, nd, flags, r0, c0, rows, bw, wc, sum, rinv);
+    gemv_store_packed<DT, MAXR>(a, nd, flags, r0, c0, rows, bw, wc, sum, rinv, pf);
     return;
   }
   const int units = rows * (bw / 8);
@@ -915,16 +971,17 @@ __device__ __forceinline__ void gemv_body(const KArgs& a, const mk_instr& in, co
   }
 }
 
-template <int DT, int MAXR>
+template <int DT, int MAXR, int S = 0>
 __device__ __forceinline__ void gemv_body_s0(const KArgs& a, const mk_instr& in, const mk_node& nd, char* smem,
                                              u32x4 (&B)[kGemvBufs][kGemvBatch], const mk_instr* nx,
                                              const mk_node* nxd, int s0) {
-  switch (s0) {
-    case 0: gemv_body<DT, MAXR, 0>(a, in, nd, smem, B, nx, nxd); break;
-    case 1: gemv_body<DT, MAXR, 1>(a, in, nd, smem, B, nx, nxd); break;
-    case 2: gemv_body<DT, MAXR, 2>(a, in, nd, smem, B, nx, nxd); break;
-    default: gemv_body<DT, MAXR, 3>(a, in, nd, smem, B, nx, nxd); break;
+  if constexpr (S + 1 < kGemvBufs) {
+    if (s0 != S) {
+      gemv_body_s0<DT, MAXR, S + 1>(a, in, nd, smem, B, nx, nxd, s0);
+      return;
+    }
   }
+  gemv_body<DT, MAXR, S>(a, in, nd, smem, B, nx, nxd);
 }
 
 // Runs `in` with its stream starting at buffer s0; returns the buffer where
