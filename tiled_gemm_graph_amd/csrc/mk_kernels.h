@@ -38,6 +38,11 @@ constexpr int kSmemBytes = 144 * 1024;   // dynamic tile arena (LDS); 160 KB per
 constexpr int kMaxNodes = 48;           // node descriptors cached in LDS
 constexpr int kGemvBatch = 4;           // 16-byte weight chunks per thread per batch
 constexpr int kGemvBufs = 3;            // weight batches in flight per thread
+// GEMV body LDS: activations (and later the finished sums), then the
+// partial sums of one row: wc * kpad <= 2016 floats for every tile width.
+constexpr int kGemvXsFloats = 16384;
+constexpr int kGemvRedFloats = 2016;
+static_assert((kGemvXsFloats + 8 * kGemvRedFloats + 4 * 8) * 4 <= kSmemBytes, "GEMV body LDS");
 
 struct KArgs {
   const mk_instr* instrs;   // [n_iters][ncu]
@@ -57,6 +62,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned short u16;
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // ---------------------------------------------------------------- numerics
@@ -112,6 +118,12 @@ __device__ __forceinline__ f32x16 mfma32(const u32x4& a, const u32x4& b, f32x16 
 }
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
+
+// Lane-permuted copy of v (DPP control CTRL, within rows of 16 lanes).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
+}
 
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
@@ -738,58 +750,114 @@ __device__ __forceinline__ int packed_col(const mk_node& nd, bool rot, int pos) 
   return h * hd + (w >> 1) + (w & 1) * (hd >> 1);
 }
 
-// Bias and residual of the pair a controller lane stores first (unit u =
-// lane), loaded while the weight stream runs: [bias0, bias1, res0, res1].
-template <int DT>
-__device__ __forceinline__ void gemv_packed_prefetch(const KArgs& a, const mk_node& nd, int flags, int r0,
-                                                     int c0, int rows, int bw, float (&pf)[4]) {
+// Everything the store of a controller lane's first pair (unit u = lane)
+// needs except the sums: prepared while the weight waves stream.
+struct PackedEp {
+  long off[2];   // output element offsets
+  float add[2];  // bias + residual
+  float cs, sn;  // rotation of the pair (ROPE)
+  float sc;      // 1 / rms of the row (RMSNORM_INPUT), else 1
+  int s0;        // sum index of the first column (m * wc + q)
+  bool rot;
+  bool pair;     // the two outputs are adjacent and 4-byte aligned
+};
+
+template <int DT, int MAXR>
+__device__ __forceinline__ void gemv_packed_prepare(const KArgs& a, const mk_node& nd, int flags, int r0,
+                                                    int c0, int rows, int bw, int wc, const float* sq,
+                                                    PackedEp& ep) {
   const int npair = bw >> 1, u = threadIdx.x & 63;
-  if (!(flags & (MK_EP_BIAS | MK_EP_RESIDUAL)) || u >= rows * npair) return;
+  if (u >= rows * npair) return;
   const int m = u / npair, q = (u - m * npair) * 2, gr = r0 + m;
   const bool rot = (flags & MK_EP_ROPE) && c0 + q < nd.rope_cols;
+  ep.rot = rot;
+  ep.s0 = m * wc + q;
 #pragma unroll
   for (int e = 0; e < 2; ++e) {
     const int c = packed_col(nd, rot, c0 + q + e);
-    if (flags & MK_EP_BIAS) pf[e] = to_f<DT>(buf<const u16>(a, nd.bias)[(long)gr * nd.bias.ld + c]);
-    if (flags & MK_EP_RESIDUAL) pf[2 + e] = to_f<DT>(buf<const u16>(a, nd.res)[(long)gr * nd.res.ld + c]);
+    ep.off[e] = (long)gr * nd.out.ld + c;
+    float x = 0.f;
+    if (flags & MK_EP_BIAS) x += to_f<DT>(buf<const u16>(a, nd.bias)[(long)gr * nd.bias.ld + c]);
+    if (flags & MK_EP_RESIDUAL) x += to_f<DT>(buf<const u16>(a, nd.res)[(long)gr * nd.res.ld + c]);
+    ep.add[e] = x;
+  }
+  ep.pair = !rot && ep.off[1] == ep.off[0] + 1 && (ep.off[0] & 1) == 0;
+  if (rot) {
+    const int hd = nd.head_dim;
+    const int c = packed_col(nd, true, c0 + q);
+    const float* tab = buf<float>(a, nd.aux) + (long)gr * hd;  // [cos(half) | sin(half)]
+    const int i = c - (c / hd) * hd;
+    ep.cs = tab[i];
+    ep.sn = tab[(hd >> 1) + i];
+  }
+  ep.sc = 1.0f;
+  if (flags & MK_EP_RMSNORM_INPUT) {
+    const float s2 = sq[m] + sq[MAXR + m] + sq[2 * MAXR + m] + sq[3 * MAXR + m];
+    ep.sc = 1.0f / sqrtf(s2 / (float)nd.K + nd.eps);
   }
 }
 
 template <int DT, int MAXR>
 __device__ __forceinline__ void gemv_store_packed(const KArgs& a, const mk_node& nd, int flags, int r0,
                                                   int c0, int rows, int bw, int wc, const float* sum,
-                                                  const float (&rinv)[MAXR], const float (&pf)[4]) {
+                                                  const float (&rinv)[MAXR], const PackedEp& ep) {
   const bool silu_mul = flags & MK_EP_SILU_MUL, rope = flags & MK_EP_ROPE;
   const int hd = nd.head_dim, hh = hd >> 1;
   const int npair = bw >> 1;
   u16* O = buf<u16>(a, nd.out);
   for (int u = threadIdx.x; u < rows * npair; u += 64) {
-    const int m = u / npair, q = (u - m * npair) * 2;
-    const int gr = r0 + m;
-    float sc = 1.0f;
+    const bool first = u == (int)threadIdx.x;
+    float v[2], cs = 0.f, sn = 0.f;
+    long off[2];
+    bool rot;
+    if (first) {
+      // prepared during the weight stream
 #pragma unroll
-    for (int mm = 0; mm < MAXR; ++mm)
-      if (mm == m) sc = rinv[mm];
-    const bool rot = rope && c0 + q < nd.rope_cols;
-    const bool first = u == (int)threadIdx.x;   // operands prefetched during the stream
-    float v[2];
-    int col[2];
+      for (int e = 0; e < 2; ++e) {
+        float x = sum[ep.s0 + e] * ep.sc;
+        if (silu_mul) x = silu(x) * (sum[ep.s0 + bw + e] * ep.sc);
+        v[e] = x + ep.add[e];
+        off[e] = ep.off[e];
+      }
+      if (ep.pair) {
+        // one 4-byte store for both outputs
+        float y[2];
 #pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const int c = packed_col(nd, rot, c0 + q + e);
-      col[e] = c;
-      float x = sum[m * wc + q + e] * sc;
-      if (silu_mul) x = silu(x) * (sum[m * wc + bw + q + e] * sc);
-      if (flags & MK_EP_BIAS)
-        x += first ? pf[e] : to_f<DT>(buf<const u16>(a, nd.bias)[(long)gr * nd.bias.ld + c]);
-      if (flags & MK_EP_RESIDUAL)
-        x += first ? pf[2 + e] : to_f<DT>(buf<const u16>(a, nd.res)[(long)gr * nd.res.ld + c]);
-      v[e] = x;
+        for (int e = 0; e < 2; ++e) y[e] = (flags & MK_EP_RELU) ? fmaxf(v[e], 0.0f) : v[e];
+        const uint32_t w2 = (uint32_t)from_f<DT>(y[0]) | ((uint32_t)from_f<DT>(y[1]) << 16);
+        __hip_atomic_store(reinterpret_cast<uint32_t*>(O + off[0]), w2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        continue;
+      }
+      rot = ep.rot;
+      cs = ep.cs;
+      sn = ep.sn;
+    } else {
+      const int m = u / npair, q = (u - m * npair) * 2;
+      const int gr = r0 + m;
+      float sc = 1.0f;
+#pragma unroll
+      for (int mm = 0; mm < MAXR; ++mm)
+        if (mm == m) sc = rinv[mm];
+      rot = rope && c0 + q < nd.rope_cols;
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int c = packed_col(nd, rot, c0 + q + e);
+        off[e] = (long)gr * nd.out.ld + c;
+        float x = sum[m * wc + q + e] * sc;
+        if (silu_mul) x = silu(x) * (sum[m * wc + bw + q + e] * sc);
+        if (flags & MK_EP_BIAS) x += to_f<DT>(buf<const u16>(a, nd.bias)[(long)gr * nd.bias.ld + c]);
+        if (flags & MK_EP_RESIDUAL) x += to_f<DT>(buf<const u16>(a, nd.res)[(long)gr * nd.res.ld + c]);
+        v[e] = x;
+      }
+      if (rot) {
+        const float* tab = buf<float>(a, nd.aux) + (long)gr * hd;  // [cos(half) | sin(half)]
+        const int c = packed_col(nd, true, c0 + q);
+        const int i = c - (c / hd) * hd;
+        cs = tab[i];
+        sn = tab[hh + i];
+      }
     }
     if (rot) {
-      const float* tab = buf<float>(a, nd.aux) + (long)gr * hd;  // [cos(half) | sin(half)]
-      const int i = col[0] - (col[0] / hd) * hd;
-      const float cs = tab[i], sn = tab[hh + i];
       const float x1 = v[0], x2 = v[1];
       v[0] = x1 * cs - x2 * sn;
       v[1] = x2 * cs + x1 * sn;
@@ -799,8 +867,7 @@ __device__ __forceinline__ void gemv_store_packed(const KArgs& a, const mk_node&
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
       const float y = (flags & MK_EP_RELU) ? fmaxf(v[e], 0.0f) : v[e];
-      __hip_atomic_store(O + (long)gr * nd.out.ld + col[e], from_f<DT>(y), __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(O + off[e], from_f<DT>(y), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 }
@@ -820,9 +887,13 @@ __device__ __forceinline__ void gemv_body(const KArgs& a, const mk_instr& in, co
   const int bw = g.bw, wc = g.wc, kn = g.kn;
   const int xstride = (kn + 3) & ~3;
   float* xs = reinterpret_cast<float*>(smem);   // [rows][xstride], rows * kn <= 16384 (8192 if rows > 1)
-  float* red = xs + rows * xstride;             // [kpar][MAXR][wc], kpar * wc <= 1536
-  float* sum = red + 1536 * MAXR;               // [MAXR][wc], wc <= 1536
-  float* sq = sum + 1536 * MAXR;                // [4 waves][MAXR] sums of squares
+  // red holds the kpar partial sums of each output contiguously, kpad
+  // apart; sum (the finished outputs) reuses the activation area, which no
+  // wave reads once every wave has passed the barrier after its stream.
+  const int kpad = g.kpar >= 8 ? (g.kpar + 3) & ~3 : g.kpar;
+  float* red = xs + kGemvXsFloats;              // [rows][wc][kpad]
+  float* sum = xs;                              // [rows][wc]
+  float* sq = red + kGemvRedFloats * MAXR;      // [4 waves][MAXR] sums of squares
   {
     // All four waves stage the activation chunk (gamma-scaled under
     // RMSNORM_INPUT) with every load of a thread in flight at once (at most
@@ -873,8 +944,9 @@ __device__ __forceinline__ void gemv_body(const KArgs& a, const mk_instr& in, co
     }
   }
   lds_barrier();
-  float pf[4] = {0.f, 0.f, 0.f, 0.f};
-  if (nd.layout == 1 && wave_id() == 0) gemv_packed_prefetch<DT>(a, nd, flags, r0, c0, rows, bw, pf);
+  PackedEp ep;
+  if (nd.layout == 1 && wave_id() == 0 && !(flags & MK_EP_PARTIAL))
+    gemv_packed_prepare<DT, MAXR>(a, nd, flags, r0, c0, rows, bw, wc, sq, ep);
   if (wave_id() != 0) {
     float acc[MAXR][8];
 #pragma unroll
@@ -911,29 +983,53 @@ __device__ __forceinline__ void gemv_body(const KArgs& a, const mk_instr& in, co
       }
     }
     if (g.active) {
+      // partial kr of output (m, cg * 8 + e); threads kr < kpad - kpar also
+      // zero the padding slots kpar + kr
+      float* rp = red + (g.cg * 8) * kpad + g.kr;
+      const bool pad = g.kr < kpad - g.kpar;
 #pragma unroll
       for (int m = 0; m < MAXR; ++m)
         if (m < rows)
 #pragma unroll
-          for (int e = 0; e < 8; ++e) red[(g.kr * MAXR + m) * wc + g.cg * 8 + e] = acc[m][e];
+          for (int e = 0; e < 8; ++e) {
+            rp[(m * wc + e) * kpad] = acc[m][e];
+            if (pad) rp[(m * wc + e) * kpad + g.kpar] = 0.f;
+          }
     }
   }
   lds_barrier();
   {
-    // All waves sum the kpar row groups: tpu consecutive lanes per output,
-    // each adding groups sub, sub + tpu, ..., then a butterfly over the tpu
-    // lanes (a fixed order, so every run gives the same bits).
+    // All waves finish the sums: tpu consecutive lanes per output, each
+    // adding 16-byte groups of its partials, then a fixed DPP pattern over
+    // the tpu lanes (every run gives the same bits).
     const int nout = rows * wc;
     int tpu = 1;
     while (tpu < 16 && tpu * 2 * nout <= kThreads) tpu *= 2;
+    const int sub = t & (tpu - 1);
+    const bool vec = kpad != g.kpar || (g.kpar & 3) == 0;
     for (int o0 = 0; o0 < nout; o0 += kThreads / tpu) {
-      const int o = o0 + t / tpu, sub = t % tpu;
+      const int o = o0 + t / tpu;
       float v = 0.f;
       if (o < nout) {
-        const int m = o / wc, w = o - m * wc;
-        for (int q = sub; q < g.kpar; q += tpu) v += red[(q * MAXR + m) * wc + w];
+        if (vec) {
+          const f32x4* r4 = reinterpret_cast<const f32x4*>(red + o * kpad);
+          const int nq = kpad >> 2;
+          f32x4 p0 = {0.f, 0.f, 0.f, 0.f}, p1 = {0.f, 0.f, 0.f, 0.f};
+          int j = sub;
+          for (; j + tpu < nq; j += 2 * tpu) {
+            p0 += r4[j];
+            p1 += r4[j + tpu];
+          }
+          if (j < nq) p0 += r4[j];
+          v = ((p0[0] + p1[0]) + (p0[1] + p1[1])) + ((p0[2] + p1[2]) + (p0[3] + p1[3]));
+        } else {
+          for (int q = sub; q < g.kpar; q += tpu) v += red[o * kpad + q];
+        }
       }
-      for (int off = tpu >> 1; off > 0; off >>= 1) v += __shfl_xor(v, off);
+      if (tpu >= 16) v += dpp_f<0x140>(v);   // row mirror
+      if (tpu >= 8) v += dpp_f<0x141>(v);    // half-row mirror
+      if (tpu >= 4) v += dpp_f<0x4E>(v);     // lanes ^ 2
+      if (tpu >= 2) v += dpp_f<0xB1>(v);     // lanes ^ 1
       if (sub == 0 && o < nout) sum[o] = v;
     }
   }
@@ -954,7 +1050,7 @@ __device__ __forceinline__ void gemv_body(const KArgs& a, const mk_instr& in, co
     rinv[m] = rms ? 1.0f / sqrtf((sq[m] + sq[MAXR + m] + sq[2 * MAXR + m] + sq[3 * MAXR + m]) / (float)nd.K + nd.eps)
                   : 1.0f;
   if (nd.layout) {
-    gemv_store_packed<DT, MAXR>(a, nd, flags, r0, c0, rows, bw, wc, sum, rinv, pf);
+    gemv_store_packed<DT, MAXR>(a, nd, flags, r0, c0, rows, bw, wc, sum, rinv, ep);
     return;
   }
   const int units = rows * (bw / 8);
@@ -1282,11 +1378,21 @@ __device__ __forceinline__ void elementwise_tile(const KArgs& a, const mk_instr&
 }
 
 // -------------------------------------------------------------- dispatch
-template <int DT>
+// Op families compiled into a kernel instance.  A plan runs on the smallest
+// instance whose families cover its instructions: leaving the other bodies
+// out keeps their registers and code away from the loop that runs.
+constexpr unsigned kOpGemm = 1, kOpGemv = 2, kOpOther = 4, kOpAll = 7;
+__host__ __device__ constexpr unsigned op_family(int opcode) {
+  return opcode == MK_I_NOOP ? 0u : opcode == MK_I_GEMM ? kOpGemm : opcode == MK_I_GEMV ? kOpGemv : kOpOther;
+}
+
+template <unsigned OPS, int DT>
 __device__ __forceinline__ void run_body(const KArgs& a, const mk_instr& in, const mk_node& nd, char* smem) {
+  if (!(op_family(in.opcode) & OPS)) return;
   switch (in.opcode) {
     case MK_I_GEMM:
-      if (nd.layout == 2) {
+      if constexpr (!(OPS & kOpGemm)) break;
+      else if (nd.layout == 2) {
         if (nd.tile_m == 256 && nd.tile_n == 128) gemm_packed_tile<256, 128, DT>(a, in, nd, smem);
         else if (nd.tile_m == 128 && nd.tile_n == 256) gemm_packed_tile<128, 256, DT>(a, in, nd, smem);
         else gemm_packed_tile<128, 128, DT>(a, in, nd, smem);
@@ -1295,24 +1401,32 @@ __device__ __forceinline__ void run_body(const KArgs& a, const mk_instr& in, con
       else if (nd.tile_m == 128 && nd.tile_n == 64) gemm_tile<128, 64, DT>(a, in, nd, smem);
       else gemm_tile<64, 64, DT>(a, in, nd, smem);
       break;
-    case MK_I_GEMV: {
-      u32x4 B[kGemvBufs][kGemvBatch];
-      gemv_prologue(a, in, nd, B);
-      gemv_body_rows<DT>(a, in, nd, smem, B, nullptr, nullptr, 0);
+    case MK_I_GEMV:
+      if constexpr (OPS & kOpGemv) {
+        u32x4 B[kGemvBufs][kGemvBatch];
+        gemv_prologue(a, in, nd, B);
+        gemv_body_rows<DT>(a, in, nd, smem, B, nullptr, nullptr, 0);
+      }
       break;
-    }
-    case MK_I_REDUCE: reduce_tile<DT>(a, in, nd, smem); break;
-    case MK_I_RMSNORM: rmsnorm_tile<DT>(a, in, nd, smem); break;
-    case MK_I_ATTENTION: attention_tile<DT>(a, in, nd, smem); break;
-    case MK_I_EW_ADD:
-    case MK_I_EW_RELU: elementwise_tile<DT>(a, in, nd); break;
-    default: break;
+    default:
+      if constexpr (OPS & kOpOther) {
+        switch (in.opcode) {
+          case MK_I_REDUCE: reduce_tile<DT>(a, in, nd, smem); break;
+          case MK_I_RMSNORM: rmsnorm_tile<DT>(a, in, nd, smem); break;
+          case MK_I_ATTENTION: attention_tile<DT>(a, in, nd, smem); break;
+          case MK_I_EW_ADD:
+          case MK_I_EW_RELU: elementwise_tile<DT>(a, in, nd); break;
+          default: break;
+        }
+      }
+      break;
   }
 }
 
+template <unsigned OPS>
 __device__ __forceinline__ void run_instr(const KArgs& a, const mk_instr& in, const mk_node& nd, char* smem) {
-  if (nd.dtype == MK_BF16) run_body<MK_BF16>(a, in, nd, smem);
-  else run_body<MK_F16>(a, in, nd, smem);
+  if (nd.dtype == MK_BF16) run_body<OPS, MK_BF16>(a, in, nd, smem);
+  else run_body<OPS, MK_F16>(a, in, nd, smem);
 }
 
 // ----------------------------------------------------- counters and waits
@@ -1414,6 +1528,7 @@ __device__ __forceinline__ void store_ahead(const Loop& L, int it, int w) {
 }
 
 // One generic iteration.  Returns false if the run was aborted.
+template <unsigned OPS>
 __device__ __forceinline__ bool generic_iter(const Loop& L, int it, int& w) {
   const KArgs& a = L.a;
   const int gidx = it * a.ncu + L.vcu;
@@ -1424,7 +1539,7 @@ __device__ __forceinline__ bool generic_iter(const Loop& L, int it, int& w) {
   if (in.opcode != MK_I_NOOP) {
     const mk_node& nd = L.nodes[in.node];
     if (tr) stamp(a, gidx, 1, wall_clock64());
-    run_instr(a, in, nd, L.smem);
+    run_instr<OPS>(a, in, nd, L.smem);
     if (tr) stamp(a, gidx, 2, wall_clock64());
     release_dests(a, in);
     if (tr) stamp(a, gidx, 3, wall_clock64());
@@ -1490,6 +1605,7 @@ __device__ __forceinline__ int gemv_streak(const Loop& L, int& it, int& w) {
 
 }  // namespace mkd
 
+template <unsigned OPS>
 __global__ void __launch_bounds__(256, 1) mk_persistent(mkd::KArgs args) {
   // Read the arguments in place (kernarg segment, constant memory): the
   // buffer table is indexed with runtime slots, which would otherwise force
@@ -1512,19 +1628,22 @@ __global__ void __launch_bounds__(256, 1) mk_persistent(mkd::KArgs args) {
   int it = 0, w = 0;
   while (it < a.n_iters) {
     const mk_instr& in = s_in[it % 3];
-    if (in.opcode == MK_I_GEMV) {
-      const int st = s_nodes[in.node].dtype == MK_BF16 ? mkd::gemv_streak<MK_BF16>(L, it, w)
-                                                      : mkd::gemv_streak<MK_F16>(L, it, w);
-      if (st < 0) return;
-      continue;
+    if constexpr ((OPS & mkd::kOpGemv) != 0) {
+      if (in.opcode == MK_I_GEMV) {
+        const int st = s_nodes[in.node].dtype == MK_BF16 ? mkd::gemv_streak<MK_BF16>(L, it, w)
+                                                        : mkd::gemv_streak<MK_F16>(L, it, w);
+        if (st < 0) return;
+        continue;
+      }
     }
-    if (!mkd::generic_iter(L, it, w)) return;
+    if (!mkd::generic_iter<OPS>(L, it, w)) return;
     ++it;
   }
 }
 
 // Per-op baseline: one launch per node, one workgroup per instruction, no
 // counters (stream order carries the dependencies).
+template <unsigned OPS>
 __global__ void __launch_bounds__(256, 1) mk_node_kernel(mkd::KArgs args) {
   const mkd::KArgs& a = *(const mkd::KArgs*)__builtin_amdgcn_kernarg_segment_ptr();
   (void)args;
@@ -1537,5 +1656,5 @@ __global__ void __launch_bounds__(256, 1) mk_node_kernel(mkd::KArgs args) {
   if (s_in.opcode == MK_I_NOOP) return;
   mkd::copy_words(reinterpret_cast<int*>(&s_nd), reinterpret_cast<const int*>(a.nodes + s_in.node));
   __syncthreads();
-  mkd::run_instr(a, s_in, s_nd, smem);
+  mkd::run_instr<OPS>(a, s_in, s_nd, smem);
 }

@@ -27,6 +27,7 @@ struct mk_plan_device {
   std::vector<void*> owned;   // by slot (plan-owned buffers), else nullptr
   long long spin_ticks = 0;
   int max_target = 1;
+  unsigned ops = 0;           // op families of the plan's instructions
 };
 
 // Packed column tiles of a row-major weight src [K][ld] (the layout of
@@ -91,6 +92,18 @@ __global__ void mk_pack_gemm_kernel(const unsigned short* __restrict__ src, unsi
 
 namespace {
 
+// Smallest compiled kernel instance whose op families cover `ops`.
+const void* persistent_for(unsigned ops) {
+  if ((ops & ~mkd::kOpGemv) == 0) return reinterpret_cast<const void*>(mk_persistent<mkd::kOpGemv>);
+  if ((ops & mkd::kOpGemv) == 0) return reinterpret_cast<const void*>(mk_persistent<mkd::kOpGemm | mkd::kOpOther>);
+  return reinterpret_cast<const void*>(mk_persistent<mkd::kOpAll>);
+}
+const void* node_kernel_for(unsigned ops) {
+  if ((ops & ~mkd::kOpGemv) == 0) return reinterpret_cast<const void*>(mk_node_kernel<mkd::kOpGemv>);
+  if ((ops & mkd::kOpGemv) == 0) return reinterpret_cast<const void*>(mk_node_kernel<mkd::kOpGemm | mkd::kOpOther>);
+  return reinterpret_cast<const void*>(mk_node_kernel<mkd::kOpAll>);
+}
+
 using mk::set_error;
 
 mk_status hip_fail(hipError_t e, const char* what) {
@@ -146,11 +159,13 @@ mk_status ensure_device(mk_plan* p) {
     set_error("device does not support cooperative launch");
     return MK_E_UNSUPPORTED;
   }
-  int blocks = 0;
-  HIPCHK(hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, mk_persistent, mkd::kThreads, 0));
-  if (blocks < 1) {
-    set_error("persistent kernel does not fit one workgroup per CU");
-    return MK_E_UNSUPPORTED;
+  for (const void* k : {persistent_for(mkd::kOpAll), persistent_for(mkd::kOpGemv), persistent_for(mkd::kOpGemm | mkd::kOpOther)}) {
+    int blocks = 0;
+    HIPCHK(hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, k, mkd::kThreads, 0));
+    if (blocks < 1) {
+      set_error("persistent kernel does not fit one workgroup per CU");
+      return MK_E_UNSUPPORTED;
+    }
   }
   auto* d = new mk_plan_device();
   d->device = dev;
@@ -173,6 +188,7 @@ mk_status ensure_device(mk_plan* p) {
   if ((e = hipMalloc(&d->d_err, 8 * sizeof(int))) != hipSuccess) return bail(e, "hipMalloc error record");
   if ((e = hipMemset(d->d_err, 0, 8 * sizeof(int))) != hipSuccess) return bail(e, "hipMemset error record");
   for (int32_t t : p->targets) d->max_target = std::max(d->max_target, (int)t);
+  for (const mk_instr& r : p->records) d->ops |= mkd::op_family(r.opcode);
   // plan-owned buffers: intermediates, split-K partials, constant tables
   d->owned.assign(p->slot_owner.size(), nullptr);
   for (size_t s = 0; s < p->slot_owner.size(); ++s) {
@@ -258,13 +274,12 @@ mk_status megakernel_run_traced(mk_plan* p, void* const* buffers, int n_buffers,
     p->epoch = 0;
   }
   a.epoch = (int)(p->epoch + 1);
+  const void* kernel = persistent_for(p->dev->ops);
+  void* args[] = {&a};
   if (p->opts.cooperative) {
-    void* args[] = {&a};
-    HIPCHK(hipLaunchCooperativeKernel(reinterpret_cast<const void*>(mk_persistent), dim3(p->opts.num_cus),
-                                      dim3(mkd::kThreads), args, 0, s));
+    HIPCHK(hipLaunchCooperativeKernel(kernel, dim3(p->opts.num_cus), dim3(mkd::kThreads), args, 0, s));
   } else {
-    hipLaunchKernelGGL(mk_persistent, dim3(p->opts.num_cus), dim3(mkd::kThreads), 0, s, a);
-    HIPCHK(hipGetLastError());
+    HIPCHK(hipLaunchKernel(kernel, dim3(p->opts.num_cus), dim3(mkd::kThreads), args, 0, s));
   }
   p->epoch += 1;
   return MK_OK;
@@ -285,8 +300,10 @@ mk_status megakernel_run_per_op(mk_plan* p, void* const* buffers, int n_buffers,
     if (n.ins.empty()) continue;
     a.first = n.start;
     a.count = (int)n.ins.size();
-    hipLaunchKernelGGL(mk_node_kernel, dim3(a.count), dim3(mkd::kThreads), 0, s, a);
-    HIPCHK(hipGetLastError());
+    unsigned ops = 0;
+    for (int i = 0; i < a.count; ++i) ops |= mkd::op_family(p->records[n.start + i].opcode);
+    void* args[] = {&a};
+    HIPCHK(hipLaunchKernel(node_kernel_for(ops), dim3(a.count), dim3(mkd::kThreads), args, 0, s));
   }
   return MK_OK;
 }
