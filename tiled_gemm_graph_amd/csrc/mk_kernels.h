@@ -143,8 +143,10 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
 
 // Barrier that orders LDS traffic only (global loads stay in flight).
 __device__ __forceinline__ void lds_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
   __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0); vmcnt and expcnt untouched
   __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
 // Wave index as a scalar: branches on it are taken per wave (no exec
@@ -153,9 +155,12 @@ __device__ __forceinline__ void lds_barrier() {
 // code that every wave runs would also drain the other waves' streams.
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6); }
 
+// Base of operand o.  The slot is the same in every lane; saying so keeps
+// the table read a scalar load instead of a vector-memory load that would
+// have to complete behind every load a wave has in flight.
 template <typename T>
 __device__ __forceinline__ T* buf(const KArgs& a, const mk_operand& o) {
-  return reinterpret_cast<T*>(a.bufs[o.slot]) + o.off;
+  return reinterpret_cast<T*>(a.bufs[__builtin_amdgcn_readfirstlane(o.slot)]) + o.off;
 }
 
 // ------------------------------------------------------------- epilogue
