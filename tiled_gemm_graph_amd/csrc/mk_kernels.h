@@ -1588,6 +1588,11 @@ __device__ __forceinline__ int gemv_streak(const Loop& L, int& it, int& w) {
     if (tr) stamp(a, gidx, 0, wall_clock64());
     if (!wait_sources(L, in, it, gidx, w)) return -1;
     if (tr) stamp(a, gidx, 1, wall_clock64());
+    // Record it + 2 goes to its slot now, while its load is surely complete:
+    // after the release it would wait behind the release's own atomic (the
+    // vector-memory counter retires in order).  Nothing reads that slot
+    // before the next counter wait's barrier.
+    store_ahead(L, it, w);
     // the next record became visible with the barrier in wait_sources
     const mk_instr* nx = nullptr;
     const mk_node* nxd = nullptr;
@@ -1602,7 +1607,6 @@ __device__ __forceinline__ int gemv_streak(const Loop& L, int& it, int& w) {
     if (tr) stamp(a, gidx, 2, wall_clock64());
     release_gemv(a, in, nd);
     if (tr) stamp(a, gidx, 3, wall_clock64());
-    store_ahead(L, it, w);
     ++it;
     if (!nx) return 0;
   }
