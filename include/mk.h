@@ -44,11 +44,13 @@
 extern "C" {
 #endif
 
-#define MK_ABI_VERSION 1
+#define MK_ABI_VERSION 2
 #define MK_MAX_TENSORS 64       /* graph tensors incl. views and internals */
 #define MK_MAX_SRC 16           /* counters one instruction waits on       */
 #define MK_MAX_DST 8            /* counters one instruction arrives on     */
 #define MK_INSTR_WORDS 64       /* int32 words per instruction record      */
+#define MK_SLICE_MIN 32         /* counters with at least this target are
+                                   kept as one slot per arrival (below)    */
 #define MK_NODE_WORDS 64        /* int32 words per node descriptor         */
 
 typedef enum {
@@ -189,11 +191,26 @@ typedef struct {
   int32_t c0, c1;      /* output columns [c0, c1) (attention: head h in c0)*/
   int32_t k0, k1;      /* K range of a GEMM / GEMV instruction             */
   int32_t split_idx;   /* K chunk index (partials plane)                   */
-  int32_t src_id[MK_MAX_SRC];
-  int32_t src_target[MK_MAX_SRC];
-  int32_t dst_id[MK_MAX_DST];
-  int32_t reserved[MK_INSTR_WORDS - 16 - 2 * MK_MAX_SRC - MK_MAX_DST];
+  int32_t src_id[MK_MAX_SRC];     /* counters waited on, ascending        */
+  int32_t src_target[MK_MAX_SRC]; /* their targets (arrivals per run)     */
+  int32_t dst_id[MK_MAX_DST];     /* counters arrived on, ascending       */
+  int32_t dst_rank[MK_MAX_DST];   /* position of this instruction among the
+                                     arrivals of dst_id[k], ordered by
+                                     instruction index, when that counter's
+                                     target is >= MK_SLICE_MIN; else -1   */
 } mk_instr;
+
+/* Counters in device memory.  Counter b takes `stride` int32 slots at
+ * b * stride (stride = 1 when no target reaches MK_SLICE_MIN, else the
+ * largest such target rounded up to 32).  A counter with target T <
+ * MK_SLICE_MIN lives in its first slot: each arrival adds 1 (agent-scope
+ * atomic) and a waiter needs epoch * T there.  A counter with T >=
+ * MK_SLICE_MIN is sliced: arrival r (dst_rank) stores the epoch into slot r
+ * and a waiter needs every one of its T slots at the epoch.  Either way the
+ * counter's value, the sum of its slots, is epoch * T after a run, and a
+ * sliced counter's arrivals meet no contended read-modify-write: hundreds of
+ * producers adding to one word serialise at the memory side, which made up
+ * most of a whole-grid counter wait. */
 
 /* Operand of a node: buffer-table slot, element offset and row stride. */
 typedef struct {
@@ -325,8 +342,9 @@ mk_status mk_plan_weight_layout(const mk_plan *p, int32_t tensor, int32_t *packe
  * does not pack. */
 mk_status mk_plan_pack_weight(mk_plan *p, int32_t tensor, const void *src, void *dst,
                               void *stream);
-/* Copy the counters to host memory after a run (synchronises `stream`).
- * After e runs every counter equals e * its target. */
+/* Copy the counters (each the sum of its slots) to host memory after a run
+ * (synchronises `stream`).  After e runs every counter equals e * its
+ * target. */
 mk_status mk_plan_read_counters(mk_plan *p, int32_t *host, int64_t n, void *stream);
 /* Runs so far (the epoch the next run waits against is this + 1). */
 mk_status mk_plan_epoch(const mk_plan *p, int64_t *epoch);

@@ -85,6 +85,12 @@ BIAS, RELU, RESIDUAL, SILU_MUL, RMSNORM_INPUT, ROPE, PARTIAL = (
     1, 2, 4, 8, 16, 32, 64)
 
 MAX_SRC, MAX_DST = 16, 8
+# Counters with at least this many arrivals are kept as one slot per arrival
+# (this library's encoding of a counter in device memory, not a step of the
+# method): each arriving instruction then carries its rank, its position
+# among the counter's arrivals in instruction order; smaller counters carry
+# rank -1.
+SLICE_MIN = 32
 DTYPE_BYTES = {"f16": 2, "bf16": 2, "f32": 4}
 
 
@@ -530,12 +536,13 @@ def schedule(g: Graph, ncu: int, cluster_size: int = 1, reuse: int = 0) -> Sched
     order = sorted(keys.values(), key=lambda b: (b["first"], b["kind"], b["node"]))
     targets = [len(b["arrive"]) for b in order]
     src: Dict[int, List[Tuple[int, int]]] = {}
-    dst: Dict[int, List[int]] = {}
+    dst: Dict[int, List[Tuple[int, int]]] = {}
     for bid, b in enumerate(order):
         for i in b["wait"]:
             src.setdefault(i, []).append((bid, len(b["arrive"])))
-        for i in b["arrive"]:
-            dst.setdefault(i, []).append(bid)
+        sliced = len(b["arrive"]) >= SLICE_MIN
+        for rank, i in enumerate(b["arrive"]):
+            dst.setdefault(i, []).append((bid, rank if sliced else -1))
             assert i < b["first"], "dependency must point to a lower index"
 
     records = []

@@ -25,7 +25,7 @@ def test_library_exports_every_declared_symbol():
     for n in names:
         assert hasattr(lib, n), n
     assert set(L.EXPORTS) <= set(names)
-    assert lib.mk_abi_version() == 1
+    assert lib.mk_abi_version() == 2
 
 
 def test_struct_layout_matches_decoder(tmp_path):
@@ -35,10 +35,10 @@ def test_struct_layout_matches_decoder(tmp_path):
 #include <stdio.h>
 #include "mk.h"
 int main(void) {
-  printf("%zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu\\n", sizeof(mk_instr), sizeof(mk_node),
+  printf("%zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu\\n", sizeof(mk_instr), sizeof(mk_node),
     offsetof(mk_instr, opcode)/4, offsetof(mk_instr, n_src)/4, offsetof(mk_instr, coord)/4,
     offsetof(mk_instr, r0)/4, offsetof(mk_instr, split_idx)/4, offsetof(mk_instr, src_id)/4,
-    offsetof(mk_instr, src_target)/4, offsetof(mk_instr, dst_id)/4,
+    offsetof(mk_instr, src_target)/4, offsetof(mk_instr, dst_id)/4, offsetof(mk_instr, dst_rank)/4,
     sizeof(mk_tile), sizeof(mk_op_attrs));
   printf("%zu %zu %zu\\n", sizeof(mk_build_options), sizeof(mk_plan_stats), sizeof(mk_run_error));
   return 0;
@@ -49,9 +49,10 @@ int main(void) {
     l1, l2 = subprocess.check_output([str(exe)]).decode().split("\n")[:2]
     v = [int(x) for x in l1.split()]
     assert v[:2] == [256, 256]
-    assert v[2:10] == [L.W_OPCODE, L.W_NSRC, L.W_COORD, L.W_R0, L.W_SPLIT, L.W_SRC_ID,
-                       L.W_SRC_TGT, L.W_DST_ID]
-    assert v[10] == ctypes.sizeof(L.Tile) and v[11] == ctypes.sizeof(L.OpAttrs)
+    assert v[2:11] == [L.W_OPCODE, L.W_NSRC, L.W_COORD, L.W_R0, L.W_SPLIT, L.W_SRC_ID,
+                       L.W_SRC_TGT, L.W_DST_ID, L.W_DST_RANK]
+    assert L.W_DST_RANK + L.MAX_DST == L.INSTR_WORDS
+    assert v[11] == ctypes.sizeof(L.Tile) and v[12] == ctypes.sizeof(L.OpAttrs)
     w = [int(x) for x in l2.split()]
     assert w == [ctypes.sizeof(L.BuildOptions), ctypes.sizeof(L.PlanStats),
                  ctypes.sizeof(L.RunError)]
@@ -226,3 +227,29 @@ def test_unsupported_profile_builds_but_does_not_run():
     with pytest.raises(L.MkError) as e:
         plan.run([], stream=0)
     assert e.value.status == L.MK_E_UNSUPPORTED
+
+
+@pytest.mark.parametrize("wl", ["decode", "layer", "mlp3"])
+def test_arrival_ranks_slice_large_counters(wl):
+    # A counter with target >= SLICE_MIN is one slot per arrival: its
+    # arrivals carry ranks 0 .. target-1 in instruction order; a smaller
+    # counter's arrivals carry -1.
+    d = workloads.small_dims(wl) if wl != "decode" else workloads.default_dims(wl)
+    plan = G.build(wl, d).build(num_cus=256)
+    targets = list(plan.barriers())
+    arrivals = {}
+    for rec in plan.decoded():
+        for (b, rank) in rec[8]:
+            arrivals.setdefault(b, []).append((rec[0], rank))
+    assert sorted(arrivals) == list(range(len(targets)))
+    sliced = 0
+    for b, arr in arrivals.items():
+        assert len(arr) == targets[b]
+        ranks = [r for (_, r) in sorted(arr)]
+        if targets[b] >= L.SLICE_MIN:
+            sliced += 1
+            assert ranks == list(range(targets[b]))
+        else:
+            assert ranks == [-1] * targets[b]
+    if wl == "decode":
+        assert sliced >= 3   # the whole-grid waits between the four GEMVs

@@ -31,6 +31,8 @@ W_R0, W_R1, W_C0, W_C1, W_K0, W_K1, W_SPLIT = 9, 10, 11, 12, 13, 14, 15
 W_SRC_ID = 16
 W_SRC_TGT = W_SRC_ID + MAX_SRC
 W_DST_ID = W_SRC_TGT + MAX_SRC
+W_DST_RANK = W_DST_ID + MAX_DST
+SLICE_MIN = 32   # counters with a target this large are one slot per arrival
 
 
 class MkError(RuntimeError):
@@ -124,7 +126,7 @@ def load() -> ctypes.CDLL:
         f = getattr(L, name)
         f.argtypes = args
         f.restype = res
-    if L.mk_abi_version() != 1:
+    if L.mk_abi_version() != 2:
         raise ImportError("libmk.so ABI version mismatch")
     _lib = L
     return L

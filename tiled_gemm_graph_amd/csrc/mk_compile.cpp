@@ -929,7 +929,7 @@ struct Compiler {
     const I64 n_iters = cdiv(p.n_instr, ncu);
     p.records.assign((size_t)(n_iters * ncu), mk_instr{});
     std::vector<std::vector<std::pair<int, int>>> src(p.n_instr);
-    std::vector<std::vector<int>> dst(p.n_instr);
+    std::vector<std::vector<std::pair<int, int>>> dst(p.n_instr);   // (counter, arrival rank or -1)
     p.targets.clear();
     I64 n_in = 0, n_re = 0;
     for (size_t b = 0; b < bars.size(); ++b) {
@@ -938,9 +938,13 @@ struct Compiler {
       p.targets.push_back(tgt);
       (B.kind ? n_re : n_in)++;
       for (int i : B.wait) src[i].push_back({(int)b, tgt});
-      for (int i : B.arrive) {
+      std::vector<int> arrive = B.arrive;
+      std::sort(arrive.begin(), arrive.end());
+      const bool sliced = tgt >= MK_SLICE_MIN;
+      for (size_t r = 0; r < arrive.size(); ++r) {
+        const int i = arrive[r];
         if (i >= B.first) fail(MK_E_INVALID, "internal: dependency on a later instruction");
-        dst[i].push_back((int)b);
+        dst[i].push_back({(int)b, sliced ? (int)r : -1});
       }
     }
     for (size_t ni = 0; ni < p.nodes.size(); ++ni) {
@@ -984,7 +988,10 @@ struct Compiler {
           r.src_id[k] = s[k].first;
           r.src_target[k] = s[k].second;
         }
-        for (size_t k = 0; k < t.size(); ++k) r.dst_id[k] = t[k];
+        for (size_t k = 0; k < t.size(); ++k) {
+          r.dst_id[k] = t[k].first;
+          r.dst_rank[k] = t[k].second;
+        }
       }
     }
     mk_plan_stats& st = p.stats;

@@ -53,6 +53,7 @@ struct KArgs {
   int n_iters, ncu, epoch;
   int first, count;         // per-op mode: records [first, first + count)
   int n_nodes;
+  int ctr_stride;           // int32 slots per counter (see mk.h)
   unsigned long long* trace; // optional: 4 wall-clock stamps per instruction
   void* bufs[MK_MAX_TENSORS];
 };
@@ -1439,15 +1440,28 @@ __device__ __forceinline__ void copy_words(int* dst, const int* src) {
   if (threadIdx.x < 64) dst[threadIdx.x] = src[threadIdx.x];
 }
 
+// Arrival on the destination counters, lane k of the controller wave
+// taking dst k: a sliced counter's slot dst_rank receives the epoch, others
+// get an agent-scope add (the counter layout of mk.h).  Callers have made
+// the instruction's results visible at agent scope first.
+__device__ __forceinline__ void arrive(const KArgs& a, const mk_instr& in) {
+  const int lane = threadIdx.x & 63;
+  if (lane < in.n_dst) {
+    int* c = a.counters + (long)in.dst_id[lane] * a.ctr_stride;
+    const int rank = in.dst_rank[lane];
+    if (rank >= 0) __hip_atomic_store(c + rank, a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else __hip_atomic_fetch_add(c, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
 __device__ __forceinline__ void release_dests(const KArgs& a, const mk_instr& in) {
   // every wave: its stores have completed; then one lane makes them visible
   // at agent scope and arrives on each destination counter
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  if (threadIdx.x == 0 && in.n_dst) {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    for (int k = 0; k < in.n_dst; ++k)
-      __hip_atomic_fetch_add(a.counters + in.dst_id[k], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (wave_id() == 0 && in.n_dst) {
+    if (threadIdx.x == 0) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    arrive(a, in);
   }
 }
 
@@ -1488,36 +1502,86 @@ __device__ __forceinline__ int fetch_ahead(const Loop& L, int it) {
 // waves then meet at an LDS-only barrier, so the weight waves keep their
 // loads in flight.
 // Returns false (uniformly) if the run was aborted.
-__device__ __forceinline__ bool wait_sources(const Loop& L, const mk_instr& in, int it, int gidx, int& w) {
+// Controller wave: wait until every source counter holds its target for
+// this run.  The counters' slots are polled in groups of up to four (a
+// counter below MK_SLICE_MIN is one group of one slot), each lane taking up
+// to kPollGroups groups at a time, so all waits overlap.  Returns whether
+// every source cleared (false: the run was aborted).  No barrier.
+constexpr int kPollGroups = 2;
+__device__ __forceinline__ bool poll_sources(const Loop& L, const mk_instr& in, int gidx) {
   const KArgs& a = L.a;
-  if (wave_id() == 0) {
-    w = fetch_ahead(L, it);
-    // lane k polls source counter k, so the waits overlap
-    const int lane = threadIdx.x;
-    int ok = 1;
-    if (lane < in.n_src) {
-      const int id = in.src_id[lane];
-      const int need = a.epoch * in.src_target[lane];
-      const long long t0 = wall_clock64();
-      int v;
-      while ((v = __hip_atomic_load(a.counters + id, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) < need) {
-        if (__hip_atomic_load(a.err + 6, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) { ok = 0; break; }
-        if (wall_clock64() - t0 > a.spin_ticks) {
-          if (atomicCAS(a.err, 0, (int)MK_E_DEADLOCK) == 0) {
-            a.err[1] = L.vcu; a.err[2] = gidx; a.err[3] = id; a.err[4] = v; a.err[5] = need;
-          }
-          __hip_atomic_store(a.err + 6, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          ok = 0;
+  const int lane = threadIdx.x & 63;
+  const int ns = in.n_src;
+  int groups = 0;
+  for (int k = 0; k < ns; ++k) {
+    const int T = in.src_target[k];
+    groups += T >= MK_SLICE_MIN ? (T + 3) >> 2 : 1;
+  }
+  int ok = 1;
+  for (int g0 = 0; g0 < groups; g0 += 64 * kPollGroups) {
+    // this lane's groups: first slot, slot count, value needed per slot
+    const int* p[kPollGroups];
+    int cnt[kPollGroups], need[kPollGroups], cid[kPollGroups];
+#pragma unroll
+    for (int j = 0; j < kPollGroups; ++j) {
+      cnt[j] = 0;
+      p[j] = a.counters;
+      need[j] = 0;
+      cid[j] = 0;
+      int g = g0 + lane + 64 * j;
+      if (g >= groups) continue;
+      for (int k = 0; k < ns; ++k) {
+        const int T = in.src_target[k];
+        const bool sl = T >= MK_SLICE_MIN;
+        const int w = sl ? (T + 3) >> 2 : 1;
+        if (g < w) {
+          p[j] = a.counters + (long)in.src_id[k] * a.ctr_stride + (sl ? 4 * g : 0);
+          cnt[j] = sl ? min(4, T - 4 * g) : 1;
+          need[j] = sl ? a.epoch : a.epoch * T;
+          cid[j] = in.src_id[k];
           break;
         }
-        __builtin_amdgcn_s_sleep(1);
+        g -= w;
       }
     }
-    const int all_ok = __all(ok);
-    if (lane == 0) {
-      if (all_ok && in.n_src) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-      *L.flag = all_ok;
+    const long long t0 = wall_clock64();
+    for (;;) {
+      int ready = 1, seen = 0, want = 0, who = 0;
+#pragma unroll
+      for (int j = 0; j < kPollGroups; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (e < cnt[j]) {
+            const int v = __hip_atomic_load(p[j] + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (v < need[j] && ready) {
+              ready = 0;
+              seen = v;
+              want = need[j];
+              who = cid[j];
+            }
+          }
+      if (ready) break;
+      if (__hip_atomic_load(a.err + 6, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) { ok = 0; break; }
+      if (wall_clock64() - t0 > a.spin_ticks) {
+        if (atomicCAS(a.err, 0, (int)MK_E_DEADLOCK) == 0) {
+          a.err[1] = L.vcu; a.err[2] = gidx; a.err[3] = who; a.err[4] = seen; a.err[5] = want;
+        }
+        __hip_atomic_store(a.err + 6, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        ok = 0;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
     }
+    if (!__all(ok)) return false;
+  }
+  if (ns && lane == 0) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  return true;
+}
+__device__ __forceinline__ bool wait_sources(const Loop& L, const mk_instr& in, int it, int gidx, int& w) {
+  if (wave_id() == 0) {
+    w = fetch_ahead(L, it);
+    const bool ok = poll_sources(L, in, gidx);
+    if (threadIdx.x == 0) *L.flag = ok;
   }
   lds_barrier();
   return *L.flag != 0;
@@ -1562,10 +1626,9 @@ __device__ __forceinline__ void release_gemv(const KArgs& a, const mk_instr& in,
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   __builtin_amdgcn_s_waitcnt(0);  // wave 0's stores have completed
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  if (threadIdx.x == 0 && in.n_dst) {
-    if (!nd.layout) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    for (int k = 0; k < in.n_dst; ++k)
-      __hip_atomic_fetch_add(a.counters + in.dst_id[k], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (in.n_dst) {
+    if (!nd.layout && threadIdx.x == 0) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    arrive(a, in);
   }
 }
 

@@ -27,6 +27,8 @@ struct mk_plan_device {
   std::vector<void*> owned;   // by slot (plan-owned buffers), else nullptr
   long long spin_ticks = 0;
   int max_target = 1;
+  int ctr_stride = 1;         // int32 slots per counter (counter layout of mk.h)
+  size_t ctr_slots = 1;
   unsigned ops = 0;           // op families of the plan's instructions
 };
 
@@ -182,9 +184,11 @@ mk_status ensure_device(mk_plan* p) {
   if ((e = hipMalloc(&d->d_nodes, std::max<size_t>(nd_bytes, 256))) != hipSuccess) return bail(e, "hipMalloc nodes");
   if (nd_bytes && (e = hipMemcpy(d->d_nodes, p->node_descs.data(), nd_bytes, hipMemcpyHostToDevice)) != hipSuccess)
     return bail(e, "hipMemcpy nodes");
-  const size_t nb = std::max<size_t>(p->targets.size(), 1);
-  if ((e = hipMalloc(&d->d_counters, nb * sizeof(int))) != hipSuccess) return bail(e, "hipMalloc counters");
-  if ((e = hipMemset(d->d_counters, 0, nb * sizeof(int))) != hipSuccess) return bail(e, "hipMemset counters");
+  for (int32_t t : p->targets)
+    if (t >= MK_SLICE_MIN) d->ctr_stride = std::max(d->ctr_stride, (int)((t + 31) / 32 * 32));
+  d->ctr_slots = std::max<size_t>(p->targets.size(), 1) * (size_t)d->ctr_stride;
+  if ((e = hipMalloc(&d->d_counters, d->ctr_slots * sizeof(int))) != hipSuccess) return bail(e, "hipMalloc counters");
+  if ((e = hipMemset(d->d_counters, 0, d->ctr_slots * sizeof(int))) != hipSuccess) return bail(e, "hipMemset counters");
   if ((e = hipMalloc(&d->d_err, 8 * sizeof(int))) != hipSuccess) return bail(e, "hipMalloc error record");
   if ((e = hipMemset(d->d_err, 0, 8 * sizeof(int))) != hipSuccess) return bail(e, "hipMemset error record");
   for (int32_t t : p->targets) d->max_target = std::max(d->max_target, (int)t);
@@ -246,6 +250,7 @@ mk_status fill_args(mk_plan* p, void* const* buffers, int n_buffers, mkd::KArgs&
   a.instrs = p->dev->d_instrs;
   a.nodes = p->dev->d_nodes;
   a.counters = p->dev->d_counters;
+  a.ctr_stride = p->dev->ctr_stride;
   a.err = p->dev->d_err;
   a.spin_ticks = p->dev->spin_ticks;
   a.n_iters = (int)p->stats.n_iters;
@@ -270,7 +275,7 @@ mk_status megakernel_run_traced(mk_plan* p, void* const* buffers, int n_buffers,
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   // counters hold epoch * target; restart from zero well before int32 overflow
   if ((p->epoch + 1) * (int64_t)p->dev->max_target > (1LL << 30)) {
-    HIPCHK(hipMemsetAsync(p->dev->d_counters, 0, std::max<size_t>(p->targets.size(), 1) * sizeof(int), s));
+    HIPCHK(hipMemsetAsync(p->dev->d_counters, 0, p->dev->ctr_slots * sizeof(int), s));
     p->epoch = 0;
   }
   a.epoch = (int)(p->epoch + 1);
@@ -320,7 +325,7 @@ mk_status mk_plan_check(mk_plan* p, void* stream, mk_run_error* err) {
     if (h[0] != 0 || h[6] != 0) {
       // the aborted run left counters mid-epoch: start over from zero
       HIPCHK(hipMemset(p->dev->d_err, 0, 8 * sizeof(int)));
-      HIPCHK(hipMemset(p->dev->d_counters, 0, std::max<size_t>(p->targets.size(), 1) * sizeof(int)));
+      HIPCHK(hipMemset(p->dev->d_counters, 0, p->dev->ctr_slots * sizeof(int)));
       p->epoch = 0;
       if (err) *err = r;
       set_error("counter wait gave up: cu " + std::to_string(r.cu) + " instr " + std::to_string(r.instr) +
@@ -342,7 +347,18 @@ mk_status mk_plan_read_counters(mk_plan* p, int32_t* host, int64_t n, void* stre
   }
   HIPCHK(hipStreamSynchronize(reinterpret_cast<hipStream_t>(stream)));
   if (!p->targets.empty())
-    HIPCHK(hipMemcpy(host, p->dev->d_counters, p->targets.size() * sizeof(int32_t), hipMemcpyDeviceToHost));
+  {
+    // each counter is the sum of its slots
+    std::vector<int32_t> slots(p->dev->ctr_slots);
+    HIPCHK(hipMemcpy(slots.data(), p->dev->d_counters, slots.size() * sizeof(int32_t), hipMemcpyDeviceToHost));
+    const int st = p->dev->ctr_stride;
+    for (size_t b = 0; b < p->targets.size(); ++b) {
+      const int w = p->targets[b] >= MK_SLICE_MIN ? p->targets[b] : 1;
+      int64_t v = 0;
+      for (int k = 0; k < w; ++k) v += slots[b * st + k];
+      host[b] = (int32_t)v;
+    }
+  }
   return MK_OK;
 }
 

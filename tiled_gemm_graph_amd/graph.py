@@ -214,14 +214,14 @@ class Plan:
 
     def decoded(self) -> List[tuple]:
         """Records as (index, cu, iteration, opcode, flags, node, coords,
-        ((counter, target), ...), (counter, ...))."""
+        ((counter, target), ...), ((counter, arrival rank or -1), ...))."""
         w = self.instructions()
         ncu = self.stats().num_cus
         out = []
         for i, r in enumerate(w):
             ns, nd = int(r[L.W_NSRC]), int(r[L.W_NDST])
             src = tuple((int(r[L.W_SRC_ID + k]), int(r[L.W_SRC_TGT + k])) for k in range(ns))
-            dst = tuple(int(r[L.W_DST_ID + k]) for k in range(nd))
+            dst = tuple((int(r[L.W_DST_ID + k]), int(r[L.W_DST_RANK + k])) for k in range(nd))
             out.append((i, i % ncu, i // ncu, int(r[L.W_OPCODE]), int(r[L.W_FLAGS]),
                         int(r[L.W_NODE]), tuple(int(x) for x in r[L.W_COORD:L.W_COORD + 4]),
                         src, dst))
