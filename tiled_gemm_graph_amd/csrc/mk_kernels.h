@@ -1579,7 +1579,7 @@ __device__ __forceinline__ bool poll_sources(const Loop& L, const mk_instr& in, 
 }
 __device__ __forceinline__ bool wait_sources(const Loop& L, const mk_instr& in, int it, int gidx, int& w) {
   if (wave_id() == 0) {
-    w = fetch_ahead(L, it);
+    if (it > 0) w = fetch_ahead(L, it);
     const bool ok = poll_sources(L, in, gidx);
     if (threadIdx.x == 0) *L.flag = ok;
   }
@@ -1591,8 +1591,10 @@ __device__ __forceinline__ bool wait_sources(const Loop& L, const mk_instr& in, 
 // Every wave has passed this iteration's barriers, so none still reads the
 // record of iteration it - 1 that the slot held; the next iteration's
 // barrier publishes it.
+// (records 0, 1 and 2 are copied in at the start, so iteration 0 has
+// nothing to fetch or store)
 __device__ __forceinline__ void store_ahead(const Loop& L, int it, int w) {
-  if (wave_id() == 0 && it + 2 < L.a.n_iters)
+  if (wave_id() == 0 && it > 0 && it + 2 < L.a.n_iters)
     reinterpret_cast<int*>(&L.slots[(it + 2) % 3])[threadIdx.x & 63] = w;
 }
 
@@ -1693,7 +1695,7 @@ __global__ void __launch_bounds__(256, 1) mk_persistent(mkd::KArgs args) {
   const int vcu = (a.ncu % 8 == 0) ? (b % 8) * (a.ncu / 8) + b / 8 : b;
   for (int i = t; i < a.n_nodes * 64; i += mkd::kThreads)
     reinterpret_cast<int*>(s_nodes)[i] = reinterpret_cast<const int*>(a.nodes)[i];
-  for (int r = 0; r < 2 && r < a.n_iters; ++r)
+  for (int r = 0; r < 3 && r < a.n_iters; ++r)
     mkd::copy_words(reinterpret_cast<int*>(&s_in[r]), reinterpret_cast<const int*>(a.instrs + (long)r * a.ncu + vcu));
   __syncthreads();
   const mkd::Loop L{a, s_in, s_nodes, &s_flag, smem, vcu};
