@@ -97,11 +97,13 @@ namespace {
 // Smallest compiled kernel instance whose op families cover `ops`.
 const void* persistent_for(unsigned ops) {
   if ((ops & ~mkd::kOpGemv) == 0) return reinterpret_cast<const void*>(mk_persistent<mkd::kOpGemv>);
+  if ((ops & ~mkd::kOpGemm) == 0) return reinterpret_cast<const void*>(mk_persistent<mkd::kOpGemm>);
   if ((ops & mkd::kOpGemv) == 0) return reinterpret_cast<const void*>(mk_persistent<mkd::kOpGemm | mkd::kOpOther>);
   return reinterpret_cast<const void*>(mk_persistent<mkd::kOpAll>);
 }
 const void* node_kernel_for(unsigned ops) {
   if ((ops & ~mkd::kOpGemv) == 0) return reinterpret_cast<const void*>(mk_node_kernel<mkd::kOpGemv>);
+  if ((ops & ~mkd::kOpGemm) == 0) return reinterpret_cast<const void*>(mk_node_kernel<mkd::kOpGemm>);
   if ((ops & mkd::kOpGemv) == 0) return reinterpret_cast<const void*>(mk_node_kernel<mkd::kOpGemm | mkd::kOpOther>);
   return reinterpret_cast<const void*>(mk_node_kernel<mkd::kOpAll>);
 }
@@ -161,7 +163,8 @@ mk_status ensure_device(mk_plan* p) {
     set_error("device does not support cooperative launch");
     return MK_E_UNSUPPORTED;
   }
-  for (const void* k : {persistent_for(mkd::kOpAll), persistent_for(mkd::kOpGemv), persistent_for(mkd::kOpGemm | mkd::kOpOther)}) {
+  for (const void* k : {persistent_for(mkd::kOpAll), persistent_for(mkd::kOpGemv), persistent_for(mkd::kOpGemm),
+                        persistent_for(mkd::kOpGemm | mkd::kOpOther)}) {
     int blocks = 0;
     HIPCHK(hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, k, mkd::kThreads, 0));
     if (blocks < 1) {
