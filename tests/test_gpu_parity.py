@@ -2,6 +2,8 @@
 
 Every case prints its name and shapes before touching the GPU.
 """
+import ctypes
+
 import numpy as np
 import pytest
 import torch
@@ -179,3 +181,30 @@ def test_gemv_tile_shapes(bn, split):
     r.out.zero_()
     r.forward_per_op(); torch.cuda.synchronize()
     assert torch.equal(first, r.out)
+
+
+def test_tiny_spin_limit_gives_up_and_recovers():
+    # Counter waits bounded at 1 us give up long before the producers of the
+    # next node finish: the run ends (every workgroup exits) with
+    # MK_E_DEADLOCK and a record of the wait that gave up; the plan's
+    # counters start over from zero, and a plan with the default bound on the
+    # same inputs still matches the oracle.
+    d = workloads.default_dims("decode")
+    inp = workloads.generate("decode", d)
+    say("[gpu] decode full, spin_limit_us=1 (bounded waits give up)")
+    r = G.Runner("decode", d, inp, spin_limit_us=1)
+    r.forward()
+    err = L.RunError()
+    st = r.plan._lib.mk_plan_check(r.plan._p, r.plan._stream(None), ctypes.byref(err))
+    assert st == L.MK_E_DEADLOCK
+    assert err.code == L.MK_E_DEADLOCK
+    n_bar = len(r.plan.barriers())
+    assert 0 <= err.cu < 256 and 0 <= err.instr < r.plan.stats().n_instr
+    assert 0 <= err.barrier < n_bar and err.value < err.need
+    assert not np.any(r.plan.read_counters())
+    say("[gpu] decode full, default bound after the abort")
+    r2 = _run("decode", d, inp)
+    rel = rel_fro(to_np(r2.out), OG.run("decode", inp, d))
+    say(f"  rel={rel:.3e}")
+    assert rel <= TOL["bf16"]
+    _counters_ok(r2, 1)
