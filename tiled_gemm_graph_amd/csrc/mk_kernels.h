@@ -171,7 +171,23 @@ __device__ __forceinline__ T* buf(const KArgs& a, const mk_operand& o) {
 // at w + half for SILU_MUL).  gr, gc: global row / output column.  ROPE
 // rotates the values after BIAS and RESIDUAL, so the partner columns (half
 // a head away) take the same steps first.
-template <int DT, typename Raw>
+// 16-byte store that writes through to the device-coherent level (agent
+// scope, as the agent-scope atomic stores of the packed GEMV do): a release
+// after it needs only its completion, not an L2 write-back.
+__device__ __forceinline__ void store16_wt(void* p, const u32x4& v) {
+  asm volatile("global_store_dwordx4 %0, %1, off sc1" : : "v"(p), "v"(v) : "memory");
+}
+__device__ __forceinline__ void store_f32x8_wt(float* p, const float* s) {
+  u32x4 lo, hi;
+  lo.x = __float_as_uint(s[0]); lo.y = __float_as_uint(s[1]); lo.z = __float_as_uint(s[2]); lo.w = __float_as_uint(s[3]);
+  hi.x = __float_as_uint(s[4]); hi.y = __float_as_uint(s[5]); hi.z = __float_as_uint(s[6]); hi.w = __float_as_uint(s[7]);
+  store16_wt(p, lo);
+  store16_wt(p + 4, hi);
+}
+
+// WT: store through to the device-coherent level (GEMM and GEMV outputs,
+// released without an L2 write-back).
+template <int DT, bool WT = false, typename Raw>
 __device__ __forceinline__ void epilogue8(const KArgs& a, const mk_node& nd, int flags, int gr,
                                           int gc, int w, int half, Raw raw) {
   auto pre = [&](int ww, int cc, float* v) __attribute__((always_inline)) {
@@ -219,7 +235,9 @@ __device__ __forceinline__ void epilogue8(const KArgs& a, const mk_node& nd, int
 #pragma unroll
     for (int e = 0; e < 8; ++e) v[e] = fmaxf(v[e], 0.0f);
   }
-  *reinterpret_cast<u32x4*>(buf<u16>(a, nd.out) + (long)gr * nd.out.ld + gc) = pack8<DT>(v);
+  u16* dst = buf<u16>(a, nd.out) + (long)gr * nd.out.ld + gc;
+  if constexpr (WT) store16_wt(dst, pack8<DT>(v));
+  else *reinterpret_cast<u32x4*>(dst) = pack8<DT>(v);
 }
 
 // ------------------------------------------------------------------ GEMM
@@ -354,10 +372,7 @@ __device__ __forceinline__ void gemm_tile(const KArgs& a, const mk_instr& in, co
       const int j = w < half ? w : w - half;
       if (gr >= r1 || c0 + j >= c1) continue;
       const int gc = (silu && w >= half) ? N + c0 + j : c0 + j;
-      float4* dst = reinterpret_cast<float4*>(P + (long)gr * nd.part.ld + gc);
-      const float* s = Cs + row * CS + w;
-      dst[0] = make_float4(s[0], s[1], s[2], s[3]);
-      dst[1] = make_float4(s[4], s[5], s[6], s[7]);
+      store_f32x8_wt(P + (long)gr * nd.part.ld + gc, Cs + row * CS + w);
     }
     return;
   }
@@ -367,7 +382,7 @@ __device__ __forceinline__ void gemm_tile(const KArgs& a, const mk_instr& in, co
     const int row = u / (half / 8), w = (u % (half / 8)) * 8;
     const int gr = r0 + row, gc = c0 + w;
     if (gr >= r1 || gc >= c1) continue;
-    epilogue8<DT>(a, nd, flags, gr, gc, w, half, [&](int ww, float* o) {
+    epilogue8<DT, true>(a, nd, flags, gr, gc, w, half, [&](int ww, float* o) {
       const float* s = Cs + row * CS + ww;
 #pragma unroll
       for (int e = 0; e < 8; ++e) o[e] = s[e];
@@ -603,10 +618,8 @@ __device__ __forceinline__ void gemm_packed_tile(const KArgs& a, const mk_instr&
           pc = c0 + w;
           if (pc >= c1) continue;
         }
-        float4* dst = reinterpret_cast<float4*>(buf<float>(a, nd.part) + (long)in.split_idx * nd.part_plane +
-                                                (long)gr * nd.part.ld + pc);
-        dst[0] = make_float4(src[w], src[w + 1], src[w + 2], src[w + 3]);
-        dst[1] = make_float4(src[w + 4], src[w + 5], src[w + 6], src[w + 7]);
+        store_f32x8_wt(buf<float>(a, nd.part) + (long)in.split_idx * nd.part_plane + (long)gr * nd.part.ld + pc,
+                       src + w);
         continue;
       }
       int gc, ww, half;
@@ -623,7 +636,7 @@ __device__ __forceinline__ void gemm_packed_tile(const KArgs& a, const mk_instr&
         half = BN;
       }
       if (gc >= c1) continue;
-      epilogue8<DT>(a, nd, flags, gr, gc, ww, half, [&](int x, float* o) {
+      epilogue8<DT, true>(a, nd, flags, gr, gc, ww, half, [&](int x, float* o) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) o[e] = src[x + e];
       });
@@ -1046,7 +1059,8 @@ __device__ __forceinline__ void gemv_body(const KArgs& a, const mk_instr& in, co
     for (int i = t; i < rows * wc; i += 64) {
       const int m = i / wc, w = i % wc;
       const int gc = (silu && w >= bw) ? N + c0 + (w - bw) : c0 + w;
-      P[(long)(r0 + m) * nd.part.ld + gc] = sum[m * wc + w];
+      __hip_atomic_store(P + (long)(r0 + m) * nd.part.ld + gc, sum[m * wc + w], __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
     }
     return;
   }
@@ -1066,7 +1080,7 @@ __device__ __forceinline__ void gemv_body(const KArgs& a, const mk_instr& in, co
 #pragma unroll
     for (int mm = 0; mm < MAXR; ++mm)
       if (mm == m) sc = rinv[mm];
-    epilogue8<DT>(a, nd, flags, r0 + m, c0 + w, w, bw, [&](int ww, float* o) {
+    epilogue8<DT, true>(a, nd, flags, r0 + m, c0 + w, w, bw, [&](int ww, float* o) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) o[e] = sum[m * wc + ww + e] * sc;
     });
@@ -1486,7 +1500,8 @@ __device__ __forceinline__ void release_dests(const KArgs& a, const mk_instr& in
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (wave_id() == 0 && in.n_dst) {
-    if (threadIdx.x == 0) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    // GEMM tiles stored through to the coherent level: completion suffices
+    if (threadIdx.x == 0 && in.opcode != MK_I_GEMM) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     arrive(a, in);
   }
 }
@@ -1645,19 +1660,17 @@ __device__ __forceinline__ bool generic_iter(const Loop& L, int it, int& w) {
   return true;
 }
 
-// Release of a GEMV instruction: only the controller wave stored results.
-// A packed tile stored them with agent-scope (write-through) stores, so
-// their completion is enough and the L2 write-back of an agent-scope
-// release fence (about 1.7 us) is skipped; other tiles take the fence.
+// Release of a GEMV instruction: only the controller wave stored results,
+// all of them with stores that write through to the device-coherent level
+// (agent-scope atomic stores, or store16_wt), so their completion is enough
+// and the L2 write-back of an agent-scope release fence (about 1.7 us) is
+// skipped.
 __device__ __forceinline__ void release_gemv(const KArgs& a, const mk_instr& in, const mk_node& nd) {
   if (wave_id() != 0) return;
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   __builtin_amdgcn_s_waitcnt(0);  // wave 0's stores have completed
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  if (in.n_dst) {
-    if (!nd.layout && threadIdx.x == 0) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    arrive(a, in);
-  }
+  if (in.n_dst) arrive(a, in);
 }
 
 // A run of GEMV instructions with the weight stream carried across them.
