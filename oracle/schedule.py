@@ -233,6 +233,11 @@ def lower(g: Graph, ncu: int = 256) -> List[Node]:
                                       (k.tensor, k.box(0, kend, kh * d, kh * d + d)),
                                       (v.tensor, v.box(0, kend, kh * d, kh * d + d))],
                                      [(op.out, o.box(q0, q1, h * d, h * d + d))]))
+            # instruction j shares its CU with j + ncu: reverse every other
+            # run of ncu (most keys first, then fewest first) so each CU's
+            # causal work evens out
+            for c0 in range(ncu, len(ins), 2 * ncu):
+                ins[c0:c0 + ncu] = ins[c0:c0 + ncu][::-1]
             nodes.append(Node(oi, ATTENTION, 0, op.out, [q, k, v], ins))
         elif op.kind in ("add", "relu"):
             a = op.ins["a"]

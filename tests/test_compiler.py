@@ -253,3 +253,17 @@ def test_arrival_ranks_slice_large_counters(wl):
             assert ranks == [-1] * targets[b]
     if wl == "decode":
         assert sliced >= 3   # the whole-grid waits between the four GEMVs
+
+
+def test_causal_attention_work_even_across_cus():
+    # Each CU's attention blocks add up to about the same number of keys
+    # (instruction j and j + num_cus share a CU; runs alternate direction).
+    d = workloads.default_dims("layer")
+    plan = G.build("layer", d).build(num_cus=256)
+    w = plan.instructions()
+    att = np.nonzero(w[:, L.W_OPCODE] == L.I_ATTENTION)[0]
+    keys = np.zeros(256)
+    for i in att:
+        keys[i % 256] += w[i, L.W_R0 + 5]          # k1: keys the block visits
+    busy = keys[keys > 0]
+    assert busy.max() / busy.min() <= 1.15, (busy.min(), busy.max())

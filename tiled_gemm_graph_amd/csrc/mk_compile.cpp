@@ -649,6 +649,13 @@ struct Compiler {
         n.ins.push_back(in);
       }
     }
+    // Instruction j runs on the same CU as j + num_cus.  The list runs from
+    // the most keys (last query block) to the fewest, and every other run of
+    // num_cus instructions is reversed, so each CU's blocks add up to about
+    // the same work under the causal mask (a static form of longest-first
+    // scheduling).
+    for (size_t c0 = ncu; c0 < n.ins.size(); c0 += 2 * (size_t)ncu)
+      std::reverse(n.ins.begin() + c0, n.ins.begin() + std::min(n.ins.size(), c0 + (size_t)ncu));
     mk_node& dd = n.desc;
     dd.opcode = MK_I_ATTENTION;
     dd.dtype = dt;
