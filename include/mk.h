@@ -49,7 +49,7 @@ extern "C" {
 #define MK_MAX_SRC 16           /* counters one instruction waits on       */
 #define MK_MAX_DST 8            /* counters one instruction arrives on     */
 #define MK_INSTR_WORDS 64       /* int32 words per instruction record      */
-#define MK_SLICE_MIN 32         /* counters with at least this target are
+#define MK_SLICE_MAX 256        /* counters with at most this target are
                                    kept as one slot per arrival (below)    */
 #define MK_NODE_WORDS 64        /* int32 words per node descriptor         */
 
@@ -197,20 +197,21 @@ typedef struct {
   int32_t dst_rank[MK_MAX_DST];   /* position of this instruction among the
                                      arrivals of dst_id[k], ordered by
                                      instruction index, when that counter's
-                                     target is >= MK_SLICE_MIN; else -1   */
+                                     target is <= MK_SLICE_MAX; else -1   */
 } mk_instr;
 
 /* Counters in device memory.  Counter b takes `stride` int32 slots at
- * b * stride (stride = 1 when no target reaches MK_SLICE_MIN, else the
- * largest such target rounded up to 32).  A counter with target T <
- * MK_SLICE_MIN lives in its first slot: each arrival adds 1 (agent-scope
- * atomic) and a waiter needs epoch * T there.  A counter with T >=
- * MK_SLICE_MIN is sliced: arrival r (dst_rank) stores the epoch into slot r
- * and a waiter needs every one of its T slots at the epoch.  Either way the
- * counter's value, the sum of its slots, is epoch * T after a run, and a
- * sliced counter's arrivals meet no contended read-modify-write: hundreds of
- * producers adding to one word serialise at the memory side, which made up
- * most of a whole-grid counter wait. */
+ * b * stride, stride being the largest target up to MK_SLICE_MAX rounded up
+ * to 32 (so every counter starts a 128-byte line of its own).  A counter
+ * with target T <= MK_SLICE_MAX is sliced: arrival r (dst_rank) stores the
+ * epoch into slot r and a waiter needs every one of its T slots at the
+ * epoch.  A counter with a larger target lives in its first slot: each
+ * arrival adds 1 (agent-scope atomic) and a waiter needs epoch * T there.
+ * Either way the counter's value, the sum of its slots, is epoch * T after
+ * a run.  A sliced counter's arrivals meet no contended read-modify-write:
+ * hundreds of producers adding to one word serialise at the memory side,
+ * which made up most of a whole-grid counter wait, and even a handful of
+ * producers adding to one word wait on each other's round trips. */
 
 /* Operand of a node: buffer-table slot, element offset and row stride. */
 typedef struct {

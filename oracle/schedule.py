@@ -85,12 +85,12 @@ BIAS, RELU, RESIDUAL, SILU_MUL, RMSNORM_INPUT, ROPE, PARTIAL = (
     1, 2, 4, 8, 16, 32, 64)
 
 MAX_SRC, MAX_DST = 16, 8
-# Counters with at least this many arrivals are kept as one slot per arrival
+# Counters with at most this many arrivals are kept as one slot per arrival
 # (this library's encoding of a counter in device memory, not a step of the
 # method): each arriving instruction then carries its rank, its position
-# among the counter's arrivals in instruction order; smaller counters carry
+# among the counter's arrivals in instruction order; larger counters carry
 # rank -1.
-SLICE_MIN = 32
+SLICE_MAX = 256
 DTYPE_BYTES = {"f16": 2, "bf16": 2, "f32": 4}
 
 
@@ -545,7 +545,7 @@ def schedule(g: Graph, ncu: int, cluster_size: int = 1, reuse: int = 0) -> Sched
     for bid, b in enumerate(order):
         for i in b["wait"]:
             src.setdefault(i, []).append((bid, len(b["arrive"])))
-        sliced = len(b["arrive"]) >= SLICE_MIN
+        sliced = len(b["arrive"]) <= SLICE_MAX
         for rank, i in enumerate(b["arrive"]):
             dst.setdefault(i, []).append((bid, rank if sliced else -1))
             assert i < b["first"], "dependency must point to a lower index"

@@ -229,30 +229,30 @@ def test_unsupported_profile_builds_but_does_not_run():
     assert e.value.status == L.MK_E_UNSUPPORTED
 
 
-@pytest.mark.parametrize("wl", ["decode", "layer", "mlp3"])
-def test_arrival_ranks_slice_large_counters(wl):
-    # A counter with target >= SLICE_MIN is one slot per arrival: its
-    # arrivals carry ranks 0 .. target-1 in instruction order; a smaller
+@pytest.mark.parametrize("wl,reuse", [("decode", 0), ("layer", 0), ("mlp3", 0), ("layer", 1)])
+def test_arrival_ranks_slice_counters(wl, reuse):
+    # A counter with target <= SLICE_MAX is one slot per arrival: its
+    # arrivals carry ranks 0 .. target-1 in instruction order; a larger
     # counter's arrivals carry -1.
-    d = workloads.small_dims(wl) if wl != "decode" else workloads.default_dims(wl)
-    plan = G.build(wl, d).build(num_cus=256)
+    d = workloads.default_dims(wl) if wl in ("decode", "layer") else workloads.small_dims(wl)
+    plan = G.build(wl, d).build(num_cus=256, reuse=reuse)
     targets = list(plan.barriers())
     arrivals = {}
     for rec in plan.decoded():
         for (b, rank) in rec[8]:
             arrivals.setdefault(b, []).append((rec[0], rank))
     assert sorted(arrivals) == list(range(len(targets)))
-    sliced = 0
+    whole = 0
     for b, arr in arrivals.items():
         assert len(arr) == targets[b]
         ranks = [r for (_, r) in sorted(arr)]
-        if targets[b] >= L.SLICE_MIN:
-            sliced += 1
+        if targets[b] <= L.SLICE_MAX:
             assert ranks == list(range(targets[b]))
         else:
+            whole += 1
             assert ranks == [-1] * targets[b]
-    if wl == "decode":
-        assert sliced >= 3   # the whole-grid waits between the four GEMVs
+    # the full layer's reuse barriers wait on more arrivals than SLICE_MAX
+    assert (whole > 0) == (wl == "layer" and reuse == 1)
 
 
 def test_causal_attention_work_even_across_cus():

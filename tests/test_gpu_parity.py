@@ -141,6 +141,21 @@ def test_full_size_layer():
     _counters_ok(r, 1)
 
 
+def test_full_size_layer_buffer_reuse():
+    # With buffer reuse the layer's reuse barriers wait on more arrivals than
+    # L.SLICE_MAX, so they run as single atomic words beside sliced counters.
+    d = workloads.default_dims("layer")
+    inp = workloads.generate("layer", d)
+    r = _run("layer", d, inp, n=2, reuse=1)
+    assert r.plan.barriers().max() > L.SLICE_MAX
+    ref = OG.layer(inp, d)
+    got = to_np(r.out)
+    rel = rel_fro(got, ref)
+    say(f"  layer full reuse=1: rel={rel:.3e} maxabs={max_abs(got, ref)}")
+    assert rel <= TOL["bf16"]
+    _counters_ok(r, 2)
+
+
 def test_empty_rows_graph_runs():
     g = G.Graph()
     x = g.tensor("x", "f16", (0, 64), "input")

@@ -32,7 +32,7 @@ W_SRC_ID = 16
 W_SRC_TGT = W_SRC_ID + MAX_SRC
 W_DST_ID = W_SRC_TGT + MAX_SRC
 W_DST_RANK = W_DST_ID + MAX_DST
-SLICE_MIN = 32   # counters with a target this large are one slot per arrival
+SLICE_MAX = 256  # counters with at most this target are one slot per arrival
 
 
 class MkError(RuntimeError):

@@ -947,7 +947,7 @@ struct Compiler {
       for (int i : B.wait) src[i].push_back({(int)b, tgt});
       std::vector<int> arrive = B.arrive;
       std::sort(arrive.begin(), arrive.end());
-      const bool sliced = tgt >= MK_SLICE_MIN;
+      const bool sliced = tgt <= MK_SLICE_MAX;
       for (size_t r = 0; r < arrive.size(); ++r) {
         const int i = arrive[r];
         if (i >= B.first) fail(MK_E_INVALID, "internal: dependency on a later instruction");

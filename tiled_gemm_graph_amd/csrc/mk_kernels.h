@@ -1545,7 +1545,7 @@ __device__ __forceinline__ int fetch_ahead(const Loop& L, int it) {
 // Returns false (uniformly) if the run was aborted.
 // Controller wave: wait until every source counter holds its target for
 // this run.  The counters' slots are polled in groups of up to four (a
-// counter below MK_SLICE_MIN is one group of one slot), each lane taking up
+// counter above MK_SLICE_MAX is one group of one slot), each lane taking up
 // to kPollGroups groups at a time, so all waits overlap.  Returns whether
 // every source cleared (false: the run was aborted).  No barrier.
 constexpr int kPollGroups = 2;
@@ -1556,7 +1556,7 @@ __device__ __forceinline__ bool poll_sources(const Loop& L, const mk_instr& in, 
   int groups = 0;
   for (int k = 0; k < ns; ++k) {
     const int T = in.src_target[k];
-    groups += T >= MK_SLICE_MIN ? (T + 3) >> 2 : 1;
+    groups += T <= MK_SLICE_MAX ? (T + 3) >> 2 : 1;
   }
   int ok = 1;
   for (int g0 = 0; g0 < groups; g0 += 64 * kPollGroups) {
@@ -1573,7 +1573,7 @@ __device__ __forceinline__ bool poll_sources(const Loop& L, const mk_instr& in, 
       if (g >= groups) continue;
       for (int k = 0; k < ns; ++k) {
         const int T = in.src_target[k];
-        const bool sl = T >= MK_SLICE_MIN;
+        const bool sl = T <= MK_SLICE_MAX;
         const int w = sl ? (T + 3) >> 2 : 1;
         if (g < w) {
           p[j] = a.counters + (long)in.src_id[k] * a.ctr_stride + (sl ? 4 * g : 0);

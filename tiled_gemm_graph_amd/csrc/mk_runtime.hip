@@ -188,7 +188,7 @@ mk_status ensure_device(mk_plan* p) {
   if (nd_bytes && (e = hipMemcpy(d->d_nodes, p->node_descs.data(), nd_bytes, hipMemcpyHostToDevice)) != hipSuccess)
     return bail(e, "hipMemcpy nodes");
   for (int32_t t : p->targets)
-    if (t >= MK_SLICE_MIN) d->ctr_stride = std::max(d->ctr_stride, (int)((t + 31) / 32 * 32));
+    if (t <= MK_SLICE_MAX) d->ctr_stride = std::max(d->ctr_stride, (int)((t + 31) / 32 * 32));
   d->ctr_slots = std::max<size_t>(p->targets.size(), 1) * (size_t)d->ctr_stride;
   if ((e = hipMalloc(&d->d_counters, d->ctr_slots * sizeof(int))) != hipSuccess) return bail(e, "hipMalloc counters");
   if ((e = hipMemset(d->d_counters, 0, d->ctr_slots * sizeof(int))) != hipSuccess) return bail(e, "hipMemset counters");
@@ -356,7 +356,7 @@ mk_status mk_plan_read_counters(mk_plan* p, int32_t* host, int64_t n, void* stre
     HIPCHK(hipMemcpy(slots.data(), p->dev->d_counters, slots.size() * sizeof(int32_t), hipMemcpyDeviceToHost));
     const int st = p->dev->ctr_stride;
     for (size_t b = 0; b < p->targets.size(); ++b) {
-      const int w = p->targets[b] >= MK_SLICE_MIN ? p->targets[b] : 1;
+      const int w = p->targets[b] <= MK_SLICE_MAX ? p->targets[b] : 1;
       int64_t v = 0;
       for (int k = 0; k < w; ++k) v += slots[b * st + k];
       host[b] = (int32_t)v;
