@@ -296,54 +296,72 @@ __device__ __forceinline__ void gemm_tile(const KArgs& a, const mk_instr& in, co
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-  u32x4 ra[A_CHUNKS], rb[RB];
-  auto gload = [&](int kt) __attribute__((always_inline)) {
+  // Global loads run D K steps ahead in a register ring (slot kt % D holds
+  // step kt), about 128 registers whatever the tile: with one K step's MFMA
+  // work as small as a 64 x 64 tile's, a single step of look-ahead leaves
+  // every step waiting out a full memory round trip.  Steps past the end
+  // re-read the last one, so every step issues the same loads and each wait
+  // leaves the younger steps in flight.
+  constexpr int SREGS = 4 * (A_CHUNKS + RB);   // registers per K step
+  constexpr int D = (128 / SREGS) < 2 ? 2 : (128 / SREGS) > 8 ? 8 : (128 / SREGS);
+  u32x4 ra[D][A_CHUNKS], rb[D][RB];
+  auto gload = [&](int kt, int slot) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < A_CHUNKS; ++i) ra[i] = *reinterpret_cast<const u32x4*>(a_src[i] + kt * kBK);
+    for (int i = 0; i < A_CHUNKS; ++i) ra[slot][i] = *reinterpret_cast<const u32x4*>(a_src[i] + kt * kBK);
 #pragma unroll
-    for (int r = 0; r < RB; ++r) rb[r] = *reinterpret_cast<const u32x4*>(b_src + (long)(kt * kBK + r) * ldb);
+    for (int r = 0; r < RB; ++r) rb[slot][r] = *reinterpret_cast<const u32x4*>(b_src + (long)(kt * kBK + r) * ldb);
   };
-  auto swrite = [&](int st) __attribute__((always_inline)) {
+  auto swrite = [&](int st, int slot) __attribute__((always_inline)) {
     u16* as = As + st * A_STAGE;
 #pragma unroll
-    for (int i = 0; i < A_CHUNKS; ++i) *reinterpret_cast<u32x4*>(as + a_dst[i]) = ra[i];
+    for (int i = 0; i < A_CHUNKS; ++i) *reinterpret_cast<u32x4*>(as + a_dst[i]) = ra[slot][i];
     // transpose RB (k) x 8 (n) into 8 rows of Bt[n][k], RB k-values each
     u16* bs = Bs + st * B_STAGE + wcol * LDS_ROW + kq * RB;
 #pragma unroll
     for (int n = 0; n < 8; ++n) {
       if constexpr (RB == 4) {
-        *reinterpret_cast<u32x2*>(bs + n * LDS_ROW) = u32x2{pick2(rb[0], rb[1], n), pick2(rb[2], rb[3], n)};
+        *reinterpret_cast<u32x2*>(bs + n * LDS_ROW) =
+            u32x2{pick2(rb[slot][0], rb[slot][1], n), pick2(rb[slot][2], rb[slot][3], n)};
       } else {
-        *reinterpret_cast<uint32_t*>(bs + n * LDS_ROW) = pick2(rb[0], rb[1], n);
+        *reinterpret_cast<uint32_t*>(bs + n * LDS_ROW) = pick2(rb[slot][0], rb[slot][1], n);
       }
     }
   };
 
   const int nk = (k1 - k0) / kBK;
-  gload(0);
-  swrite(0);
+  if (nk > 0) {
+#pragma unroll
+    for (int s = 0; s < D - 1; ++s) gload(min(s, nk - 1), s);
+    swrite(0, 0);
+  }
   __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int st = kt & 1;
-    if (kt + 1 < nk) gload(kt + 1);
-    const u16* as = As + st * A_STAGE;
-    const u16* bs = Bs + st * B_STAGE;
+  for (int kt0 = 0; kt0 < nk; kt0 += D) {
 #pragma unroll
-    for (int kk = 0; kk < kBK / 16; ++kk) {
-      u32x4 af[FM], bf[FN];
+    for (int u = 0; u < D; ++u) {
+      const int kt = kt0 + u;
+      if (kt >= nk) break;
+      gload(min(kt + D - 1, nk - 1), (u + D - 1) % D);
+      const u16* as = As + (kt & 1) * A_STAGE;
+      const u16* bs = Bs + (kt & 1) * B_STAGE;
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
-        af[i] = *reinterpret_cast<const u32x4*>(as + (wm * WM + i * 32 + (lane & 31)) * LDS_ROW + kk * 16 + (lane >> 5) * 8);
+      for (int kk = 0; kk < kBK / 16; ++kk) {
+        u32x4 af[FM], bf[FN];
 #pragma unroll
-      for (int j = 0; j < FN; ++j)
-        bf[j] = *reinterpret_cast<const u32x4*>(bs + (wn * WN + j * 32 + (lane & 31)) * LDS_ROW + kk * 16 + (lane >> 5) * 8);
+        for (int i = 0; i < FM; ++i)
+          af[i] = *reinterpret_cast<const u32x4*>(as + (wm * WM + i * 32 + (lane & 31)) * LDS_ROW + kk * 16 +
+                                                  (lane >> 5) * 8);
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
+        for (int j = 0; j < FN; ++j)
+          bf[j] = *reinterpret_cast<const u32x4*>(bs + (wn * WN + j * 32 + (lane & 31)) * LDS_ROW + kk * 16 +
+                                                  (lane >> 5) * 8);
 #pragma unroll
-        for (int j = 0; j < FN; ++j) acc[i][j] = mfma32<DT>(af[i], bf[j], acc[i][j]);
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j) acc[i][j] = mfma32<DT>(af[i], bf[j], acc[i][j]);
+      }
+      if (kt + 1 < nk) swrite((kt + 1) & 1, (u + 1) % D);
+      __syncthreads();
     }
-    if (kt + 1 < nk) swrite(st ^ 1);
-    __syncthreads();
   }
 
   // accumulators -> fp32 LDS tile Cs[BM][BNK + 4]
@@ -428,7 +446,8 @@ __device__ __forceinline__ void g2lds16(const void* src, void* lds) {
 // the caller orders the loads itself (wait_vmcnt before the barrier that
 // precedes a stage's use).  dst is the wave-uniform LDS byte address of the
 // 1 KB block (lane L writes byte L * 16 of it); it travels in M0, which is
-// restored, so the compiler's own use of M0 is undisturbed.
+// restored, so the compiler's own use of M0 is undisturbed.  (readfirstlane:
+// the compiler cannot always prove dst uniform, and M0 takes a scalar.)
 __device__ __forceinline__ void g2lds16_asm(const void* src, unsigned dst) {
   unsigned saved;
   asm volatile(
@@ -438,7 +457,7 @@ __device__ __forceinline__ void g2lds16_asm(const void* src, unsigned dst) {
       "global_load_lds_dwordx4 %2, off\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
-      : "s"(dst), "v"(src)
+      : "s"(__builtin_amdgcn_readfirstlane(dst)), "v"(src)
       : "memory");
 }
 
