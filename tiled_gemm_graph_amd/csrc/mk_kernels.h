@@ -287,6 +287,11 @@ __device__ __forceinline__ void gemm_tile(const KArgs& a, const mk_instr& in, co
     gcol = min(c0 + wcol, N - 8);
   }
   const u16* b_src = B + (long)(k0 + kq * RB) * ldb + gcol;
+  // Bt row r keeps its 16-byte k chunk c at c ^ ((r >> 3) & 7): the eight
+  // rows a thread writes share r >> 3 = wcol / 8, and without the swizzle
+  // the threads of one k group (same kq, wcol 8 apart) would all write the
+  // same bank.  MFMA operand reads apply the same swizzle.
+  const int b_kswz = ((((kq * RB) >> 3) ^ (ncg & 7)) << 3) + ((kq * RB) & 7);
 
   f32x16 acc[FM][FN];
 #pragma unroll
@@ -316,7 +321,7 @@ __device__ __forceinline__ void gemm_tile(const KArgs& a, const mk_instr& in, co
 #pragma unroll
     for (int i = 0; i < A_CHUNKS; ++i) *reinterpret_cast<u32x4*>(as + a_dst[i]) = ra[slot][i];
     // transpose RB (k) x 8 (n) into 8 rows of Bt[n][k], RB k-values each
-    u16* bs = Bs + st * B_STAGE + wcol * LDS_ROW + kq * RB;
+    u16* bs = Bs + st * B_STAGE + wcol * LDS_ROW + b_kswz;
 #pragma unroll
     for (int n = 0; n < 8; ++n) {
       if constexpr (RB == 4) {
@@ -351,9 +356,10 @@ __device__ __forceinline__ void gemm_tile(const KArgs& a, const mk_instr& in, co
           af[i] = *reinterpret_cast<const u32x4*>(as + (wm * WM + i * 32 + (lane & 31)) * LDS_ROW + kk * 16 +
                                                   (lane >> 5) * 8);
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
-          bf[j] = *reinterpret_cast<const u32x4*>(bs + (wn * WN + j * 32 + (lane & 31)) * LDS_ROW + kk * 16 +
-                                                  (lane >> 5) * 8);
+        for (int j = 0; j < FN; ++j) {
+          const int row = wn * WN + j * 32 + (lane & 31);
+          bf[j] = *reinterpret_cast<const u32x4*>(bs + row * LDS_ROW + (((kk * 2 + (lane >> 5)) ^ ((row >> 3) & 7)) << 3));
+        }
 #pragma unroll
         for (int i = 0; i < FM; ++i)
 #pragma unroll
