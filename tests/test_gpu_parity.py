@@ -44,10 +44,13 @@ def test_tiny_gemm_identity_is_exact():
     _counters_ok(r, 1)
 
 
-@pytest.mark.parametrize("tile", [dict(bm=64, bn=64, gemv=0), dict(bm=128, bn=128, gemv=0),
-                                  dict(bm=64, bn=128, gemv=0), dict(bm=128, bn=64, gemv=0)])
-def test_gemm_tiles_vs_oracle(tile):
-    d = dict(layers=2, m=200, h=256)
+@pytest.mark.parametrize("tile,h", [(dict(bm=64, bn=64, gemv=0), 256), (dict(bm=128, bn=128, gemv=0), 256),
+                                    (dict(bm=64, bn=128, gemv=0), 256), (dict(bm=128, bn=64, gemv=0), 256),
+                                    (dict(bm=64, bn=64, gemv=0), 576), (dict(bm=128, bn=128, gemv=0), 576)])
+def test_gemm_tiles_vs_oracle(tile, h):
+    # h = 256: fewer K steps than the row-major body's load ring is deep;
+    # h = 576: nine K steps, one more than the deepest ring
+    d = dict(layers=2, m=200, h=h)
     inp = workloads.generate("mlp3", d)
     r = _run("mlp3", d, inp, tiles=[tile])
     ref = OG.mlp3(inp)
