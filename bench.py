@@ -130,7 +130,7 @@ def cpu_baseline(workload, dims, inp, budget_s):
             "sample": sample}
 
 
-def bench_one(workload, steps, warmup, cpu_budget, do_check=True):
+def bench_one(workload, steps, warmup, cpu_budget, do_check=True, sync="tiles"):
     import numpy as np
     import torch
 
@@ -140,7 +140,7 @@ def bench_one(workload, steps, warmup, cpu_budget, do_check=True):
     dims = workloads.default_dims(workload)
     log(f"[bench] {workload} dims={dims}: drawing inputs")
     inp = workloads.generate(workload, dims)
-    r = G.Runner(workload, dims, inp, device="cuda")
+    r = G.Runner(workload, dims, inp, device="cuda", sync=1 if sync == "levels" else 0)
     st = r.plan.stats()
     log(f"[bench] plan: {st.n_instr} instructions, {st.n_iters} waves, {st.n_barriers} counters")
     r.forward()
@@ -167,7 +167,8 @@ def bench_one(workload, steps, warmup, cpu_budget, do_check=True):
     gbs = st.bytes / (us * 1e-6) / 1e9
     tfl = st.flops / (us * 1e-6) / 1e12
     bound = BOUND[workload]
-    traffic = measured_traffic(workload)
+    # the counter summaries are taken on the per-tile-counter plans
+    traffic = measured_traffic(workload) if sync == "tiles" else None
     if bound == "hbm":
         roof = {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": gbs / PEAK_HBM_GBS, "traffic": traffic}
@@ -189,7 +190,7 @@ def bench_one(workload, steps, warmup, cpu_budget, do_check=True):
         "data": "synthetic (seeded torch CPU generator, normal distributions of the workload spec)",
         "config": {"workload": DESCR[workload], "name": workload, "dims": dims,
                    "instructions": int(st.n_instr), "counters": int(st.n_barriers),
-                   "launches_per_forward": 1},
+                   "sync": sync, "launches_per_forward": 1},
         "gbps": gbs,
         "tflops": tfl,
         "alg_bytes": st.bytes,
@@ -231,6 +232,9 @@ def main():
     ap.add_argument("--all", action="store_true", help="one JSON line per workload")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-check", action="store_true")
+    ap.add_argument("--sync", choices=["tiles", "levels"], default="tiles",
+                    help="per-tile dependency counters (default) or one counter per "
+                         "level boundary, for A/B comparison")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="only time a plain copy of this many MiB (counter calibration)")
     ap.add_argument("--source-hash", action="store_true",
@@ -252,7 +256,7 @@ def main():
         return
     wls = ["decode", "mlp3", "prefill", "decode_gemm", "layer"] if args.all else [args.workload]
     for wl in wls:
-        line = bench_one(wl, args.steps, args.warmup, args.cpu_seconds, not args.no_check)
+        line = bench_one(wl, args.steps, args.warmup, args.cpu_seconds, not args.no_check, args.sync)
         print(json.dumps(line), flush=True)
 
 

@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define MK_ABI_VERSION 2
+#define MK_ABI_VERSION 3
 #define MK_MAX_TENSORS 64       /* graph tensors incl. views and internals */
 #define MK_MAX_SRC 16           /* counters one instruction waits on       */
 #define MK_MAX_DST 8            /* counters one instruction arrives on     */
@@ -159,6 +159,16 @@ typedef struct {
                            op.  0: GEMMs whenever it qualifies, GEMVs when
                            it also has at least num_cus 8-column tiles;
                            1: never; 2: whenever it qualifies               */
+  int32_t sync;         /* 0: per-tile counters (a consumer waits on the
+                           producer tiles it reads); 1: level-synchronous
+                           ("Implementing a Mega Kernel for B300", section
+                           on task levels): a node's level is one more than
+                           its producers' highest level, raised to keep
+                           levels non-decreasing in node order, and every
+                           instruction of level L waits on one counter that
+                           all instructions of level L - 1 arrive on, as a
+                           grid barrier per level would.  Reuse barriers
+                           are kept as they are.  For A/B comparison.       */
 } mk_build_options;
 
 typedef struct {

@@ -438,10 +438,51 @@ class Schedule:
         return self.waves * self.ncu - self.n_instr
 
 
-def schedule(g: Graph, ncu: int, cluster_size: int = 1, reuse: int = 0) -> Schedule:
+def _level_barriers(nodes, deps, n_instr: int) -> Dict[tuple, dict]:
+    """Level-synchronous barriers ("Implementing a Mega Kernel for B300",
+    section 7, computing the levels).
+
+    The page gives a task the level 1 + max(level of its parents), level 0
+    without parents, and runs the levels one after another with a grid-wide
+    barrier between them.  Here a task is an instruction and its parents are
+    the producer instructions in its dependency sets.  Reading taken for this
+    library's fixed placement (instructions run in list order on their CUs):
+    an instruction's level is raised to the previous instruction's level
+    where it is lower, so every level is a contiguous run of the list.  The
+    barrier between levels L - 1 and L becomes one counter: all real
+    instructions of level L - 1 arrive, all of level L wait."""
+    owner = {}
+    for ni, n in enumerate(nodes):
+        for j in range(len(n.instrs)):
+            owner[n.start + j] = ni
+    level = [0] * n_instr
+    for i in range(n_instr):
+        lv = level[i - 1] if i > 0 else 0
+        for producer_set in deps.get(i, {}).values():
+            for a in producer_set:
+                lv = max(lv, level[a] + 1)
+        level[i] = lv
+    by_level: Dict[int, List[int]] = {}
+    for i in range(n_instr):
+        if i in owner:
+            by_level.setdefault(level[i], []).append(i)
+    keys: Dict[tuple, dict] = {}
+    for lv in sorted(by_level):
+        if lv == 0:
+            continue
+        below, here = by_level[lv - 1], by_level[lv]
+        keys[("level", lv)] = dict(first=here[0], kind=0, node=owner[below[0]],
+                                   arrive=list(below), wait=list(here))
+    return keys
+
+
+def schedule(g: Graph, ncu: int, cluster_size: int = 1, reuse: int = 0,
+             sync: str = "tiles") -> Schedule:
     """Derive the full schedule.  ``reuse``: 0 = no pooling, 1 = pool
     intermediates, 2 = pool intermediates and let graph outputs take pooled
-    slots (the dispatcher-owned outputs of MegaKittens Internals, sec. 07)."""
+    slots (the dispatcher-owned outputs of MegaKittens Internals, sec. 07).
+    ``sync``: "tiles" = one counter per (producer node, dependency set);
+    "levels" = one counter per level boundary (see ``_level_barriers``)."""
     nodes = lower(g, ncu)
     # phase 1: count and place
     pos = 0
@@ -531,6 +572,10 @@ def schedule(g: Graph, ncu: int, cluster_size: int = 1, reuse: int = 0) -> Sched
             if k not in keys:
                 keys[k] = dict(first=i, kind=0, node=p, arrive=sorted(s), wait=[])
             keys[k]["wait"].append(i)
+    if sync == "levels":
+        keys = _level_barriers(nodes, deps, n_instr)
+    elif sync != "tiles":
+        raise ValueError(sync)
     for (ni, slot, old) in reuse_events:
         n = nodes[ni]
         arrive = sorted(gidx(nodes[r], j) for r in readers[old]

@@ -25,7 +25,7 @@ def test_library_exports_every_declared_symbol():
     for n in names:
         assert hasattr(lib, n), n
     assert set(L.EXPORTS) <= set(names)
-    assert lib.mk_abi_version() == 2
+    assert lib.mk_abi_version() == 3
 
 
 def test_struct_layout_matches_decoder(tmp_path):
@@ -100,12 +100,12 @@ def _oracle_tiles(tiles):
     return out
 
 
-def _compare(wl, dims, tiles=None, reuse=0, ncu=256):
+def _compare(wl, dims, tiles=None, reuse=0, ncu=256, sync=0):
     g = G.build(wl, dims, tiles)
-    plan = g.build(num_cus=ncu, reuse=reuse)
+    plan = g.build(num_cus=ncu, reuse=reuse, sync=sync)
     chosen = _oracle_tiles(plan.op_tiles())
     og = S.workload_graph(wl, dims, chosen if wl != "mlp3" else [chosen[0]])
-    sc = S.schedule(og, ncu=ncu, reuse=reuse)
+    sc = S.schedule(og, ncu=ncu, reuse=reuse, sync="levels" if sync else "tiles")
     got = plan.decoded()
     assert len(got) == len(sc.records)
     for a, b in zip(got, sc.records):
@@ -129,6 +129,22 @@ def test_full_size_lists_match_oracle(wl):
     for i, ds in sc.deps.items():
         for st in ds.values():
             assert max(st) < i
+
+
+@pytest.mark.parametrize("wl", workloads.WORKLOADS)
+def test_level_sync_lists_match_oracle(wl):
+    # level-synchronous mode, full and reduced sizes, with and without reuse
+    for dims, ncu in ((workloads.default_dims(wl), 256), (workloads.small_dims(wl), 16)):
+        plan, _ = _compare(wl, dims, ncu=ncu, sync=1)
+        # one counter per level boundary: at most one wait per instruction
+        assert max(len(rec[7]) for rec in plan.decoded()) <= 1
+    _compare(wl, workloads.small_dims(wl), ncu=16, reuse=1, sync=1)
+
+
+def test_sync_option_checked():
+    g = G.build("mlp3", workloads.small_dims("mlp3"))
+    with pytest.raises(L.MkError):
+        g.build(sync=2)
 
 
 @pytest.mark.parametrize("wl", workloads.WORKLOADS)

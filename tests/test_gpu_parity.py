@@ -159,6 +159,37 @@ def test_full_size_layer_buffer_reuse():
     _counters_ok(r, 2)
 
 
+@pytest.mark.parametrize("wl", workloads.WORKLOADS)
+def test_level_sync_parity(wl):
+    # Level-synchronous plans (one counter per level boundary) compute the
+    # same bytes as the per-tile-counter plans.
+    d = workloads.small_dims(wl)
+    inp = workloads.generate(wl, d)
+    r = _run(wl, d, inp, n=2, sync=1)
+    ref = OG.run(wl, inp, d)
+    got = to_np(r.out)
+    rel = rel_fro(got, ref)
+    say(f"  {wl} levels: rel={rel:.3e} maxabs={max_abs(got, ref)}")
+    assert rel <= TOL[G.DTYPE[wl]]
+    _counters_ok(r, 2)
+    t = _run(wl, d, inp)
+    assert torch.equal(t.out, r.out), "level-synchronous plan differs from the per-tile plan"
+
+
+def test_level_sync_full_layer():
+    # full-size layer: level counters of 768 and 1792 arrivals exceed the
+    # slice cap and run as single atomic words
+    d = workloads.default_dims("layer")
+    inp = workloads.generate("layer", d)
+    r = _run("layer", d, inp, sync=1)
+    assert r.plan.barriers().max() > L.SLICE_MAX
+    ref = OG.layer(inp, d)
+    rel = rel_fro(to_np(r.out), ref)
+    say(f"  layer full levels: rel={rel:.3e}")
+    assert rel <= TOL["bf16"]
+    _counters_ok(r, 1)
+
+
 def test_empty_rows_graph_runs():
     g = G.Graph()
     x = g.tensor("x", "f16", (0, 64), "input")

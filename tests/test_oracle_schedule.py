@@ -127,6 +127,47 @@ def test_box_deps_equal_last_writer_map(wl, reuse):
             assert max(s) < i
 
 
+@pytest.mark.parametrize("wl", sorted(TINY))
+def test_level_barriers_order_every_dependency(wl):
+    # Level-synchronous mode: following the counters back from an instruction
+    # must reach every instruction whose output it reads (the last-writer map,
+    # computed without the oracle's dependency sets); every arrival precedes
+    # its waiters; each instruction waits on at most one counter.
+    d, tiles = TINY[wl]
+    g = S.workload_graph(wl, d, tiles)
+    sc = S.schedule(g, ncu=4, sync="levels")
+    lw = _last_writer_deps(sc, g)
+    arrivals = {}
+    for rec in sc.records:
+        for (b, _) in rec[8]:
+            arrivals.setdefault(b, []).append(rec[0])
+    before = {}
+    for rec in sorted(sc.records):
+        i, reached = rec[0], set()
+        assert len(rec[7]) <= 1
+        for (b, tgt) in rec[7]:
+            assert tgt == len(arrivals[b])
+            for a in arrivals[b]:
+                assert a < i
+                reached.add(a)
+                reached |= before[a]
+        before[i] = reached
+    for i, ds in lw.items():
+        for st in ds.values():
+            assert set(st) <= before[i], (wl, i)
+
+
+def test_level_barriers_of_a_chain():
+    # A 3-layer chain of 4 x 4 tiles: levels 0, 1, 2, so two counters, each
+    # with one arrival per tile of the layer below (the page's level rule:
+    # one more than the highest parent level).
+    g = S.mlp3_graph(3, 64, 64, dict(bm=16, bn=16))
+    sc = S.schedule(g, ncu=8, sync="levels")
+    assert sc.targets == [16, 16]
+    tiles = S.schedule(g, ncu=8)
+    assert len(tiles.targets) > 2   # per-tile mode: one counter per row block
+
+
 def test_reuse_barrier_waits_for_all_old_readers():
     g = S.mlp3_graph(5, 64, 64, dict(bm=16, bn=16))
     sc = S.schedule(g, ncu=8, reuse=1)

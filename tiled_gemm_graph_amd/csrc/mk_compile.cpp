@@ -913,11 +913,61 @@ struct Compiler {
       B.first = B.wait.front();
       bars.push_back(B);
     }
+    if (p.opts.sync == 1) level_barriers();
     std::stable_sort(bars.begin(), bars.end(), [](const Bar& a, const Bar& b) {
       if (a.first != b.first) return a.first < b.first;
       if (a.kind != b.kind) return a.kind < b.kind;
       return a.node < b.node;
     });
+  }
+
+  // Level-synchronous mode ("Implementing a Mega Kernel for B300", section 7,
+  // computing the levels): an instruction's level is one more than the
+  // highest level among the producer instructions it reads from (0 without
+  // any), and the tile counters give way to one counter per level boundary:
+  // every instruction of level L waits for all instructions of level L - 1,
+  // as a grid barrier between levels would.  Instructions run in list order
+  // on their CUs, so a level is raised to the previous instruction's level
+  // where it is lower: the levels then cover contiguous runs of the list and
+  // no instruction waits on a later one.
+  void level_barriers() {
+    std::vector<int> node_of((size_t)p.n_instr, -1);
+    for (size_t ni = 0; ni < p.nodes.size(); ++ni)
+      for (size_t j = 0; j < p.nodes[ni].ins.size(); ++j) node_of[(size_t)p.nodes[ni].start + j] = (int)ni;
+    std::vector<std::vector<int>> parents((size_t)p.n_instr);
+    for (const Bar& B : bars)
+      if (B.kind == 0)
+        for (int i : B.wait) parents[(size_t)i].insert(parents[(size_t)i].end(), B.arrive.begin(), B.arrive.end());
+    std::vector<int> level((size_t)p.n_instr, 0);
+    int prev = 0;
+    for (I64 i = 0; i < p.n_instr; ++i) {
+      int lv = prev;
+      for (int a : parents[(size_t)i]) lv = std::max(lv, level[(size_t)a] + 1);
+      level[(size_t)i] = lv;
+      prev = lv;
+    }
+    // real instructions of each level, in list order
+    std::vector<std::vector<int>> members;
+    for (I64 i = 0; i < p.n_instr; ++i) {
+      if (node_of[(size_t)i] < 0) continue;
+      const int lv = level[(size_t)i];
+      if ((int)members.size() <= lv) members.resize((size_t)lv + 1);
+      members[(size_t)lv].push_back((int)i);
+    }
+    std::vector<Bar> kept;
+    for (Bar& B : bars)
+      if (B.kind != 0) kept.push_back(std::move(B));
+    for (size_t lv = 1; lv < members.size(); ++lv) {
+      if (members[lv].empty() || members[lv - 1].empty()) fail(MK_E_INVALID, "internal: empty level");
+      Bar B;
+      B.kind = 0;
+      B.node = node_of[(size_t)members[lv - 1].front()];
+      B.arrive = members[lv - 1];
+      B.wait = members[lv];
+      B.first = B.wait.front();
+      kept.push_back(std::move(B));
+    }
+    bars = std::move(kept);
   }
 
   // ----------------------------------------------------------------- emit
@@ -1203,6 +1253,7 @@ mk_status megakernel_build(const mk_graph* g, const mk_build_options* opts, mk_p
   if (p->opts.spin_limit_us <= 0) p->opts.spin_limit_us = 2000000;
   if (p->opts.reuse < 0 || p->opts.reuse > 2) { delete p; set_error("reuse must be 0, 1 or 2"); return MK_E_INVALID; }
   if (p->opts.pack < 0 || p->opts.pack > 2) { delete p; set_error("pack must be 0, 1 or 2"); return MK_E_INVALID; }
+  if (p->opts.sync < 0 || p->opts.sync > 1) { delete p; set_error("sync must be 0 or 1"); return MK_E_INVALID; }
   bool has_out = false;
   for (const OpRec& op : g->ops) has_out |= g->t[op.out].role == MK_OUTPUT;
   if (!g->ops.empty() && !has_out) { delete p; set_error("graph has no OUTPUT tensor"); return MK_E_INVALID; }

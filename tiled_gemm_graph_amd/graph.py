@@ -120,10 +120,10 @@ class Graph:
     # compile -----------------------------------------------------------
     def build(self, num_cus: int = 0, cluster_size: int = 0, reuse: int = 0,
               gemv_max_m: int = 0, spin_limit_us: int = 0, cooperative: int = 0,
-              pack: int = 0) -> "Plan":
+              pack: int = 0, sync: int = 0) -> "Plan":
         opts = L.BuildOptions(num_cus=num_cus, cluster_size=cluster_size, reuse=reuse,
                               gemv_max_m=gemv_max_m, spin_limit_us=spin_limit_us,
-                              cooperative=cooperative, pack=pack)
+                              cooperative=cooperative, pack=pack, sync=sync)
         p = c_void_p()
         L.check(self._lib.megakernel_build(self._g, byref(opts), byref(p)))
         return Plan(p, self)
