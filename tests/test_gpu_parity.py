@@ -190,6 +190,37 @@ def test_level_sync_full_layer():
     _counters_ok(r, 1)
 
 
+@pytest.mark.parametrize("h", [256, 1024])
+def test_unfused_mlp_elementwise_bodies(h):
+    # The nine-op form of the 3-layer MLP (plain GEMM, then the bias add and
+    # the ReLU as standalone elementwise instructions), against the oracle's
+    # fused definition: the fp16 roundings between the ops stay well inside
+    # the fp16 tolerance.
+    d = dict(layers=3, m=200 if h == 256 else 1024, h=h)
+    inp = workloads.generate("mlp3", d)
+    g = G.build("mlp3", d, fused=False)
+    say(f"[gpu] unfused mlp3 dims={d}")
+    plan = g.build()
+    assert sum(1 for r in plan.decoded() if r[3] in (6, 7)) > 0   # EW_ADD / EW_RELU
+    bufs = {k: v.cuda().contiguous() for k, v in inp.items()}
+    out = torch.empty(d["m"], h, dtype=torch.float16, device="cuda")
+    bufs["y2"] = out
+    plan.run(bufs)
+    plan.check()
+    torch.cuda.synchronize()
+    ref = OG.mlp3(inp)
+    rel = rel_fro(to_np(out), ref)
+    say(f"  unfused mlp3 h={h}: rel={rel:.3e} maxabs={max_abs(to_np(out), ref)}")
+    assert rel <= TOL["f16"]
+    _counters_ok_plan(plan, 1)
+
+
+def _counters_ok_plan(plan, epochs):
+    c = plan.read_counters()
+    t = plan.barriers().astype(np.int64)
+    assert np.array_equal(c, epochs * t), "counters != epoch * target"
+
+
 def test_empty_rows_graph_runs():
     g = G.Graph()
     x = g.tensor("x", "f16", (0, 64), "input")
