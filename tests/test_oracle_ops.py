@@ -203,7 +203,7 @@ def test_row_selection_matches_full():
                                    rtol=1e-5, atol=1e-5)
 
 
-def test_flops_match_survey_numbers():
+def test_flops_match_closed_forms():
     # Algorithmic flop counts per workload at full size (2*M*N*K per GEMM
     # plus 4*H*d*S(S+1)/2 for causal attention), in GFLOP.
     want = dict(mlp3=6.44, decode=0.44, prefill=4947.8, decode_gemm=317.8, layer=927.7)
