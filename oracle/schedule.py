@@ -609,6 +609,13 @@ def schedule(g: Graph, ncu: int, cluster_size: int = 1, reuse: int = 0,
             else:
                 records.append((i, i % ncu, i // ncu, NOOP, 0, n_i, (0, 0, 0, 0),
                                 (), ()))
+    # Instructions between nodes (the alignment gap before a GEMM node that
+    # starts on an XCD block boundary) are Noops of no node; the library's
+    # record encoding gives them node 0.
+    covered = {r[0] for r in records}
+    records += [(i, i % ncu, i // ncu, NOOP, 0, 0, (0, 0, 0, 0), (), ())
+                for i in range(n_instr) if i not in covered]
+    records.sort(key=lambda r: r[0])
     return Schedule(nodes, n_instr, ncu, records, targets,
                     sum(1 for b in order if b["kind"] == 0),
                     sum(1 for b in order if b["kind"] == 1),
