@@ -1226,10 +1226,85 @@ __device__ __forceinline__ void reduce_tile(const KArgs& a, const mk_instr& in, 
 }
 
 // --------------------------------------------------------------- RMSNORM
+// Rows [r0, r1) of y = x * rsqrt(mean(x^2) + eps) * gamma, up to 16
+// 16-byte chunks per thread in registers: the loads of a whole group of
+// rows are in flight together, each wave adds up the squares of every row,
+// and one barrier exchanges the wave sums, so a group costs one memory
+// round trip instead of two per row.
+template <int DT, int CPT>
+__device__ __forceinline__ void rmsnorm_rows(const KArgs& a, const mk_instr& in, const mk_node& nd, char* smem) {
+  constexpr int RMAX = 16 / CPT;                // rows per group
+  const int t = threadIdx.x, H = nd.N, w = wave_id();
+  float* part = reinterpret_cast<float*>(smem);  // [4 waves][RMAX] sums of squares
+  const u16* X = buf<const u16>(a, nd.a);
+  const u16* G = buf<const u16>(a, nd.gamma);
+  u16* O = buf<u16>(a, nd.out);
+  u32x4 gv[CPT];
+#pragma unroll
+  for (int c = 0; c < CPT; ++c) {
+    const int k = (t + c * kThreads) * 8;
+    if (k < H) gv[c] = *reinterpret_cast<const u32x4*>(G + k);
+  }
+  for (int g0 = in.r0; g0 < in.r1; g0 += RMAX) {
+    const int nr = min(RMAX, in.r1 - g0);
+    u32x4 xv[RMAX][CPT];
+#pragma unroll
+    for (int rr = 0; rr < RMAX; ++rr)
+#pragma unroll
+      for (int c = 0; c < CPT; ++c) {
+        const int k = (t + c * kThreads) * 8;
+        if (rr < nr && k < H) xv[rr][c] = *reinterpret_cast<const u32x4*>(X + (long)(g0 + rr) * nd.a.ld + k);
+      }
+#pragma unroll
+    for (int rr = 0; rr < RMAX; ++rr) {
+      float sq = 0.f;
+      if (rr < nr) {
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) {
+          const int k = (t + c * kThreads) * 8;
+          if (k < H) {
+            float f[8];
+            unpack8<DT>(xv[rr][c], f);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) sq += f[e] * f[e];
+          }
+        }
+      }
+      sq = wave_sum(sq);
+      if ((t & 63) == 0) part[w * RMAX + rr] = sq;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int rr = 0; rr < RMAX; ++rr) {
+      if (rr >= nr) continue;
+      const float tot = (part[rr] + part[RMAX + rr]) + (part[2 * RMAX + rr] + part[3 * RMAX + rr]);
+      const float rinv = 1.0f / sqrtf(tot / (float)H + nd.eps);
+#pragma unroll
+      for (int c = 0; c < CPT; ++c) {
+        const int k = (t + c * kThreads) * 8;
+        if (k < H) {
+          float f[8], gm[8];
+          unpack8<DT>(xv[rr][c], f);
+          unpack8<DT>(gv[c], gm);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) f[e] = f[e] * rinv * gm[e];
+          *reinterpret_cast<u32x4*>(O + (long)(g0 + rr) * nd.out.ld + k) = pack8<DT>(f);
+        }
+      }
+    }
+    __syncthreads();   // part is rewritten by the next group
+  }
+}
+
 template <int DT>
 __device__ __forceinline__ void rmsnorm_tile(const KArgs& a, const mk_instr& in, const mk_node& nd, char* smem) {
   const int t = threadIdx.x;
   const int H = nd.N;
+  const int cpt = (H / 8 + kThreads - 1) / kThreads;   // 16-byte chunks per thread and row
+  if (cpt <= 1) return rmsnorm_rows<DT, 1>(a, in, nd, smem);
+  if (cpt <= 2) return rmsnorm_rows<DT, 2>(a, in, nd, smem);
+  if (cpt <= 4) return rmsnorm_rows<DT, 4>(a, in, nd, smem);
+  // wider rows: one row at a time, streamed
   float* scratch = reinterpret_cast<float*>(smem);
   const u16* X = buf<const u16>(a, nd.a);
   const u16* G = buf<const u16>(a, nd.gamma);
