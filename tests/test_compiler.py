@@ -141,18 +141,22 @@ def test_level_sync_lists_match_oracle(wl):
     _compare(wl, workloads.small_dims(wl), ncu=16, reuse=1, sync=1)
 
 
-@pytest.mark.parametrize("wl,ncu", [("decode_gemm", 32), ("decode_gemm", 64), ("layer", 24)])
-def test_lists_with_alignment_gaps_match_oracle(wl, ncu):
+def test_lists_with_alignment_gaps_match_oracle():
     # A GEMM node of at least num_cus instructions starts on a multiple of
     # num_cus / 8, which can leave Noop instructions between two nodes.
-    plan, sc = _compare(wl, workloads.small_dims(wl), ncu=ncu)
-    covered = set()
-    for n in sc.nodes:
-        covered |= set(range(n.start, n.end))
-    gaps = [i for i in range(sc.n_instr) if i not in covered]
-    assert gaps
-    for i in gaps:
-        assert plan.decoded()[i][3] == 0   # Noop
+    # Whether a plan has such a gap depends on the tile choices, so several
+    # placements are compared and at least one must have one.
+    n_gaps = 0
+    for wl, ncu in (("layer", 24), ("decode_gemm", 32), ("decode_gemm", 64), ("layer", 40)):
+        plan, sc = _compare(wl, workloads.small_dims(wl), ncu=ncu)
+        covered = set()
+        for n in sc.nodes:
+            covered |= set(range(n.start, n.end))
+        gaps = [i for i in range(sc.n_instr) if i not in covered]
+        for i in gaps:
+            assert plan.decoded()[i][3] == 0   # Noop
+        n_gaps += len(gaps)
+    assert n_gaps > 0
 
 
 def test_sync_option_checked():
