@@ -941,16 +941,20 @@ __device__ __forceinline__ void gemv_body(const KArgs& a, const mk_instr& in, co
   {
     // All four waves stage the activation chunk (gamma-scaled under
     // RMSNORM_INPUT) with every load of a thread in flight at once (at most
-    // 8: rows * kn / 8 <= 2048 chunks); each wave adds up its squares.
+    // 8: rows * kn / 8 <= 2048 chunks; a thread past the end loads nothing,
+    // where clamped re-reads of the last chunk had cost about 1.5 us per
+    // decode forward); each wave adds up its squares.
     const u16* A = buf<const u16>(a, nd.a) + (long)r0 * nd.a.ld + k0;
     const int kc8 = kn / 8, nch = rows * kc8;
     u32x4 xv[8], gv[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const int i = min(t + j * kThreads, nch - 1);
-      const int m = i / kc8, kc = (i - m * kc8) * 8;
-      xv[j] = *reinterpret_cast<const u32x4*>(A + (long)m * nd.a.ld + kc);
-      if (rms) gv[j] = *reinterpret_cast<const u32x4*>(buf<const u16>(a, nd.gamma) + k0 + kc);
+      const int i = t + j * kThreads;
+      if (i < nch) {
+        const int m = i / kc8, kc = (i - m * kc8) * 8;
+        xv[j] = *reinterpret_cast<const u32x4*>(A + (long)m * nd.a.ld + kc);
+        if (rms) gv[j] = *reinterpret_cast<const u32x4*>(buf<const u16>(a, nd.gamma) + k0 + kc);
+      }
     }
     float sqt[MAXR];
 #pragma unroll
