@@ -1,13 +1,16 @@
-"""Benchmark: one forward of a tile graph as one persistent megakernel launch.
+"""Benchmark: each workload graph as one persistent megakernel launch per forward.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--all]
 
-A step is one forward of the whole graph (every instruction of the plan) on
-seeded synthetic inputs already resident in HBM.  The default workload is
-the batch-1 decoder-layer GEMV chain (hidden 4096, QKV 6144, gate_up 28672,
-down 14336, bf16).  Prints one JSON line: µs per forward, achieved GB/s or
-TFLOP/s against the MI355X roofline, the same graph launched one op at a
-time, and the CPU oracle timed on the host as a reported baseline.
+A step is one forward of a whole graph (every instruction of its plan) on
+seeded synthetic inputs already resident in HBM.  The default run measures
+all five graphs and prints ONE JSON line headlined by the largest, the
+prefill GEMM chain (M = 8192, X@W1 then relu(.@W2), fp16); its "graphs"
+block carries, per graph: µs per forward, achieved TFLOP/s or GB/s against
+the MI355X roofline, the same graph launched one op at a time, the same
+plan on the work queue, parity against the CPU oracle (full outputs) and
+the oracle timed on the host.  ``--workload NAME`` prints one line for one
+graph, ``--all`` one line per graph.
 """
 import argparse
 import json
@@ -130,81 +133,120 @@ def cpu_baseline(workload, dims, inp, budget_s):
             "sample": sample}
 
 
-def bench_one(workload, steps, warmup, cpu_budget, do_check=True, sync="tiles"):
+def parity(got, ref):
+    """rel-Frobenius and max-abs error (with its index) in fp64."""
     import numpy as np
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    d = np.abs(got - ref)
+    i = int(np.argmax(d))
+    return {"rel_err": float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-12)),
+            "max_abs_err": float(d.reshape(-1)[i]),
+            "max_abs_at": [int(x) for x in np.unravel_index(i, d.shape)]}
+
+
+def roofline(workload, st, us, traffic):
+    gbs = st.bytes / (us * 1e-6) / 1e9
+    tfl = st.flops / (us * 1e-6) / 1e12
+    if BOUND[workload] == "hbm":
+        return {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": gbs / PEAK_HBM_GBS, "traffic": traffic}
+    return {"bound": "mfma", "achieved": tfl, "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s",
+            "frac": tfl / PEAK_MFMA_TFLOPS, "traffic": traffic}
+
+
+def bench_graph(workload, steps, warmup, cpu_budget, do_check=True, sync="tiles", queue_ab=True,
+                clock=False):
+    """Measure one graph: the megakernel, its per-op version, the same plan
+    on the work queue; parity against the oracle on the whole output."""
     import torch
 
     import workloads
     from tiled_gemm_graph_amd import graphs as G
+    from tiled_gemm_graph_amd import trace as TR
 
     dims = workloads.default_dims(workload)
     log(f"[bench] {workload} dims={dims}: drawing inputs")
     inp = workloads.generate(workload, dims)
     r = G.Runner(workload, dims, inp, device="cuda", sync=1 if sync == "levels" else 0)
     st = r.plan.stats()
-    log(f"[bench] plan: {st.n_instr} instructions, {st.n_iters} waves, {st.n_barriers} counters")
+    log(f"[bench] {workload} plan: {st.n_instr} instructions, {st.n_iters} waves, "
+        f"{st.n_barriers} counters")
     r.forward()
     r.plan.check()
     torch.cuda.synchronize()
-    out = {}
+    res = {"workload": DESCR[workload], "name": workload, "dims": dims,
+           "instructions": int(st.n_instr), "counters": int(st.n_barriers), "sync": sync,
+           "alg_flops": st.flops, "alg_bytes": st.bytes,
+           "dtype": "bf16" if G.DTYPE[workload] == "bf16" else "f16"}
     if do_check:
         from oracle import graphs as OG
-        got = r.out.float().cpu().numpy().astype(np.float64)
-        if workload in ("prefill", "decode_gemm"):
-            rows = [0, dims["m"] // 2 + 1, dims["m"] - 1]
-            ref = OG.run(workload, inp, dims, rows=rows).astype(np.float64)
-            got = got[rows]
-        else:
-            ref = OG.run(workload, inp, dims).astype(np.float64)
-        rel = float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-12))
-        out["rel_err"] = rel
-        out["max_abs_err"] = float(np.max(np.abs(got - ref)))
-        log(f"[bench] parity vs oracle: rel {rel:.3e}")
+        log(f"[bench] {workload}: oracle on the whole output")
+        res.update(parity(r.out.float().cpu().numpy(), OG.run(workload, inp, dims)))
+        log(f"[bench] {workload} parity: rel {res['rel_err']:.3e} max-abs {res['max_abs_err']:.3e}")
     ms = time_forwards(r.forward, steps, warmup)
     r.plan.check()
     ms_op = time_forwards(r.forward_per_op, steps, warmup)
-    us = ms * 1e3
-    gbs = st.bytes / (us * 1e-6) / 1e9
-    tfl = st.flops / (us * 1e-6) / 1e12
-    bound = BOUND[workload]
+    res["us"] = ms * 1e3
+    res["ms_per_step"] = ms
+    res["per_op_us"] = ms_op * 1e3
+    res["speedup_vs_per_op"] = ms_op / ms
+    if queue_ab and sync == "tiles":
+        qp = r.alt_plan(queue=1)
+        r.forward(plan=qp)
+        qp.check()
+        ms_q = time_forwards(lambda: r.forward(plan=qp), steps, warmup)
+        qp.check()
+        res["queue_us"] = ms_q * 1e3
+        del qp
+    if clock:
+        _, mhz = TR.capture(r, with_clock=True)
+        res["core_clock_mhz"] = mhz
+    res["gbps"] = st.bytes / (res["us"] * 1e-6) / 1e9
+    res["tflops"] = st.flops / (res["us"] * 1e-6) / 1e12
     # the counter summaries are taken on the per-tile-counter plans
-    traffic = measured_traffic(workload) if sync == "tiles" else None
-    if bound == "hbm":
-        roof = {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": gbs / PEAK_HBM_GBS, "traffic": traffic}
+    res["roofline"] = roofline(workload, st, res["us"], measured_traffic(workload) if sync == "tiles" else None)
+    log(f"[bench] {workload}: {res['us']:.1f} us/forward, per-op {res['per_op_us']:.1f}"
+        + (f", queue {res['queue_us']:.1f}" if "queue_us" in res else ""))
+    if cpu_budget > 0:
+        log(f"[bench] {workload}: timing the CPU oracle (~{cpu_budget:.0f} s)")
+        res["cpu_baseline"] = cpu_baseline(workload, dims, inp, cpu_budget)
     else:
-        roof = {"bound": "mfma", "achieved": tfl, "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s",
-                "frac": tfl / PEAK_MFMA_TFLOPS, "traffic": traffic}
+        res["cpu_baseline"] = None
+    del r
+    torch.cuda.empty_cache()
+    return res
+
+
+def line_for(head, steps, warmup, graphs=None):
+    """The driver's JSON line for graph result ``head``."""
     line = {
         "metric": METRIC,
-        "value": us,
+        "value": head["us"],
         "unit": "us/forward",
         "n_gpus": 1,
         "steps": steps,
         "warmup": warmup,
-        "ms_per_step": ms,
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if G.DTYPE[workload] == "bf16" else "f16",
+        "dtype": head["dtype"],
         "data": "synthetic (seeded torch CPU generator, normal distributions of the workload spec)",
-        "config": {"workload": DESCR[workload], "name": workload, "dims": dims,
-                   "instructions": int(st.n_instr), "counters": int(st.n_barriers),
-                   "sync": sync, "launches_per_forward": 1},
-        "gbps": gbs,
-        "tflops": tfl,
-        "alg_bytes": st.bytes,
-        "alg_flops": st.flops,
-        "per_op_us": ms_op * 1e3,
-        "speedup_vs_per_op": ms_op / ms,
-        "roofline": roof,
+        "config": {"workload": head["workload"], "name": head["name"], "dims": head["dims"],
+                   "instructions": head["instructions"], "counters": head["counters"],
+                   "sync": head["sync"], "launches_per_forward": 1},
+        "roofline": head["roofline"],
+        "cpu_baseline": head["cpu_baseline"],
     }
-    line.update(out)
-    if cpu_budget > 0:
-        log(f"[bench] timing the CPU oracle (~{cpu_budget:.0f} s)")
-        line["cpu_baseline"] = cpu_baseline(workload, dims, inp, cpu_budget)
-    else:
-        line["cpu_baseline"] = None
+    for k in ("per_op_us", "speedup_vs_per_op", "queue_us", "rel_err", "max_abs_err", "max_abs_at",
+              "gbps", "tflops", "alg_bytes", "alg_flops", "core_clock_mhz"):
+        if k in head:
+            line[k] = head[k]
+    if "core_clock_mhz" in head:
+        line["peak_at_measured_clock_tflops"] = PEAK_MFMA_TFLOPS * head["core_clock_mhz"] / 2400.0
+    if graphs is not None:
+        line["graphs"] = graphs
     return line
 
 
@@ -225,13 +267,16 @@ def copy_calibration(mib, steps):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="decode",
-                    choices=["mlp3", "decode", "prefill", "decode_gemm", "layer"])
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=None,
+                    choices=["mlp3", "decode", "prefill", "decode_gemm", "layer"],
+                    help="one graph only (default: all five in one line, headlined by prefill)")
     ap.add_argument("--all", action="store_true", help="one JSON line per workload")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="oracle timing budget of the headline graph (the others get a quarter)")
     ap.add_argument("--no-check", action="store_true")
+    ap.add_argument("--no-queue", action="store_true", help="skip the work-queue A/B")
     ap.add_argument("--sync", choices=["tiles", "levels"], default="tiles",
                     help="per-tile dependency counters (default) or one counter per "
                          "level boundary, for A/B comparison")
@@ -254,10 +299,23 @@ def main():
     if args.copy_mib:
         copy_calibration(args.copy_mib, args.steps)
         return
-    wls = ["decode", "mlp3", "prefill", "decode_gemm", "layer"] if args.all else [args.workload]
-    for wl in wls:
-        line = bench_one(wl, args.steps, args.warmup, args.cpu_seconds, not args.no_check, args.sync)
-        print(json.dumps(line), flush=True)
+    kw = dict(do_check=not args.no_check, sync=args.sync, queue_ab=not args.no_queue)
+    if args.workload:
+        res = bench_graph(args.workload, args.steps, args.warmup, args.cpu_seconds, clock=True, **kw)
+        print(json.dumps(line_for(res, args.steps, args.warmup)), flush=True)
+        return
+    order = ["prefill", "decode", "mlp3", "decode_gemm", "layer"]
+    results = {}
+    for wl in order:
+        head = wl == "prefill"
+        results[wl] = bench_graph(wl, args.steps, args.warmup,
+                                  args.cpu_seconds if head else args.cpu_seconds / 4,
+                                  clock=head, **kw)
+        if args.all:
+            print(json.dumps(line_for(results[wl], args.steps, args.warmup)), flush=True)
+    if not args.all:
+        print(json.dumps(line_for(results["prefill"], args.steps, args.warmup, graphs=results)),
+              flush=True)
 
 
 if __name__ == "__main__":

@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define MK_ABI_VERSION 3
+#define MK_ABI_VERSION 4
 #define MK_MAX_TENSORS 64       /* graph tensors incl. views and internals */
 #define MK_MAX_SRC 16           /* counters one instruction waits on       */
 #define MK_MAX_DST 8            /* counters one instruction arrives on     */
@@ -169,6 +169,25 @@ typedef struct {
                            all instructions of level L - 1 arrive on, as a
                            grid barrier per level would.  Reuse barriers
                            are kept as they are.  For A/B comparison.       */
+  int32_t queue;        /* 0: static placement, instruction i on workgroup
+                           i mod num_cus in iteration i / num_cus
+                           (MegaKittens Internals, section 05); 1: a work
+                           queue ("MegaKittens Internals", section 07,
+                           global-work-queue mode): each workgroup takes the
+                           next instruction index from a device counter
+                           with an atomic add, two ahead of the one it runs.
+                           Indices are taken in list order and every
+                           dependency points to a lower index, so the
+                           lowest unfinished index is always running and
+                           any number of resident workgroups completes the
+                           run.  The records and counters are the same in
+                           both modes.                                      */
+  int32_t debug_poison; /* 1: before every run fill each plan-owned
+                           intermediate (and split-K partial buffer) with
+                           all-ones bytes, a NaN in fp16, bf16 and fp32, so
+                           a read of a value no instruction of this run has
+                           written shows up in the output.  Debug aid; one
+                           extra fill launch per buffer per run.            */
 } mk_build_options;
 
 typedef struct {
@@ -276,43 +295,108 @@ mk_status mk_graph_op(mk_graph *g, mk_op_kind kind, const int32_t *in, int n_in,
                       int32_t out, const mk_op_attrs *attrs);
 
 /* ---- compile (host only, no GPU needed) -------------------------------- */
+/* Compile graph g into a plan: lower every op into tile instructions with
+ * read and write boxes, place instruction i on CU i mod num_cus in
+ * iteration i / num_cus, give tensors buffer slots (pooled under `reuse`),
+ * derive one counter per (producer node, dependency set) with target = the
+ * set's size, and pack the 256-byte records (MegaKittens Internals, section
+ * 04, the scheduler's four phases, and section 05, placement; the split-K
+ * GEMV tasks and epilogue flags of "Implementing a Mega Kernel for B300",
+ * section 2).  opts may be NULL (all defaults).  On MK_OK *plan is a new
+ * plan owned by the caller (mk_plan_destroy); the graph may be destroyed
+ * afterwards.  Errors: MK_E_INVALID (shapes, dtypes, non-topological
+ * order), MK_E_LIMIT (more than MK_MAX_SRC / MK_MAX_DST counters on one
+ * instruction, more than MK_MAX_TENSORS slots); *plan is NULL then.  A
+ * valid graph the GPU kernels do not implement still builds (for host
+ * profiles) and its runs fail with MK_E_UNSUPPORTED. */
 mk_status megakernel_build(const mk_graph *g, const mk_build_options *opts,
                            mk_plan **plan);
+/* Free a plan and its device state (records, counters, intermediates).
+ * The caller must have synchronised every stream the plan ran on. */
 void mk_plan_destroy(mk_plan *p);
 
 /* ---- run --------------------------------------------------------------- */
-/* One forward as one persistent cooperative launch on `stream` (a
- * hipStream_t; 0 = null stream).  buffers[i] is the device pointer of tensor
- * id i for every caller-owned tensor (inputs, weights, outputs); entries of
- * views and intermediates are ignored.  A weight the plan packs
- * (mk_plan_weight_layout) is passed as its packed buffer.  Asynchronous: call mk_plan_check to
- * learn whether a counter wait gave up. */
+/* One forward as one persistent launch of num_cus workgroups on `stream`
+ * (a hipStream_t; 0 = the null stream): each workgroup walks its column of
+ * the instruction list, waits until every source counter of an
+ * instruction reaches epoch * target, runs the tile body and arrives on the
+ * destination counters (MegaKittens Internals, section 07, one launch per
+ * call, and sections 08-09, the interpreter loop; "Beating torch.compile
+ * with Megakernels in CuTe DSL", "Cooperative Kernel" and "Dependency
+ * Management and Scheduling").  buffers[i] is the device pointer of tensor
+ * id i for every caller-owned tensor (inputs, weights, outputs), 16-byte
+ * aligned; entries of views and intermediates are ignored; n_buffers is at
+ * least the number of graph tensors.  A weight the plan packs
+ * (mk_plan_weight_layout) is passed as its packed buffer.
+ *
+ * Residency: with opts.cooperative = 0 the launch is an ordinary one, and
+ * the kernel's LDS use allows one workgroup per CU, so all num_cus
+ * workgroups are resident together only when no other work holds a CU.
+ * Under the static placement a workgroup that never becomes resident
+ * leaves its instructions unrun: the other workgroups' waits then give up
+ * after spin_limit_us and the run ends with the error record set.  With
+ * opts.queue = 1 instructions are taken from a work queue in list order
+ * and any number of resident workgroups completes the run.
+ * opts.cooperative = 1 has the runtime guarantee residency.
+ *
+ * Asynchronous: returns once the launch is queued; call mk_plan_check to
+ * learn whether a counter wait gave up.  Errors: MK_E_UNSUPPORTED (plan
+ * the kernels do not implement, or built for another CU count),
+ * MK_E_INVALID (missing or misaligned buffer, plan uploaded to another
+ * device), MK_E_HIP (runtime call failed), MK_E_DEADLOCK (an earlier run
+ * of this plan is known, from the host-visible copy of its error record,
+ * to have given up and mk_plan_check has not been called since; nothing
+ * is launched). */
 mk_status megakernel_run(mk_plan *p, void *const *buffers, int n_buffers, void *stream);
 /* megakernel_run that also writes four wall-clock stamps per executed
  * instruction (fetched, counters satisfied, body done, released) to the
- * caller-owned device array trace[4 * n_iters * num_cus] (uint64, indexed
- * by instruction index; Noop slots are left untouched).  The stamps come
- * from the GPU's constant-rate wall clock; a debugging aid after the
+ * caller-owned device array trace[4 * n_iters * num_cus + 4 * num_cus]
+ * (uint64; instruction i at 4 * i, Noop slots left untouched).  The stamps
+ * come from the GPU's constant-rate wall clock; a debugging aid after the
  * intra-kernel timing of "Beating torch.compile with Megakernels in CuTe
- * DSL", "Intrakernel Profiling". */
+ * DSL", "Intrakernel Profiling".  The last 4 * num_cus words hold, for
+ * workgroup b at 4 * (n_iters * num_cus + b): the wall clock and the
+ * shader-clock counter when it starts, then both again when it finishes
+ * (left untouched if it exits early), so that the core clock during the
+ * run is (d shader clock) / (d wall clock) * mk_wall_clock_khz. */
 mk_status megakernel_run_traced(mk_plan *p, void *const *buffers, int n_buffers, void *stream,
                                 uint64_t *trace);
-/* Same graph, same tile bodies, one launch per node and no counters. */
+/* The per-op baseline: the same records and tile bodies, one ordinary
+ * launch per node (grid = the node's instruction count) with stream order
+ * in place of counters; the comparison that "Beating torch.compile with
+ * Megakernels in CuTe DSL", "Takeaways", makes against one launch per op.
+ * Arguments, ownership and errors as megakernel_run. */
 mk_status megakernel_run_per_op(mk_plan *p, void *const *buffers, int n_buffers,
                                 void *stream);
 /* Synchronise `stream` and read the plan's error record. */
 mk_status mk_plan_check(mk_plan *p, void *stream, mk_run_error *err);
 
 /* ---- introspection ----------------------------------------------------- */
+/* Plan statistics: instruction and wave counts, counters, slots (the
+ * scheduler figures MegaKittens Internals, section 04, reports for its
+ * worked example) and the algorithmic flops and HBM bytes of the graph,
+ * computed from the graph that was compiled ("Implementing a Mega Kernel
+ * for B300", the section on measuring: count from the graph that runs,
+ * not from hand-typed shapes).  MK_E_INVALID on a null argument. */
 mk_status mk_plan_stats_get(const mk_plan *p, mk_plan_stats *out);
-/* Records, n_instr of them, MK_INSTR_WORDS int32 each (pointer owned by the
- * plan).  coord: GEMM/GEMV (tm, tn, s, dup copy); REDUCE (tm, tn, 0, 0);
- * RMSNORM (row block, 0, 0, 0); ATTENTION (q block, head, 0, 0);
- * EW_* (tile row, tile col, 0, 0). */
+/* The flat instruction list (MegaKittens Internals, section 04, phase 4,
+ * emit, and section 06, the fixed 256-byte record): n_instr records of
+ * MK_INSTR_WORDS int32 each, laid out as mk_instr, record i for CU
+ * i mod num_cus.  *words points into the plan and stays valid until
+ * mk_plan_destroy.  coord: GEMM/GEMV (tm, tn, s, dup copy); REDUCE
+ * (tm, tn, 0, 0); RMSNORM (row block, 0, 0, 0); ATTENTION (q block, head,
+ * 0, 0); EW_* (tile row, tile col, 0, 0).  MK_E_INVALID on a null
+ * argument. */
 mk_status mk_plan_instructions(const mk_plan *p, const int32_t **words,
                                int64_t *n_instr, int32_t *words_per_instr);
 mk_status mk_plan_nodes(const mk_plan *p, const int32_t **words, int64_t *n_nodes,
                         int32_t *words_per_node);
+/* Target of every counter (MegaKittens Internals, section 04, phase 3:
+ * one barrier per (producer node, dependency set), target = the number of
+ * producer instructions in the set; reuse barriers count every reader of a
+ * pooled slot's previous tensor).  Counter ids are canonical: ordered by
+ * the first instruction that waits on them, input barriers before reuse
+ * barriers, then by producer node.  *targets points into the plan. */
 mk_status mk_plan_barriers(const mk_plan *p, const int32_t **targets, int64_t *n);
 /* slot of each tensor id (-1 for views and unused tensors). */
 mk_status mk_plan_slots(const mk_plan *p, const int32_t **slot_of_tensor, int64_t *n);
@@ -354,8 +438,11 @@ mk_status mk_plan_weight_layout(const mk_plan *p, int32_t tensor, int32_t *packe
 mk_status mk_plan_pack_weight(mk_plan *p, int32_t tensor, const void *src, void *dst,
                               void *stream);
 /* Copy the counters (each the sum of its slots) to host memory after a run
- * (synchronises `stream`).  After e runs every counter equals e * its
- * target. */
+ * (synchronises `stream`); host has room for n >= the number of counters.
+ * After e completed runs every counter equals e * its target, the
+ * post-run check of MegaKittens Internals, section 07 (counters return to
+ * a known state between calls; here by epochs instead of zeroing).
+ * MK_E_INVALID if host is null or too small, MK_E_HIP on a runtime error. */
 mk_status mk_plan_read_counters(mk_plan *p, int32_t *host, int64_t n, void *stream);
 /* Runs so far (the epoch the next run waits against is this + 1). */
 mk_status mk_plan_epoch(const mk_plan *p, int64_t *epoch);

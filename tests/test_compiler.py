@@ -25,7 +25,7 @@ def test_library_exports_every_declared_symbol():
     for n in names:
         assert hasattr(lib, n), n
     assert set(L.EXPORTS) <= set(names)
-    assert lib.mk_abi_version() == 3
+    assert lib.mk_abi_version() == 4
 
 
 def test_struct_layout_matches_decoder(tmp_path):
@@ -301,3 +301,39 @@ def test_causal_attention_work_even_across_cus():
         keys[i % 256] += w[i, L.W_R0 + 5]          # k1: keys the block visits
     busy = keys[keys > 0]
     assert busy.max() / busy.min() <= 1.15, (busy.min(), busy.max())
+
+
+def _produced_b_graph(tile=None):
+    g = G.Graph()
+    x = g.tensor("x", "f16", (64, 64), "input")
+    w1 = g.tensor("w1", "f16", (64, 128), "weight")
+    v = g.tensor("v", "f16", (1, 64), "input")
+    y = g.tensor("y", "f16", (64, 128), "intermediate")
+    z = g.tensor("z", "f16", (1, 128), "output")
+    g.gemm(x, w1, y)
+    g.gemm(v, y, z, tile=tile)
+    return g
+
+
+def test_small_m_gemm_on_a_produced_b_is_not_a_gemv():
+    # The GEMV body streams B before the instruction's counters clear, which
+    # is only right for weights and inputs: an M = 1 product whose B is an
+    # earlier op's output takes the GEMM body, and forcing the GEMV body on
+    # it leaves a plan the GPU refuses (stats.reserved = 1: unsupported).
+    plan = _produced_b_graph().build()
+    assert plan.op_tile(1)["gemv"] == 0
+    assert {r[3] for r in plan.decoded() if r[5] == 1} == {L.I_GEMM}
+    assert plan.stats().reserved == 0
+    forced = _produced_b_graph(tile=dict(gemv=1)).build()
+    assert forced.stats().reserved == 1
+
+
+def test_new_build_options_are_validated():
+    g = _produced_b_graph()
+    for opt in ("queue", "debug_poison"):
+        with pytest.raises(L.MkError):
+            g.build(**{opt: 2})
+    # the work queue changes no record: same list, same counters
+    a, b = g.build(), g.build(queue=1, debug_poison=1)
+    assert np.array_equal(a.instructions(), b.instructions())
+    assert np.array_equal(a.barriers(), b.barriers())

@@ -59,7 +59,8 @@ class OpAttrs(Structure):
 class BuildOptions(Structure):
     _fields_ = [("num_cus", c_int32), ("cluster_size", c_int32), ("reuse", c_int32),
                 ("gemv_max_m", c_int32), ("spin_limit_us", c_int64),
-                ("cooperative", c_int32), ("pack", c_int32), ("sync", c_int32)]
+                ("cooperative", c_int32), ("pack", c_int32), ("sync", c_int32),
+                ("queue", c_int32), ("debug_poison", c_int32)]
 
 
 class PlanStats(Structure):
@@ -126,7 +127,7 @@ def load() -> ctypes.CDLL:
         f = getattr(L, name)
         f.argtypes = args
         f.restype = res
-    if L.mk_abi_version() != 3:
+    if L.mk_abi_version() != 4:
         raise ImportError("libmk.so ABI version mismatch")
     _lib = L
     return L

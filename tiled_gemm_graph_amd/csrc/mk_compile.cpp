@@ -126,8 +126,12 @@ struct Compiler {
   }
 
   // ---------------------------------------------------------------- tiles
+  // b_produced: B is written by an earlier op.  The GEMV body streams B
+  // before the instruction's counters clear (only weights may be read that
+  // early, MegaKittens Internals, section 09), so such a GEMM takes the
+  // GEMM body, whose loads all follow the wait.
   mk_tile choose_gemm_tile(const OpRec& op, I64 M, I64 N, I64 K, bool silu, int dt,
-                           bool packable) {
+                           bool packable, bool b_produced) {
     mk_tile t = op.attrs.tile;
     if (t.dup <= 0) t.dup = 1;
     if (t.gemv < 0 || t.gemv > 1) fail(MK_E_INVALID, "tile.gemv must be 0 or 1");
@@ -135,7 +139,7 @@ struct Compiler {
     if (t.layout == 2 && !packable)
       fail(MK_E_INVALID, "a packed weight must be a whole 2-D weight tensor read by no other op");
     const bool explicit_gemv = op.attrs.tile.gemv != 0 || op.attrs.tile.bm != 0;
-    if (!explicit_gemv && M <= p.opts.gemv_max_m) t.gemv = 1;
+    if (!explicit_gemv && M <= p.opts.gemv_max_m && !b_produced) t.gemv = 1;
     const bool rope = op.attrs.epilogue & MK_EP_ROPE;
     const I64 hd = op.attrs.head_dim > 0 ? op.attrs.head_dim : 1;
     if (t.gemv) {
@@ -329,7 +333,8 @@ struct Compiler {
     // A weight may be packed when the op reads it whole and alone.
     bool packable = !T[op.in[1]].is_view && T[B.tensor].role == MK_WEIGHT && uses[B.tensor] == 1 &&
                     (dt == MK_F16 || dt == MK_BF16) && K % 8 == 0 && N % 8 == 0;
-    mk_tile t = choose_gemm_tile(op, M, N, K, silu, dt, packable);
+    const bool b_produced = T[B.tensor].role == MK_OUTPUT || T[B.tensor].role == MK_INTERMEDIATE;
+    mk_tile t = choose_gemm_tile(op, M, N, K, silu, dt, packable, b_produced);
     if (t.bm <= 0 || t.bn <= 0 || t.split <= 0 || t.dup <= 0)
       fail(MK_E_INVALID, "bad GEMM tile");
     int S = t.split;
@@ -343,6 +348,7 @@ struct Compiler {
     if (N % 8) unsup("GEMM N must be a multiple of 8");
     if (gemv) {
       int wc = t.bn * (silu ? 2 : 1);
+      if (b_produced) unsup("the GEMV body reads B before its counters clear: B must be a weight or input");
       if (t.bm > 8) unsup("GEMV body handles at most 8 rows per tile");
       if (wc > 1536 || wc % 8) unsup("GEMV weight tile must be <= 1536 columns, multiple of 8");
       if (K % 8) unsup("GEMV K must be a multiple of 8");
@@ -1257,6 +1263,12 @@ mk_status megakernel_build(const mk_graph* g, const mk_build_options* opts, mk_p
   if (p->opts.reuse < 0 || p->opts.reuse > 2) { delete p; set_error("reuse must be 0, 1 or 2"); return MK_E_INVALID; }
   if (p->opts.pack < 0 || p->opts.pack > 2) { delete p; set_error("pack must be 0, 1 or 2"); return MK_E_INVALID; }
   if (p->opts.sync < 0 || p->opts.sync > 1) { delete p; set_error("sync must be 0 or 1"); return MK_E_INVALID; }
+  if (p->opts.queue < 0 || p->opts.queue > 1) { delete p; set_error("queue must be 0 or 1"); return MK_E_INVALID; }
+  if (p->opts.debug_poison < 0 || p->opts.debug_poison > 1) {
+    delete p;
+    set_error("debug_poison must be 0 or 1");
+    return MK_E_INVALID;
+  }
   bool has_out = false;
   for (const OpRec& op : g->ops) has_out |= g->t[op.out].role == MK_OUTPUT;
   if (!g->ops.empty() && !has_out) { delete p; set_error("graph has no OUTPUT tensor"); return MK_E_INVALID; }

@@ -55,6 +55,10 @@ struct KArgs {
   int n_nodes;
   int ctr_stride;           // int32 slots per counter (see mk.h)
   unsigned long long* trace; // optional: 4 wall-clock stamps per instruction
+  int* abort_host;          // host-visible copy of the abort flag (pinned memory)
+  int* ticket;              // work-queue mode: two ticket words, run e uses e & 1
+  int queue;                // 1: instructions taken from the work queue
+  int n_instr;              // list length (work-queue mode)
   void* bufs[MK_MAX_TENSORS];
 };
 
@@ -1628,7 +1632,32 @@ struct Loop {
   int* flag;
   char* smem;
   int vcu;
+  int* idx;             // work-queue mode: record index of each slot, -1 = none
 };
+
+// Record index of local iteration it (the slot it % 3 holds it), and
+// whether there is one.  Static placement: column vcu of the list.  Work
+// queue: the index taken from the queue for that iteration.
+__device__ __forceinline__ int rec_index(const Loop& L, int it) {
+  return L.a.queue ? L.idx[it % 3] : it * L.a.ncu + L.vcu;
+}
+__device__ __forceinline__ bool has_rec(const Loop& L, int it) {
+  return L.a.queue ? L.idx[it % 3] >= 0 : it < L.a.n_iters;
+}
+
+// Work-queue mode, controller wave: the next instruction index, or -1 when
+// the list is exhausted (lane 0 takes it with one agent-scope atomic add;
+// every lane gets the value).  Indices come out in list order across the
+// grid.  The two ticket words alternate between runs: run e counts on word
+// e & 1 and clears word (e + 1) & 1, which the previous run (finished, by
+// stream order) used and the next run counts on.
+__device__ __forceinline__ int take_ticket(const KArgs& a) {
+  int tk = 0;
+  if ((threadIdx.x & 63) == 0)
+    tk = __hip_atomic_fetch_add(a.ticket + (a.epoch & 1), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  tk = __shfl(tk, 0, 64);
+  return tk < a.n_instr ? tk : -1;
+}
 
 __device__ __forceinline__ void stamp(const KArgs& a, int gidx, int k, unsigned long long v) {
   a.trace[4 * (long)gidx + k] = v;
@@ -1639,6 +1668,10 @@ __device__ __forceinline__ void stamp(const KArgs& a, int gidx, int k, unsigned 
 __device__ __forceinline__ int fetch_ahead(const Loop& L, int it) {
   const long r = min(it + 2, L.a.n_iters - 1);
   return reinterpret_cast<const int*>(L.a.instrs + r * L.a.ncu + L.vcu)[threadIdx.x & 63];
+}
+// Wave 0, work-queue mode: this lane's word of record tk (0 when tk < 0).
+__device__ __forceinline__ int fetch_record(const Loop& L, int tk) {
+  return tk >= 0 ? reinterpret_cast<const int*>(L.a.instrs + tk)[threadIdx.x & 63] : 0;
 }
 
 // Start of iteration it.  Wave 0 issues the load of record it + 2 (used at
@@ -1710,6 +1743,7 @@ __device__ __forceinline__ bool poll_sources(const Loop& L, const mk_instr& in, 
       if (wall_clock64() - t0 > a.spin_ticks) {
         if (atomicCAS(a.err, 0, (int)MK_E_DEADLOCK) == 0) {
           a.err[1] = L.vcu; a.err[2] = gidx; a.err[3] = who; a.err[4] = seen; a.err[5] = want;
+          if (a.abort_host) __hip_atomic_store(a.abort_host, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
         }
         __hip_atomic_store(a.err + 6, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         ok = 0;
@@ -1722,10 +1756,22 @@ __device__ __forceinline__ bool poll_sources(const Loop& L, const mk_instr& in, 
   if (ns && lane == 0) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   return true;
 }
-__device__ __forceinline__ bool wait_sources(const Loop& L, const mk_instr& in, int it, int gidx, int& w) {
+// Work-queue mode: the ticket for iteration it + 2 is taken before the poll
+// (its round trip overlaps the wait) and the record is loaded after it; tk
+// carries the index to store_ahead.  Once the queue has run dry (iteration
+// it + 1 got no index) no further ticket is taken.
+__device__ __forceinline__ bool wait_sources(const Loop& L, const mk_instr& in, int it, int gidx, int& w,
+                                             int& tk) {
   if (wave_id() == 0) {
-    if (it > 0) w = fetch_ahead(L, it);
-    const bool ok = poll_sources(L, in, gidx);
+    bool ok;
+    if (L.a.queue) {
+      tk = L.idx[(it + 1) % 3] >= 0 ? take_ticket(L.a) : -1;
+      ok = poll_sources(L, in, gidx);
+      w = fetch_record(L, tk);
+    } else {
+      if (it > 0) w = fetch_ahead(L, it);
+      ok = poll_sources(L, in, gidx);
+    }
     if (threadIdx.x == 0) *L.flag = ok;
   }
   lds_barrier();
@@ -1738,20 +1784,29 @@ __device__ __forceinline__ bool wait_sources(const Loop& L, const mk_instr& in, 
 // barrier publishes it.
 // (records 0, 1 and 2 are copied in at the start, so iteration 0 has
 // nothing to fetch or store)
-__device__ __forceinline__ void store_ahead(const Loop& L, int it, int w) {
-  if (wave_id() == 0 && it > 0 && it + 2 < L.a.n_iters)
+// Work-queue mode: slot (it + 2) % 3 takes record tk and idx its index
+// (-1 ends the loop there); records of iterations 0 and 1 are fetched at
+// the start.
+__device__ __forceinline__ void store_ahead(const Loop& L, int it, int w, int tk) {
+  if (wave_id() != 0) return;
+  if (L.a.queue) {
+    if (tk >= 0) reinterpret_cast<int*>(&L.slots[(it + 2) % 3])[threadIdx.x & 63] = w;
+    if (threadIdx.x == 0) L.idx[(it + 2) % 3] = tk;
+  } else if (it > 0 && it + 2 < L.a.n_iters) {
     reinterpret_cast<int*>(&L.slots[(it + 2) % 3])[threadIdx.x & 63] = w;
+  }
 }
 
 // One generic iteration.  Returns false if the run was aborted.
 template <unsigned OPS>
 __device__ __forceinline__ bool generic_iter(const Loop& L, int it, int& w) {
   const KArgs& a = L.a;
-  const int gidx = it * a.ncu + L.vcu;
+  const int gidx = rec_index(L, it);
   const mk_instr& in = L.slots[it % 3];
   const bool tr = a.trace && threadIdx.x == 0 && in.opcode != MK_I_NOOP;
   if (tr) stamp(a, gidx, 0, wall_clock64());
-  if (!wait_sources(L, in, it, gidx, w)) return false;
+  int tk = -1;
+  if (!wait_sources(L, in, it, gidx, w, tk)) return false;
   if (in.opcode != MK_I_NOOP) {
     const mk_node& nd = L.nodes[in.node];
     if (tr) stamp(a, gidx, 1, wall_clock64());
@@ -1760,7 +1815,7 @@ __device__ __forceinline__ bool generic_iter(const Loop& L, int it, int& w) {
     release_dests(a, in);
     if (tr) stamp(a, gidx, 3, wall_clock64());
   }
-  store_ahead(L, it, w);
+  store_ahead(L, it, w, tk);
   return true;
 }
 
@@ -1789,22 +1844,24 @@ __device__ __forceinline__ int gemv_streak(const Loop& L, int& it, int& w) {
     gemv_prologue(a, in, L.nodes[in.node], B);
   }
   for (;;) {
-    const int gidx = it * a.ncu + L.vcu;
+    const int gidx = rec_index(L, it);
     const mk_instr& in = L.slots[it % 3];
     const mk_node& nd = L.nodes[in.node];
     const bool tr = a.trace && threadIdx.x == 0;
     if (tr) stamp(a, gidx, 0, wall_clock64());
-    if (!wait_sources(L, in, it, gidx, w)) return -1;
+    int tk = -1;
+    if (!wait_sources(L, in, it, gidx, w, tk)) return -1;
     if (tr) stamp(a, gidx, 1, wall_clock64());
     // Record it + 2 goes to its slot now, while its load is surely complete:
     // after the release it would wait behind the release's own atomic (the
     // vector-memory counter retires in order).  Nothing reads that slot
-    // before the next counter wait's barrier.
-    store_ahead(L, it, w);
+    // before the next counter wait's barrier.  (In work-queue mode the
+    // record load was issued after the poll, so it is parked after the body.)
+    if (!a.queue) store_ahead(L, it, w, tk);
     // the next record became visible with the barrier in wait_sources
     const mk_instr* nx = nullptr;
     const mk_node* nxd = nullptr;
-    if (it + 1 < a.n_iters) {
+    if (has_rec(L, it + 1)) {
       const mk_instr& c = L.slots[(it + 1) % 3];
       if (c.opcode == MK_I_GEMV && L.nodes[c.node].dtype == nd.dtype) {
         nx = &c;
@@ -1812,6 +1869,7 @@ __device__ __forceinline__ int gemv_streak(const Loop& L, int& it, int& w) {
       }
     }
     s0 = gemv_body_rows<DT>(a, in, nd, L.smem, B, nx, nxd, s0);
+    if (a.queue) store_ahead(L, it, w, tk);
     if (tr) stamp(a, gidx, 2, wall_clock64());
     release_gemv(a, in, nd);
     if (tr) stamp(a, gidx, 3, wall_clock64());
@@ -1832,6 +1890,7 @@ __global__ void __launch_bounds__(256, 1) mk_persistent(mkd::KArgs args) {
   __shared__ mk_instr s_in[3];
   __shared__ mk_node s_nodes[mkd::kMaxNodes];
   __shared__ int s_flag;
+  __shared__ int s_idx[3];
   __shared__ __attribute__((aligned(16))) char smem[mkd::kSmemBytes];
   const int t = threadIdx.x;
   const int b = blockIdx.x;
@@ -1842,12 +1901,35 @@ __global__ void __launch_bounds__(256, 1) mk_persistent(mkd::KArgs args) {
   const int vcu = b;
   for (int i = t; i < a.n_nodes * 64; i += mkd::kThreads)
     reinterpret_cast<int*>(s_nodes)[i] = reinterpret_cast<const int*>(a.nodes)[i];
-  for (int r = 0; r < 3 && r < a.n_iters; ++r)
-    mkd::copy_words(reinterpret_cast<int*>(&s_in[r]), reinterpret_cast<const int*>(a.instrs + (long)r * a.ncu + vcu));
+  if (a.queue) {
+    // clear the other ticket word for the next run; take iterations 0 and 1
+    if (b == 0 && t == 0) __hip_atomic_store(a.ticket + ((a.epoch + 1) & 1), 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (t < 64) {
+      const int t0 = mkd::take_ticket(a);
+      const int t1 = t0 >= 0 ? mkd::take_ticket(a) : -1;
+      if (t0 >= 0) mkd::copy_words(reinterpret_cast<int*>(&s_in[0]), reinterpret_cast<const int*>(a.instrs + t0));
+      if (t1 >= 0) mkd::copy_words(reinterpret_cast<int*>(&s_in[1]), reinterpret_cast<const int*>(a.instrs + t1));
+      if (t == 0) {
+        s_idx[0] = t0;
+        s_idx[1] = t1;
+        s_idx[2] = -1;
+      }
+    }
+  } else {
+    for (int r = 0; r < 3 && r < a.n_iters; ++r)
+      mkd::copy_words(reinterpret_cast<int*>(&s_in[r]), reinterpret_cast<const int*>(a.instrs + (long)r * a.ncu + vcu));
+  }
   __syncthreads();
-  const mkd::Loop L{a, s_in, s_nodes, &s_flag, smem, vcu};
+  // traced runs: the constant-rate wall clock and the shader clock at the
+  // start and end of each workgroup (their ratio is the core clock)
+  unsigned long long* clk = a.trace ? a.trace + 4 * ((long)a.n_iters * a.ncu + b) : nullptr;
+  if (clk && t == 0) {
+    clk[0] = wall_clock64();
+    clk[1] = __builtin_amdgcn_s_memtime();
+  }
+  const mkd::Loop L{a, s_in, s_nodes, &s_flag, smem, vcu, s_idx};
   int it = 0, w = 0;
-  while (it < a.n_iters) {
+  while (mkd::has_rec(L, it)) {
     const mk_instr& in = s_in[it % 3];
     if constexpr ((OPS & mkd::kOpGemv) != 0) {
       if (in.opcode == MK_I_GEMV) {
@@ -1859,6 +1941,10 @@ __global__ void __launch_bounds__(256, 1) mk_persistent(mkd::KArgs args) {
     }
     if (!mkd::generic_iter<OPS>(L, it, w)) return;
     ++it;
+  }
+  if (clk && t == 0) {
+    clk[2] = wall_clock64();
+    clk[3] = __builtin_amdgcn_s_memtime();
   }
 }
 

@@ -24,13 +24,24 @@ struct mk_plan_device {
   mk_node* d_nodes = nullptr;
   int* d_counters = nullptr;
   int* d_err = nullptr;
+  int* h_abort = nullptr;     // pinned host copy of the abort flag
   std::vector<void*> owned;   // by slot (plan-owned buffers), else nullptr
+  std::vector<size_t> owned_bytes;
+  std::vector<char> poison;   // by slot: filled with NaN bytes before a run
   long long spin_ticks = 0;
   int max_target = 1;
   int ctr_stride = 1;         // int32 slots per counter (counter layout of mk.h)
-  size_t ctr_slots = 1;
+  size_t ctr_slots = 1;       // counter slots; the two work-queue ticket
+                              // words follow on a 128-byte line of their own
   unsigned ops = 0;           // op families of the plan's instructions
 };
+constexpr size_t kTicketPad = 32;   // int32 words after the counter slots
+
+// Fill n 32-bit words with v (the NaN poison of debug_poison runs).
+__global__ void mk_fill_kernel(uint32_t* __restrict__ p, size_t n, uint32_t v) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+    p[i] = v;
+}
 
 // Packed column tiles of a row-major weight src [K][ld] (the layout of
 // mk_plan_weight_layout): element e of dst [tiles][K][wc] takes src at row k
@@ -126,6 +137,7 @@ void free_device(mk_plan_device* d) {
   if (d->d_nodes) (void)hipFree(d->d_nodes);
   if (d->d_counters) (void)hipFree(d->d_counters);
   if (d->d_err) (void)hipFree(d->d_err);
+  if (d->h_abort) (void)hipHostFree(d->h_abort);
   for (void* q : d->owned)
     if (q) (void)hipFree(q);
   delete d;
@@ -190,19 +202,27 @@ mk_status ensure_device(mk_plan* p) {
   for (int32_t t : p->targets)
     if (t <= MK_SLICE_MAX) d->ctr_stride = std::max(d->ctr_stride, (int)((t + 31) / 32 * 32));
   d->ctr_slots = std::max<size_t>(p->targets.size(), 1) * (size_t)d->ctr_stride;
-  if ((e = hipMalloc(&d->d_counters, d->ctr_slots * sizeof(int))) != hipSuccess) return bail(e, "hipMalloc counters");
-  if ((e = hipMemset(d->d_counters, 0, d->ctr_slots * sizeof(int))) != hipSuccess) return bail(e, "hipMemset counters");
+  const size_t ctr_bytes = (d->ctr_slots + kTicketPad) * sizeof(int);
+  if ((e = hipMalloc(&d->d_counters, ctr_bytes)) != hipSuccess) return bail(e, "hipMalloc counters");
+  if ((e = hipMemset(d->d_counters, 0, ctr_bytes)) != hipSuccess) return bail(e, "hipMemset counters");
   if ((e = hipMalloc(&d->d_err, 8 * sizeof(int))) != hipSuccess) return bail(e, "hipMalloc error record");
   if ((e = hipMemset(d->d_err, 0, 8 * sizeof(int))) != hipSuccess) return bail(e, "hipMemset error record");
+  if ((e = hipHostMalloc(reinterpret_cast<void**>(&d->h_abort), sizeof(int), hipHostMallocMapped)) != hipSuccess)
+    return bail(e, "hipHostMalloc abort flag");
+  *reinterpret_cast<volatile int*>(d->h_abort) = 0;
   for (int32_t t : p->targets) d->max_target = std::max(d->max_target, (int)t);
   for (const mk_instr& r : p->records) d->ops |= mkd::op_family(r.opcode);
   // plan-owned buffers: intermediates, split-K partials, constant tables
   d->owned.assign(p->slot_owner.size(), nullptr);
+  d->owned_bytes.assign(p->slot_owner.size(), 0);
+  d->poison.assign(p->slot_owner.size(), 0);
   for (size_t s = 0; s < p->slot_owner.size(); ++s) {
     const mk::Tensor& t = p->tensors[p->slot_owner[s]];
     if (t.role != MK_INTERMEDIATE) continue;
-    size_t bytes = std::max<mk::I64>(p->slot_bytes[s], 16);
+    const size_t bytes = ((size_t)std::max<mk::I64>(p->slot_bytes[s], 16) + 15) / 16 * 16;
     if ((e = hipMalloc(&d->owned[s], bytes)) != hipSuccess) return bail(e, "hipMalloc intermediate");
+    d->owned_bytes[s] = bytes;
+    d->poison[s] = t.const_kind == 0 && p->opts.debug_poison;
     if (t.const_kind == 1) {
       // rotary table: row p = [cos(p*th_i) for i < half | sin(p*th_i) for i < half],
       // th_i = theta^(-2i / head_dim), evaluated in double
@@ -253,6 +273,10 @@ mk_status fill_args(mk_plan* p, void* const* buffers, int n_buffers, mkd::KArgs&
   a.instrs = p->dev->d_instrs;
   a.nodes = p->dev->d_nodes;
   a.counters = p->dev->d_counters;
+  a.ticket = p->dev->d_counters + p->dev->ctr_slots;
+  a.queue = p->opts.queue;
+  a.n_instr = (int)p->n_instr;
+  a.abort_host = p->dev->h_abort;
   a.ctr_stride = p->dev->ctr_stride;
   a.err = p->dev->d_err;
   a.spin_ticks = p->dev->spin_ticks;
@@ -274,12 +298,24 @@ mk_status megakernel_run_traced(mk_plan* p, void* const* buffers, int n_buffers,
   mkd::KArgs a;
   if ((st = fill_args(p, buffers, n_buffers, a)) != MK_OK) return st;
   a.trace = reinterpret_cast<unsigned long long*>(trace);
+  if (*reinterpret_cast<volatile int*>(p->dev->h_abort)) {
+    set_error("an earlier run of this plan gave up a counter wait; call mk_plan_check first");
+    return MK_E_DEADLOCK;
+  }
   if (p->n_instr == 0) return MK_OK;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   // counters hold epoch * target; restart from zero well before int32 overflow
   if ((p->epoch + 1) * (int64_t)p->dev->max_target > (1LL << 30)) {
-    HIPCHK(hipMemsetAsync(p->dev->d_counters, 0, p->dev->ctr_slots * sizeof(int), s));
+    HIPCHK(hipMemsetAsync(p->dev->d_counters, 0, (p->dev->ctr_slots + kTicketPad) * sizeof(int), s));
     p->epoch = 0;
+  }
+  for (size_t k = 0; k < p->dev->owned.size(); ++k) {
+    if (!p->dev->poison[k]) continue;
+    const size_t n = p->dev->owned_bytes[k] / 4;
+    const int blocks = (int)std::min<size_t>((n + 255) / 256, 4096);
+    hipLaunchKernelGGL(mk_fill_kernel, dim3(blocks), dim3(256), 0, s, static_cast<uint32_t*>(p->dev->owned[k]), n,
+                       0xffffffffu);
+    HIPCHK(hipGetLastError());
   }
   a.epoch = (int)(p->epoch + 1);
   const void* kernel = persistent_for(p->dev->ops);
@@ -328,7 +364,8 @@ mk_status mk_plan_check(mk_plan* p, void* stream, mk_run_error* err) {
     if (h[0] != 0 || h[6] != 0) {
       // the aborted run left counters mid-epoch: start over from zero
       HIPCHK(hipMemset(p->dev->d_err, 0, 8 * sizeof(int)));
-      HIPCHK(hipMemset(p->dev->d_counters, 0, p->dev->ctr_slots * sizeof(int)));
+      HIPCHK(hipMemset(p->dev->d_counters, 0, (p->dev->ctr_slots + kTicketPad) * sizeof(int)));
+      *reinterpret_cast<volatile int*>(p->dev->h_abort) = 0;
       p->epoch = 0;
       if (err) *err = r;
       set_error("counter wait gave up: cu " + std::to_string(r.cu) + " instr " + std::to_string(r.instr) +

@@ -120,10 +120,11 @@ class Graph:
     # compile -----------------------------------------------------------
     def build(self, num_cus: int = 0, cluster_size: int = 0, reuse: int = 0,
               gemv_max_m: int = 0, spin_limit_us: int = 0, cooperative: int = 0,
-              pack: int = 0, sync: int = 0) -> "Plan":
+              pack: int = 0, sync: int = 0, queue: int = 0, debug_poison: int = 0) -> "Plan":
         opts = L.BuildOptions(num_cus=num_cus, cluster_size=cluster_size, reuse=reuse,
                               gemv_max_m=gemv_max_m, spin_limit_us=spin_limit_us,
-                              cooperative=cooperative, pack=pack, sync=sync)
+                              cooperative=cooperative, pack=pack, sync=sync, queue=queue,
+                              debug_poison=debug_poison)
         p = c_void_p()
         L.check(self._lib.megakernel_build(self._g, byref(opts), byref(p)))
         return Plan(p, self)
@@ -249,16 +250,19 @@ class Plan:
         return c_void_p(stream if isinstance(stream, int) else stream.cuda_stream)
 
     def run(self, buffers, stream=None) -> None:
-        """One forward: one persistent cooperative launch on ``stream``."""
+        """One forward: one persistent launch of num_cus workgroups on
+        ``stream`` (an ordinary launch unless the plan was built with
+        ``cooperative=1``; residency as described at megakernel_run)."""
         arr = self._ptrs(buffers)
         L.check(self._lib.megakernel_run(self._p, arr, len(arr), self._stream(stream)))
 
     def run_traced(self, buffers, trace, stream=None) -> None:
         """One forward that also records 4 wall-clock stamps per instruction
-        into ``trace`` (a device int64 tensor of 4 * n_iters * num_cus)."""
+        into ``trace`` (a device int64 tensor of 4 * n_iters * num_cus +
+        4 * num_cus; the tail holds per-workgroup clock pairs, see mk.h)."""
         arr = self._ptrs(buffers)
         st = self.stats()
-        if trace.numel() < 4 * st.n_iters * st.num_cus:
+        if trace.numel() < 4 * st.n_iters * st.num_cus + 4 * st.num_cus:
             raise ValueError("trace buffer too small")
         L.check(self._lib.megakernel_run_traced(self._p, arr, len(arr), self._stream(stream),
                                                 c_void_p(trace.data_ptr())))

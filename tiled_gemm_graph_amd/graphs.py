@@ -42,33 +42,36 @@ def _t(tiles, i):
 
 
 def build(workload: str, dims: Dict[str, int], tiles: Optional[Sequence[dict]] = None,
-          fused: bool = True, w_first: bool = False) -> Graph:
+          fused: bool = True, w_first: bool = False, dtype: Optional[str] = None) -> Graph:
+    """``dtype`` overrides mlp3's fp16 (the traced MLP of MegaKittens
+    Internals, section 02, is bf16)."""
     g = Graph()
     d = dims
     if workload == "mlp3":
         Lh, M, H = d["layers"], d["m"], d["h"]
+        dt = dtype or "f16"
         if w_first:
-            W = g.tensor("W", "f16", (Lh, H, H), "weight")
-            x = g.tensor("x", "f16", (M, H), "input")
-            b = g.tensor("b", "f16", (Lh, M, H), "weight")
+            W = g.tensor("W", dt, (Lh, H, H), "weight")
+            x = g.tensor("x", dt, (M, H), "input")
+            b = g.tensor("b", dt, (Lh, M, H), "weight")
         else:
-            x = g.tensor("x", "f16", (M, H), "input")
-            W = g.tensor("W", "f16", (Lh, H, H), "weight")
-            b = g.tensor("b", "f16", (Lh, M, H), "weight")
+            x = g.tensor("x", dt, (M, H), "input")
+            W = g.tensor("W", dt, (Lh, H, H), "weight")
+            b = g.tensor("b", dt, (Lh, M, H), "weight")
         cur = x
         for i in range(Lh):
             last = i == Lh - 1
             if fused:
-                y = g.tensor(f"y{i}", "f16", (M, H), "output" if last else "intermediate")
+                y = g.tensor(f"y{i}", dt, (M, H), "output" if last else "intermediate")
                 g.gemm(cur, g.select0(W, i), y, L.EP_BIAS | L.EP_RELU, bias=g.select0(b, i),
                        tile=_t(tiles, i) if tiles and len(tiles) > 1 else _t(tiles, 0))
                 cur = y
             else:
-                mm = g.tensor(f"mm{i}", "f16", (M, H), "intermediate")
+                mm = g.tensor(f"mm{i}", dt, (M, H), "intermediate")
                 g.gemm(cur, g.select0(W, i), mm, 0, tile=tiles[0]["gemm"] if tiles else None)
-                ad = g.tensor(f"add{i}", "f16", (M, H), "intermediate")
+                ad = g.tensor(f"add{i}", dt, (M, H), "intermediate")
                 g.add(mm, g.select0(b, i), ad, tile=tiles[0]["ew"] if tiles else None)
-                r = g.tensor(f"relu{i}" if not last else f"y{i}", "f16", (M, H),
+                r = g.tensor(f"relu{i}" if not last else f"y{i}", dt, (M, H),
                              "output" if last else "intermediate")
                 g.relu(ad, r, tile=tiles[0]["ew"] if tiles else None)
                 cur = r
@@ -180,8 +183,20 @@ class Runner:
         self.bufs[self.out_name] = self.out
         self.run_bufs[self.out_name] = self.out
 
-    def forward(self, stream=None):
-        self.plan.run(self.run_bufs, stream)
+    def alt_plan(self, **opts) -> Plan:
+        """Another plan of the same graph (e.g. ``queue=1``); it must read
+        its weights in the same layouts, so it runs on this runner's
+        buffers."""
+        p = self.graph.build(**opts)
+        if sorted(p.packed_weights()) != sorted(self.packed):
+            raise ValueError("alternative plan packs other weights")
+        for name, buf in self.packed.items():
+            if p.weight_layout(name)[1] != buf.numel() * buf.element_size():
+                raise ValueError(f"alternative plan packs {name} in another layout")
+        return p
+
+    def forward(self, stream=None, plan: Optional[Plan] = None):
+        (plan or self.plan).run(self.run_bufs, stream)
         return self.out
 
     def forward_per_op(self, stream=None):

@@ -27,16 +27,33 @@ def wall_clock_khz() -> int:
     return v.value
 
 
-def capture(runner) -> np.ndarray:
-    """One traced forward; returns int64 [n_instr, 4] stamps (0 for Noops)."""
+def capture(runner, with_clock: bool = False):
+    """One traced forward; returns int64 [n_instr, 4] stamps (0 for Noops),
+    and with ``with_clock`` also the core clock in MHz over the run."""
     import torch
     st = runner.plan.stats()
-    n = 4 * st.n_iters * st.num_cus
+    n = 4 * st.n_iters * st.num_cus + 4 * st.num_cus
     buf = torch.zeros(n, dtype=torch.int64, device=runner.out.device)
     runner.plan.run_traced(runner.run_bufs, buf)
     runner.plan.check()
     torch.cuda.synchronize()
-    return buf.view(-1, 4).cpu().numpy()[: st.n_instr]
+    h = buf.view(-1, 4).cpu().numpy()
+    stamps = h[: st.n_instr]
+    if not with_clock:
+        return stamps
+    return stamps, core_clock_mhz(h[st.n_iters * st.num_cus:], wall_clock_khz())
+
+
+def core_clock_mhz(clk: np.ndarray, khz: int) -> float:
+    """Shader-clock ticks over wall-clock ticks, summed over the workgroups
+    that recorded both ends ([num_cus, 4]: wall0, shader0, wall1, shader1),
+    times the wall-clock rate."""
+    ok = (clk[:, 2] > clk[:, 0]) & (clk[:, 3] > clk[:, 1])
+    if not ok.any():
+        return float("nan")
+    dw = float((clk[ok, 2] - clk[ok, 0]).sum())
+    ds = float((clk[ok, 3] - clk[ok, 1]).sum())
+    return ds / dw * khz / 1000.0
 
 
 def summarize(plan, tr: np.ndarray, khz: int = 100000) -> Dict:

@@ -177,8 +177,14 @@ def _draw(ts: TensorSpec, g: torch.Generator) -> torch.Tensor:
 
 
 def generate(workload: str, dims: Dict[str, int] | None = None,
-             seed: int = 0) -> Dict[str, torch.Tensor]:
-    """Draw every tensor of ``workload`` (CPU, storage dtype), in order."""
+             seed: int = 0, dtype: torch.dtype | None = None) -> Dict[str, torch.Tensor]:
+    """Draw every tensor of ``workload`` (CPU, storage dtype), in order.
+
+    ``dtype`` replaces every tensor's storage dtype (the same normals,
+    rounded once to that dtype instead)."""
     g = torch.Generator(device="cpu")
     g.manual_seed(seed)
-    return {ts.name: _draw(ts, g) for ts in spec(workload, dims)}
+    specs = spec(workload, dims)
+    if dtype is not None:
+        specs = [dataclasses.replace(ts, dtype=dtype) for ts in specs]
+    return {ts.name: _draw(ts, g) for ts in specs}
