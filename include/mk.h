@@ -368,6 +368,24 @@ mk_status megakernel_run_traced(mk_plan *p, void *const *buffers, int n_buffers,
  * Arguments, ownership and errors as megakernel_run. */
 mk_status megakernel_run_per_op(mk_plan *p, void *const *buffers, int n_buffers,
                                 void *stream);
+/* megakernel_run for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  It calls no hipMalloc, hipFree or other allocating routine:
+ * the plan's error record, counters, records, node table and plan-owned
+ * intermediates live in a file-scope device array of 64 MiB per GPU,
+ * held from the library's load until the process ends.  Every call
+ * clears the error record and counters with a fill kernel, uploads the
+ * plan's records, node table and constant tables (asynchronous copies
+ * from host memory the plan owns; keep the plan alive until the stream has
+ * passed them), then launches as megakernel_run.  The array keeps the last
+ * call's contents and is shared by every call on that GPU, whatever the
+ * plan: calls that overlap on one GPU (other streams, other threads) race
+ * and give wrong results.  Errors: MK_E_LIMIT when the plan needs more
+ * than 64 MiB (the message gives the size; nothing is launched), and those
+ * of megakernel_run, except that no earlier abort is refused (each call
+ * starts from a cleared record).  mk_plan_check afterwards reads the error
+ * record of the last allocation-free call on the plan's device. */
+mk_status megakernel_run_noalloc(mk_plan *p, void *const *buffers, int n_buffers, void *stream);
 /* Synchronise `stream` and read the plan's error record. */
 mk_status mk_plan_check(mk_plan *p, void *stream, mk_run_error *err);
 

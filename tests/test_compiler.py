@@ -337,3 +337,14 @@ def test_new_build_options_are_validated():
     a, b = g.build(), g.build(queue=1, debug_poison=1)
     assert np.array_equal(a.instructions(), b.instructions())
     assert np.array_equal(a.barriers(), b.barriers())
+
+
+def test_noalloc_size_limit_checked_before_any_gpu_call():
+    # the full decoder layer needs about 150 MB of intermediates, beyond the
+    # allocation-free path's 64 MiB: refused with MK_E_LIMIT, no GPU touched
+    plan = G.build("layer", workloads.default_dims("layer")).build()
+    assert plan.stats().intermediate_bytes > 64 << 20
+    with pytest.raises(L.MkError) as ei:
+        plan.run_noalloc([0] * 64, stream=0)
+    assert ei.value.status == L.MK_E_LIMIT
+    assert "64" in str(ei.value) or "67108864" in str(ei.value)

@@ -78,7 +78,7 @@ class RunError(Structure):
 EXPORTS = [
     "mk_graph_create", "mk_graph_destroy", "mk_graph_tensor", "mk_graph_view", "mk_graph_op",
     "megakernel_build", "mk_plan_destroy", "megakernel_run", "megakernel_run_traced",
-    "megakernel_run_per_op",
+    "megakernel_run_per_op", "megakernel_run_noalloc",
     "mk_plan_check", "mk_plan_stats_get", "mk_plan_instructions", "mk_plan_nodes",
     "mk_plan_barriers", "mk_plan_slots", "mk_plan_op_tile", "mk_plan_read_counters",
     "mk_plan_epoch", "mk_plan_weight_layout", "mk_plan_pack_weight", "mk_wall_clock_khz",
@@ -108,6 +108,7 @@ def load() -> ctypes.CDLL:
         "megakernel_run": ([vp, POINTER(c_void_p), c_int, vp], c_int),
         "megakernel_run_traced": ([vp, POINTER(c_void_p), c_int, vp, vp], c_int),
         "megakernel_run_per_op": ([vp, POINTER(c_void_p), c_int, vp], c_int),
+        "megakernel_run_noalloc": ([vp, POINTER(c_void_p), c_int, vp], c_int),
         "mk_plan_check": ([vp, vp, POINTER(RunError)], c_int),
         "mk_plan_stats_get": ([vp, POINTER(PlanStats)], c_int),
         "mk_plan_instructions": ([vp, POINTER(i32p), i64p, i32p], c_int),

@@ -1108,6 +1108,27 @@ struct Compiler {
     p.stats.bytes = bytes;
   }
 
+  // Contents of the compiler's constant tables, by slot.  Rotary table
+  // (const_kind 1): row p = [cos(p th_i) for i < half | sin(p th_i) for
+  // i < half], th_i = theta^(-2i / head_dim), evaluated in double.
+  void const_tables() {
+    p.const_data.assign(p.slot_owner.size(), {});
+    for (size_t s = 0; s < p.slot_owner.size(); ++s) {
+      const Tensor& t = p.tensors[p.slot_owner[s]];
+      if (t.const_kind != 1) continue;
+      const int half = t.rope_half;
+      const I64 rows = t.shape[2];
+      std::vector<float>& tab = p.const_data[s];
+      tab.resize((size_t)rows * 2 * half);
+      for (I64 pos = 0; pos < rows; ++pos)
+        for (int i = 0; i < half; ++i) {
+          const double th = std::pow((double)t.rope_theta, -2.0 * i / (2.0 * half));
+          tab[(size_t)pos * 2 * half + i] = (float)std::cos((double)pos * th);
+          tab[(size_t)pos * 2 * half + half + i] = (float)std::sin((double)pos * th);
+        }
+    }
+  }
+
   void run() {
     p.tensors = g.t;
     p.n_graph_tensors = (int)g.t.size();
@@ -1119,6 +1140,7 @@ struct Compiler {
     derive_barriers();
     emit();
     algorithmic_counts();
+    const_tables();
     p.stats.reserved = unsupported.empty() ? 0 : 1;
     unsupported_reason = unsupported;
   }

@@ -116,7 +116,9 @@ struct mk_plan {
   int64_t n_instr = 0;
   int64_t epoch = 0;
   std::string unsupported;          // why the GPU path cannot run it ("" = runnable)
+  std::vector<std::vector<float>> const_data;  // by slot: contents of constant tables
   mk_plan_device* dev = nullptr;
+  int noalloc_device = -1;          // device of the last megakernel_run_noalloc call
 };
 
 namespace mk {

@@ -10,6 +10,7 @@
 
 #include <cmath>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -36,6 +37,9 @@ struct mk_plan_device {
   unsigned ops = 0;           // op families of the plan's instructions
 };
 constexpr size_t kTicketPad = 32;   // int32 words after the counter slots
+
+// The array behind megakernel_run_noalloc (64 MiB per GPU, see below).
+static __device__ __align__(256) unsigned char scratch[(size_t)64 << 20];
 
 // Fill n 32-bit words with v (the NaN poison of debug_poison runs).
 __global__ void mk_fill_kernel(uint32_t* __restrict__ p, size_t n, uint32_t v) {
@@ -223,20 +227,10 @@ mk_status ensure_device(mk_plan* p) {
     if ((e = hipMalloc(&d->owned[s], bytes)) != hipSuccess) return bail(e, "hipMalloc intermediate");
     d->owned_bytes[s] = bytes;
     d->poison[s] = t.const_kind == 0 && p->opts.debug_poison;
-    if (t.const_kind == 1) {
-      // rotary table: row p = [cos(p*th_i) for i < half | sin(p*th_i) for i < half],
-      // th_i = theta^(-2i / head_dim), evaluated in double
-      const int half = t.rope_half, rows = (int)t.shape[2];
-      std::vector<float> tab((size_t)rows * 2 * half);
-      for (int pos = 0; pos < rows; ++pos)
-        for (int i = 0; i < half; ++i) {
-          const double th = std::pow((double)t.rope_theta, -2.0 * i / (2.0 * half));
-          tab[(size_t)pos * 2 * half + i] = (float)std::cos(pos * th);
-          tab[(size_t)pos * 2 * half + half + i] = (float)std::sin(pos * th);
-        }
-      if ((e = hipMemcpy(d->owned[s], tab.data(), tab.size() * sizeof(float), hipMemcpyHostToDevice)) != hipSuccess)
-        return bail(e, "hipMemcpy rope table");
-    }
+    const std::vector<float>& tab = p->const_data[s];
+    if (!tab.empty() &&
+        (e = hipMemcpy(d->owned[s], tab.data(), tab.size() * sizeof(float), hipMemcpyHostToDevice)) != hipSuccess)
+      return bail(e, "hipMemcpy constant table");
   }
   int rate_khz = 0;
   if ((e = hipDeviceGetAttribute(&rate_khz, hipDeviceAttributeWallClockRate, dev)) != hipSuccess)
@@ -245,6 +239,12 @@ mk_status ensure_device(mk_plan* p) {
   d->spin_ticks = (long long)(p->opts.spin_limit_us * (double)rate_khz / 1000.0);
   p->dev = d;
   return MK_OK;
+}
+
+unsigned ops_of(const mk_plan* p) {
+  unsigned ops = 0;
+  for (const mk_instr& r : p->records) ops |= mkd::op_family(r.opcode);
+  return ops;
 }
 
 mk_status fill_args(mk_plan* p, void* const* buffers, int n_buffers, mkd::KArgs& a) {
@@ -283,6 +283,76 @@ mk_status fill_args(mk_plan* p, void* const* buffers, int n_buffers, mkd::KArgs&
   a.n_iters = (int)p->stats.n_iters;
   a.ncu = p->opts.num_cus;
   a.n_nodes = (int)p->node_descs.size();
+  return MK_OK;
+}
+
+// ------------------------------------------------- allocation-free runs
+// Device memory of megakernel_run_noalloc: one array per GPU, held until the
+// process ends and shared by every such call on that GPU.  In host code the
+// array's name only stands in for the symbol; its device address comes from
+// hipGetSymbolAddress, once per device, and only that address is used.
+constexpr size_t kScratchBytes = sizeof(scratch);
+constexpr int kMaxDevices = 64;
+void* g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Counter layout of a plan (mk.h): slots per counter and in all.
+void counter_layout(const mk_plan* p, int& stride, size_t& slots, int& max_target) {
+  stride = 1;
+  max_target = 1;
+  for (int32_t t : p->targets) {
+    if (t <= MK_SLICE_MAX) stride = std::max(stride, (int)((t + 31) / 32 * 32));
+    max_target = std::max(max_target, (int)t);
+  }
+  slots = std::max<size_t>(p->targets.size(), 1) * (size_t)stride;
+}
+
+// Where a plan's device state sits in the array: the error record, the
+// counters and ticket words (cleared by every call), the records, the node
+// table, then one region per plan-owned buffer.
+struct NoallocLayout {
+  size_t err = 0, ctr = 0, rec = 0, nodes = 0, total = 0;
+  int ctr_stride = 1, max_target = 1;
+  size_t ctr_slots = 1;
+  std::vector<size_t> slot_off;   // by slot, for plan-owned buffers
+};
+NoallocLayout noalloc_layout(const mk_plan* p) {
+  NoallocLayout L;
+  counter_layout(p, L.ctr_stride, L.ctr_slots, L.max_target);
+  L.err = 0;
+  L.ctr = 256;
+  L.rec = align256(L.ctr + (L.ctr_slots + kTicketPad) * sizeof(int));
+  L.nodes = align256(L.rec + p->records.size() * sizeof(mk_instr));
+  size_t off = align256(L.nodes + p->node_descs.size() * sizeof(mk_node));
+  L.slot_off.assign(p->slot_owner.size(), 0);
+  for (size_t s = 0; s < p->slot_owner.size(); ++s) {
+    if (p->tensors[p->slot_owner[s]].role != MK_INTERMEDIATE) continue;
+    L.slot_off[s] = off;
+    off = align256(off + (size_t)std::max<mk::I64>(p->slot_bytes[s], 16));
+  }
+  L.total = off;
+  return L;
+}
+
+// Device address of this device's array (looked up on the first call).
+mk_status scratch_for(int dev, unsigned char** out) {
+  if (dev < 0 || dev >= kMaxDevices) {
+    set_error("device index beyond the allocation-free path's table");
+    return MK_E_UNSUPPORTED;
+  }
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* ptr = nullptr;
+    HIPCHK(hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)));
+    if (!ptr) {
+      set_error("hipGetSymbolAddress gave a null address for the scratch array");
+      return MK_E_HIP;
+    }
+    g_scratch[dev] = ptr;
+  }
+  *out = static_cast<unsigned char*>(g_scratch[dev]);
   return MK_OK;
 }
 
@@ -352,9 +422,143 @@ mk_status megakernel_run_per_op(mk_plan* p, void* const* buffers, int n_buffers,
   return MK_OK;
 }
 
+mk_status megakernel_run_noalloc(mk_plan* p, void* const* buffers, int n_buffers, void* stream) {
+  if (!p) { set_error("null plan"); return MK_E_INVALID; }
+  const char* why = mk_plan_unsupported_reason(p);
+  if (why && *why) {
+    set_error(std::string("plan cannot run on the GPU: ") + why);
+    return MK_E_UNSUPPORTED;
+  }
+  if (p->opts.reuse == 2) {
+    set_error("reuse mode 2 (outputs in pooled slots) is a host-only profile");
+    return MK_E_UNSUPPORTED;
+  }
+  const NoallocLayout lay = noalloc_layout(p);
+  if (lay.total > kScratchBytes) {
+    set_error("plan needs " + std::to_string(lay.total) + " bytes of device state (records, counters, " +
+              "intermediates); the allocation-free path holds at most " + std::to_string(kScratchBytes));
+    return MK_E_LIMIT;
+  }
+  if (n_buffers < p->n_graph_tensors) {
+    set_error("buffers must have one entry per graph tensor id");
+    return MK_E_INVALID;
+  }
+  int dev = 0;
+  HIPCHK(hipGetDevice(&dev));
+  int ncu = 0;
+  HIPCHK(hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev));
+  if (ncu != p->opts.num_cus) {
+    set_error("plan was built for " + std::to_string(p->opts.num_cus) + " CUs, device has " + std::to_string(ncu));
+    return MK_E_UNSUPPORTED;
+  }
+  unsigned char* base = nullptr;
+  mk_status st = scratch_for(dev, &base);
+  if (st != MK_OK) return st;
+  mkd::KArgs a;
+  std::memset(&a, 0, sizeof(a));
+  for (size_t k = 0; k < p->slot_owner.size(); ++k) {
+    const int tid = p->slot_owner[k];
+    if (p->tensors[tid].role == MK_INTERMEDIATE) {
+      a.bufs[k] = base + lay.slot_off[k];
+      continue;
+    }
+    if (!buffers || !buffers[tid]) {
+      set_error("missing device buffer for tensor id " + std::to_string(tid));
+      return MK_E_INVALID;
+    }
+    if (reinterpret_cast<uintptr_t>(buffers[tid]) % 16) {
+      set_error("device buffer of tensor id " + std::to_string(tid) + " is not 16-byte aligned");
+      return MK_E_INVALID;
+    }
+    a.bufs[k] = buffers[tid];
+  }
+  int rate_khz = 0;
+  HIPCHK(hipDeviceGetAttribute(&rate_khz, hipDeviceAttributeWallClockRate, dev));
+  if (rate_khz <= 0) rate_khz = 100000;
+  a.instrs = reinterpret_cast<const mk_instr*>(base + lay.rec);
+  a.nodes = reinterpret_cast<const mk_node*>(base + lay.nodes);
+  a.counters = reinterpret_cast<int*>(base + lay.ctr);
+  a.ticket = a.counters + lay.ctr_slots;
+  a.err = reinterpret_cast<int*>(base + lay.err);
+  a.abort_host = nullptr;
+  a.queue = p->opts.queue;
+  a.n_instr = (int)p->n_instr;
+  a.ctr_stride = lay.ctr_stride;
+  a.spin_ticks = (long long)(p->opts.spin_limit_us * (double)rate_khz / 1000.0);
+  a.n_iters = (int)p->stats.n_iters;
+  a.ncu = p->opts.num_cus;
+  a.n_nodes = (int)p->node_descs.size();
+  a.epoch = 1;   // counters start from zero on every call
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  // the array keeps the previous call's contents: clear the error record,
+  // counters and ticket words (a fill kernel, not a memset), upload this
+  // plan's records, node table and constant tables
+  {
+    const size_t words = lay.rec / 4;
+    hipLaunchKernelGGL(mk_fill_kernel, dim3((unsigned)std::min<size_t>((words + 255) / 256, 1024)), dim3(256), 0, s,
+                       reinterpret_cast<uint32_t*>(base), words, 0u);
+    HIPCHK(hipGetLastError());
+  }
+  if (!p->records.empty())
+    HIPCHK(hipMemcpyAsync(base + lay.rec, p->records.data(), p->records.size() * sizeof(mk_instr),
+                          hipMemcpyHostToDevice, s));
+  if (!p->node_descs.empty())
+    HIPCHK(hipMemcpyAsync(base + lay.nodes, p->node_descs.data(), p->node_descs.size() * sizeof(mk_node),
+                          hipMemcpyHostToDevice, s));
+  for (size_t k = 0; k < p->slot_owner.size(); ++k) {
+    if (p->tensors[p->slot_owner[k]].role != MK_INTERMEDIATE) continue;
+    const std::vector<float>& tab = p->const_data[k];
+    if (!tab.empty()) {
+      HIPCHK(hipMemcpyAsync(base + lay.slot_off[k], tab.data(), tab.size() * sizeof(float), hipMemcpyHostToDevice, s));
+    } else if (p->opts.debug_poison) {
+      const size_t words = align256((size_t)std::max<mk::I64>(p->slot_bytes[k], 16)) / 4;
+      hipLaunchKernelGGL(mk_fill_kernel, dim3((unsigned)std::min<size_t>((words + 255) / 256, 4096)), dim3(256), 0,
+                         s, reinterpret_cast<uint32_t*>(base + lay.slot_off[k]), words, 0xffffffffu);
+      HIPCHK(hipGetLastError());
+    }
+  }
+  p->noalloc_device = dev;
+  if (p->n_instr == 0) return MK_OK;
+  const void* kernel = persistent_for(ops_of(p));
+  void* args[] = {&a};
+  if (p->opts.cooperative) {
+    HIPCHK(hipLaunchCooperativeKernel(kernel, dim3(p->opts.num_cus), dim3(mkd::kThreads), args, 0, s));
+  } else {
+    HIPCHK(hipLaunchKernel(kernel, dim3(p->opts.num_cus), dim3(mkd::kThreads), args, 0, s));
+  }
+  return MK_OK;
+}
+
 mk_status mk_plan_check(mk_plan* p, void* stream, mk_run_error* err) {
   if (!p) { set_error("null plan"); return MK_E_INVALID; }
   mk_run_error r{};
+  if (p->noalloc_device >= 0) {
+    // the allocation-free path's error record (the last such call on that device)
+    int cur = 0;
+    HIPCHK(hipGetDevice(&cur));
+    unsigned char* base = nullptr;
+    HIPCHK(hipSetDevice(p->noalloc_device));
+    mk_status st = scratch_for(p->noalloc_device, &base);
+    if (st == MK_OK) {
+      int h[8];
+      hipError_t e1 = hipStreamSynchronize(reinterpret_cast<hipStream_t>(stream));
+      hipError_t e2 = e1 == hipSuccess ? hipMemcpy(h, base, sizeof(h), hipMemcpyDeviceToHost) : e1;
+      (void)hipSetDevice(cur);
+      if (e2 != hipSuccess) return hip_fail(e2, "reading the allocation-free error record");
+      p->noalloc_device = -1;   // reported once; the next call clears the record
+      if (h[0] != 0 || h[6] != 0) {
+        r.code = h[0]; r.cu = h[1]; r.instr = h[2]; r.barrier = h[3]; r.value = h[4]; r.need = h[5];
+        if (err) *err = r;
+        set_error("counter wait gave up (allocation-free run): cu " + std::to_string(r.cu) + " instr " +
+                  std::to_string(r.instr) + " counter " + std::to_string(r.barrier) + " value " +
+                  std::to_string(r.value) + " need " + std::to_string(r.need));
+        return MK_E_DEADLOCK;
+      }
+    } else {
+      (void)hipSetDevice(cur);
+      return st;
+    }
+  }
   if (p->dev) {
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     HIPCHK(hipStreamSynchronize(s));

@@ -272,6 +272,12 @@ class Plan:
         arr = self._ptrs(buffers)
         L.check(self._lib.megakernel_run_per_op(self._p, arr, len(arr), self._stream(stream)))
 
+    def run_noalloc(self, buffers, stream=None) -> None:
+        """One forward through megakernel_run_noalloc: the plan's device
+        state in the library's fixed per-GPU array, no allocation."""
+        arr = self._ptrs(buffers)
+        L.check(self._lib.megakernel_run_noalloc(self._p, arr, len(arr), self._stream(stream)))
+
     def check(self, stream=None) -> L.RunError:
         """Synchronise and raise MkError(MK_E_DEADLOCK) if a wait gave up."""
         err = L.RunError()
