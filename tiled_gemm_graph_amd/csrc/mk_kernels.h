@@ -27,6 +27,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "mk.h"
 
 namespace mkd {
@@ -160,6 +162,17 @@ __device__ __forceinline__ void lds_barrier() {
 // code that every wave runs would also drain the other waves' streams.
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6); }
 
+// A value every lane holds the same (record and node fields read from LDS),
+// moved to a scalar register: loop bounds and branches on it become scalar
+// branches instead of exec-masked ones.
+__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ const char* uni_ptr(const void* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<const char*>(((uint64_t)hi << 32) | lo);
+}
+
 // Base of operand o.  The slot is the same in every lane; saying so keeps
 // the table read a scalar load instead of a vector-memory load that would
 // have to complete behind every load a wave has in flight.
@@ -261,14 +274,14 @@ __device__ __forceinline__ void gemm_tile(const KArgs& a, const mk_instr& in, co
   u16* Bs = As + 2 * A_STAGE;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int flags = in.flags;
+  const int flags = uni(in.flags);
   const bool silu = flags & MK_EP_SILU_MUL;
   const int half = silu ? BNK / 2 : BNK;
-  const int M = nd.M, N = nd.N;
-  const int r0 = in.r0, c0 = in.c0, k0 = in.k0, k1 = in.k1;
+  const int M = uni(nd.M), N = uni(nd.N);
+  const int r0 = uni(in.r0), c0 = uni(in.c0), k0 = uni(in.k0), k1 = uni(in.k1);
   const u16* A = buf<const u16>(a, nd.a);
   const u16* B = buf<const u16>(a, nd.b);
-  const long lda = nd.a.ld, ldb = nd.b.ld;
+  const long lda = uni(nd.a.ld), ldb = uni(nd.b.ld);
 
   // per-thread global addresses
   const u16* a_src[A_CHUNKS];
@@ -436,13 +449,6 @@ __device__ __forceinline__ void gemm_tile(const KArgs& a, const mk_instr& in, co
 // gate and up columns of one output (SILU_MUL) WN/2 columns apart inside a
 // wave's half, and a rotary partner is head_dim/2 columns away in the same
 // wave, so both partners of every pair are in the same lane.
-// s_waitcnt with vmcnt(N) only (expcnt and lgkmcnt left alone).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N <= 63, "vmcnt is 6 bits");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0f70);
-}
-
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef const __attribute__((address_space(1))) void gbl_void_t;
 
@@ -471,60 +477,30 @@ __device__ __forceinline__ void g2lds16_asm(const void* src, unsigned dst) {
       : "memory");
 }
 
-// One K step of the packed GEMM: issue the direct-to-LDS loads of a later
-// stage into `nxt` (when issue is set) and run this stage's MFMAs from
-// `cur`.  The two stage buffers are distinct restrict pointers so the
-// waitcnt pass knows the operand reads cannot alias the loads in flight and
-// does not drain them; completion is awaited explicitly (wait_vmcnt) before
-// the barrier that precedes a stage's use.
-template <int BM, int BN, int DT>
-struct PackedGemmStep {
-  static constexpr int ROWB = 128, A_BYTES = BM * ROWB;
-  static constexpr int WM = BM / 2, WN = BN / 2, FM = WM / 32, FN = WN / 32;
-  static constexpr int A_LOADS = BM / 32, B_LOADS = BN / 32;
-  // nxt_lds: LDS byte address of the stage being filled; wave_s: the wave
-  // index as a scalar.
-  __device__ __forceinline__ static void run(const char* __restrict__ cur, unsigned nxt_lds, bool issue,
-                                             const u16* a_lane, const int (&a_off)[A_LOADS], int a_koff,
-                                             const u16* bk, const int (&b_off)[B_LOADS], int wave_s, int lane,
-                                             int wm, int wn, f32x16 (&acc)[FM][FN]) {
-    if (issue) {
-#pragma unroll
-      for (int i = 0; i < A_LOADS; ++i)
-        g2lds16_asm(a_lane + a_off[i] + a_koff, nxt_lds + (8 * (wave_s + 4 * i)) * ROWB);
-#pragma unroll
-      for (int i = 0; i < B_LOADS; ++i)
-        g2lds16_asm(bk + b_off[i], nxt_lds + A_BYTES + (8 * (wave_s + 4 * i)) * ROWB);
-    }
-    const char* as = cur;
-    const char* bs = cur + A_BYTES;
-    // operand fragments of the four 16-deep sub-steps, double-buffered so
-    // the LDS reads of sub-step kk + 1 are in flight during kk's MFMAs
-    u32x4 af[2][FM], bf[2][FN];
-    auto load = [&](int kk, int b) __attribute__((always_inline)) {
-      const int c = kk * 2 + (lane >> 5);
-#pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        const int row = wm * WM + i * 32 + (lane & 31);
-        af[b][i] = *reinterpret_cast<const u32x4*>(as + row * ROWB + ((c ^ ((row >> 1) & 7)) << 4));
-      }
-#pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const int row = wn * WN + j * 32 + (lane & 31);
-        bf[b][j] = *reinterpret_cast<const u32x4*>(bs + row * ROWB + ((c ^ ((row >> 1) & 7)) << 4));
-      }
-    };
-    load(0, 0);
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      if (kk + 1 < 4) load(kk + 1, (kk + 1) & 1);
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j) acc[i][j] = mfma32<DT>(af[kk & 1][i], bf[kk & 1][j], acc[i][j]);
-    }
-  }
-};
+// The same load with a scalar base address and a 32-bit per-lane byte
+// offset (the SADDR form): the per-stage address step is a scalar add, and
+// the per-lane part never changes, so a load costs no vector instruction.
+__device__ __forceinline__ void g2lds16_sb(const void* sbase, unsigned voff, unsigned dst) {
+  unsigned saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %2, %3\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(__builtin_amdgcn_readfirstlane(dst)), "v"(voff), "s"(sbase)
+      : "memory");
+}
+
+// s_waitcnt with vmcnt(N) and lgkmcnt(0) (expcnt left alone): this wave's
+// LDS reads have completed and at most N of its vector-memory loads are
+// still in flight.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_lgkm0() {
+  static_assert(N >= 0 && N <= 63, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0070);
+}
 
 // Workgroup barrier with no memory fence: the caller has already waited
 // for the operations the barrier publishes (LDS is coherent within the CU);
@@ -535,53 +511,64 @@ __device__ __forceinline__ void bare_barrier() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-template <int BM, int BN, int DT>
+// NW waves (4 or 8) in a (NW / 2) x 2 grid, each WM x WN = BM / (NW / 2) x
+// BN / 2.  With eight waves two share each SIMD, so one wave's MFMAs run
+// while the other issues loads or waits at a barrier.
+template <int BM, int BN, int DT, int NW = 4>
 __device__ __forceinline__ void gemm_packed_tile(const KArgs& a, const mk_instr& in, const mk_node& nd,
                                                  char* smem) {
+  constexpr int NT = NW * 64;
   constexpr int ROWB = 128;                         // bytes per LDS row: 64 k values
   constexpr int A_BYTES = BM * ROWB, STAGE = (BM + BN) * ROWB;
-  constexpr int WM = BM / 2, WN = BN / 2, FM = WM / 32, FN = WN / 32;
-  constexpr int A_LOADS = BM / 32, B_LOADS = BN / 32;  // 16-byte loads per thread per stage
+  constexpr int WGM = NW / 2;                       // wave rows (two wave columns)
+  constexpr int WM = BM / WGM, WN = BN / 2, FM = WM / 32, FN = WN / 32;
+  static_assert(FM >= 1 && FN >= 1, "every wave holds whole 32 x 32 blocks");
+  constexpr int A_LOADS = BM / (8 * NW), B_LOADS = BN / (8 * NW);  // 16-byte loads per thread per stage
+  static_assert(A_LOADS * 8 * NW == BM && B_LOADS * 8 * NW == BN, "loads cover the tile");
   constexpr int ST = (kSmemBytes / STAGE) < 4 ? (kSmemBytes / STAGE) : 4;
   static_assert(ST >= 2, "two stages must fit in LDS");
   constexpr int L = A_LOADS + B_LOADS;                 // loads per thread per stage
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int flags = in.flags;
-  const int M = nd.M, N = nd.N, K = nd.K;
-  const int r0 = in.r0, c0 = in.c0, k0 = in.k0, k1 = in.k1;
+  const int flags = uni(in.flags);
+  const int M = uni(nd.M), N = uni(nd.N), K = uni(nd.K);
+  const int r0 = uni(in.r0), c0 = uni(in.c0), k0 = uni(in.k0), k1 = uni(in.k1);
   const u16* A = buf<const u16>(a, nd.a);
-  const long lda = nd.a.ld;
+  const long lda = uni(nd.a.ld);
 
-  // Load instruction i of this wave fills rows 8 * (wave + 4 * i) .. + 8 of
+  // Load instruction i of this wave fills rows 8 * (wave + NW * i) .. + 8 of
   // its operand: lane -> row (lane >> 3), physical chunk (lane & 7).  The
-  // rows of one lane are 32 apart, so they share the swizzle chunk; their
-  // element offsets fit in 32 bits (A has fewer than 2^31 elements).
+  // rows of one lane are 8 NW apart, so they share the swizzle chunk.  Each
+  // load is a scalar base (the operand at this K stage) plus a fixed 32-bit
+  // byte offset per lane (A has fewer than 2^31 elements).
   const int row0 = 8 * wave + (lane >> 3);
-  const u16* a_lane = A + k0 + (((lane & 7) ^ ((row0 >> 1) & 7)) << 3);
-  int a_off[A_LOADS];
+  const unsigned a_chunk = ((lane & 7) ^ ((row0 >> 1) & 7)) << 4;   // bytes
+  unsigned a_vo[A_LOADS];
 #pragma unroll
-  for (int i = 0; i < A_LOADS; ++i) a_off[i] = min(r0 + row0 + 32 * i, M - 1) * (int)lda;
+  for (int i = 0; i < A_LOADS; ++i) a_vo[i] = (unsigned)(min(r0 + row0 + 8 * NW * i, M - 1) * (int)lda) * 2u + a_chunk;
   const long nkt = K / 64;
-  const u16* b_base = buf<const u16>(a, nd.b) + ((long)in.coord[1] * nkt + k0 / 64) * (long)BN * 64;
-  int b_off[B_LOADS];
+  const char* a_sb = uni_ptr(A + k0);
+  const char* b_sb = uni_ptr(buf<const u16>(a, nd.b) + ((long)uni(in.coord[1]) * nkt + k0 / 64) * (long)BN * 64);
+  unsigned b_vo[B_LOADS];
 #pragma unroll
   for (int i = 0; i < B_LOADS; ++i) {
-    const int row = 8 * (wave + 4 * i) + (lane >> 3);
+    const int row = 8 * (wave + NW * i) + (lane >> 3);
     const int c = (lane & 7) ^ ((row >> 1) & 7);
-    b_off[i] = row * 64 + c * 8;
+    b_vo[i] = (unsigned)(row * 64 + c * 8) * 2u;
   }
   // LDS byte address of the arena (a generic pointer to LDS keeps the LDS
   // offset in its low 32 bits) and the wave index, both as scalars
   const unsigned smem_lds = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)smem);
   const int wave_s = wave_id();
-  auto issue = [&](int kt, int st) __attribute__((always_inline)) {
-    const unsigned as = smem_lds + st * STAGE;
-#pragma unroll
-    for (int i = 0; i < A_LOADS; ++i) g2lds16_asm(a_lane + a_off[i] + kt * 64, as + (8 * (wave_s + 4 * i)) * ROWB);
-    const u16* bk = b_base + (long)kt * BN * 64;
-#pragma unroll
-    for (int i = 0; i < B_LOADS; ++i) g2lds16_asm(bk + b_off[i], as + A_BYTES + (8 * (wave_s + 4 * i)) * ROWB);
+  // load q (< L) of K stage kt into stage buffer b
+  auto load_one = [&](int kt, int b, int q) __attribute__((always_inline)) {
+    const unsigned dst = smem_lds + b * STAGE;
+    if (q < A_LOADS) {
+      g2lds16_sb(a_sb + kt * 128, a_vo[q], dst + (8 * (wave_s + NW * q)) * ROWB);
+    } else {
+      const int i = q - A_LOADS;
+      g2lds16_sb(b_sb + (long)kt * (BN * 128), b_vo[i], dst + A_BYTES + (8 * (wave_s + NW * i)) * ROWB);
+    }
   };
 
   f32x16 acc[FM][FN];
@@ -592,34 +579,107 @@ __device__ __forceinline__ void gemm_packed_tile(const KArgs& a, const mk_instr&
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
+  // Operand fragments of the four 16-deep sub-steps of a stage,
+  // double-buffered: the LDS reads of sub-step kk + 1 are in flight during
+  // kk's MFMAs, and those of the next stage's first sub-step during this
+  // stage's last one, so no sub-step waits out a whole LDS round trip.
+  u32x4 af[2][FM], bf[2][FN];
+  auto frags = [&](const char* __restrict__ st, int kk, int b) __attribute__((always_inline)) {
+    const int c = kk * 2 + (lane >> 5);
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int row = wm * WM + i * 32 + (lane & 31);
+      af[b][i] = *reinterpret_cast<const u32x4*>(st + row * ROWB + ((c ^ ((row >> 1) & 7)) << 4));
+    }
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int row = wn * WN + j * 32 + (lane & 31);
+      bf[b][j] = *reinterpret_cast<const u32x4*>(st + A_BYTES + row * ROWB + ((c ^ ((row >> 1) & 7)) << 4));
+    }
+  };
+  auto mma = [&](int kk, int q) __attribute__((always_inline)) {
+    const int i = q / FN, j = q % FN;
+    acc[i][j] = mfma32<DT>(af[kk & 1][i], bf[kk & 1][j], acc[i][j]);
+  };
+  // Wait until stage s has landed in this wave, leaving the `younger`
+  // stages issued after it in flight (each stage is L loads per thread),
+  // and until this wave's LDS reads are done.
+  // (younger <= ST - 1: at most 3 stages, 3 L <= 24 loads)
+  auto land = [&](int younger) __attribute__((always_inline)) {
+    if (younger >= 3) wait_vmcnt_lgkm0<(ST >= 4 ? 3 * L : 0)>();
+    else if (younger == 2) wait_vmcnt_lgkm0<(ST >= 3 ? 2 * L : 0)>();
+    else if (younger == 1) wait_vmcnt_lgkm0<L>();
+    else wait_vmcnt_lgkm0<0>();
+  };
+
+  // Stages 0 .. ST-1 fill every buffer first; stage kt + ST is issued once
+  // every wave has finished reading stage kt (its buffer), right after the
+  // barrier that also publishes stage kt + 1.  That barrier sits before
+  // stage kt's last sub-step, whose MFMAs then cover the first LDS reads of
+  // stage kt + 1 and the issue of stage kt + ST's loads, one or two loads
+  // after each MFMA.  So while stage kt is read, stages kt + 1 .. kt + ST - 1
+  // are in flight, and waiting for stage kt + 1 leaves ST - 2 younger ones.
+  constexpr int NQ = FM * FN;   // MFMAs per sub-step
   const int nk = (k1 - k0) / 64;
 #pragma unroll
-  for (int s = 0; s < ST - 1; ++s)
-    if (s < nk) issue(s, s);
-  for (int kt = 0; kt < nk; ++kt) {
-    // stage kt has landed once at most min(ST - 2, nk - 1 - kt) younger
-    // stages of this wave are still in flight; then every wave's part is
-    // visible after the barrier, and the buffer of stage kt - 1 is free
-    const int younger = min(ST - 2, nk - 1 - kt);
-    if (younger >= 2 && ST >= 4) wait_vmcnt<2 * L>();
-    else if (younger >= 1) wait_vmcnt<L>();
-    else wait_vmcnt<0>();
+  for (int s = 0; s < ST; ++s)
+    if (s < nk)
+#pragma unroll
+      for (int q = 0; q < L; ++q) load_one(s, s, q);
+  if (nk > 0) {
+    land(min(ST - 1, nk - 1));
     bare_barrier();
-    const int kn = kt + ST - 1;
-    PackedGemmStep<BM, BN, DT>::run(smem + (kt % ST) * STAGE, smem_lds + (kn % ST) * STAGE, kn < nk, a_lane, a_off,
-                                    kn * 64, b_base + (long)kn * BN * 64, b_off, wave_s, lane, wm, wn, acc);
+    frags(smem, 0, 0);
+  }
+  // Stage kt in buffer U = kt % ST (a compile-time index in each copy).  One
+  // straight path for every stage (the last one waits for nothing and reads
+  // a stale buffer it does not use): only the issue of the next stage's loads
+  // is conditional, so the accumulators are never merged from two paths.
+  auto stage = [&](auto U, int kt) __attribute__((always_inline)) {
+    constexpr int u = decltype(U)::value;
+    const char* __restrict__ cur = smem + u * STAGE;
+#pragma unroll
+    for (int kk = 0; kk < 3; ++kk) {
+      frags(cur, kk + 1, (kk + 1) & 1);
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) mma(kk, q);
+    }
+    land(min(ST - 2, nk - 2 - kt));
+    bare_barrier();
+    frags(smem + ((u + 1) % ST) * STAGE, 0, 0);
+    const bool more = kt + ST < nk;
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      mma(3, q);
+      if (more) {
+#pragma unroll
+        for (int l = q * L / NQ; l < (q + 1) * L / NQ; ++l) load_one(kt + ST, u, l);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  for (int kt0 = 0; kt0 < nk; kt0 += ST) {
+    stage(std::integral_constant<int, 0>{}, kt0);
+    if (kt0 + 1 < nk) stage(std::integral_constant<int, 1>{}, kt0 + 1);
+    if constexpr (ST > 2) {
+      if (kt0 + 2 < nk) stage(std::integral_constant<int, 2>{}, kt0 + 2);
+    }
+    if constexpr (ST > 3) {
+      if (kt0 + 3 < nk) stage(std::integral_constant<int, (ST > 3 ? 3 : 0)>{}, kt0 + 3);
+    }
   }
 
   // ---- epilogue, one 32-row strip of each wave row at a time: the
-  // accumulators go to an fp32 LDS strip Cs[64][BN + 4] (LDS row sr holds
-  // tile row (sr / 32) * WM + i * 32 + sr % 32), then 8-column units run
-  // the epilogue.  acc[i][j][e] is tile row wm*WM + i*32 + 8*(e>>2) +
+  // accumulators go to an fp32 LDS strip Cs[32 WGM][BN + 4] (LDS row sr
+  // holds tile row (sr / 32) * WM + i * 32 + sr % 32), then 8-column units
+  // run the epilogue.  acc[i][j][e] is tile row wm*WM + i*32 + 8*(e>>2) +
   // 4*(lane>>5) + (e&3), weight column wn*WN + j*32 + (lane&31).
   constexpr int CS = BN + 4;
+  static_assert(32 * WGM * CS * 4 <= kSmemBytes, "epilogue strip fits the arena");
   float* Cs = reinterpret_cast<float*>(smem);
   const int r1 = in.r1, c1 = in.c1;
   const bool silu_mul = flags & MK_EP_SILU_MUL;
-  constexpr int UNITS = 64 * BN / 8;   // 8-column units of a strip (weight columns)
+  constexpr int UNITS = 32 * WGM * BN / 8;   // 8-column units of a strip (weight columns)
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
     __syncthreads();   // the previous strip (or the last K stage) is consumed
@@ -630,7 +690,7 @@ __device__ __forceinline__ void gemm_packed_tile(const KArgs& a, const mk_instr&
         Cs[(wm * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3)) * CS + wn * WN + jj * 32 + (lane & 31)] =
             acc[i][jj][e];
     __syncthreads();
-    for (int u = t; u < UNITS; u += kThreads) {
+    for (int u = t; u < UNITS; u += NT) {
       const int sr = u / (BN / 8), w = (u % (BN / 8)) * 8;   // strip row, weight column
       const int gr = r0 + (sr >> 5) * WM + i * 32 + (sr & 31);
       if (gr >= r1) continue;
@@ -1517,9 +1577,9 @@ typedef __attribute__((address_space(3))) const mk_instr InstrL;
 typedef __attribute__((address_space(3))) const mk_node NodeL;
 typedef __attribute__((address_space(3))) char CharL;
 
-template <int BM, int BN, int DT>
+template <int BM, int BN, int DT, int NW = 4>
 __device__ __attribute__((noinline)) void gemm_packed_call(ArgsK* a, InstrL* in, NodeL* nd, CharL* smem) {
-  gemm_packed_tile<BM, BN, DT>(*(const KArgs*)a, *(const mk_instr*)in, *(const mk_node*)nd, (char*)smem);
+  gemm_packed_tile<BM, BN, DT, NW>(*(const KArgs*)a, *(const mk_instr*)in, *(const mk_node*)nd, (char*)smem);
 }
 template <int BM, int BN, int DT>
 __device__ __attribute__((noinline)) void gemm_call(ArgsK* a, InstrL* in, NodeL* nd, CharL* smem) {
@@ -1534,13 +1594,24 @@ __host__ __device__ constexpr unsigned op_family(int opcode) {
   return opcode == MK_I_NOOP ? 0u : opcode == MK_I_GEMM ? kOpGemm : opcode == MK_I_GEMV ? kOpGemv : kOpOther;
 }
 
-template <unsigned OPS, int DT>
+// NT threads per workgroup: 256 (four waves) for every instance, or 512
+// (eight waves, two per SIMD) for the instance that runs plans made only of
+// packed GEMM tiles, whose body is then the eight-wave one.
+template <unsigned OPS, int DT, int NT>
 __device__ __forceinline__ void run_body(const KArgs& a, const mk_instr& in, const mk_node& nd, char* smem) {
   if (!(op_family(in.opcode) & OPS)) return;
   switch (in.opcode) {
     case MK_I_GEMM:
       if constexpr (!(OPS & kOpGemm)) break;
-      else {
+      else if constexpr (NT == 512) {
+        ArgsK* ak = (ArgsK*)&a;
+        InstrL* il = (InstrL*)&in;
+        NodeL* nl = (NodeL*)&nd;
+        CharL* sl = (CharL*)smem;
+        if (nd.tile_m == 256 && nd.tile_n == 128) gemm_packed_call<256, 128, DT, 8>(ak, il, nl, sl);
+        else if (nd.tile_m == 128 && nd.tile_n == 256) gemm_packed_call<128, 256, DT, 8>(ak, il, nl, sl);
+        else gemm_packed_call<128, 128, DT, 8>(ak, il, nl, sl);
+      } else {
         ArgsK* ak = (ArgsK*)&a;
         InstrL* il = (InstrL*)&in;
         NodeL* nl = (NodeL*)&nd;
@@ -1577,10 +1648,10 @@ __device__ __forceinline__ void run_body(const KArgs& a, const mk_instr& in, con
   }
 }
 
-template <unsigned OPS>
+template <unsigned OPS, int NT>
 __device__ __forceinline__ void run_instr(const KArgs& a, const mk_instr& in, const mk_node& nd, char* smem) {
-  if (nd.dtype == MK_BF16) run_body<OPS, MK_BF16>(a, in, nd, smem);
-  else run_body<OPS, MK_F16>(a, in, nd, smem);
+  if (nd.dtype == MK_BF16) run_body<OPS, MK_BF16, NT>(a, in, nd, smem);
+  else run_body<OPS, MK_F16, NT>(a, in, nd, smem);
 }
 
 // ----------------------------------------------------- counters and waits
@@ -1798,7 +1869,7 @@ __device__ __forceinline__ void store_ahead(const Loop& L, int it, int w, int tk
 }
 
 // One generic iteration.  Returns false if the run was aborted.
-template <unsigned OPS>
+template <unsigned OPS, int NT>
 __device__ __forceinline__ bool generic_iter(const Loop& L, int it, int& w) {
   const KArgs& a = L.a;
   const int gidx = rec_index(L, it);
@@ -1810,7 +1881,7 @@ __device__ __forceinline__ bool generic_iter(const Loop& L, int it, int& w) {
   if (in.opcode != MK_I_NOOP) {
     const mk_node& nd = L.nodes[in.node];
     if (tr) stamp(a, gidx, 1, wall_clock64());
-    run_instr<OPS>(a, in, nd, L.smem);
+    run_instr<OPS, NT>(a, in, nd, L.smem);
     if (tr) stamp(a, gidx, 2, wall_clock64());
     release_dests(a, in);
     if (tr) stamp(a, gidx, 3, wall_clock64());
@@ -1880,8 +1951,8 @@ __device__ __forceinline__ int gemv_streak(const Loop& L, int& it, int& w) {
 
 }  // namespace mkd
 
-template <unsigned OPS>
-__global__ void __launch_bounds__(256, 1) mk_persistent(mkd::KArgs args) {
+template <unsigned OPS, int NT = 256>
+__global__ void __launch_bounds__(NT, 1) mk_persistent(mkd::KArgs args) {
   // Read the arguments in place (kernarg segment, constant memory): the
   // buffer table is indexed with runtime slots, which would otherwise force
   // a private copy of the whole struct.
@@ -1899,7 +1970,7 @@ __global__ void __launch_bounds__(256, 1) mk_persistent(mkd::KArgs args) {
   // Keeping 32 consecutive instructions on one XCD instead (for L2 sharing)
   // measured 0-3 % slower on every workload.
   const int vcu = b;
-  for (int i = t; i < a.n_nodes * 64; i += mkd::kThreads)
+  for (int i = t; i < a.n_nodes * 64; i += NT)
     reinterpret_cast<int*>(s_nodes)[i] = reinterpret_cast<const int*>(a.nodes)[i];
   if (a.queue) {
     // clear the other ticket word for the next run; take iterations 0 and 1
@@ -1939,7 +2010,7 @@ __global__ void __launch_bounds__(256, 1) mk_persistent(mkd::KArgs args) {
         continue;
       }
     }
-    if (!mkd::generic_iter<OPS>(L, it, w)) return;
+    if (!mkd::generic_iter<OPS, NT>(L, it, w)) return;
     ++it;
   }
   if (clk && t == 0) {
@@ -1950,8 +2021,8 @@ __global__ void __launch_bounds__(256, 1) mk_persistent(mkd::KArgs args) {
 
 // Per-op baseline: one launch per node, one workgroup per instruction, no
 // counters (stream order carries the dependencies).
-template <unsigned OPS>
-__global__ void __launch_bounds__(256, 1) mk_node_kernel(mkd::KArgs args) {
+template <unsigned OPS, int NT = 256>
+__global__ void __launch_bounds__(NT, 1) mk_node_kernel(mkd::KArgs args) {
   const mkd::KArgs& a = *(const mkd::KArgs*)__builtin_amdgcn_kernarg_segment_ptr();
   (void)args;
   __shared__ mk_instr s_in;
@@ -1963,5 +2034,5 @@ __global__ void __launch_bounds__(256, 1) mk_node_kernel(mkd::KArgs args) {
   if (s_in.opcode == MK_I_NOOP) return;
   mkd::copy_words(reinterpret_cast<int*>(&s_nd), reinterpret_cast<const int*>(a.nodes + s_in.node));
   __syncthreads();
-  mkd::run_instr<OPS>(a, s_in, s_nd, smem);
+  mkd::run_instr<OPS, NT>(a, s_in, s_nd, smem);
 }

@@ -109,18 +109,37 @@ __global__ void mk_pack_gemm_kernel(const unsigned short* __restrict__ src, unsi
 
 namespace {
 
-// Smallest compiled kernel instance whose op families cover `ops`.
-const void* persistent_for(unsigned ops) {
-  if ((ops & ~mkd::kOpGemv) == 0) return reinterpret_cast<const void*>(mk_persistent<mkd::kOpGemv>);
-  if ((ops & ~mkd::kOpGemm) == 0) return reinterpret_cast<const void*>(mk_persistent<mkd::kOpGemm>);
-  if ((ops & mkd::kOpGemv) == 0) return reinterpret_cast<const void*>(mk_persistent<mkd::kOpGemm | mkd::kOpOther>);
-  return reinterpret_cast<const void*>(mk_persistent<mkd::kOpAll>);
+// The kernel instance a plan (or node) runs on and its workgroup size: the
+// eight-wave instance when every instruction is a packed GEMM tile,
+// otherwise the smallest four-wave instance whose op families cover `ops`.
+struct Launch {
+  const void* fn;
+  int threads;
+};
+bool packed_gemm_only(const mk_plan* p) {
+  bool any = false;
+  for (const mk::Node& n : p->nodes) {
+    if (n.ins.empty()) continue;
+    if (n.opcode != MK_I_GEMM || n.desc.layout != 2) return false;
+    any = true;
+  }
+  return any;
 }
-const void* node_kernel_for(unsigned ops) {
-  if ((ops & ~mkd::kOpGemv) == 0) return reinterpret_cast<const void*>(mk_node_kernel<mkd::kOpGemv>);
-  if ((ops & ~mkd::kOpGemm) == 0) return reinterpret_cast<const void*>(mk_node_kernel<mkd::kOpGemm>);
-  if ((ops & mkd::kOpGemv) == 0) return reinterpret_cast<const void*>(mk_node_kernel<mkd::kOpGemm | mkd::kOpOther>);
-  return reinterpret_cast<const void*>(mk_node_kernel<mkd::kOpAll>);
+Launch persistent_for(unsigned ops, bool wide) {
+  if (wide && ops == mkd::kOpGemm) return {reinterpret_cast<const void*>(mk_persistent<mkd::kOpGemm, 512>), 512};
+  if ((ops & ~mkd::kOpGemv) == 0) return {reinterpret_cast<const void*>(mk_persistent<mkd::kOpGemv>), 256};
+  if ((ops & ~mkd::kOpGemm) == 0) return {reinterpret_cast<const void*>(mk_persistent<mkd::kOpGemm>), 256};
+  if ((ops & mkd::kOpGemv) == 0)
+    return {reinterpret_cast<const void*>(mk_persistent<mkd::kOpGemm | mkd::kOpOther>), 256};
+  return {reinterpret_cast<const void*>(mk_persistent<mkd::kOpAll>), 256};
+}
+Launch node_kernel_for(unsigned ops, bool wide) {
+  if (wide && ops == mkd::kOpGemm) return {reinterpret_cast<const void*>(mk_node_kernel<mkd::kOpGemm, 512>), 512};
+  if ((ops & ~mkd::kOpGemv) == 0) return {reinterpret_cast<const void*>(mk_node_kernel<mkd::kOpGemv>), 256};
+  if ((ops & ~mkd::kOpGemm) == 0) return {reinterpret_cast<const void*>(mk_node_kernel<mkd::kOpGemm>), 256};
+  if ((ops & mkd::kOpGemv) == 0)
+    return {reinterpret_cast<const void*>(mk_node_kernel<mkd::kOpGemm | mkd::kOpOther>), 256};
+  return {reinterpret_cast<const void*>(mk_node_kernel<mkd::kOpAll>), 256};
 }
 
 using mk::set_error;
@@ -179,10 +198,11 @@ mk_status ensure_device(mk_plan* p) {
     set_error("device does not support cooperative launch");
     return MK_E_UNSUPPORTED;
   }
-  for (const void* k : {persistent_for(mkd::kOpAll), persistent_for(mkd::kOpGemv), persistent_for(mkd::kOpGemm),
-                        persistent_for(mkd::kOpGemm | mkd::kOpOther)}) {
+  for (const Launch& k : {persistent_for(mkd::kOpAll, false), persistent_for(mkd::kOpGemv, false),
+                          persistent_for(mkd::kOpGemm, false), persistent_for(mkd::kOpGemm | mkd::kOpOther, false),
+                          persistent_for(mkd::kOpGemm, true)}) {
     int blocks = 0;
-    HIPCHK(hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, k, mkd::kThreads, 0));
+    HIPCHK(hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, k.fn, k.threads, 0));
     if (blocks < 1) {
       set_error("persistent kernel does not fit one workgroup per CU");
       return MK_E_UNSUPPORTED;
@@ -388,12 +408,12 @@ mk_status megakernel_run_traced(mk_plan* p, void* const* buffers, int n_buffers,
     HIPCHK(hipGetLastError());
   }
   a.epoch = (int)(p->epoch + 1);
-  const void* kernel = persistent_for(p->dev->ops);
+  const Launch k = persistent_for(p->dev->ops, packed_gemm_only(p));
   void* args[] = {&a};
   if (p->opts.cooperative) {
-    HIPCHK(hipLaunchCooperativeKernel(kernel, dim3(p->opts.num_cus), dim3(mkd::kThreads), args, 0, s));
+    HIPCHK(hipLaunchCooperativeKernel(k.fn, dim3(p->opts.num_cus), dim3(k.threads), args, 0, s));
   } else {
-    HIPCHK(hipLaunchKernel(kernel, dim3(p->opts.num_cus), dim3(mkd::kThreads), args, 0, s));
+    HIPCHK(hipLaunchKernel(k.fn, dim3(p->opts.num_cus), dim3(k.threads), args, 0, s));
   }
   p->epoch += 1;
   return MK_OK;
@@ -417,7 +437,9 @@ mk_status megakernel_run_per_op(mk_plan* p, void* const* buffers, int n_buffers,
     unsigned ops = 0;
     for (int i = 0; i < a.count; ++i) ops |= mkd::op_family(p->records[n.start + i].opcode);
     void* args[] = {&a};
-    HIPCHK(hipLaunchKernel(node_kernel_for(ops), dim3(a.count), dim3(mkd::kThreads), args, 0, s));
+    const bool wide = n.opcode == MK_I_GEMM && n.desc.layout == 2;
+    const Launch k = node_kernel_for(ops, wide);
+    HIPCHK(hipLaunchKernel(k.fn, dim3(a.count), dim3(k.threads), args, 0, s));
   }
   return MK_OK;
 }
@@ -519,12 +541,12 @@ mk_status megakernel_run_noalloc(mk_plan* p, void* const* buffers, int n_buffers
   }
   p->noalloc_device = dev;
   if (p->n_instr == 0) return MK_OK;
-  const void* kernel = persistent_for(ops_of(p));
+  const Launch k = persistent_for(ops_of(p), packed_gemm_only(p));
   void* args[] = {&a};
   if (p->opts.cooperative) {
-    HIPCHK(hipLaunchCooperativeKernel(kernel, dim3(p->opts.num_cus), dim3(mkd::kThreads), args, 0, s));
+    HIPCHK(hipLaunchCooperativeKernel(k.fn, dim3(p->opts.num_cus), dim3(k.threads), args, 0, s));
   } else {
-    HIPCHK(hipLaunchKernel(kernel, dim3(p->opts.num_cus), dim3(mkd::kThreads), args, 0, s));
+    HIPCHK(hipLaunchKernel(k.fn, dim3(p->opts.num_cus), dim3(k.threads), args, 0, s));
   }
   return MK_OK;
 }
