@@ -36,8 +36,10 @@ DESCR = {
                    "MLP up N=28672, MLP down K=28672, fp16",
     "layer": "Llama-style decoder layer prefill, seq 2048, hidden 4096, 32/8 heads of 128, causal "
              "attention, RMSNorm, rotary, SiLU*mul MLP inter 14336, bf16",
+    "decode_kv": "decoder layer at batch 1 with split-KV attention over a 4096-row KV cache (new token "
+                 "at position 4095, rotary and append), hidden 4096, 32/8 heads of 128, inter 14336, bf16",
 }
-BOUND = dict(mlp3="mfma", decode="hbm", prefill="mfma", decode_gemm="hbm", layer="mfma")
+BOUND = dict(mlp3="mfma", decode="hbm", prefill="mfma", decode_gemm="hbm", layer="mfma", decode_kv="hbm")
 KERNEL = "mk_persistent"
 CSRC = os.path.join(ROOT, "tiled_gemm_graph_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
@@ -192,13 +194,14 @@ def bench_graph(workload, steps, warmup, cpu_budget, do_check=True, sync="tiles"
     res["per_op_us"] = ms_op * 1e3
     res["speedup_vs_per_op"] = ms_op / ms
     if queue_ab and sync == "tiles":
-        qp = r.alt_plan(queue=1)
-        r.forward(plan=qp)
-        qp.check()
-        ms_q = time_forwards(lambda: r.forward(plan=qp), steps, warmup)
-        qp.check()
-        res["queue_us"] = ms_q * 1e3
-        del qp
+        for q, key in ((1, "queue_us"), (2, "xcd_queue_us")):
+            qp = r.alt_plan(queue=q)
+            r.forward(plan=qp)
+            qp.check()
+            ms_q = time_forwards(lambda: r.forward(plan=qp), steps, warmup)
+            qp.check()
+            res[key] = ms_q * 1e3
+            del qp
     if clock:
         _, mhz = TR.capture(r, with_clock=True)
         res["core_clock_mhz"] = mhz
@@ -207,7 +210,7 @@ def bench_graph(workload, steps, warmup, cpu_budget, do_check=True, sync="tiles"
     # the counter summaries are taken on the per-tile-counter plans
     res["roofline"] = roofline(workload, st, res["us"], measured_traffic(workload) if sync == "tiles" else None)
     log(f"[bench] {workload}: {res['us']:.1f} us/forward, per-op {res['per_op_us']:.1f}"
-        + (f", queue {res['queue_us']:.1f}" if "queue_us" in res else ""))
+        + (f", queue {res['queue_us']:.1f}, per-XCD queues {res['xcd_queue_us']:.1f}" if "queue_us" in res else ""))
     if cpu_budget > 0:
         log(f"[bench] {workload}: timing the CPU oracle (~{cpu_budget:.0f} s)")
         res["cpu_baseline"] = cpu_baseline(workload, dims, inp, cpu_budget)
@@ -239,7 +242,7 @@ def line_for(head, steps, warmup, graphs=None):
         "roofline": head["roofline"],
         "cpu_baseline": head["cpu_baseline"],
     }
-    for k in ("per_op_us", "speedup_vs_per_op", "queue_us", "rel_err", "max_abs_err", "max_abs_at",
+    for k in ("per_op_us", "speedup_vs_per_op", "queue_us", "xcd_queue_us", "rel_err", "max_abs_err", "max_abs_at",
               "gbps", "tflops", "alg_bytes", "alg_flops", "core_clock_mhz"):
         if k in head:
             line[k] = head[k]
@@ -270,7 +273,7 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=None,
-                    choices=["mlp3", "decode", "prefill", "decode_gemm", "layer"],
+                    choices=["mlp3", "decode", "prefill", "decode_gemm", "layer", "decode_kv"],
                     help="one graph only (default: all five in one line, headlined by prefill)")
     ap.add_argument("--all", action="store_true", help="one JSON line per workload")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -304,7 +307,7 @@ def main():
         res = bench_graph(args.workload, args.steps, args.warmup, args.cpu_seconds, clock=True, **kw)
         print(json.dumps(line_for(res, args.steps, args.warmup)), flush=True)
         return
-    order = ["prefill", "decode", "mlp3", "decode_gemm", "layer"]
+    order = ["prefill", "decode", "mlp3", "decode_gemm", "layer", "decode_kv"]
     results = {}
     for wl in order:
         head = wl == "prefill"

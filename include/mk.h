@@ -62,7 +62,9 @@ typedef enum {
   MK_E_DEADLOCK = 5     /* a counter wait exceeded the spin limit        */
 } mk_status;
 
-typedef enum { MK_F16 = 1, MK_BF16 = 2, MK_F32 = 3 } mk_dtype;
+typedef enum { MK_F16 = 1, MK_BF16 = 2, MK_F32 = 3,
+               MK_I32 = 4   /* runtime scalars only (the decode position) */
+} mk_dtype;
 
 typedef enum {
   MK_INPUT = 0,        /* caller-owned activation input                  */
@@ -76,7 +78,27 @@ typedef enum {
   MK_OP_RMSNORM = 2,   /* in: x, gamma                                   */
   MK_OP_ATTENTION = 3, /* in: q, k, v (column ranges of a QKV tensor)    */
   MK_OP_ADD = 4,       /* in: a, b  (same shape, no broadcasting)        */
-  MK_OP_RELU = 5       /* in: a                                          */
+  MK_OP_RELU = 5,      /* in: a                                          */
+  MK_OP_DECODE_ATTENTION = 6
+                       /* in: q [1, Hq*d], k_new [1, Hkv*d], v_new [1,
+                          Hkv*d] (column ranges of the QKV output),
+                          k_cache [S_max, Hkv*d], v_cache [S_max, Hkv*d]
+                          (caller-owned INPUT tensors), pos (INPUT, MK_I32,
+                          one element: the position p of the new token,
+                          read at run time, 0 <= p < S_max); out o [1,
+                          Hq*d].  With rotary embedding at position p
+                          (rotate-half pairs, base rope_theta) applied to q
+                          and k_new: o[h] = sum over keys j <= p of
+                          softmax_j(q'_h . K_j / sqrt(d)) V_j for kv head
+                          h / (Hq / Hkv), where K_j, V_j are cache row j for
+                          j < p and the rotated k_new (rounded to the cache
+                          dtype) and v_new for j = p.  The op also writes
+                          those two values into row p of k_cache and
+                          v_cache (the append), which no other op of the
+                          graph may read.  Split over the cache in chunks of
+                          tile.bq keys ("Implementing a Mega Kernel for
+                          B300", section 2: flash-decoding partials and a
+                          log-sum-exp combine)                             */
 } mk_op_kind;
 
 /* GEMM epilogue flags ("Implementing a Mega Kernel for B300", section 2:
@@ -99,7 +121,8 @@ enum {
 /* Instruction opcodes (the record's first word). */
 enum {
   MK_I_NOOP = 0, MK_I_GEMM = 1, MK_I_GEMV = 2, MK_I_REDUCE = 3,
-  MK_I_RMSNORM = 4, MK_I_ATTENTION = 5, MK_I_EW_ADD = 6, MK_I_EW_RELU = 7
+  MK_I_RMSNORM = 4, MK_I_ATTENTION = 5, MK_I_EW_ADD = 6, MK_I_EW_RELU = 7,
+  MK_I_ATTN_PARTIAL = 8, MK_I_ATTN_COMBINE = 9
 };
 
 /* Tile parameters of one op; 0 in any field = the compiler's choice.
@@ -114,6 +137,8 @@ enum {
  * tile's weight columns, bn or 2 * bn under SILU_MUL; a K split is
  * allowed).
  * RMSNORM: rows per instruction.  ATTENTION: bq query rows per instruction.
+ * DECODE_ATTENTION: bq cache keys per partial instruction (a multiple of
+ * 64; 0: about Hkv * ceil(S_max / bq) = num_cus instructions).
  * ADD / RELU: er x ec tiles. */
 typedef struct {
   int32_t bm, bn, split, dup, gemv;
@@ -180,8 +205,14 @@ typedef struct {
                            dependency points to a lower index, so the
                            lowest unfinished index is always running and
                            any number of resident workgroups completes the
-                           run.  The records and counters are the same in
-                           both modes.                                      */
+                           run.  2: one such queue per XCD: workgroup w
+                           takes, in list order, the instructions i with
+                           i mod 8 = w mod 8 (those static placement puts
+                           on its XCD), so tiles keep their L2 neighbours;
+                           the run completes while every residue class mod
+                           8 has a resident workgroup (num_cus a multiple
+                           of 8).  The records and counters are the same in
+                           every mode.                                      */
   int32_t debug_poison; /* 1: before every run fill each plan-owned
                            intermediate (and split-K partial buffer) with
                            all-ones bytes, a NaN in fp16, bf16 and fp32, so
@@ -403,7 +434,8 @@ mk_status mk_plan_stats_get(const mk_plan *p, mk_plan_stats *out);
  * i mod num_cus.  *words points into the plan and stays valid until
  * mk_plan_destroy.  coord: GEMM/GEMV (tm, tn, s, dup copy); REDUCE
  * (tm, tn, 0, 0); RMSNORM (row block, 0, 0, 0); ATTENTION (q block, head,
- * 0, 0); EW_* (tile row, tile col, 0, 0).  MK_E_INVALID on a null
+ * 0, 0); EW_* (tile row, tile col, 0, 0); ATTN_PARTIAL (key chunk, kv
+ * head, 0, 0); ATTN_COMBINE (kv head, 0, 0, 0).  MK_E_INVALID on a null
  * argument. */
 mk_status mk_plan_instructions(const mk_plan *p, const int32_t **words,
                                int64_t *n_instr, int32_t *words_per_instr);

@@ -145,6 +145,44 @@ def layer(inp: Dict[str, torch.Tensor], dims: Dict[str, int],
     return out
 
 
+def decode_kv(inp: Dict[str, torch.Tensor], dims: Dict[str, int],
+              mirror: bool = False, dt=F32, return_cache: bool = False):
+    """The batch-1 decoder layer with its attention over a KV cache.
+
+    qkv = rms(x, g1) @ Wqkv; q, k, v = the [Q | K | V] column blocks;
+    o = decode_attention(q, k, v, caches, pos) (rotary at position pos, the
+    new k and v appended as cache row pos, stored in the caches' bf16);
+    h = o @ Wo + x; gu = rms(h, g2) @ Wgu; a = silu(gu[:, :I]) * gu[:, I:];
+    out = a @ Wd + h.  "Implementing a Mega Kernel for B300", section 1 (the
+    decoder layer's ops: RMS + QKV, RoPE + append, attention, O + residual,
+    RMS + gate_up with SiLU-mul, down + residual).
+    """
+    bf = torch.bfloat16
+    nq, nkv, hd, I = dims["n_q"], dims["n_kv"], dims["head_dim"], dims["inter"]
+    Hq, Hkv = nq // hd, nkv // hd
+    pos = int(inp["pos"].reshape(-1)[0])
+    x = _np(inp["x"], dt)
+    qkv = _store(ops.gemm(ops.rmsnorm(x, _np(inp["g1"], dt), dt=dt),
+                          _np(inp["Wqkv"], dt), dt), bf, mirror)
+    q = qkv[0, :nq].reshape(Hq, hd)
+    k = qkv[0, nq:nq + nkv].reshape(Hkv, hd)
+    v = qkv[0, nq + nkv:].reshape(Hkv, hd)
+    kc = _np(inp["k_cache"], dt).reshape(-1, Hkv, hd)
+    vc = _np(inp["v_cache"], dt).reshape(-1, Hkv, hd)
+    def bf16(z):
+        return torch.from_numpy(np.ascontiguousarray(z, dtype=np.float32)).to(bf).to(
+            torch.float32).numpy().astype(dt, copy=False)
+    o, krow, vrow = ops.decode_attention(q, k, v, kc, vc, pos, dt=dt, round_kv=bf16)
+    o = _store(o.reshape(1, nq), bf, mirror)
+    h = _store(ops.gemm(o, _np(inp["Wo"], dt), dt) + x, bf, mirror)
+    gu = ops.gemm(ops.rmsnorm(h, _np(inp["g2"], dt), dt=dt), _np(inp["Wgu"], dt), dt)
+    a = _store(ops.silu_mul(gu, I), bf, mirror)
+    out = ops.gemm(a, _np(inp["Wd"], dt), dt) + h
+    if return_cache:
+        return out, dict(k_row=krow.reshape(-1), v_row=vrow.reshape(-1), o=o, qkv=qkv)
+    return out
+
+
 def run(workload: str, inp: Dict[str, torch.Tensor], dims: Dict[str, int],
         rows: Optional[Sequence[int]] = None, mirror: bool = False,
         dt=F32) -> np.ndarray:
@@ -160,6 +198,8 @@ def run(workload: str, inp: Dict[str, torch.Tensor], dims: Dict[str, int],
     if workload == "layer":
         out = layer(inp, dims, mirror, dt)
         return out if rows is None else out[list(rows)]
+    if workload == "decode_kv":
+        return decode_kv(inp, dims, mirror, dt)
     raise KeyError(workload)
 
 

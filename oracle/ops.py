@@ -120,3 +120,38 @@ def causal_gqa_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray,
         p = p / np.sum(p, axis=1, keepdims=True)
         out[:, h, :] = p @ v[:, kh, :].astype(dt)
     return out
+
+
+def decode_attention(q: np.ndarray, k_new: np.ndarray, v_new: np.ndarray,
+                     k_cache: np.ndarray, v_cache: np.ndarray, pos: int,
+                     theta: float = 10000.0, dt=F32, round_kv=None):
+    """Attention of one new token over a KV cache, q [Hq, d], k_new and
+    v_new [Hkv, d], caches [S_max, Hkv, d], position p = pos.
+
+    The new token's query and key are rotated at position p (``rope``);
+    its key and value join the cache as row p (``round_kv``, if given, is
+    applied to the rotated key and the value first: the storage rounding of
+    the append); then o[h] = sum over j <= p of softmax_j(q'_h . K_j /
+    sqrt(d)) V_j with kv head h // (Hq / Hkv) -- the plain softmax over the
+    p + 1 keys, no splitting.  "Implementing a Mega Kernel for B300",
+    section 2 (decode attention over the cache after the rotary step that
+    appends the current k, v).  Returns (o [Hq, d], k row p, v row p).
+    """
+    Hq, d = q.shape
+    Hkv = k_new.shape[0]
+    qr = rope(q[None].astype(dt), pos0=pos, theta=theta, dt=dt)[0]
+    kr = rope(k_new[None].astype(dt), pos0=pos, theta=theta, dt=dt)[0]
+    vr = v_new.astype(dt)
+    if round_kv is not None:
+        kr, vr = round_kv(kr), round_kv(vr)
+    K = np.concatenate([k_cache[:pos].astype(dt), kr[None]], axis=0)   # [p + 1, Hkv, d]
+    V = np.concatenate([v_cache[:pos].astype(dt), vr[None]], axis=0)
+    scale = dt(1.0 / np.sqrt(d))
+    o = np.empty((Hq, d), dtype=dt)
+    group = Hq // Hkv
+    for h in range(Hq):
+        g = h // group
+        sc = (K[:, g, :] @ qr[h]) * scale
+        e = np.exp(sc - np.max(sc))
+        o[h] = (e / np.sum(e)) @ V[:, g, :]
+    return o, kr, vr

@@ -330,9 +330,11 @@ def test_small_m_gemm_on_a_produced_b_is_not_a_gemv():
 
 def test_new_build_options_are_validated():
     g = _produced_b_graph()
-    for opt in ("queue", "debug_poison"):
+    for opt, bad in (("queue", 3), ("debug_poison", 2)):
         with pytest.raises(L.MkError):
-            g.build(**{opt: 2})
+            g.build(**{opt: bad})
+    with pytest.raises(L.MkError):
+        g.build(queue=2, num_cus=100)   # per-XCD queues need a multiple of 8
     # the work queue changes no record: same list, same counters
     a, b = g.build(), g.build(queue=1, debug_poison=1)
     assert np.array_equal(a.instructions(), b.instructions())

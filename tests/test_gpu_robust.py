@@ -31,7 +31,7 @@ def _counters_ok(plan, epochs):
     assert np.array_equal(c, epochs * t), "counters != epoch * target"
 
 
-@pytest.mark.parametrize("poison,queue", [(0, 0), (1, 0), (1, 1)])
+@pytest.mark.parametrize("poison,queue", [(0, 0), (1, 0), (1, 1), (1, 2)])
 @pytest.mark.parametrize("wl", workloads.WORKLOADS)
 def test_alternating_inputs_each_run_checked(wl, poison, queue):
     d = workloads.small_dims(wl)
@@ -57,16 +57,17 @@ def test_alternating_inputs_each_run_checked(wl, poison, queue):
     _counters_ok(r.plan, 3)
 
 
+@pytest.mark.parametrize("queue", [1, 2])
 @pytest.mark.parametrize("wl", workloads.WORKLOADS)
-def test_work_queue_same_bytes_as_static(wl):
+def test_work_queue_same_bytes_as_static(wl, queue):
     d = workloads.small_dims(wl)
     inp = workloads.generate(wl, d)
-    say(f"[gpu] queue vs static {wl} dims={d}")
+    say(f"[gpu] queue={queue} vs static {wl} dims={d}")
     r = G.Runner(wl, d, inp)
     r.forward()
     r.plan.check()
     ref = r.out.clone()
-    qp = r.alt_plan(queue=1)
+    qp = r.alt_plan(queue=queue)
     for _ in range(3):
         r.out.zero_()
         r.forward(plan=qp)
@@ -76,17 +77,17 @@ def test_work_queue_same_bytes_as_static(wl):
     _counters_ok(qp, 3)
 
 
-@pytest.mark.parametrize("wl", ["decode", "layer"])
-def test_work_queue_full_size(wl):
+@pytest.mark.parametrize("wl,queue", [("decode", 1), ("layer", 1), ("prefill", 2), ("layer", 2)])
+def test_work_queue_full_size(wl, queue):
     d = workloads.default_dims(wl)
     inp = workloads.generate(wl, d)
-    say(f"[gpu] queue full size {wl}")
-    r = G.Runner(wl, d, inp, queue=1)
+    say(f"[gpu] queue={queue} full size {wl}")
+    r = G.Runner(wl, d, inp, queue=queue)
     for _ in range(2):
         r.forward()
         r.plan.check()
     torch.cuda.synchronize()
-    assert_parity(to_np(r.out), OG.run(wl, inp, d), G.DTYPE[wl], f"{wl} full, queue")
+    assert_parity(to_np(r.out), OG.run(wl, inp, d), G.DTYPE[wl], f"{wl} full, queue={queue}")
     _counters_ok(r.plan, 2)
 
 

@@ -17,6 +17,8 @@ weights are built so that a plausible miswiring gives a different answer:
 * prefill: ReLU only on the second product.  ("Hand-writing a Blackwell
   GEMM", "Two workloads, not one".)
 * decode_gemm: attention-out reads the query slice of the QKV output.
+* decode_kv: attention over the cache reads the V block, cache rows below
+  the position and the appended new value, then the decode wiring.
 * silu_mul: silu of the gate half times the up half.
 """
 import math
@@ -233,3 +235,36 @@ def test_mlp3_bias_before_relu_every_layer():
             row.append(max(y + 1.0, 0.0))
         want.append(row)
     _close(graphs.mlp3(inp), want, rtol=1e-6, atol=1e-6)
+
+
+def test_decode_kv_wiring_closed_form():
+    # q = k = 0 (their Wqkv blocks are zero) makes every score equal, so each
+    # head's attention output is the mean of its kv head's cache values 0..p-1
+    # and the new value; v_new selects the first n_kv columns of xn.  Pins:
+    # attention reads the V block (not K), cache rows below p only, the new
+    # value as row p, the GQA map, then O + x, gate_up on h, down + h.
+    H, hd, Hq, Hkv, I, Smax, p = 16, 8, 2, 1, 16, 7, 4
+    nq, nkv = Hq * hd, Hkv * hd
+    d = dict(m=1, hidden=H, n_q=nq, n_kv=nkv, head_dim=hd, inter=I, s_max=Smax, pos=p)
+    inp = workloads.generate("decode_kv", d)
+    bf = torch.bfloat16
+    Wqkv = torch.zeros(H, nq + 2 * nkv, dtype=bf)
+    Wqkv[:nkv, nq + nkv:] = torch.eye(nkv, dtype=bf)
+    inp["Wqkv"] = Wqkv
+    inp["Wo"] = torch.eye(nq, H, dtype=bf)
+    c = 0.5
+    inp["Wgu"] = torch.cat([c * torch.eye(H, I, dtype=bf), torch.eye(H, I, dtype=bf)], 1)
+    inp["Wd"] = torch.eye(I, H, dtype=bf)
+    inp["g1"] = _gamma(H, 1.0, 0.25)
+    inp["g2"] = _gamma(H, 0.5, 0.5)
+    vc = inp["v_cache"].float().tolist()
+    x = [float(v) for v in inp["x"][0].float()]
+    xn = _rms_row(x, [float(v) for v in inp["g1"].float()])
+    # the appended value is stored in the cache's bf16
+    vnew = [float(torch.tensor(v).to(bf).float()) for v in xn[:nkv]]
+    mean = [(sum(vc[j][t] for j in range(p)) + vnew[t]) / (p + 1) for t in range(nkv)]
+    o = mean * Hq                              # every query head reads kv head 0
+    h = [a + b for a, b in zip(o, x)]
+    hn = _rms_row(h, [float(v) for v in inp["g2"].float()])
+    out = [_silu(c * v) * v + hh for v, hh in zip(hn, h)]
+    _close(graphs.decode_kv(inp, d)[0], out, rtol=1e-4, atol=1e-4)

@@ -16,12 +16,14 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmk.so")
 MK_OK, MK_E_INVALID, MK_E_UNSUPPORTED, MK_E_LIMIT, MK_E_HIP, MK_E_DEADLOCK = range(6)
 STATUS_NAMES = ["MK_OK", "MK_E_INVALID", "MK_E_UNSUPPORTED", "MK_E_LIMIT", "MK_E_HIP",
                 "MK_E_DEADLOCK"]
-MK_F16, MK_BF16, MK_F32 = 1, 2, 3
+MK_F16, MK_BF16, MK_F32, MK_I32 = 1, 2, 3, 4
 MK_INPUT, MK_WEIGHT, MK_OUTPUT, MK_INTERMEDIATE = 0, 1, 2, 3
-MK_OP_GEMM, MK_OP_RMSNORM, MK_OP_ATTENTION, MK_OP_ADD, MK_OP_RELU = 1, 2, 3, 4, 5
+MK_OP_GEMM, MK_OP_RMSNORM, MK_OP_ATTENTION, MK_OP_ADD, MK_OP_RELU, MK_OP_DECODE_ATTENTION = (
+    1, 2, 3, 4, 5, 6)
 EP_BIAS, EP_RELU, EP_RESIDUAL, EP_SILU_MUL, EP_RMSNORM_INPUT, EP_ROPE, EP_PARTIAL = (
     1, 2, 4, 8, 16, 32, 64)
-I_NOOP, I_GEMM, I_GEMV, I_REDUCE, I_RMSNORM, I_ATTENTION, I_EW_ADD, I_EW_RELU = range(8)
+(I_NOOP, I_GEMM, I_GEMV, I_REDUCE, I_RMSNORM, I_ATTENTION, I_EW_ADD, I_EW_RELU, I_ATTN_PARTIAL,
+ I_ATTN_COMBINE) = range(10)
 MAX_TENSORS, MAX_SRC, MAX_DST, INSTR_WORDS, NODE_WORDS = 64, 16, 8, 64, 64
 
 # word offsets of mk_instr (mirrors the struct; checked by tests)

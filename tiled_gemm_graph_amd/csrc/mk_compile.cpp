@@ -21,7 +21,7 @@ namespace mk {
 
 static thread_local std::string g_err;
 void set_error(const std::string& m) { g_err = m; }
-int dtype_bytes(mk_dtype d) { return d == MK_F32 ? 4 : 2; }
+int dtype_bytes(mk_dtype d) { return d == MK_F32 || d == MK_I32 ? 4 : 2; }
 
 namespace {
 
@@ -295,6 +295,7 @@ struct Compiler {
         case MK_OP_ATTENTION: tile = lower_attention((int)oi, op); break;
         case MK_OP_ADD:
         case MK_OP_RELU: tile = lower_elementwise((int)oi, op); break;
+        case MK_OP_DECODE_ATTENTION: tile = lower_decode_attention((int)oi, op); break;
         default: fail(MK_E_INVALID, "unknown op kind");
       }
       p.op_tiles.push_back(tile);
@@ -720,6 +721,127 @@ struct Compiler {
     return t;
   }
 
+  // Split-KV decode attention ("Implementing a Mega Kernel for B300",
+  // section 2, flash-decoding): a partial node of one instruction per (key
+  // chunk c, kv head g), which rotates q and k_new at the run-time position
+  // p, appends the rotated k_new and v_new to row p of the caches (the
+  // instruction whose chunk holds p), and writes, for each query head of
+  // the group, the chunk's running max m, sum of exp2 l and unnormalised
+  // output (fp32) to P [chunks, Hq, d + 4]; then a combine node of one
+  // instruction per kv head that merges the chunks j0 <= p by log-sum-exp
+  // and writes o.  Operand slots of the partial node's descriptor: a = q,
+  // b = k_new, res = v_new, bias = k_cache, gamma = v_cache, out = P,
+  // aux = rotary table [S_max, d], part = pos; combine: a = P, out = o,
+  // part = pos.
+  mk_tile lower_decode_attention(int oi, const OpRec& op) {
+    const auto& T = p.tensors;
+    Edge q = edge_of(T, op.in[0]), kn = edge_of(T, op.in[1]), vn = edge_of(T, op.in[2]);
+    Edge kc = edge_of(T, op.in[3]), vc = edge_of(T, op.in[4]), ps = edge_of(T, op.in[5]);
+    Edge o = edge_of(T, op.out);
+    const int Hq = op.attrs.n_heads, Hkv = op.attrs.n_kv_heads, d = op.attrs.head_dim;
+    if (Hq <= 0 || Hkv <= 0 || d <= 0 || Hq % Hkv) fail(MK_E_INVALID, "DECODE_ATTENTION heads");
+    for (const Edge* e : {&q, &kn, &vn, &kc, &vc, &o})
+      if (!is2d(*e)) fail(MK_E_INVALID, "DECODE_ATTENTION operands must be 2-D");
+    if (q.rows() != 1 || kn.rows() != 1 || vn.rows() != 1 || o.rows() != 1)
+      fail(MK_E_INVALID, "DECODE_ATTENTION decodes one token: q, k_new, v_new and o have one row");
+    if (q.cols() != (I64)Hq * d || o.cols() != (I64)Hq * d || kn.cols() != (I64)Hkv * d ||
+        vn.cols() != (I64)Hkv * d)
+      fail(MK_E_INVALID, "DECODE_ATTENTION shapes: q, o [1, Hq*d]; k_new, v_new [1, Hkv*d]");
+    const I64 S = kc.rows();
+    if (S < 1 || vc.rows() != S || kc.cols() != (I64)Hkv * d || vc.cols() != (I64)Hkv * d)
+      fail(MK_E_INVALID, "DECODE_ATTENTION caches must be [S_max, Hkv*d]");
+    for (const Edge* e : {&kc, &vc}) {
+      const Tensor& t = T[e->tensor];
+      if (T[op.in[e == &kc ? 3 : 4]].is_view || t.role != MK_INPUT)
+        fail(MK_E_INVALID, "DECODE_ATTENTION caches must be whole caller-owned INPUT tensors");
+    }
+    {
+      const Tensor& t = T[ps.tensor];
+      if (t.dt != MK_I32 || t.role != MK_INPUT || numel(t.shape) != 1 || T[op.in[5]].is_view)
+        fail(MK_E_INVALID, "DECODE_ATTENTION pos must be a one-element MK_I32 INPUT tensor");
+    }
+    const mk_dtype dt = T[q.tensor].dt;
+    for (const Edge* e : {&kn, &vn, &kc, &vc, &o})
+      if (T[e->tensor].dt != dt) fail(MK_E_INVALID, "DECODE_ATTENTION dtypes differ");
+    if (dt != MK_F16 && dt != MK_BF16) unsup("DECODE_ATTENTION dtype must be fp16 or bf16");
+    if (d != 128) unsup("DECODE_ATTENTION body needs head_dim 128");
+    const int G = Hq / Hkv;
+    if (G > 8) unsup("DECODE_ATTENTION body handles at most 8 query heads per kv head");
+    mk_tile t = op.attrs.tile;
+    if (t.bq <= 0) {
+      const I64 per = cdiv(S * Hkv, ncu);
+      t.bq = (int)std::min<I64>(256, std::max<I64>(64, cdiv(per, 64) * 64));
+    }
+    if (t.bq % 64 || t.bq > 256) unsup("DECODE_ATTENTION chunks are 64, 128, 192 or 256 keys");
+    const I64 C = t.bq, NC = cdiv(S, C), W = d + 4;
+    const int pt = add_internal(MK_F32, {1, NC, Hq, W});
+    const int rope_t = add_internal(MK_F32, {1, 1, S, d});
+    p.tensors[rope_t].const_kind = 1;
+    p.tensors[rope_t].rope_half = d / 2;
+    p.tensors[rope_t].rope_theta = op.attrs.rope_theta > 0 ? op.attrs.rope_theta : 10000.f;
+    Edge P = edge_of(p.tensors, pt);
+    Node n;
+    n.op = oi;
+    n.opcode = MK_I_ATTN_PARTIAL;
+    n.out = pt;
+    n.edges = {q, kn, vn, kc, vc, ps};
+    for (I64 c = 0; c < NC; ++c)
+      for (int g = 0; g < Hkv; ++g) {
+        Instr in;
+        in.coord[0] = (int32_t)c;
+        in.coord[1] = g;
+        in.r0 = (int32_t)(c * C);
+        in.r1 = (int32_t)std::min(S, (c + 1) * C);
+        in.c0 = g;
+        in.c1 = G;
+        in.reads.push_back({q.tensor, box2(q, 0, 1, (I64)g * G * d, (I64)(g + 1) * G * d)});
+        in.reads.push_back({kn.tensor, box2(kn, 0, 1, (I64)g * d, (I64)(g + 1) * d)});
+        in.reads.push_back({vn.tensor, box2(vn, 0, 1, (I64)g * d, (I64)(g + 1) * d)});
+        in.reads.push_back({kc.tensor, box2(kc, in.r0, in.r1, (I64)g * d, (I64)(g + 1) * d)});
+        in.reads.push_back({vc.tensor, box2(vc, in.r0, in.r1, (I64)g * d, (I64)(g + 1) * d)});
+        in.reads.push_back({ps.tensor, full_box(T[ps.tensor])});
+        in.writes.push_back({pt, Box{{0, c, (I64)g * G, 0}, {1, c + 1, (I64)(g + 1) * G, W}}});
+        n.ins.push_back(in);
+      }
+    mk_node& dd = n.desc;
+    dd.opcode = MK_I_ATTN_PARTIAL;
+    dd.dtype = dt;
+    dd.M = 1;
+    dd.N = (int32_t)NC;
+    dd.K = (int32_t)C;
+    dd.heads = Hq;
+    dd.kv_heads = Hkv;
+    dd.head_dim = d;
+    dd.seq = (int32_t)S;
+    dd.scale = 1.0f / std::sqrt((float)d);
+    p.nodes.push_back(n);
+    node_edges.push_back({{"a", q}, {"b", kn}, {"res", vn}, {"bias", kc}, {"gamma", vc}, {"out", P},
+                          {"aux", edge_of(p.tensors, rope_t)}, {"part", ps}});
+    Node m;
+    m.op = oi;
+    m.opcode = MK_I_ATTN_COMBINE;
+    m.out = op.out;
+    m.edges = {P, ps};
+    for (int g = 0; g < Hkv; ++g) {
+      Instr in;
+      in.coord[0] = g;
+      in.r0 = 0;
+      in.r1 = 1;
+      in.c0 = g;
+      in.c1 = G;
+      in.reads.push_back({pt, Box{{0, 0, (I64)g * G, 0}, {1, NC, (I64)(g + 1) * G, W}}});
+      in.reads.push_back({ps.tensor, full_box(T[ps.tensor])});
+      in.writes.push_back({op.out, box2(o, 0, 1, (I64)g * G * d, (I64)(g + 1) * G * d)});
+      m.ins.push_back(in);
+    }
+    mk_node& md = m.desc;
+    md = dd;
+    md.opcode = MK_I_ATTN_COMBINE;
+    p.nodes.push_back(m);
+    node_edges.push_back({{"a", P}, {"out", o}, {"part", ps}});
+    return t;
+  }
+
   std::vector<std::map<std::string, Edge>> node_edges;
 
   // -------------------------------------------------------------- placing
@@ -1088,6 +1210,10 @@ struct Compiler {
         Edge q = edge_of(p.tensors, op.in[0]);
         double S = (double)q.rows(), hd = op.attrs.head_dim, H = op.attrs.n_heads;
         flops += op.attrs.causal ? 4.0 * H * hd * S * (S + 1) / 2 : 4.0 * H * hd * S * S;
+      } else if (op.kind == MK_OP_DECODE_ATTENTION) {
+        // counted over the whole cache (the position is known only at run time)
+        Edge kc = edge_of(p.tensors, op.in[3]);
+        flops += 4.0 * op.attrs.n_heads * op.attrs.head_dim * (double)kc.rows();
       }
       for (int id : op.in) {
         Edge e = edge_of(p.tensors, id);
@@ -1170,7 +1296,7 @@ void mk_graph_destroy(mk_graph* g) { delete g; }
 mk_status mk_graph_tensor(mk_graph* g, mk_dtype dt, int ndim, const int64_t* shape,
                           mk_role role, int32_t* id) {
   if (!g || !shape || !id) { set_error("null argument"); return MK_E_INVALID; }
-  if (dt != MK_F16 && dt != MK_BF16 && dt != MK_F32) { set_error("bad dtype"); return MK_E_INVALID; }
+  if (dt != MK_F16 && dt != MK_BF16 && dt != MK_F32 && dt != MK_I32) { set_error("bad dtype"); return MK_E_INVALID; }
   if (ndim < 1 || ndim > 4) { set_error("tensors have 1..4 dims"); return MK_E_INVALID; }
   if (role < MK_INPUT || role > MK_INTERMEDIATE) { set_error("bad role"); return MK_E_INVALID; }
   if ((int)g->t.size() >= MK_MAX_TENSORS) { set_error("more than MK_MAX_TENSORS tensors"); return MK_E_LIMIT; }
@@ -1232,6 +1358,7 @@ mk_status mk_graph_op(mk_graph* g, mk_op_kind kind, const int32_t* in, int n_in,
     case MK_OP_ATTENTION: want = 3; break;
     case MK_OP_ADD: want = 2; break;
     case MK_OP_RELU: want = 1; break;
+    case MK_OP_DECODE_ATTENTION: want = 6; break;
     default: set_error("unknown op kind"); return MK_E_INVALID;
   }
   if (kind != MK_OP_GEMM && a.epilogue) { set_error("epilogue flags apply to GEMM only"); return MK_E_INVALID; }
@@ -1285,7 +1412,12 @@ mk_status megakernel_build(const mk_graph* g, const mk_build_options* opts, mk_p
   if (p->opts.reuse < 0 || p->opts.reuse > 2) { delete p; set_error("reuse must be 0, 1 or 2"); return MK_E_INVALID; }
   if (p->opts.pack < 0 || p->opts.pack > 2) { delete p; set_error("pack must be 0, 1 or 2"); return MK_E_INVALID; }
   if (p->opts.sync < 0 || p->opts.sync > 1) { delete p; set_error("sync must be 0 or 1"); return MK_E_INVALID; }
-  if (p->opts.queue < 0 || p->opts.queue > 1) { delete p; set_error("queue must be 0 or 1"); return MK_E_INVALID; }
+  if (p->opts.queue < 0 || p->opts.queue > 2) { delete p; set_error("queue must be 0, 1 or 2"); return MK_E_INVALID; }
+  if (p->opts.queue == 2 && p->opts.num_cus % 8) {
+    delete p;
+    set_error("queue = 2 (one queue per XCD) needs num_cus to be a multiple of 8");
+    return MK_E_INVALID;
+  }
   if (p->opts.debug_poison < 0 || p->opts.debug_poison > 1) {
     delete p;
     set_error("debug_poison must be 0 or 1");

@@ -1539,6 +1539,181 @@ __device__ __forceinline__ void attention_tile(const KArgs& a, const mk_instr& i
   }
 }
 
+// ----------------------------------------------- split-KV decode attention
+// Partial: keys [r0, min(r1, p + 1)) of kv head g = c0 for its G = c1 query
+// heads, p the run-time position (the pos tensor, operand `part`).  One
+// thread per key for the scores (its 256-byte key row against the rotated
+// queries, read from LDS as broadcasts), a wave-then-LDS max and sum per
+// head, then P V with lanes over head dimensions.  Writes, per query head,
+// the unnormalised output, the running max m (log2 units) and the sum of
+// exp2 l to P[chunk][head][d + 4].  The instruction whose chunk holds p
+// rotates k_new, rounds it to the cache dtype, and appends it and v_new to
+// row p of the caches; key p is scored with that rounded value.
+template <int DT>
+__device__ __forceinline__ void attn_partial_tile(const KArgs& a, const mk_instr& in, const mk_node& nd, char* smem) {
+  constexpr int D = 128, HALF = 64;
+  const int t = threadIdx.x, lane = t & 63, w = wave_id();
+  const int g = uni(in.c0), G = uni(in.c1), S = uni(nd.seq), Hq = uni(nd.heads);
+  const int p = uni(*buf<const int>(a, nd.part));
+  const int j0 = uni(in.r0), r1 = uni(in.r1);
+  if (p < 0 || p >= S || j0 > p) return;   // empty chunk: the combine skips it
+  const int j1 = min(r1, p + 1), nk = j1 - j0;
+  const bool own = p < r1;                  // this chunk holds key p
+  float* qs = reinterpret_cast<float*>(smem);        // [G][D] rotated q * scale * log2(e)
+  float* kn = qs + 8 * D;                            // [D] rotated k_new (rounded)
+  float* vv = kn + D;                                // [D] v_new
+  float* pc = vv + D;                                // [G][256] exp2 weights
+  float* red = pc + 8 * 256;                         // [4 waves][8] per-wave max / sum
+  const float* tab = buf<const float>(a, nd.aux) + (long)p * D;   // [cos | sin] of position p
+  const float c = nd.scale * 1.4426950408889634f;
+  {
+    const u16* Q = buf<const u16>(a, nd.a) + (long)g * G * D;
+    for (int u = t; u < G * HALF; u += kThreads) {
+      const int h = u / HALF, i = u - h * HALF;
+      const float x1 = to_f<DT>(Q[h * D + i]), x2 = to_f<DT>(Q[h * D + i + HALF]);
+      const float cs = tab[i], sn = tab[HALF + i];
+      qs[h * D + i] = (x1 * cs - x2 * sn) * c;
+      qs[h * D + i + HALF] = (x2 * cs + x1 * sn) * c;
+    }
+    if (own && t < HALF) {
+      const u16* Kn = buf<const u16>(a, nd.b) + (long)g * D;
+      const u16* Vn = buf<const u16>(a, nd.res) + (long)g * D;
+      u16* Kc = buf<u16>(a, nd.bias) + (long)p * nd.bias.ld + (long)g * D;
+      u16* Vc = buf<u16>(a, nd.gamma) + (long)p * nd.gamma.ld + (long)g * D;
+      const float x1 = to_f<DT>(Kn[t]), x2 = to_f<DT>(Kn[t + HALF]);
+      const float cs = tab[t], sn = tab[HALF + t];
+      const u16 y1 = from_f<DT>(x1 * cs - x2 * sn), y2 = from_f<DT>(x2 * cs + x1 * sn);
+      Kc[t] = y1;
+      Kc[t + HALF] = y2;
+      kn[t] = to_f<DT>(y1);
+      kn[t + HALF] = to_f<DT>(y2);
+      const u16 v1 = Vn[t], v2 = Vn[t + HALF];
+      Vc[t] = v1;
+      Vc[t + HALF] = v2;
+      vv[t] = to_f<DT>(v1);
+      vv[t + HALF] = to_f<DT>(v2);
+    }
+  }
+  __syncthreads();
+  // scores: thread t holds key j0 + t
+  float sc[8];
+#pragma unroll
+  for (int h = 0; h < 8; ++h) sc[h] = -INFINITY;
+  const int j = j0 + t;
+  if (t < nk) {
+#pragma unroll
+    for (int h = 0; h < 8; ++h) sc[h] = 0.f;
+    if (j == p) {
+      for (int dd = 0; dd < D; ++dd) {
+        const float kx = kn[dd];
+#pragma unroll
+        for (int h = 0; h < 8; ++h)
+          if (h < G) sc[h] = fmaf(qs[h * D + dd], kx, sc[h]);
+      }
+    } else {
+      const u16* Kr = buf<const u16>(a, nd.bias) + (long)j * nd.bias.ld + (long)g * D;
+      u32x4 kr[D / 8];
+#pragma unroll
+      for (int q = 0; q < D / 8; ++q) kr[q] = *reinterpret_cast<const u32x4*>(Kr + q * 8);
+#pragma unroll
+      for (int q = 0; q < D / 8; ++q) {
+        float kf[8];
+        unpack8<DT>(kr[q], kf);
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+#pragma unroll
+          for (int h = 0; h < 8; ++h)
+            if (h < G) sc[h] = fmaf(qs[h * D + q * 8 + e], kf[e], sc[h]);
+      }
+    }
+  }
+  // per head: max over the chunk, then exp2 weights and their sum
+  float mx[8], ls[8];
+#pragma unroll
+  for (int h = 0; h < 8; ++h) {
+    float v = sc[h];
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    if (lane == 0) red[w * 8 + h] = v;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int h = 0; h < 8; ++h) mx[h] = fmaxf(fmaxf(red[h], red[8 + h]), fmaxf(red[16 + h], red[24 + h]));
+  __syncthreads();
+#pragma unroll
+  for (int h = 0; h < 8; ++h) {
+    const float e = t < nk && h < G ? exp2f(sc[h] - mx[h]) : 0.f;
+    if (h < G) pc[h * 256 + t] = e;
+    const float v = wave_sum(e);
+    if (lane == 0) red[w * 8 + h] = v;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int h = 0; h < 8; ++h) ls[h] = (red[h] + red[8 + h]) + (red[16 + h] + red[24 + h]);
+  // P V: wave w takes heads w, w + 4; lane holds dimensions 2 lane, 2 lane + 1
+  float* P = buf<float>(a, nd.out) + (long)in.coord[0] * Hq * (D + 4);
+  for (int h = w; h < G; h += 4) {
+    float o0 = 0.f, o1 = 0.f;
+    const u16* Vr = buf<const u16>(a, nd.gamma) + (long)j0 * nd.gamma.ld + (long)g * D + 2 * lane;
+    const int nc = own ? nk - 1 : nk;     // cache rows (key p comes from vv)
+#pragma unroll 4
+    for (int k = 0; k < nc; ++k) {
+      const uint32_t v2 = *reinterpret_cast<const uint32_t*>(Vr + (long)k * nd.gamma.ld);
+      const float e = pc[h * 256 + k];
+      o0 = fmaf(e, to_f<DT>((u16)(v2 & 0xffff)), o0);
+      o1 = fmaf(e, to_f<DT>((u16)(v2 >> 16)), o1);
+    }
+    if (own) {
+      const float e = pc[h * 256 + nk - 1];
+      o0 = fmaf(e, vv[2 * lane], o0);
+      o1 = fmaf(e, vv[2 * lane + 1], o1);
+    }
+    float hm = 0.f, hl = 0.f;
+#pragma unroll
+    for (int hh = 0; hh < 8; ++hh)
+      if (hh == h) { hm = mx[hh]; hl = ls[hh]; }
+    float* dst = P + (long)(g * G + h) * (D + 4);
+    dst[2 * lane] = o0;
+    dst[2 * lane + 1] = o1;
+    if (lane == 0) {
+      dst[D] = hm;
+      dst[D + 1] = hl;
+    }
+  }
+}
+
+// Combine: for each query head of kv head g = c0, merge the chunks c <=
+// p / chunk (each holds at least key c * chunk <= p) by log-sum-exp:
+// M = max m_c, o = sum 2^(m_c - M) o_c / sum 2^(m_c - M) l_c.
+template <int DT>
+__device__ __forceinline__ void attn_combine_tile(const KArgs& a, const mk_instr& in, const mk_node& nd) {
+  constexpr int D = 128, W = D + 4;
+  const int t = threadIdx.x;
+  const int g = uni(in.c0), G = uni(in.c1), S = uni(nd.seq), Hq = uni(nd.heads), C = uni(nd.K);
+  const int p = uni(*buf<const int>(a, nd.part));
+  u16* O = buf<u16>(a, nd.out) + (long)g * G * D;
+  if (p < 0 || p >= S) {
+    for (int u = t; u < G * D; u += kThreads) O[u] = 0;
+    return;
+  }
+  const int nc = p / C + 1;
+  const float* P = buf<const float>(a, nd.a);
+  for (int u = t; u < G * D; u += kThreads) {
+    const int h = u / D, dd = u - h * D;
+    const float* ph = P + (long)(g * G + h) * W;
+    float M = -INFINITY;
+    for (int k = 0; k < nc; ++k) M = fmaxf(M, ph[(long)k * Hq * W + D]);
+    float num = 0.f, den = 0.f;
+    for (int k = 0; k < nc; ++k) {
+      const float* pk = ph + (long)k * Hq * W;
+      const float sc = exp2f(pk[D] - M);
+      num = fmaf(sc, pk[dd], num);
+      den = fmaf(sc, pk[D + 1], den);
+    }
+    O[u] = from_f<DT>(num / den);
+  }
+}
+
 // ----------------------------------------------------------- elementwise
 template <int DT>
 __device__ __forceinline__ void elementwise_tile(const KArgs& a, const mk_instr& in, const mk_node& nd) {
@@ -1639,6 +1814,8 @@ __device__ __forceinline__ void run_body(const KArgs& a, const mk_instr& in, con
           case MK_I_REDUCE: reduce_tile<DT>(a, in, nd, smem); break;
           case MK_I_RMSNORM: rmsnorm_tile<DT>(a, in, nd, smem); break;
           case MK_I_ATTENTION: attention_tile<DT>(a, in, nd, smem); break;
+          case MK_I_ATTN_PARTIAL: attn_partial_tile<DT>(a, in, nd, smem); break;
+          case MK_I_ATTN_COMBINE: attn_combine_tile<DT>(a, in, nd); break;
           case MK_I_EW_ADD:
           case MK_I_EW_RELU: elementwise_tile<DT>(a, in, nd); break;
           default: break;
@@ -1718,16 +1895,21 @@ __device__ __forceinline__ bool has_rec(const Loop& L, int it) {
 
 // Work-queue mode, controller wave: the next instruction index, or -1 when
 // the list is exhausted (lane 0 takes it with one agent-scope atomic add;
-// every lane gets the value).  Indices come out in list order across the
-// grid.  The two ticket words alternate between runs: run e counts on word
-// e & 1 and clears word (e + 1) & 1, which the previous run (finished, by
-// stream order) used and the next run counts on.
-__device__ __forceinline__ int take_ticket(const KArgs& a) {
+// every lane gets the value).  queue = 1: one queue, indices in list order
+// across the grid.  queue = 2: one queue per XCD, workgroup vcu taking from
+// queue q = vcu mod 8 the indices i with i mod 8 = q in list order (the
+// instructions static placement gives that XCD), so a tile keeps the L2 its
+// neighbours use.  Each queue has two ticket words that alternate between
+// runs: run e counts on word e & 1 and clears word (e + 1) & 1, which the
+// previous run (finished, by stream order) used and the next run counts on.
+__device__ __forceinline__ int take_ticket(const KArgs& a, int vcu) {
+  const int q = a.queue == 2 ? (vcu & 7) : 0;
   int tk = 0;
   if ((threadIdx.x & 63) == 0)
-    tk = __hip_atomic_fetch_add(a.ticket + (a.epoch & 1), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    tk = __hip_atomic_fetch_add(a.ticket + 2 * q + (a.epoch & 1), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   tk = __shfl(tk, 0, 64);
-  return tk < a.n_instr ? tk : -1;
+  const long idx = a.queue == 2 ? (long)tk * 8 + q : (long)tk;
+  return idx < a.n_instr ? (int)idx : -1;
 }
 
 __device__ __forceinline__ void stamp(const KArgs& a, int gidx, int k, unsigned long long v) {
@@ -1836,7 +2018,7 @@ __device__ __forceinline__ bool wait_sources(const Loop& L, const mk_instr& in, 
   if (wave_id() == 0) {
     bool ok;
     if (L.a.queue) {
-      tk = L.idx[(it + 1) % 3] >= 0 ? take_ticket(L.a) : -1;
+      tk = L.idx[(it + 1) % 3] >= 0 ? take_ticket(L.a, L.vcu) : -1;
       ok = poll_sources(L, in, gidx);
       w = fetch_record(L, tk);
     } else {
@@ -1974,10 +2156,11 @@ __global__ void __launch_bounds__(NT, 1) mk_persistent(mkd::KArgs args) {
     reinterpret_cast<int*>(s_nodes)[i] = reinterpret_cast<const int*>(a.nodes)[i];
   if (a.queue) {
     // clear the other ticket word for the next run; take iterations 0 and 1
-    if (b == 0 && t == 0) __hip_atomic_store(a.ticket + ((a.epoch + 1) & 1), 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (b == 0 && t < 8)
+      __hip_atomic_store(a.ticket + 2 * t + ((a.epoch + 1) & 1), 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (t < 64) {
-      const int t0 = mkd::take_ticket(a);
-      const int t1 = t0 >= 0 ? mkd::take_ticket(a) : -1;
+      const int t0 = mkd::take_ticket(a, vcu);
+      const int t1 = t0 >= 0 ? mkd::take_ticket(a, vcu) : -1;
       if (t0 >= 0) mkd::copy_words(reinterpret_cast<int*>(&s_in[0]), reinterpret_cast<const int*>(a.instrs + t0));
       if (t1 >= 0) mkd::copy_words(reinterpret_cast<int*>(&s_in[1]), reinterpret_cast<const int*>(a.instrs + t1));
       if (t == 0) {

@@ -131,6 +131,8 @@ Launch persistent_for(unsigned ops, bool wide) {
   if ((ops & ~mkd::kOpGemm) == 0) return {reinterpret_cast<const void*>(mk_persistent<mkd::kOpGemm>), 256};
   if ((ops & mkd::kOpGemv) == 0)
     return {reinterpret_cast<const void*>(mk_persistent<mkd::kOpGemm | mkd::kOpOther>), 256};
+  if ((ops & mkd::kOpGemm) == 0)
+    return {reinterpret_cast<const void*>(mk_persistent<mkd::kOpGemv | mkd::kOpOther>), 256};
   return {reinterpret_cast<const void*>(mk_persistent<mkd::kOpAll>), 256};
 }
 Launch node_kernel_for(unsigned ops, bool wide) {
@@ -139,6 +141,8 @@ Launch node_kernel_for(unsigned ops, bool wide) {
   if ((ops & ~mkd::kOpGemm) == 0) return {reinterpret_cast<const void*>(mk_node_kernel<mkd::kOpGemm>), 256};
   if ((ops & mkd::kOpGemv) == 0)
     return {reinterpret_cast<const void*>(mk_node_kernel<mkd::kOpGemm | mkd::kOpOther>), 256};
+  if ((ops & mkd::kOpGemm) == 0)
+    return {reinterpret_cast<const void*>(mk_node_kernel<mkd::kOpGemv | mkd::kOpOther>), 256};
   return {reinterpret_cast<const void*>(mk_node_kernel<mkd::kOpAll>), 256};
 }
 
@@ -200,7 +204,7 @@ mk_status ensure_device(mk_plan* p) {
   }
   for (const Launch& k : {persistent_for(mkd::kOpAll, false), persistent_for(mkd::kOpGemv, false),
                           persistent_for(mkd::kOpGemm, false), persistent_for(mkd::kOpGemm | mkd::kOpOther, false),
-                          persistent_for(mkd::kOpGemm, true)}) {
+                          persistent_for(mkd::kOpGemm, true), persistent_for(mkd::kOpGemv | mkd::kOpOther, false)}) {
     int blocks = 0;
     HIPCHK(hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, k.fn, k.threads, 0));
     if (blocks < 1) {

@@ -16,7 +16,7 @@ import numpy as np
 
 from . import _lib as L
 
-_DT = {"f16": L.MK_F16, "bf16": L.MK_BF16, "f32": L.MK_F32}
+_DT = {"f16": L.MK_F16, "bf16": L.MK_BF16, "f32": L.MK_F32, "i32": L.MK_I32}
 _ROLE = {"input": L.MK_INPUT, "weight": L.MK_WEIGHT, "output": L.MK_OUTPUT,
          "intermediate": L.MK_INTERMEDIATE}
 
@@ -27,7 +27,8 @@ def _dt(x) -> int:
     if isinstance(x, str):
         return _DT[x]
     import torch
-    return {torch.float16: L.MK_F16, torch.bfloat16: L.MK_BF16, torch.float32: L.MK_F32}[x]
+    return {torch.float16: L.MK_F16, torch.bfloat16: L.MK_BF16, torch.float32: L.MK_F32,
+            torch.int32: L.MK_I32}[x]
 
 
 def _tile(t: Optional[Dict[str, int]]) -> L.Tile:
@@ -110,6 +111,16 @@ class Graph:
         at = L.OpAttrs(n_heads=heads, n_kv_heads=kv_heads, head_dim=head_dim,
                        causal=int(causal), tile=_tile(tile))
         self._op(L.MK_OP_ATTENTION, [q, k, v], out, at)
+
+    def decode_attention(self, q: int, k_new: int, v_new: int, k_cache: int, v_cache: int,
+                         pos: int, out: int, heads: int, kv_heads: int, head_dim: int,
+                         rope_theta: float = 0.0, tile: Dict[str, int] = None) -> None:
+        """Split-KV attention of one new token over a KV cache, with rotary
+        embedding at the run-time position ``pos`` and the append of the
+        new k, v to the caches (MK_OP_DECODE_ATTENTION in mk.h)."""
+        at = L.OpAttrs(n_heads=heads, n_kv_heads=kv_heads, head_dim=head_dim,
+                       rope_theta=rope_theta, tile=_tile(tile))
+        self._op(L.MK_OP_DECODE_ATTENTION, [q, k_new, v_new, k_cache, v_cache, pos], out, at)
 
     def add(self, a: int, b: int, out: int, tile: Dict[str, int] = None) -> None:
         self._op(L.MK_OP_ADD, [a, b], out, L.OpAttrs(tile=_tile(tile)))

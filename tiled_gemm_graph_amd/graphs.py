@@ -25,8 +25,9 @@ from typing import Dict, List, Optional, Sequence
 from . import _lib as L
 from .graph import Graph, Plan
 
-OUTPUT = dict(mlp3=None, decode="out", prefill="Z", decode_gemm="D", layer="out")
-DTYPE = dict(mlp3="f16", decode="bf16", prefill="f16", decode_gemm="f16", layer="bf16")
+OUTPUT = dict(mlp3=None, decode="out", prefill="Z", decode_gemm="D", layer="out", decode_kv="out")
+DTYPE = dict(mlp3="f16", decode="bf16", prefill="f16", decode_gemm="f16", layer="bf16",
+             decode_kv="bf16")
 
 
 def output_name(workload: str, dims: Dict[str, int]) -> str:
@@ -119,6 +120,34 @@ def build(workload: str, dims: Dict[str, int], tiles: Optional[Sequence[dict]] =
         g.gemm(g.cols(qkv, 0, nq), Wo, h, L.EP_RESIDUAL, residual=x, tile=_t(tiles, 1))
         g.gemm(h, Wgu, a, L.EP_RMSNORM_INPUT | L.EP_SILU_MUL, gamma=g2, tile=_t(tiles, 2))
         g.gemm(a, Wd, out, L.EP_RESIDUAL, residual=h, tile=_t(tiles, 3))
+        return g
+    if workload == "decode_kv":
+        # the decode layer with its attention: rotary q, k at the run-time
+        # position, split-KV attention over the cache with the append of
+        # the new k, v, then O + residual and the MLP as in ``decode``
+        M, H, nq, nkv, I, hd = d["m"], d["hidden"], d["n_q"], d["n_kv"], d["inter"], d["head_dim"]
+        Smax = d["s_max"]
+        x = g.tensor("x", "bf16", (M, H), "input")
+        g1 = g.tensor("g1", "bf16", (H,), "weight")
+        Wqkv = g.tensor("Wqkv", "bf16", (H, nq + 2 * nkv), "weight")
+        Wo = g.tensor("Wo", "bf16", (nq, H), "weight")
+        g2 = g.tensor("g2", "bf16", (H,), "weight")
+        Wgu = g.tensor("Wgu", "bf16", (H, 2 * I), "weight")
+        Wd = g.tensor("Wd", "bf16", (I, H), "weight")
+        kc = g.tensor("k_cache", "bf16", (Smax, nkv), "input")
+        vc = g.tensor("v_cache", "bf16", (Smax, nkv), "input")
+        pos = g.tensor("pos", "i32", (1,), "input")
+        qkv = g.tensor("qkv", "bf16", (M, nq + 2 * nkv), "intermediate")
+        o = g.tensor("o", "bf16", (M, nq), "intermediate")
+        h = g.tensor("h", "bf16", (M, H), "intermediate")
+        a = g.tensor("a", "bf16", (M, I), "intermediate")
+        out = g.tensor("out", "bf16", (M, H), "output")
+        g.gemm(x, Wqkv, qkv, L.EP_RMSNORM_INPUT, gamma=g1, tile=_t(tiles, 0))
+        g.decode_attention(g.cols(qkv, 0, nq), g.cols(qkv, nq, nq + nkv), g.cols(qkv, nq + nkv, nq + 2 * nkv),
+                           kc, vc, pos, o, nq // hd, nkv // hd, hd, tile=_t(tiles, 1))
+        g.gemm(o, Wo, h, L.EP_RESIDUAL, residual=x, tile=_t(tiles, 2))
+        g.gemm(h, Wgu, a, L.EP_RMSNORM_INPUT | L.EP_SILU_MUL, gamma=g2, tile=_t(tiles, 3))
+        g.gemm(a, Wd, out, L.EP_RESIDUAL, residual=h, tile=_t(tiles, 4))
         return g
     if workload == "layer":
         S, H = d["seq"], d["hidden"]

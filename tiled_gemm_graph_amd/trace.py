@@ -18,7 +18,8 @@ import numpy as np
 
 from . import _lib as L
 
-OPCODE_NAMES = ["NOOP", "GEMM", "GEMV", "REDUCE", "RMSNORM", "ATTENTION", "EW_ADD", "EW_RELU"]
+OPCODE_NAMES = ["NOOP", "GEMM", "GEMV", "REDUCE", "RMSNORM", "ATTENTION", "EW_ADD", "EW_RELU",
+                "ATTN_PARTIAL", "ATTN_COMBINE"]
 
 
 def wall_clock_khz() -> int:

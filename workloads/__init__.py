@@ -41,6 +41,8 @@ from typing import Dict, List, Tuple
 import torch
 
 WORKLOADS = ("mlp3", "decode", "prefill", "decode_gemm", "layer")
+# graphs beyond the five configurations (built on them)
+EXTRA_WORKLOADS = ("decode_kv",)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -66,6 +68,9 @@ def default_dims(workload: str) -> Dict[str, int]:
     if workload == "layer":
         return dict(seq=2048, hidden=4096, heads=32, kv_heads=8,
                     head_dim=128, inter=14336)
+    if workload == "decode_kv":
+        return dict(m=1, hidden=4096, n_q=4096, n_kv=1024, head_dim=128, inter=14336,
+                    s_max=4096, pos=4095)
     raise KeyError(workload)
 
 
@@ -87,6 +92,9 @@ def small_dims(workload: str) -> Dict[str, int]:
     if workload == "layer":
         return dict(seq=320, hidden=512, heads=4, kv_heads=1,
                     head_dim=128, inter=768)
+    if workload == "decode_kv":
+        return dict(m=1, hidden=512, n_q=512, n_kv=256, head_dim=128, inter=768,
+                    s_max=384, pos=200)
     raise KeyError(workload)
 
 
@@ -133,6 +141,24 @@ def spec(workload: str, dims: Dict[str, int] | None = None) -> List[TensorSpec]:
             TensorSpec("Wdown", (d["n_up"], d["n_down"]), f16, 0.0,
                        1.0 / math.sqrt(d["n_up"])),
         ]
+    if workload == "decode_kv":
+        M, H, I, Smax = d["m"], d["hidden"], d["inter"], d["s_max"]
+        nqkv = d["n_q"] + 2 * d["n_kv"]
+        return [
+            TensorSpec("x", (M, H), bf16, 0.0, 1.0),
+            TensorSpec("g1", (H,), bf16, 1.0, 0.02),
+            TensorSpec("Wqkv", (H, nqkv), bf16, 0.0, 1.0 / math.sqrt(H)),
+            TensorSpec("Wo", (d["n_q"], H), bf16, 0.0, 1.0 / math.sqrt(d["n_q"])),
+            TensorSpec("g2", (H,), bf16, 1.0, 0.02),
+            TensorSpec("Wgu", (H, 2 * I), bf16, 0.0, 1.0 / math.sqrt(H)),
+            TensorSpec("Wd", (I, H), bf16, 0.0, 1.0 / math.sqrt(I)),
+            # the cache holds rotated keys and values of earlier tokens:
+            # drawn i.i.d. N(0, 1), the scale of a projected activation
+            TensorSpec("k_cache", (Smax, d["n_kv"]), bf16, 0.0, 1.0),
+            TensorSpec("v_cache", (Smax, d["n_kv"]), bf16, 0.0, 1.0),
+            # the position of the new token: a constant, no draw
+            TensorSpec("pos", (1,), torch.int32, float(d["pos"]), 0.0),
+        ]
     if workload == "layer":
         S, H = d["seq"], d["hidden"]
         nq = d["heads"] * d["head_dim"]
@@ -164,6 +190,9 @@ def _draw(ts: TensorSpec, g: torch.Generator) -> torch.Tensor:
     n = 1
     for s in ts.shape:
         n *= s
+    if not ts.dtype.is_floating_point:
+        # integer runtime scalars: the constant in ``mean``, no draw
+        return torch.full(ts.shape, int(ts.mean), dtype=ts.dtype)
     out = torch.empty(n, dtype=ts.dtype)
     # Chunked so that a 235M-element weight does not need a 1 GB fp32 temporary.
     # The stream of normals is the same as one randn(n) call would give.
@@ -186,5 +215,6 @@ def generate(workload: str, dims: Dict[str, int] | None = None,
     g.manual_seed(seed)
     specs = spec(workload, dims)
     if dtype is not None:
-        specs = [dataclasses.replace(ts, dtype=dtype) for ts in specs]
+        specs = [dataclasses.replace(ts, dtype=dtype) if ts.dtype.is_floating_point else ts
+                 for ts in specs]
     return {ts.name: _draw(ts, g) for ts in specs}
