@@ -253,6 +253,29 @@ def line_for(head, steps, warmup, graphs=None):
     return line
 
 
+def node_trace(workload, warmup):
+    """One traced forward of the megakernel after ``warmup`` untraced ones:
+    per-node start, end, wait, body and release times (markdown)."""
+    import torch
+
+    import workloads
+    from tiled_gemm_graph_amd import graphs as G
+    from tiled_gemm_graph_amd import trace as TR
+
+    dims = workloads.default_dims(workload)
+    r = G.Runner(workload, dims, workloads.generate(workload, dims), device="cuda")
+    for _ in range(max(warmup, 1)):
+        r.forward()
+    r.plan.check()
+    torch.cuda.synchronize()
+    stamps, mhz = TR.capture(r, with_clock=True)
+    khz = TR.wall_clock_khz()
+    s = TR.summarize(r.plan, stamps, khz)
+    print(f"{workload} ({DESCR[workload]}): traced forward span {s['span_us']:.1f} us, "
+          f"mean tile-body occupancy {s['body_util']:.3f}, core clock {mhz:.0f} MHz\n", flush=True)
+    print(TR.node_table(r.plan, stamps, khz), flush=True)
+
+
 def copy_calibration(mib, steps):
     """A plain device copy of known size: reads and writes ``mib`` MiB per
     launch.  Profiling it with the HBM counters gives the scale that turns
@@ -285,6 +308,8 @@ def main():
                          "level boundary, for A/B comparison")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="only time a plain copy of this many MiB (counter calibration)")
+    ap.add_argument("--node-trace", action="store_true",
+                    help="with --workload: print the per-node timeline of one traced forward")
     ap.add_argument("--source-hash", action="store_true",
                     help="print the hash of the kernel sources and exit")
     args = ap.parse_args()
@@ -301,6 +326,12 @@ def main():
         sys.exit(2)
     if args.copy_mib:
         copy_calibration(args.copy_mib, args.steps)
+        return
+    if args.node_trace:
+        if not args.workload:
+            print("--node-trace needs --workload", file=sys.stderr)
+            sys.exit(2)
+        node_trace(args.workload, args.warmup)
         return
     kw = dict(do_check=not args.no_check, sync=args.sync, queue_ab=not args.no_queue)
     if args.workload:

@@ -22,7 +22,8 @@ from tests.gpu_common import assert_parity, say, to_np
 
 pytestmark = pytest.mark.gpu
 
-ACT = dict(mlp3="x", decode="x", prefill="X", decode_gemm="X0", layer="x")
+ACT = dict(mlp3="x", decode="x", prefill="X", decode_gemm="X0", layer="x", decode_kv="x")
+ALL = tuple(workloads.WORKLOADS) + tuple(workloads.EXTRA_WORKLOADS)
 
 
 def _counters_ok(plan, epochs):
@@ -32,7 +33,7 @@ def _counters_ok(plan, epochs):
 
 
 @pytest.mark.parametrize("poison,queue", [(0, 0), (1, 0), (1, 1), (1, 2)])
-@pytest.mark.parametrize("wl", workloads.WORKLOADS)
+@pytest.mark.parametrize("wl", ALL)
 def test_alternating_inputs_each_run_checked(wl, poison, queue):
     d = workloads.small_dims(wl)
     inp_a = workloads.generate(wl, d)
@@ -58,7 +59,7 @@ def test_alternating_inputs_each_run_checked(wl, poison, queue):
 
 
 @pytest.mark.parametrize("queue", [1, 2])
-@pytest.mark.parametrize("wl", workloads.WORKLOADS)
+@pytest.mark.parametrize("wl", ALL)
 def test_work_queue_same_bytes_as_static(wl, queue):
     d = workloads.small_dims(wl)
     inp = workloads.generate(wl, d)

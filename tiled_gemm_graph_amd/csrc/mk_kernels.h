@@ -1541,153 +1541,257 @@ __device__ __forceinline__ void attention_tile(const KArgs& a, const mk_instr& i
 
 // ----------------------------------------------- split-KV decode attention
 // Partial: keys [r0, min(r1, p + 1)) of kv head g = c0 for its G = c1 query
-// heads, p the run-time position (the pos tensor, operand `part`).  One
-// thread per key for the scores (its 256-byte key row against the rotated
-// queries, read from LDS as broadcasts), a wave-then-LDS max and sum per
-// head, then P V with lanes over head dimensions.  Writes, per query head,
-// the unnormalised output, the running max m (log2 units) and the sum of
-// exp2 l to P[chunk][head][d + 4].  The instruction whose chunk holds p
-// rotates k_new, rounds it to the cache dtype, and appends it and v_new to
-// row p of the caches; key p is scored with that rounded value.
-template <int DT>
-__device__ __forceinline__ void attn_partial_tile(const KArgs& a, const mk_instr& in, const mk_node& nd, char* smem) {
-  constexpr int D = 128, HALF = 64;
+// heads, p the run-time position (the pos tensor, operand `part`).  Every
+// K and V row of the chunk's first 128 keys is requested at once: a pass
+// holds 32 keys per wave, four keys per load (16 lanes x 16 bytes cover one
+// 256-byte row).  The caches and the position are caller inputs that no
+// instruction of the plan writes before this one (row p is written by this
+// instruction and never read back), so the persistent loop issues these
+// loads before the instruction's counters clear, as it does with weights.
+// Scores reduce over the 16 lanes of a row with DPP moves; V rows go to
+// LDS.  Then the max per head (running maxima of the lanes, two cross-row
+// shuffles, LDS across waves), exp2 weights and their sum (thread per key),
+// and P V out of LDS with lanes over head dimensions, eight keys per step.
+// Writes, per query head, the unnormalised output, the running max m (log2
+// units) and the sum of exp2 l to P[chunk][head][d + 4].  The instruction
+// whose chunk holds p rotates k_new, rounds it to the cache dtype, and
+// appends it and v_new to row p of the caches; key p is scored with that
+// rounded value.
+constexpr int kAttnD = 128, kAttnPass = 128, kAttnGroups = 8;
+struct AttnPrefetch {
+  u32x4 kr[kAttnGroups], vr[kAttnGroups];   // this lane's K and V pieces of the first pass
+  int p;                                     // the position
+  float cs, sn;                              // cos and sin of position p, pair t % 64
+};
+
+// K and V pieces of pass ps: rows j0 + kl, kl = 128 ps + 32 w + 4 i + sub,
+// for kl < nr (the chunk's rows); zero beyond.
+__device__ __forceinline__ void attn_issue_kv(const KArgs& a, const mk_node& nd, int g, int j0, int nr, int ps,
+                                              u32x4* kr, u32x4* vr) {
+  const int lane = threadIdx.x & 63, w = wave_id();
+  const int sub = lane >> 4, part = lane & 15;
+  const u16* Kc = buf<const u16>(a, nd.bias) + (long)g * kAttnD + part * 8;
+  const u16* Vc = buf<const u16>(a, nd.gamma) + (long)g * kAttnD + part * 8;
+#pragma unroll
+  for (int i = 0; i < kAttnGroups; ++i) {
+    const int kl = ps * kAttnPass + w * 32 + i * 4 + sub;
+    if (kl < nr) {
+      kr[i] = *reinterpret_cast<const u32x4*>(Kc + (long)(j0 + kl) * nd.bias.ld);
+      vr[i] = *reinterpret_cast<const u32x4*>(Vc + (long)(j0 + kl) * nd.gamma.ld);
+    } else {
+      kr[i] = u32x4{0u, 0u, 0u, 0u};
+      vr[i] = u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+}
+
+__device__ __forceinline__ void attn_partial_prefetch(const KArgs& a, const mk_instr& in, const mk_node& nd,
+                                                      AttnPrefetch& f) {
+  const int j0 = uni(in.r0), S = uni(nd.seq);
+  f.p = uni(*buf<const int>(a, nd.part));
+  const int pc = min(max(f.p, 0), S - 1);     // the table row stays in bounds for any p
+  const float* tab = buf<const float>(a, nd.aux) + (long)pc * kAttnD;   // [cos | sin] of position p
+  f.cs = tab[threadIdx.x & 63];
+  f.sn = tab[64 + (threadIdx.x & 63)];
+  attn_issue_kv(a, nd, uni(in.c0), j0, uni(in.r1) - j0, 0, f.kr, f.vr);
+}
+
+template <int DT, int G8>
+__device__ __forceinline__ void attn_partial_run(const KArgs& a, const mk_instr& in, const mk_node& nd, char* smem,
+                                                 AttnPrefetch& f) {
+  constexpr int D = kAttnD, HALF = 64, KPASS = kAttnPass, GR = kAttnGroups;
+  static_assert((8 * D + D + 8 * 256 + 32) * 4 + 256 * D * 2 <= kSmemBytes, "decode attention LDS");
   const int t = threadIdx.x, lane = t & 63, w = wave_id();
+  const int sub = lane >> 4, part = lane & 15;   // key within a group of four; dimensions 8 part .. 8 part + 7
   const int g = uni(in.c0), G = uni(in.c1), S = uni(nd.seq), Hq = uni(nd.heads);
-  const int p = uni(*buf<const int>(a, nd.part));
+  const int p = f.p;
   const int j0 = uni(in.r0), r1 = uni(in.r1);
   if (p < 0 || p >= S || j0 > p) return;   // empty chunk: the combine skips it
   const int j1 = min(r1, p + 1), nk = j1 - j0;
-  const bool own = p < r1;                  // this chunk holds key p
-  float* qs = reinterpret_cast<float*>(smem);        // [G][D] rotated q * scale * log2(e)
-  float* kn = qs + 8 * D;                            // [D] rotated k_new (rounded)
-  float* vv = kn + D;                                // [D] v_new
-  float* pc = vv + D;                                // [G][256] exp2 weights
-  float* red = pc + 8 * 256;                         // [4 waves][8] per-wave max / sum
-  const float* tab = buf<const float>(a, nd.aux) + (long)p * D;   // [cos | sin] of position p
+  const bool own = p < r1;                  // this chunk holds key p, at local index nk - 1
+  float* qs = reinterpret_cast<float*>(smem);        // [G8][D] rotated q * scale * log2(e)
+  u16* knb = reinterpret_cast<u16*>(qs + 8 * D);     // [D] rotated k_new, rounded; then [D] v_new
+  u16* vnb = knb + D;
+  float* sc = qs + 9 * D;                            // [G8][256] scores, then exp2 weights
+  float* red = sc + 8 * 256;                         // [4 waves][8] per-wave max / sum
+  u16* vs = reinterpret_cast<u16*>(red + 32);        // [256][D] V rows of the chunk
+  u32x4* kr = f.kr;
+  u32x4* vr = f.vr;
   const float c = nd.scale * 1.4426950408889634f;
+  const float cs = f.cs, sn = f.sn;         // pair i = t % 64 (kThreads is a multiple of 64)
   {
     const u16* Q = buf<const u16>(a, nd.a) + (long)g * G * D;
-    for (int u = t; u < G * HALF; u += kThreads) {
+    for (int u = t; u < G8 * HALF; u += kThreads) {
       const int h = u / HALF, i = u - h * HALF;
-      const float x1 = to_f<DT>(Q[h * D + i]), x2 = to_f<DT>(Q[h * D + i + HALF]);
-      const float cs = tab[i], sn = tab[HALF + i];
-      qs[h * D + i] = (x1 * cs - x2 * sn) * c;
-      qs[h * D + i + HALF] = (x2 * cs + x1 * sn) * c;
+      float y1 = 0.f, y2 = 0.f;               // heads G .. G8 - 1 score zero
+      if (h < G) {
+        const float x1 = to_f<DT>(Q[h * D + i]), x2 = to_f<DT>(Q[h * D + i + HALF]);
+        y1 = (x1 * cs - x2 * sn) * c;
+        y2 = (x2 * cs + x1 * sn) * c;
+      }
+      qs[h * D + i] = y1;
+      qs[h * D + i + HALF] = y2;
     }
     if (own && t < HALF) {
       const u16* Kn = buf<const u16>(a, nd.b) + (long)g * D;
       const u16* Vn = buf<const u16>(a, nd.res) + (long)g * D;
-      u16* Kc = buf<u16>(a, nd.bias) + (long)p * nd.bias.ld + (long)g * D;
-      u16* Vc = buf<u16>(a, nd.gamma) + (long)p * nd.gamma.ld + (long)g * D;
+      u16* Kw = buf<u16>(a, nd.bias) + (long)p * nd.bias.ld + (long)g * D;
+      u16* Vw = buf<u16>(a, nd.gamma) + (long)p * nd.gamma.ld + (long)g * D;
       const float x1 = to_f<DT>(Kn[t]), x2 = to_f<DT>(Kn[t + HALF]);
-      const float cs = tab[t], sn = tab[HALF + t];
       const u16 y1 = from_f<DT>(x1 * cs - x2 * sn), y2 = from_f<DT>(x2 * cs + x1 * sn);
-      Kc[t] = y1;
-      Kc[t + HALF] = y2;
-      kn[t] = to_f<DT>(y1);
-      kn[t + HALF] = to_f<DT>(y2);
+      Kw[t] = y1;
+      Kw[t + HALF] = y2;
+      knb[t] = y1;
+      knb[t + HALF] = y2;
       const u16 v1 = Vn[t], v2 = Vn[t + HALF];
-      Vc[t] = v1;
-      Vc[t + HALF] = v2;
-      vv[t] = to_f<DT>(v1);
-      vv[t + HALF] = to_f<DT>(v2);
+      Vw[t] = v1;
+      Vw[t + HALF] = v2;
+      vnb[t] = v1;
+      vnb[t + HALF] = v2;
     }
   }
   __syncthreads();
-  // scores: thread t holds key j0 + t
-  float sc[8];
+  float qr[G8][8];
 #pragma unroll
-  for (int h = 0; h < 8; ++h) sc[h] = -INFINITY;
-  const int j = j0 + t;
-  if (t < nk) {
+  for (int h = 0; h < G8; ++h)
 #pragma unroll
-    for (int h = 0; h < 8; ++h) sc[h] = 0.f;
-    if (j == p) {
-      for (int dd = 0; dd < D; ++dd) {
-        const float kx = kn[dd];
+    for (int e = 0; e < 8; ++e) qr[h][e] = qs[h * D + part * 8 + e];
+  // scores: the 16 lanes of a row sum their partial dot products with DPP
+  // (every lane of the row ends with the key's score and writes it: same
+  // address, same value).  Keys past the chunk's end score -inf and get a
+  // zero V row, so the softmax and P V below run without guards.  Key p
+  // takes the rotated k_new and v_new in place of the cache row loaded for
+  // it before the append.
+  const int npass = (nk + KPASS - 1) / KPASS, nk8 = (nk + 7) & ~7;
+  const int kp = nk - 1;
+  float mloc[G8];
 #pragma unroll
-        for (int h = 0; h < 8; ++h)
-          if (h < G) sc[h] = fmaf(qs[h * D + dd], kx, sc[h]);
+  for (int h = 0; h < G8; ++h) mloc[h] = -INFINITY;
+  for (int ps = 0; ps < npass; ++ps) {
+    if (ps > 0) attn_issue_kv(a, nd, g, j0, r1 - j0, ps, kr, vr);
+    if (own && kp / KPASS == ps && w == (kp % KPASS) / 32) {
+      const int ip = (kp % 32) / 4;
+      const bool mine = sub == kp % 4;
+      const u32x4 k4 = *reinterpret_cast<const u32x4*>(knb + part * 8);
+      const u32x4 v4 = *reinterpret_cast<const u32x4*>(vnb + part * 8);
+#pragma unroll
+      for (int i = 0; i < GR; ++i)
+        if (i == ip && mine) {
+          kr[i] = k4;
+          vr[i] = v4;
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < GR; ++i) {
+      const int kl = ps * KPASS + w * 32 + i * 4 + sub;   // < 2 KPASS = 256
+      const bool valid = kl < nk;
+      float kf[8];
+      unpack8<DT>(kr[i], kf);
+#pragma unroll
+      for (int h = 0; h < G8; ++h) {
+        float v = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v = fmaf(qr[h][e], kf[e], v);
+        v += dpp_f<0x140>(v);   // row mirror
+        v += dpp_f<0x141>(v);   // half-row mirror
+        v += dpp_f<0x4E>(v);    // lanes ^ 2
+        v += dpp_f<0xB1>(v);    // lanes ^ 1
+        v = valid ? v : -INFINITY;
+        mloc[h] = fmaxf(mloc[h], v);
+        sc[h * 256 + kl] = v;
       }
-    } else {
-      const u16* Kr = buf<const u16>(a, nd.bias) + (long)j * nd.bias.ld + (long)g * D;
-      u32x4 kr[D / 8];
-#pragma unroll
-      for (int q = 0; q < D / 8; ++q) kr[q] = *reinterpret_cast<const u32x4*>(Kr + q * 8);
-#pragma unroll
-      for (int q = 0; q < D / 8; ++q) {
-        float kf[8];
-        unpack8<DT>(kr[q], kf);
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-#pragma unroll
-          for (int h = 0; h < 8; ++h)
-            if (h < G) sc[h] = fmaf(qs[h * D + q * 8 + e], kf[e], sc[h]);
-      }
+      const u32x4 zero{0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4*>(vs + (long)kl * D + part * 8) = valid ? vr[i] : zero;
     }
   }
-  // per head: max over the chunk, then exp2 weights and their sum
-  float mx[8], ls[8];
+  // per head: max over the chunk (rows of a wave, then the four waves),
+  // then exp2 weights (zero past the chunk's keys) and their sum
+  float mx[G8], ls[G8];
 #pragma unroll
-  for (int h = 0; h < 8; ++h) {
-    float v = sc[h];
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  for (int h = 0; h < G8; ++h) {
+    float v = mloc[h];
+    v = fmaxf(v, __shfl_xor(v, 16, 64));
+    v = fmaxf(v, __shfl_xor(v, 32, 64));
     if (lane == 0) red[w * 8 + h] = v;
   }
   __syncthreads();
 #pragma unroll
-  for (int h = 0; h < 8; ++h) mx[h] = fmaxf(fmaxf(red[h], red[8 + h]), fmaxf(red[16 + h], red[24 + h]));
+  for (int h = 0; h < G8; ++h) mx[h] = fmaxf(fmaxf(red[h], red[8 + h]), fmaxf(red[16 + h], red[24 + h]));
   __syncthreads();
 #pragma unroll
-  for (int h = 0; h < 8; ++h) {
-    const float e = t < nk && h < G ? exp2f(sc[h] - mx[h]) : 0.f;
-    if (h < G) pc[h * 256 + t] = e;
-    const float v = wave_sum(e);
+  for (int h = 0; h < G8; ++h) {
+    const float e = t < nk ? exp2f(sc[h * 256 + t] - mx[h]) : 0.f;
+    sc[h * 256 + t] = e;
+    float v = e;
+    v += dpp_f<0x140>(v);
+    v += dpp_f<0x141>(v);
+    v += dpp_f<0x4E>(v);
+    v += dpp_f<0xB1>(v);
+    v += __shfl_xor(v, 16, 64);
+    v += __shfl_xor(v, 32, 64);
     if (lane == 0) red[w * 8 + h] = v;
   }
   __syncthreads();
 #pragma unroll
-  for (int h = 0; h < 8; ++h) ls[h] = (red[h] + red[8 + h]) + (red[16 + h] + red[24 + h]);
-  // P V: wave w takes heads w, w + 4; lane holds dimensions 2 lane, 2 lane + 1
+  for (int h = 0; h < G8; ++h) ls[h] = (red[h] + red[8 + h]) + (red[16 + h] + red[24 + h]);
+  // P V: item u = (head u / 64, dimensions 2 (u % 64), +1); eight keys per
+  // step, every LDS read of a step issued before its multiplies
   float* P = buf<float>(a, nd.out) + (long)in.coord[0] * Hq * (D + 4);
-  for (int h = w; h < G; h += 4) {
+  for (int u = t; u < G * 64; u += kThreads) {
+    const int h = u >> 6, dp = u & 63;
+    const float* eh = sc + h * 256;
+    const u16* vcol = vs + 2 * dp;
     float o0 = 0.f, o1 = 0.f;
-    const u16* Vr = buf<const u16>(a, nd.gamma) + (long)j0 * nd.gamma.ld + (long)g * D + 2 * lane;
-    const int nc = own ? nk - 1 : nk;     // cache rows (key p comes from vv)
-#pragma unroll 4
-    for (int k = 0; k < nc; ++k) {
-      const uint32_t v2 = *reinterpret_cast<const uint32_t*>(Vr + (long)k * nd.gamma.ld);
-      const float e = pc[h * 256 + k];
-      o0 = fmaf(e, to_f<DT>((u16)(v2 & 0xffff)), o0);
-      o1 = fmaf(e, to_f<DT>((u16)(v2 >> 16)), o1);
-    }
-    if (own) {
-      const float e = pc[h * 256 + nk - 1];
-      o0 = fmaf(e, vv[2 * lane], o0);
-      o1 = fmaf(e, vv[2 * lane + 1], o1);
+    for (int k = 0; k < nk8; k += 8) {
+      const float4 ea = *reinterpret_cast<const float4*>(eh + k);
+      const float4 eb = *reinterpret_cast<const float4*>(eh + k + 4);
+      uint32_t v2[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) v2[q] = *reinterpret_cast<const uint32_t*>(vcol + (long)(k + q) * D);
+      const float ev[8] = {ea.x, ea.y, ea.z, ea.w, eb.x, eb.y, eb.z, eb.w};
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        o0 = fmaf(ev[q], to_f<DT>((u16)(v2[q] & 0xffff)), o0);
+        o1 = fmaf(ev[q], to_f<DT>((u16)(v2[q] >> 16)), o1);
+      }
     }
     float hm = 0.f, hl = 0.f;
 #pragma unroll
-    for (int hh = 0; hh < 8; ++hh)
+    for (int hh = 0; hh < G8; ++hh)
       if (hh == h) { hm = mx[hh]; hl = ls[hh]; }
     float* dst = P + (long)(g * G + h) * (D + 4);
-    dst[2 * lane] = o0;
-    dst[2 * lane + 1] = o1;
-    if (lane == 0) {
+    dst[2 * dp] = o0;
+    dst[2 * dp + 1] = o1;
+    if (dp == 0) {
       dst[D] = hm;
       dst[D + 1] = hl;
     }
   }
 }
 
+// Query heads per kv head: up to 4, or up to 8 (heads past G score zero).
+template <int DT>
+__device__ __forceinline__ void attn_partial_dispatch(const KArgs& a, const mk_instr& in, const mk_node& nd,
+                                                      char* smem, AttnPrefetch& f) {
+  if (uni(in.c1) <= 4) attn_partial_run<DT, 4>(a, in, nd, smem, f);
+  else attn_partial_run<DT, 8>(a, in, nd, smem, f);
+}
+
+template <int DT>
+__device__ __forceinline__ void attn_partial_tile(const KArgs& a, const mk_instr& in, const mk_node& nd, char* smem) {
+  AttnPrefetch f;
+  attn_partial_prefetch(a, in, nd, f);
+  attn_partial_dispatch<DT>(a, in, nd, smem, f);
+}
+
 // Combine: for each query head of kv head g = c0, merge the chunks c <=
 // p / chunk (each holds at least key c * chunk <= p) by log-sum-exp:
-// M = max m_c, o = sum 2^(m_c - M) o_c / sum 2^(m_c - M) l_c.
+// M = max m_c, o = sum 2^(m_c - M) o_c / sum 2^(m_c - M) l_c.  A thread
+// holds two output elements of one head and requests the (o, m, l) of 32
+// chunks at once; more chunks are merged 32 at a time with a running max.
 template <int DT>
 __device__ __forceinline__ void attn_combine_tile(const KArgs& a, const mk_instr& in, const mk_node& nd) {
-  constexpr int D = 128, W = D + 4;
+  constexpr int D = 128, W = D + 4, B = 32;
   const int t = threadIdx.x;
   const int g = uni(in.c0), G = uni(in.c1), S = uni(nd.seq), Hq = uni(nd.heads), C = uni(nd.K);
   const int p = uni(*buf<const int>(a, nd.part));
@@ -1697,20 +1801,41 @@ __device__ __forceinline__ void attn_combine_tile(const KArgs& a, const mk_instr
     return;
   }
   const int nc = p / C + 1;
-  const float* P = buf<const float>(a, nd.a);
-  for (int u = t; u < G * D; u += kThreads) {
-    const int h = u / D, dd = u - h * D;
-    const float* ph = P + (long)(g * G + h) * W;
-    float M = -INFINITY;
-    for (int k = 0; k < nc; ++k) M = fmaxf(M, ph[(long)k * Hq * W + D]);
-    float num = 0.f, den = 0.f;
-    for (int k = 0; k < nc; ++k) {
-      const float* pk = ph + (long)k * Hq * W;
-      const float sc = exp2f(pk[D] - M);
-      num = fmaf(sc, pk[dd], num);
-      den = fmaf(sc, pk[D + 1], den);
+  const long cst = (long)Hq * W;                                   // floats from one chunk to the next
+  for (int u = t; u < G * (D / 2); u += kThreads) {
+    const int h = u / (D / 2), dp = u - h * (D / 2);
+    const float* ph = buf<const float>(a, nd.a) + (long)(g * G + h) * W;
+    float M = -INFINITY, den = 0.f, n0 = 0.f, n1 = 0.f;
+    for (int c0 = 0; c0 < nc; c0 += B) {
+      float2 o[B], ml[B];
+#pragma unroll
+      for (int q = 0; q < B; ++q) {
+        const long off = (long)min(c0 + q, nc - 1) * cst;         // past nc: a repeat, weighted zero
+        o[q] = *reinterpret_cast<const float2*>(ph + off + 2 * dp);
+        ml[q] = *reinterpret_cast<const float2*>(ph + off + D);
+      }
+      float Mb = M;
+#pragma unroll
+      for (int q = 0; q < B; ++q) {
+        if (c0 + q >= nc) ml[q].x = -INFINITY;
+        Mb = fmaxf(Mb, ml[q].x);
+      }
+      const float r = exp2f(M - Mb);       // 0 for the first batch
+      den *= r;
+      n0 *= r;
+      n1 *= r;
+#pragma unroll
+      for (int q = 0; q < B; ++q) {
+        const float e = exp2f(ml[q].x - Mb);
+        den = fmaf(e, ml[q].y, den);
+        n0 = fmaf(e, o[q].x, n0);
+        n1 = fmaf(e, o[q].y, n1);
+      }
+      M = Mb;
     }
-    O[u] = from_f<DT>(num / den);
+    const float inv = 1.f / den;
+    O[h * D + 2 * dp] = from_f<DT>(n0 * inv);
+    O[h * D + 2 * dp + 1] = from_f<DT>(n1 * inv);
   }
 }
 
@@ -2059,6 +2184,23 @@ __device__ __forceinline__ bool generic_iter(const Loop& L, int it, int& w) {
   const bool tr = a.trace && threadIdx.x == 0 && in.opcode != MK_I_NOOP;
   if (tr) stamp(a, gidx, 0, wall_clock64());
   int tk = -1;
+  if constexpr ((OPS & kOpOther) != 0) {
+    if (in.opcode == MK_I_ATTN_PARTIAL) {
+      // the KV cache rows are requested before the counters clear
+      const mk_node& nd = L.nodes[in.node];
+      AttnPrefetch f;
+      attn_partial_prefetch(a, in, nd, f);
+      if (!wait_sources(L, in, it, gidx, w, tk)) return false;
+      if (tr) stamp(a, gidx, 1, wall_clock64());
+      if (nd.dtype == MK_BF16) attn_partial_dispatch<MK_BF16>(a, in, nd, L.smem, f);
+      else attn_partial_dispatch<MK_F16>(a, in, nd, L.smem, f);
+      if (tr) stamp(a, gidx, 2, wall_clock64());
+      release_dests(a, in);
+      if (tr) stamp(a, gidx, 3, wall_clock64());
+      store_ahead(L, it, w, tk);
+      return true;
+    }
+  }
   if (!wait_sources(L, in, it, gidx, w, tk)) return false;
   if (in.opcode != MK_I_NOOP) {
     const mk_node& nd = L.nodes[in.node];

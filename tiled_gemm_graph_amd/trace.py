@@ -86,6 +86,33 @@ def summarize(plan, tr: np.ndarray, khz: int = 100000) -> Dict:
     return dict(span_us=span, nodes=nodes, body_util=float(busy.mean() / span) if span else 0.0)
 
 
+def node_table(plan, tr: np.ndarray, khz: int = 100000) -> str:
+    """Markdown table of one traced forward, a row per lowered node: its
+    instruction count, when its first instruction started and its last one
+    released (us from the first stamp), and the median / 90th percentile of
+    the counter wait, the tile body and the release."""
+    w = plan.instructions()
+    us = 1000.0 / khz
+    live = tr[:, 0] > 0
+    t0 = tr[live, 0].min()
+    rows = ["| node | op | instrs | first start | last release | wait p50 / p90 | "
+            "body p50 / p90 / max | release p50 |",
+            "|---|---|---|---|---|---|---|---|"]
+    for nd in sorted({int(x) for x in w[live, L.W_NODE]}):
+        sel = live & (w[:, L.W_NODE] == nd)
+        st = tr[sel]
+        wait = (st[:, 1] - st[:, 0]) * us
+        body = (st[:, 2] - st[:, 1]) * us
+        rel = (st[:, 3] - st[:, 2]) * us
+        op = OPCODE_NAMES[int(w[sel, L.W_OPCODE][0])]
+        rows.append(
+            f"| {nd} | {op} | {int(sel.sum())} | {(st[:, 0].min() - t0) * us:.1f} | "
+            f"{(st[:, 3].max() - t0) * us:.1f} | {np.percentile(wait, 50):.2f} / "
+            f"{np.percentile(wait, 90):.2f} | {np.percentile(body, 50):.2f} / "
+            f"{np.percentile(body, 90):.2f} / {body.max():.2f} | {np.percentile(rel, 50):.2f} |")
+    return "\n".join(rows)
+
+
 def to_perfetto(plan, tr: np.ndarray, path: str, khz: int = 100000) -> None:
     w = plan.instructions()
     us = 1000.0 / khz
