@@ -11,11 +11,17 @@ the MI355X roofline, the same graph launched one op at a time, the same
 plan on the work queue, parity against the CPU oracle (full outputs) and
 the oracle timed on the host.  ``--workload NAME`` prints one line for one
 graph, ``--all`` one line per graph.
+
+Each graph first runs forwards for WARM_SECONDS (the clock ramps up after
+the idle spells of input generation and the oracle), then W untimed and K
+timed forwards give the headline value.  The per-op comparison alternates
+blocks of K forwards (megakernel, per-op, ...) and compares medians.
 """
 import argparse
 import json
 import math
 import os
+import statistics
 import sys
 import time
 
@@ -25,6 +31,8 @@ sys.path.insert(0, ROOT)
 METRIC = "µs/forward + TFLOP/s (% MFMA peak) or GB/s (% HBM) per graph, 1 MI355X"
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 PEAK_MFMA_TFLOPS = 2500.0   # MI355X dense fp16/bf16 MFMA
+WARM_SECONDS = 1.0          # forwards run before the timed blocks of each graph
+AB_ROUNDS = 3               # per-op blocks (and megakernel blocks) in the interleaved comparison
 
 DESCR = {
     "mlp3": "3-layer MLP x=relu(x@W[i]+b[i]), x 1024x1024, fp16",
@@ -83,6 +91,23 @@ def measured_traffic(workload):
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def warm_up(fn, seconds):
+    """Run ``fn`` until ``seconds`` of wall time have passed.  The GPU's
+    clock ramps up over tens to hundreds of milliseconds after an idle
+    spell (input generation, the CPU oracle), and a timed block that starts
+    cold reads several percent slow."""
+    import torch
+    t0 = time.time()
+    n = 0
+    while True:
+        fn()
+        n += 1
+        if n % 4 == 0:
+            torch.cuda.synchronize()
+            if time.time() - t0 >= seconds:
+                return n
 
 
 def time_forwards(fn, steps, warmup):
@@ -186,13 +211,25 @@ def bench_graph(workload, steps, warmup, cpu_budget, do_check=True, sync="tiles"
         log(f"[bench] {workload}: oracle on the whole output")
         res.update(parity(r.out.float().cpu().numpy(), OG.run(workload, inp, dims)))
         log(f"[bench] {workload} parity: rel {res['rel_err']:.3e} max-abs {res['max_abs_err']:.3e}")
+    warm_up(r.forward, WARM_SECONDS)
     ms = time_forwards(r.forward, steps, warmup)
     r.plan.check()
-    ms_op = time_forwards(r.forward_per_op, steps, warmup)
+    # megakernel against the per-op launches of the same plan: blocks of
+    # `steps` forwards in alternation (M P M P M P), medians of each, so
+    # that neither side gets the clock's ramp or drift to itself
+    mk_blocks, op_blocks = [ms], []
+    for k in range(AB_ROUNDS):
+        op_blocks.append(time_forwards(r.forward_per_op, steps, warmup))
+        if k < AB_ROUNDS - 1:
+            mk_blocks.append(time_forwards(r.forward, steps, warmup))
+    r.plan.check()
+    ms_op = statistics.median(op_blocks)
     res["us"] = ms * 1e3
     res["ms_per_step"] = ms
     res["per_op_us"] = ms_op * 1e3
-    res["speedup_vs_per_op"] = ms_op / ms
+    res["speedup_vs_per_op"] = ms_op / statistics.median(mk_blocks)
+    res["ab_blocks_us"] = {"megakernel": [round(x * 1e3, 1) for x in mk_blocks],
+                           "per_op": [round(x * 1e3, 1) for x in op_blocks]}
     if queue_ab and sync == "tiles":
         for q, key in ((1, "queue_us"), (2, "xcd_queue_us")):
             qp = r.alt_plan(queue=q)
@@ -209,7 +246,8 @@ def bench_graph(workload, steps, warmup, cpu_budget, do_check=True, sync="tiles"
     res["tflops"] = st.flops / (res["us"] * 1e-6) / 1e12
     # the counter summaries are taken on the per-tile-counter plans
     res["roofline"] = roofline(workload, st, res["us"], measured_traffic(workload) if sync == "tiles" else None)
-    log(f"[bench] {workload}: {res['us']:.1f} us/forward, per-op {res['per_op_us']:.1f}"
+    log(f"[bench] {workload}: {res['us']:.1f} us/forward, per-op {res['per_op_us']:.1f}, "
+        f"megakernel/per-op blocks {res['ab_blocks_us']['megakernel']} / {res['ab_blocks_us']['per_op']}"
         + (f", queue {res['queue_us']:.1f}, per-XCD queues {res['xcd_queue_us']:.1f}" if "queue_us" in res else ""))
     if cpu_budget > 0:
         log(f"[bench] {workload}: timing the CPU oracle (~{cpu_budget:.0f} s)")
@@ -242,7 +280,7 @@ def line_for(head, steps, warmup, graphs=None):
         "roofline": head["roofline"],
         "cpu_baseline": head["cpu_baseline"],
     }
-    for k in ("per_op_us", "speedup_vs_per_op", "queue_us", "xcd_queue_us", "rel_err", "max_abs_err", "max_abs_at",
+    for k in ("per_op_us", "speedup_vs_per_op", "ab_blocks_us", "queue_us", "xcd_queue_us", "rel_err", "max_abs_err", "max_abs_at",
               "gbps", "tflops", "alg_bytes", "alg_flops", "core_clock_mhz"):
         if k in head:
             line[k] = head[k]

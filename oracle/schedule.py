@@ -727,17 +727,18 @@ def decode_graph(d: Dict[str, int], tiles: Sequence[Dict[str, int]]) -> Graph:
 
 def layer_graph(d: Dict[str, int], tiles: Sequence[Dict[str, int]]) -> Graph:
     """Llama-style decoder layer prefill (bf16): rmsnorm; the QKV projection
-    as two GEMMs over column ranges of Wqkv (Q, and KV) with the rotary
-    epilogue on q and k; causal GQA attention; O GEMM + residual; rmsnorm;
-    gate_up GEMM with SiLU-mul; down GEMM + residual.  ``tiles`` is in op
-    order (8 entries)."""
+    as two GEMMs, over Wq and Wkv (the column blocks [Q] and [K | V] of
+    Wqkv, held as two weights), with the rotary epilogue on q and k; causal
+    GQA attention; O GEMM + residual; rmsnorm; gate_up GEMM with SiLU-mul;
+    down GEMM + residual.  ``tiles`` is in op order (8 entries)."""
     g = Graph()
     S, H = d["seq"], d["hidden"]
     Hq, Hkv, hd, I = d["heads"], d["kv_heads"], d["head_dim"], d["inter"]
     nq, nkv = Hq * hd, Hkv * hd
     x = g.tensor("x", "bf16", (S, H), "input")
     g1 = g.tensor("g1", "bf16", (H,), "weight")
-    Wqkv = g.tensor("Wqkv", "bf16", (H, nq + 2 * nkv), "weight")
+    Wq = g.tensor("Wq", "bf16", (H, nq), "weight")
+    Wkv = g.tensor("Wkv", "bf16", (H, 2 * nkv), "weight")
     Wo = g.tensor("Wo", "bf16", (nq, H), "weight")
     g2 = g.tensor("g2", "bf16", (H,), "weight")
     Wgu = g.tensor("Wgu", "bf16", (H, 2 * I), "weight")
@@ -752,10 +753,8 @@ def layer_graph(d: Dict[str, int], tiles: Sequence[Dict[str, int]]) -> Graph:
     out = g.tensor("out", "bf16", (S, H), "output")
     att = dict(heads=Hq, kv_heads=Hkv, head_dim=hd, causal=1)
     g.ops.append(Op("rmsnorm", dict(x=g.full(x), gamma=g.full(g1)), xn, 0, dict(tiles[0])))
-    g.ops.append(Op("gemm", dict(a=g.full(xn), b=g.cols(Wqkv, 0, nq)), q, ROPE,
-                    dict(tiles[1]), dict(att)))
-    g.ops.append(Op("gemm", dict(a=g.full(xn), b=g.cols(Wqkv, nq, nq + 2 * nkv)), kv, ROPE,
-                    dict(tiles[2]), dict(att)))
+    g.ops.append(Op("gemm", dict(a=g.full(xn), b=g.full(Wq)), q, ROPE, dict(tiles[1]), dict(att)))
+    g.ops.append(Op("gemm", dict(a=g.full(xn), b=g.full(Wkv)), kv, ROPE, dict(tiles[2]), dict(att)))
     g.ops.append(Op("attention", dict(q=g.full(q), k=g.cols(kv, 0, nkv),
                                       v=g.cols(kv, nkv, 2 * nkv)),
                     o, 0, dict(tiles[3]), dict(att)))

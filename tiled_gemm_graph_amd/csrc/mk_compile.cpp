@@ -252,8 +252,13 @@ struct Compiler {
       t.bm = bbm;
       t.bn = silu ? bbn / 2 : bbn;   // tile.bn counts output columns
       t.split = bs;
-      if (t.rbm <= 0) t.rbm = t.bm;
-      if (t.rbn <= 0) t.rbn = t.bn;
+      // REDUCE tiles of at most 16384 fp32 sums (64 KB of LDS), so that
+      // the eight-wave REDUCE body fits beside its per-thread partials
+      if (t.rbm <= 0) t.rbm = std::min(t.bm, 128);
+      if (t.rbn <= 0) {
+        const int cap = 16384 / (t.rbm * (silu ? 2 : 1));
+        t.rbn = std::max(8, std::min(t.bn, cap / 8 * 8));
+      }
       return t;
     }
     if (t.bm <= 0 || t.bn <= 0) {
@@ -392,6 +397,11 @@ struct Compiler {
       if (silu) fail(MK_E_INVALID, "ROPE and SILU_MUL cannot be combined");
     }
     if (gemv && !packed && S == 1 && (fl & MK_EP_ROPE)) unsup("ROPE on the row-major GEMV body needs a split");
+    // The REDUCE body keeps its tile's fp32 sums in the 144 KB LDS arena
+    // beside 320 floats of row scales and 8 floats per thread (256 threads).
+    // (and a row scale for each of at most 256 rows)
+    if (S > 1 && ((320 + 256 * 8 + (I64)t.rbm * t.rbn * (silu ? 2 : 1)) * 4 > 144 * 1024 || t.rbm > 256))
+      unsup("REDUCE tile (rbm x rbn, twice the columns under SILU_MUL) exceeds the LDS arena");
     int pt = -1;
     if (S > 1) pt = add_internal(MK_F32, {1, S, M, Nb});
     int rope_t = -1;

@@ -138,14 +138,19 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-// Sum over the workgroup; `red` holds at least 4 floats of LDS.
+// Sum over a workgroup of NT threads; `red` holds at least NT / 64 floats
+// of LDS.  The wave sums are added in wave order.
+template <int NT = kThreads>
 __device__ __forceinline__ float block_sum(float v, float* red) {
   v = wave_sum(v);
   const int w = threadIdx.x >> 6;
   __syncthreads();
   if ((threadIdx.x & 63) == 0) red[w] = v;
   __syncthreads();
-  return red[0] + red[1] + red[2] + red[3];
+  float s = red[0];
+#pragma unroll
+  for (int i = 1; i < NT / 64; ++i) s += red[i];
+  return s;
 }
 
 // Barrier that orders LDS traffic only (global loads stay in flight).
@@ -1205,7 +1210,7 @@ __device__ __forceinline__ int gemv_body_rows(const KArgs& a, const mk_instr& in
 }
 
 // ---------------------------------------------------------------- REDUCE
-template <int DT>
+template <int DT, int NT = kThreads>
 __device__ __forceinline__ void reduce_tile(const KArgs& a, const mk_instr& in, const mk_node& nd, char* smem) {
   const int t = threadIdx.x;
   const int flags = in.flags;
@@ -1218,18 +1223,18 @@ __device__ __forceinline__ void reduce_tile(const KArgs& a, const mk_instr& in, 
   float* rinv = reinterpret_cast<float*>(smem);   // [rows]
   float* scratch = rinv + 256;
   float* psum = scratch + 64;                       // [threads][8]
-  float* sum = psum + kThreads * 8;                 // [rows][wc]
+  float* sum = psum + NT * 8;                 // [rows][wc]
   if (rms) {
     const u16* X = buf<const u16>(a, nd.a);
     for (int m = 0; m < rows; ++m) {
       float s = 0.f;
-      for (int k = t * 8; k < K; k += kThreads * 8) {
+      for (int k = t * 8; k < K; k += NT * 8) {
         float f[8];
         unpack8<DT>(*reinterpret_cast<const u32x4*>(X + (long)(r0 + m) * nd.a.ld + k), f);
 #pragma unroll
         for (int e = 0; e < 8; ++e) s += f[e] * f[e];
       }
-      s = block_sum(s, scratch);
+      s = block_sum<NT>(s, scratch);
       if (t == 0) rinv[m] = 1.0f / sqrtf(s / (float)K + nd.eps);
     }
   }
@@ -1239,8 +1244,8 @@ __device__ __forceinline__ void reduce_tile(const KArgs& a, const mk_instr& in, 
   // planes sub, sub + tpu, ... in order; the tpu sums are then added in
   // thread order, so the result is the same on every run.
   int tpu = 1;
-  while (tpu * 2 * units <= kThreads && tpu * 2 <= S) tpu *= 2;
-  for (int u0 = 0; u0 < units; u0 += kThreads / tpu) {
+  while (tpu * 2 * units <= NT && tpu * 2 <= S) tpu *= 2;
+  for (int u0 = 0; u0 < units; u0 += NT / tpu) {
     const int u = u0 + t / tpu, sub = t % tpu;
     float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     if (u < units) {
@@ -1283,7 +1288,7 @@ __device__ __forceinline__ void reduce_tile(const KArgs& a, const mk_instr& in, 
     __syncthreads();
   }
   const int ounits = rows * (bw / 8);
-  for (int u = t; u < ounits; u += kThreads) {
+  for (int u = t; u < ounits; u += NT) {
     const int m = u / (bw / 8), w = (u % (bw / 8)) * 8;
     const float sc = rms ? rinv[m] : 1.0f;
     epilogue8<DT>(a, nd, flags, r0 + m, c0 + w, w, bw, [&](int ww, float* o) {
@@ -1299,18 +1304,19 @@ __device__ __forceinline__ void reduce_tile(const KArgs& a, const mk_instr& in, 
 // rows are in flight together, each wave adds up the squares of every row,
 // and one barrier exchanges the wave sums, so a group costs one memory
 // round trip instead of two per row.
-template <int DT, int CPT>
+template <int DT, int CPT, int NT = kThreads>
 __device__ __forceinline__ void rmsnorm_rows(const KArgs& a, const mk_instr& in, const mk_node& nd, char* smem) {
   constexpr int RMAX = 16 / CPT;                // rows per group
   const int t = threadIdx.x, H = nd.N, w = wave_id();
-  float* part = reinterpret_cast<float*>(smem);  // [4 waves][RMAX] sums of squares
+  constexpr int NW = NT / 64;
+  float* part = reinterpret_cast<float*>(smem);  // [NW waves][RMAX] sums of squares
   const u16* X = buf<const u16>(a, nd.a);
   const u16* G = buf<const u16>(a, nd.gamma);
   u16* O = buf<u16>(a, nd.out);
   u32x4 gv[CPT];
 #pragma unroll
   for (int c = 0; c < CPT; ++c) {
-    const int k = (t + c * kThreads) * 8;
+    const int k = (t + c * NT) * 8;
     if (k < H) gv[c] = *reinterpret_cast<const u32x4*>(G + k);
   }
   for (int g0 = in.r0; g0 < in.r1; g0 += RMAX) {
@@ -1320,7 +1326,7 @@ __device__ __forceinline__ void rmsnorm_rows(const KArgs& a, const mk_instr& in,
     for (int rr = 0; rr < RMAX; ++rr)
 #pragma unroll
       for (int c = 0; c < CPT; ++c) {
-        const int k = (t + c * kThreads) * 8;
+        const int k = (t + c * NT) * 8;
         if (rr < nr && k < H) xv[rr][c] = *reinterpret_cast<const u32x4*>(X + (long)(g0 + rr) * nd.a.ld + k);
       }
 #pragma unroll
@@ -1329,7 +1335,7 @@ __device__ __forceinline__ void rmsnorm_rows(const KArgs& a, const mk_instr& in,
       if (rr < nr) {
 #pragma unroll
         for (int c = 0; c < CPT; ++c) {
-          const int k = (t + c * kThreads) * 8;
+          const int k = (t + c * NT) * 8;
           if (k < H) {
             float f[8];
             unpack8<DT>(xv[rr][c], f);
@@ -1345,11 +1351,18 @@ __device__ __forceinline__ void rmsnorm_rows(const KArgs& a, const mk_instr& in,
 #pragma unroll
     for (int rr = 0; rr < RMAX; ++rr) {
       if (rr >= nr) continue;
-      const float tot = (part[rr] + part[RMAX + rr]) + (part[2 * RMAX + rr] + part[3 * RMAX + rr]);
+      float tot;
+      if constexpr (NW == 4) {
+        tot = (part[rr] + part[RMAX + rr]) + (part[2 * RMAX + rr] + part[3 * RMAX + rr]);
+      } else {
+        tot = part[rr];
+#pragma unroll
+        for (int i = 1; i < NW; ++i) tot += part[i * RMAX + rr];
+      }
       const float rinv = 1.0f / sqrtf(tot / (float)H + nd.eps);
 #pragma unroll
       for (int c = 0; c < CPT; ++c) {
-        const int k = (t + c * kThreads) * 8;
+        const int k = (t + c * NT) * 8;
         if (k < H) {
           float f[8], gm[8];
           unpack8<DT>(xv[rr][c], f);
@@ -1364,14 +1377,14 @@ __device__ __forceinline__ void rmsnorm_rows(const KArgs& a, const mk_instr& in,
   }
 }
 
-template <int DT>
+template <int DT, int NT = kThreads>
 __device__ __forceinline__ void rmsnorm_tile(const KArgs& a, const mk_instr& in, const mk_node& nd, char* smem) {
   const int t = threadIdx.x;
   const int H = nd.N;
-  const int cpt = (H / 8 + kThreads - 1) / kThreads;   // 16-byte chunks per thread and row
-  if (cpt <= 1) return rmsnorm_rows<DT, 1>(a, in, nd, smem);
-  if (cpt <= 2) return rmsnorm_rows<DT, 2>(a, in, nd, smem);
-  if (cpt <= 4) return rmsnorm_rows<DT, 4>(a, in, nd, smem);
+  const int cpt = (H / 8 + NT - 1) / NT;   // 16-byte chunks per thread and row
+  if (cpt <= 1) return rmsnorm_rows<DT, 1, NT>(a, in, nd, smem);
+  if (cpt <= 2) return rmsnorm_rows<DT, 2, NT>(a, in, nd, smem);
+  if (cpt <= 4) return rmsnorm_rows<DT, 4, NT>(a, in, nd, smem);
   // wider rows: one row at a time, streamed
   float* scratch = reinterpret_cast<float*>(smem);
   const u16* X = buf<const u16>(a, nd.a);
@@ -1379,15 +1392,15 @@ __device__ __forceinline__ void rmsnorm_tile(const KArgs& a, const mk_instr& in,
   u16* O = buf<u16>(a, nd.out);
   for (int r = in.r0; r < in.r1; ++r) {
     float s = 0.f;
-    for (int k = t * 8; k < H; k += kThreads * 8) {
+    for (int k = t * 8; k < H; k += NT * 8) {
       float f[8];
       unpack8<DT>(*reinterpret_cast<const u32x4*>(X + (long)r * nd.a.ld + k), f);
 #pragma unroll
       for (int e = 0; e < 8; ++e) s += f[e] * f[e];
     }
-    s = block_sum(s, scratch);
+    s = block_sum<NT>(s, scratch);
     const float rinv = 1.0f / sqrtf(s / (float)H + nd.eps);
-    for (int k = t * 8; k < H; k += kThreads * 8) {
+    for (int k = t * 8; k < H; k += NT * 8) {
       float f[8], g[8];
       unpack8<DT>(*reinterpret_cast<const u32x4*>(X + (long)r * nd.a.ld + k), f);
       unpack8<DT>(*reinterpret_cast<const u32x4*>(G + k), g);
@@ -1403,14 +1416,22 @@ __device__ __forceinline__ void rmsnorm_tile(const KArgs& a, const mk_instr& in,
 // query head h = c0 (kv head c1), keys [0, k1).  Each wave owns 32 queries.
 // S^T = K Q^T is computed so that each lane holds one query's scores, which
 // then feed the P V product as the B operand straight from registers.
-template <int DT>
+// With NT = 512 the two halves of the workgroup (waves 0-3 and 4-7, two
+// waves per SIMD) take alternate 64-key blocks, each half with its own
+// staging area and running max and sum, and merge their (o, m, l) through
+// LDS at the end (the log-sum-exp merge of two key ranges).
+template <int DT, int NT = kThreads>
 __device__ __forceinline__ void attention_tile(const KArgs& a, const mk_instr& in, const mk_node& nd, char* smem) {
-  constexpr int D = 128, KBLK = 64;
+  constexpr int D = 128, KBLK = 64, NH = NT / 256;
   constexpr int KS = D + kLdsPad;      // K tile row: 136 elements
   constexpr int VS = KBLK + kLdsPad;   // V^T tile row: 72 elements
-  u16* Ks = reinterpret_cast<u16*>(smem);            // [64][136]
-  u16* Vt = Ks + KBLK * KS;                           // [128][72]
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6, g = lane >> 5, l32 = lane & 31;
+  constexpr int HALF_ELEMS = KBLK * KS + D * VS;
+  static_assert(NH * HALF_ELEMS * 2 <= kSmemBytes && (4 * 64 * 64 + 2 * 4 * 64) * 4 <= kSmemBytes,
+                "attention LDS");
+  const int t = threadIdx.x, lane = t & 63, wave = (t >> 6) & 3, hh = t >> 8, g = lane >> 5, l32 = lane & 31;
+  const int t4 = t & 255;
+  u16* Ks = reinterpret_cast<u16*>(smem) + hh * HALF_ELEMS;   // [64][136]
+  u16* Vt = Ks + KBLK * KS;                                    // [128][72]
   const int S = nd.seq, h = in.c0, kh = in.c1;
   const int q0 = in.r0, q1 = in.r1, kend = in.k1;
   const bool causal = nd.causal;
@@ -1433,17 +1454,19 @@ __device__ __forceinline__ void attention_tile(const KArgs& a, const mk_instr& i
     for (int e = 0; e < 16; ++e) o[db][e] = 0.f;
   float mrun = -INFINITY, lsum = 0.f;
 
-  for (int kb0 = 0; kb0 < kend; kb0 += KBLK) {
+  for (int kbp = 0; kbp < kend; kbp += NH * KBLK) {
+    const int kb0 = kbp + hh * KBLK;   // this half's key block
+    const bool live = kb0 < kend;      // uniform per wave
     __syncthreads();
-    // stage K [64][128] and V^T [128][64]
+    if (live) {
+      // stage K [64][128] and V^T [128][64]
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int cidx = t + kThreads * i, key = cidx >> 4, dc = (cidx & 15) * 8;
-      const int gk = min(kb0 + key, S - 1);
-      *reinterpret_cast<u32x4*>(Ks + key * KS + dc) = *reinterpret_cast<const u32x4*>(Kp + (long)gk * ldk + dc);
-    }
-    {
-      const int dblk = t & 15, kq = t >> 4;  // 8 d x 4 keys per thread
+      for (int i = 0; i < 4; ++i) {
+        const int cidx = t4 + 256 * i, key = cidx >> 4, dc = (cidx & 15) * 8;
+        const int gk = min(kb0 + key, S - 1);
+        *reinterpret_cast<u32x4*>(Ks + key * KS + dc) = *reinterpret_cast<const u32x4*>(Kp + (long)gk * ldk + dc);
+      }
+      const int dblk = t4 & 15, kq = t4 >> 4;  // 8 d x 4 keys per thread
       u32x4 v[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -1455,6 +1478,7 @@ __device__ __forceinline__ void attention_tile(const KArgs& a, const mk_instr& i
         *reinterpret_cast<u32x2*>(Vt + (dblk * 8 + n) * VS + kq * 4) = u32x2{pick2(v[0], v[1], n), pick2(v[2], v[3], n)};
     }
     __syncthreads();
+    if (!live) continue;
     // S^T for 64 keys x 32 queries: two 32-key blocks
     f32x16 sacc[2];
 #pragma unroll
@@ -1517,22 +1541,52 @@ __device__ __forceinline__ void attention_tile(const KArgs& a, const mk_instr& i
     }
   }
   lsum += __shfl_xor(lsum, 32, 64);
+  if constexpr (NH == 2) {
+    // the second half hands its (o, m, l) to the first: o' = o0 2^(m0 - M)
+    // + o1 2^(m1 - M), l' likewise, M = max(m0, m1)
+    __syncthreads();
+    float* xo = reinterpret_cast<float*>(smem);   // [4 waves][64 values][64 lanes]
+    float* xm = xo + 4 * 64 * 64;                 // [4 waves][64 lanes]
+    float* xl = xm + 4 * 64;
+    if (hh == 1) {
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) xo[(wave * 64 + db * 16 + e) * 64 + lane] = o[db][e];
+      xm[wave * 64 + lane] = mrun;
+      xl[wave * 64 + lane] = lsum;
+    }
+    __syncthreads();
+    if (hh == 0) {
+      const float m1 = xm[wave * 64 + lane], l1 = xl[wave * 64 + lane];
+      const float mm = fmaxf(mrun, m1);
+      const float mu = mm == -INFINITY ? 0.f : mm;
+      const float a0 = exp2f(mrun - mu), a1 = exp2f(m1 - mu);
+      lsum = lsum * a0 + l1 * a1;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) o[db][e] = o[db][e] * a0 + xo[(wave * 64 + db * 16 + e) * 64 + lane] * a1;
+    }
+  }
   const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
   // O^T (d rows x 32 queries per wave) -> LDS [128 q][136] -> coalesced stores
   __syncthreads();
   u16* Os = reinterpret_cast<u16*>(smem);
+  if (hh == 0) {
 #pragma unroll
-  for (int db = 0; db < 4; ++db)
+    for (int db = 0; db < 4; ++db)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int d = db * 32 + 8 * j + 4 * g;
-      const uint32_t w0 = (uint32_t)from_f<DT>(o[db][4 * j] * inv) | ((uint32_t)from_f<DT>(o[db][4 * j + 1] * inv) << 16);
-      const uint32_t w1 = (uint32_t)from_f<DT>(o[db][4 * j + 2] * inv) | ((uint32_t)from_f<DT>(o[db][4 * j + 3] * inv) << 16);
-      *reinterpret_cast<u32x2*>(Os + (wave * 32 + l32) * KS + d) = u32x2{w0, w1};
-    }
+      for (int j = 0; j < 4; ++j) {
+        const int d = db * 32 + 8 * j + 4 * g;
+        const uint32_t w0 = (uint32_t)from_f<DT>(o[db][4 * j] * inv) | ((uint32_t)from_f<DT>(o[db][4 * j + 1] * inv) << 16);
+        const uint32_t w1 = (uint32_t)from_f<DT>(o[db][4 * j + 2] * inv) | ((uint32_t)from_f<DT>(o[db][4 * j + 3] * inv) << 16);
+        *reinterpret_cast<u32x2*>(Os + (wave * 32 + l32) * KS + d) = u32x2{w0, w1};
+      }
+  }
   __syncthreads();
   u16* O = buf<u16>(a, nd.out) + h * D;
-  for (int i = t; i < 128 * 16; i += kThreads) {
+  for (int i = t; i < 128 * 16; i += NT) {
     const int r = i >> 4, dc = (i & 15) * 8;
     if (q0 + r >= q1) continue;
     *reinterpret_cast<u32x4*>(O + (long)(q0 + r) * nd.out.ld + dc) = *reinterpret_cast<const u32x4*>(Os + r * KS + dc);
@@ -1840,7 +1894,7 @@ __device__ __forceinline__ void attn_combine_tile(const KArgs& a, const mk_instr
 }
 
 // ----------------------------------------------------------- elementwise
-template <int DT>
+template <int DT, int NT = kThreads>
 __device__ __forceinline__ void elementwise_tile(const KArgs& a, const mk_instr& in, const mk_node& nd) {
   const int t = threadIdx.x;
   const bool add = in.opcode == MK_I_EW_ADD;
@@ -1848,7 +1902,7 @@ __device__ __forceinline__ void elementwise_tile(const KArgs& a, const mk_instr&
   const u16* A = buf<const u16>(a, nd.a);
   const u16* B = add ? buf<const u16>(a, nd.b) : nullptr;
   u16* O = buf<u16>(a, nd.out);
-  for (int u = t; u < units; u += kThreads) {
+  for (int u = t; u < units; u += NT) {
     const int r = in.r0 + u / (wcols / 8), c = in.c0 + (u % (wcols / 8)) * 8;
     float x[8];
     unpack8<DT>(*reinterpret_cast<const u32x4*>(A + (long)r * nd.a.ld + c), x);
@@ -1895,8 +1949,10 @@ __host__ __device__ constexpr unsigned op_family(int opcode) {
 }
 
 // NT threads per workgroup: 256 (four waves) for every instance, or 512
-// (eight waves, two per SIMD) for the instance that runs plans made only of
-// packed GEMM tiles, whose body is then the eight-wave one.
+// (eight waves, two per SIMD) for the instances that run plans made of
+// packed GEMM tiles and the REDUCE, RMSNORM, ATTENTION and elementwise
+// bodies, each of which then runs on all eight waves (the GEMV bodies, the
+// row-major GEMM tile and decode attention exist with four waves only).
 template <unsigned OPS, int DT, int NT>
 __device__ __forceinline__ void run_body(const KArgs& a, const mk_instr& in, const mk_node& nd, char* smem) {
   if (!(op_family(in.opcode) & OPS)) return;
@@ -1936,13 +1992,17 @@ __device__ __forceinline__ void run_body(const KArgs& a, const mk_instr& in, con
     default:
       if constexpr (OPS & kOpOther) {
         switch (in.opcode) {
-          case MK_I_REDUCE: reduce_tile<DT>(a, in, nd, smem); break;
-          case MK_I_RMSNORM: rmsnorm_tile<DT>(a, in, nd, smem); break;
-          case MK_I_ATTENTION: attention_tile<DT>(a, in, nd, smem); break;
-          case MK_I_ATTN_PARTIAL: attn_partial_tile<DT>(a, in, nd, smem); break;
-          case MK_I_ATTN_COMBINE: attn_combine_tile<DT>(a, in, nd); break;
+          case MK_I_REDUCE: reduce_tile<DT, NT>(a, in, nd, smem); break;
+          case MK_I_RMSNORM: rmsnorm_tile<DT, NT>(a, in, nd, smem); break;
+          case MK_I_ATTENTION: attention_tile<DT, NT>(a, in, nd, smem); break;
+          case MK_I_ATTN_PARTIAL:
+            if constexpr (NT == kThreads) attn_partial_tile<DT>(a, in, nd, smem);
+            break;
+          case MK_I_ATTN_COMBINE:
+            if constexpr (NT == kThreads) attn_combine_tile<DT>(a, in, nd);
+            break;
           case MK_I_EW_ADD:
-          case MK_I_EW_RELU: elementwise_tile<DT>(a, in, nd); break;
+          case MK_I_EW_RELU: elementwise_tile<DT, NT>(a, in, nd); break;
           default: break;
         }
       }
@@ -2064,6 +2124,7 @@ __device__ __forceinline__ int fetch_record(const Loop& L, int tk) {
 // to kPollGroups groups at a time, so all waits overlap.  Returns whether
 // every source cleared (false: the run was aborted).  No barrier.
 constexpr int kPollGroups = 2;
+constexpr int kPollNapMax = 8;   // longest pause between polls, in units of 64 cycles
 __device__ __forceinline__ bool poll_sources(const Loop& L, const mk_instr& in, int gidx) {
   const KArgs& a = L.a;
   const int lane = threadIdx.x & 63;
@@ -2101,6 +2162,7 @@ __device__ __forceinline__ bool poll_sources(const Loop& L, const mk_instr& in, 
       }
     }
     const long long t0 = wall_clock64();
+    int nap = 1;
     for (;;) {
       int ready = 1, seen = 0, want = 0, who = 0;
 #pragma unroll
@@ -2127,7 +2189,11 @@ __device__ __forceinline__ bool poll_sources(const Loop& L, const mk_instr& in, 
         ok = 0;
         break;
       }
-      __builtin_amdgcn_s_sleep(1);
+      // back off while the wait goes on (64, 128, ... kPollNapMax x 64
+      // cycles): spinning workgroups keep re-reading the same few counter
+      // lines, traffic the producers they wait for would otherwise share
+      for (int k = 0; k < nap; ++k) __builtin_amdgcn_s_sleep(1);
+      nap = nap < kPollNapMax ? 2 * nap : kPollNapMax;
     }
     if (!__all(ok)) return false;
   }
@@ -2184,7 +2250,7 @@ __device__ __forceinline__ bool generic_iter(const Loop& L, int it, int& w) {
   const bool tr = a.trace && threadIdx.x == 0 && in.opcode != MK_I_NOOP;
   if (tr) stamp(a, gidx, 0, wall_clock64());
   int tk = -1;
-  if constexpr ((OPS & kOpOther) != 0) {
+  if constexpr ((OPS & kOpOther) != 0 && NT == kThreads) {
     if (in.opcode == MK_I_ATTN_PARTIAL) {
       // the KV cache rows are requested before the counters clear
       const mk_node& nd = L.nodes[in.node];

@@ -109,24 +109,46 @@ __global__ void mk_pack_gemm_kernel(const unsigned short* __restrict__ src, unsi
 
 namespace {
 
-// The kernel instance a plan (or node) runs on and its workgroup size: the
-// eight-wave instance when every instruction is a packed GEMM tile,
+// The kernel instance a plan (or node) runs on and its workgroup size: an
+// eight-wave instance when every instruction is a packed GEMM tile or a
+// REDUCE, RMSNORM, ATTENTION or elementwise instruction (at least one packed
+// GEMM among them) and every REDUCE tile fits the eight-wave body's LDS;
 // otherwise the smallest four-wave instance whose op families cover `ops`.
 struct Launch {
   const void* fn;
   int threads;
 };
-bool packed_gemm_only(const mk_plan* p) {
+bool wide_ok(const mk_plan* p) {
   bool any = false;
   for (const mk::Node& n : p->nodes) {
     if (n.ins.empty()) continue;
-    if (n.opcode != MK_I_GEMM || n.desc.layout != 2) return false;
-    any = true;
+    switch (n.opcode) {
+      case MK_I_GEMM:
+        if (n.desc.layout != 2) return false;
+        any = true;
+        break;
+      case MK_I_REDUCE:
+        for (const mk::Instr& in : n.ins) {
+          const long wc = (long)(in.c1 - in.c0) * ((n.flags & MK_EP_SILU_MUL) ? 2 : 1);
+          if ((320 + 512 * 8 + (long)(in.r1 - in.r0) * wc) * 4 > mkd::kSmemBytes) return false;
+        }
+        break;
+      case MK_I_RMSNORM:
+      case MK_I_ATTENTION:
+      case MK_I_EW_ADD:
+      case MK_I_EW_RELU:
+        break;
+      default:
+        return false;
+    }
   }
   return any;
 }
 Launch persistent_for(unsigned ops, bool wide) {
-  if (wide && ops == mkd::kOpGemm) return {reinterpret_cast<const void*>(mk_persistent<mkd::kOpGemm, 512>), 512};
+  if (wide && (ops & ~(mkd::kOpGemm | mkd::kOpOther)) == 0) {
+    if (ops == mkd::kOpGemm) return {reinterpret_cast<const void*>(mk_persistent<mkd::kOpGemm, 512>), 512};
+    return {reinterpret_cast<const void*>(mk_persistent<mkd::kOpGemm | mkd::kOpOther, 512>), 512};
+  }
   if ((ops & ~mkd::kOpGemv) == 0) return {reinterpret_cast<const void*>(mk_persistent<mkd::kOpGemv>), 256};
   if ((ops & ~mkd::kOpGemm) == 0) return {reinterpret_cast<const void*>(mk_persistent<mkd::kOpGemm>), 256};
   if ((ops & mkd::kOpGemv) == 0)
@@ -136,7 +158,11 @@ Launch persistent_for(unsigned ops, bool wide) {
   return {reinterpret_cast<const void*>(mk_persistent<mkd::kOpAll>), 256};
 }
 Launch node_kernel_for(unsigned ops, bool wide) {
-  if (wide && ops == mkd::kOpGemm) return {reinterpret_cast<const void*>(mk_node_kernel<mkd::kOpGemm, 512>), 512};
+  if (wide && (ops & mkd::kOpGemv) == 0) {
+    if (ops == mkd::kOpGemm) return {reinterpret_cast<const void*>(mk_node_kernel<mkd::kOpGemm, 512>), 512};
+    if (ops == mkd::kOpOther) return {reinterpret_cast<const void*>(mk_node_kernel<mkd::kOpOther, 512>), 512};
+    return {reinterpret_cast<const void*>(mk_node_kernel<mkd::kOpGemm | mkd::kOpOther, 512>), 512};
+  }
   if ((ops & ~mkd::kOpGemv) == 0) return {reinterpret_cast<const void*>(mk_node_kernel<mkd::kOpGemv>), 256};
   if ((ops & ~mkd::kOpGemm) == 0) return {reinterpret_cast<const void*>(mk_node_kernel<mkd::kOpGemm>), 256};
   if ((ops & mkd::kOpGemv) == 0)
@@ -204,7 +230,8 @@ mk_status ensure_device(mk_plan* p) {
   }
   for (const Launch& k : {persistent_for(mkd::kOpAll, false), persistent_for(mkd::kOpGemv, false),
                           persistent_for(mkd::kOpGemm, false), persistent_for(mkd::kOpGemm | mkd::kOpOther, false),
-                          persistent_for(mkd::kOpGemm, true), persistent_for(mkd::kOpGemv | mkd::kOpOther, false)}) {
+                          persistent_for(mkd::kOpGemm, true), persistent_for(mkd::kOpGemm | mkd::kOpOther, true),
+                          persistent_for(mkd::kOpGemv | mkd::kOpOther, false)}) {
     int blocks = 0;
     HIPCHK(hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, k.fn, k.threads, 0));
     if (blocks < 1) {
@@ -412,7 +439,7 @@ mk_status megakernel_run_traced(mk_plan* p, void* const* buffers, int n_buffers,
     HIPCHK(hipGetLastError());
   }
   a.epoch = (int)(p->epoch + 1);
-  const Launch k = persistent_for(p->dev->ops, packed_gemm_only(p));
+  const Launch k = persistent_for(p->dev->ops, wide_ok(p));
   void* args[] = {&a};
   if (p->opts.cooperative) {
     HIPCHK(hipLaunchCooperativeKernel(k.fn, dim3(p->opts.num_cus), dim3(k.threads), args, 0, s));
@@ -434,6 +461,7 @@ mk_status megakernel_run_per_op(mk_plan* p, void* const* buffers, int n_buffers,
   mkd::KArgs a;
   if ((st = fill_args(p, buffers, n_buffers, a)) != MK_OK) return st;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const bool plan_wide = wide_ok(p);
   for (const mk::Node& n : p->nodes) {
     if (n.ins.empty()) continue;
     a.first = n.start;
@@ -441,7 +469,10 @@ mk_status megakernel_run_per_op(mk_plan* p, void* const* buffers, int n_buffers,
     unsigned ops = 0;
     for (int i = 0; i < a.count; ++i) ops |= mkd::op_family(p->records[n.start + i].opcode);
     void* args[] = {&a};
-    const bool wide = n.opcode == MK_I_GEMM && n.desc.layout == 2;
+    // the bodies of the megakernel's instance: eight waves for every node
+    // of a plan that runs on an eight-wave instance, and for packed GEMM
+    // nodes in any plan
+    const bool wide = plan_wide || (n.opcode == MK_I_GEMM && n.desc.layout == 2);
     const Launch k = node_kernel_for(ops, wide);
     HIPCHK(hipLaunchKernel(k.fn, dim3(a.count), dim3(k.threads), args, 0, s));
   }
@@ -545,7 +576,7 @@ mk_status megakernel_run_noalloc(mk_plan* p, void* const* buffers, int n_buffers
   }
   p->noalloc_device = dev;
   if (p->n_instr == 0) return MK_OK;
-  const Launch k = persistent_for(ops_of(p), packed_gemm_only(p));
+  const Launch k = persistent_for(ops_of(p), wide_ok(p));
   void* args[] = {&a};
   if (p->opts.cooperative) {
     HIPCHK(hipLaunchCooperativeKernel(k.fn, dim3(p->opts.num_cus), dim3(k.threads), args, 0, s));

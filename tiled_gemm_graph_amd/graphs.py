@@ -155,7 +155,10 @@ def build(workload: str, dims: Dict[str, int], tiles: Optional[Sequence[dict]] =
         nq, nkv = Hq * hd, Hkv * hd
         x = g.tensor("x", "bf16", (S, H), "input")
         g1 = g.tensor("g1", "bf16", (H,), "weight")
-        Wqkv = g.tensor("Wqkv", "bf16", (H, nq + 2 * nkv), "weight")
+        # Wqkv = [Wq | Wkv], held as two weights so that each projection
+        # reads a whole weight and takes the packed GEMM body
+        Wq = g.tensor("Wq", "bf16", (H, nq), "weight")
+        Wkv = g.tensor("Wkv", "bf16", (H, 2 * nkv), "weight")
         Wo = g.tensor("Wo", "bf16", (nq, H), "weight")
         g2 = g.tensor("g2", "bf16", (H,), "weight")
         Wgu = g.tensor("Wgu", "bf16", (H, 2 * I), "weight")
@@ -168,14 +171,12 @@ def build(workload: str, dims: Dict[str, int], tiles: Optional[Sequence[dict]] =
         hn = g.tensor("hn", "bf16", (S, H), "intermediate")
         a = g.tensor("a", "bf16", (S, I), "intermediate")
         out = g.tensor("out", "bf16", (S, H), "output")
-        # The QKV projection runs as two GEMMs over column ranges of Wqkv (q,
-        # and k|v): each attention instruction then depends on one q tile set
-        # per head and one k|v set per kv head instead of a unique union.
+        # The QKV projection runs as two GEMMs (q, and k|v): each attention
+        # instruction then depends on one q tile set per head and one k|v set
+        # per kv head instead of a unique union.
         g.rmsnorm(x, g1, xn, tile=_t(tiles, 0))
-        g.gemm(xn, g.cols(Wqkv, 0, nq), q, L.EP_ROPE, head_dim=hd, rope_cols=nq,
-               tile=_t(tiles, 1))
-        g.gemm(xn, g.cols(Wqkv, nq, nq + 2 * nkv), kv, L.EP_ROPE, head_dim=hd, rope_cols=nkv,
-               tile=_t(tiles, 2))
+        g.gemm(xn, Wq, q, L.EP_ROPE, head_dim=hd, rope_cols=nq, tile=_t(tiles, 1))
+        g.gemm(xn, Wkv, kv, L.EP_ROPE, head_dim=hd, rope_cols=nkv, tile=_t(tiles, 2))
         g.attention(q, g.cols(kv, 0, nkv), g.cols(kv, nkv, 2 * nkv), o, Hq, Hkv, hd, True,
                     tile=_t(tiles, 3))
         g.gemm(o, Wo, h1, L.EP_RESIDUAL, residual=x, tile=_t(tiles, 4))
@@ -184,6 +185,18 @@ def build(workload: str, dims: Dict[str, int], tiles: Optional[Sequence[dict]] =
         g.gemm(a, Wd, out, L.EP_RESIDUAL, residual=h1, tile=_t(tiles, 7))
         return g
     raise KeyError(workload)
+
+
+def graph_inputs(workload: str, dims: Dict[str, int], inputs: Dict[str, "object"]) -> Dict[str, "object"]:
+    """The graph's input and weight tensors from a workload's inputs: the
+    layer's Wqkv is handed over as its q and k|v column blocks."""
+    out = dict(inputs)
+    if workload == "layer" and "Wqkv" in out:
+        nq = dims["heads"] * dims["head_dim"]
+        w = out.pop("Wqkv")
+        out["Wq"] = w[:, :nq].contiguous()
+        out["Wkv"] = w[:, nq:].contiguous()
+    return out
 
 
 class Runner:
@@ -195,7 +208,7 @@ class Runner:
         self.workload, self.dims = workload, dims
         self.graph = build(workload, dims, tiles)
         self.plan: Plan = self.graph.build(**opts)
-        self.bufs = {k: v.to(device).contiguous() for k, v in inputs.items()}
+        self.bufs = {k: v.to(device).contiguous() for k, v in graph_inputs(workload, dims, inputs).items()}
         # weights the plan reads as packed column tiles: pack once, run on the copy
         self.packed = {}
         for name in self.plan.packed_weights():
