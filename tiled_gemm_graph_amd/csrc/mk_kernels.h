@@ -2066,6 +2066,7 @@ struct Loop {
   char* smem;
   int vcu;
   int* idx;             // work-queue mode: record index of each slot, -1 = none
+  int* seen;            // [kSeenSlots] counters this workgroup saw complete in this run
 };
 
 // Record index of local iteration it (the slot it % 3 holds it), and
@@ -2124,13 +2125,22 @@ __device__ __forceinline__ int fetch_record(const Loop& L, int tk) {
 // to kPollGroups groups at a time, so all waits overlap.  Returns whether
 // every source cleared (false: the run was aborted).  No barrier.
 constexpr int kPollGroups = 2;
+constexpr int kSeenSlots = 64;   // direct-mapped record of counters seen complete (by id)
 constexpr int kPollNapMax = 8;   // longest pause between polls, in units of 64 cycles
 __device__ __forceinline__ bool poll_sources(const Loop& L, const mk_instr& in, int gidx) {
   const KArgs& a = L.a;
   const int lane = threadIdx.x & 63;
   const int ns = in.n_src;
+  // A counter only grows during a run, so one this workgroup has already
+  // seen complete (and acquired) is not polled again: later instructions on
+  // the same producers skip the memory round trip of the poll.
+  unsigned todo = 0;
+  for (int k = 0; k < ns; ++k)
+    if (L.seen[in.src_id[k] & (kSeenSlots - 1)] != in.src_id[k]) todo |= 1u << k;
+  if (!todo) return true;
   int groups = 0;
   for (int k = 0; k < ns; ++k) {
+    if (!((todo >> k) & 1)) continue;
     const int T = in.src_target[k];
     groups += T <= MK_SLICE_MAX ? (T + 3) >> 2 : 1;
   }
@@ -2148,6 +2158,7 @@ __device__ __forceinline__ bool poll_sources(const Loop& L, const mk_instr& in, 
       int g = g0 + lane + 64 * j;
       if (g >= groups) continue;
       for (int k = 0; k < ns; ++k) {
+        if (!((todo >> k) & 1)) continue;
         const int T = in.src_target[k];
         const bool sl = T <= MK_SLICE_MAX;
         const int w = sl ? (T + 3) >> 2 : 1;
@@ -2197,7 +2208,8 @@ __device__ __forceinline__ bool poll_sources(const Loop& L, const mk_instr& in, 
     }
     if (!__all(ok)) return false;
   }
-  if (ns && lane == 0) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  if (lane == 0) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  if (lane < ns && ((todo >> lane) & 1)) L.seen[in.src_id[lane] & (kSeenSlots - 1)] = in.src_id[lane];
   return true;
 }
 // Work-queue mode: the ticket for iteration it + 2 is taken before the poll
@@ -2352,9 +2364,11 @@ __global__ void __launch_bounds__(NT, 1) mk_persistent(mkd::KArgs args) {
   __shared__ mk_node s_nodes[mkd::kMaxNodes];
   __shared__ int s_flag;
   __shared__ int s_idx[3];
+  __shared__ int s_seen[mkd::kSeenSlots];
   __shared__ __attribute__((aligned(16))) char smem[mkd::kSmemBytes];
   const int t = threadIdx.x;
   const int b = blockIdx.x;
+  if (t < mkd::kSeenSlots) s_seen[t] = -1;
   // Workgroup b runs column b of the placement, so consecutive instructions
   // land on different XCDs (b % 8), as a grid launch would place them.
   // Keeping 32 consecutive instructions on one XCD instead (for L2 sharing)
@@ -2389,7 +2403,7 @@ __global__ void __launch_bounds__(NT, 1) mk_persistent(mkd::KArgs args) {
     clk[0] = wall_clock64();
     clk[1] = __builtin_amdgcn_s_memtime();
   }
-  const mkd::Loop L{a, s_in, s_nodes, &s_flag, smem, vcu, s_idx};
+  const mkd::Loop L{a, s_in, s_nodes, &s_flag, smem, vcu, s_idx, s_seen};
   int it = 0, w = 0;
   while (mkd::has_rec(L, it)) {
     const mk_instr& in = s_in[it % 3];
