@@ -94,14 +94,13 @@ def kernel_trace(wl, out, prof, steps, warmup, h):
         return None
     sel = [x[1] / 1000.0 for x in dur[1 + warmup:1 + warmup + steps]]
     med = statistics.median(sel)
-    n_nodes = max(1, len(node) // max(1, steps + warmup)) if node else 0
+    n_nodes = stats_of(wl)["nodes"]
     per_fwd_node = []
-    if node:
-        # the per-op forwards: warmup + timed, n_nodes launches each; keep the timed ones
+    if node and n_nodes and len(node) % n_nodes == 0:
+        # every per-op forward launches the plan's non-empty nodes in order
         body = [x[1] / 1000.0 for x in node]
-        timed = body[warmup * n_nodes:(warmup + steps) * n_nodes]
         for k in range(n_nodes):
-            per_fwd_node.append(statistics.median(timed[k::n_nodes]))
+            per_fwd_node.append(statistics.median(body[k::n_nodes]))
     rf = line.get("roofline", {})
     with open(os.path.join(prof, f"{KERNEL}_{wl}_kernel_trace.md"), "w") as f:
         f.write(f"# {KERNEL} — {wl}: {line['config']['workload']}, kernel trace\n\n")
@@ -128,9 +127,9 @@ def kernel_trace(wl, out, prof, steps, warmup, h):
         if "core_clock_mhz" in line:
             f.write(f"Core clock over the traced forward: {line['core_clock_mhz']:.0f} MHz.\n")
         if per_fwd_node:
-            f.write(f"\nPer-op launches (`mk_node_kernel`, {n_nodes} per forward), median of the timed "
-                    "forwards, us: " + ", ".join(f"{x:.1f}" for x in per_fwd_node) +
-                    f" (sum {sum(per_fwd_node):.1f}; the rest of the per-op time is launch gaps).\n")
+            f.write(f"\nPer-op launches (`mk_node_kernel`, {n_nodes} per forward), median duration of each "
+                    f"node's launches over the {len(node) // n_nodes} per-op forwards of the run, us: "
+                    + ", ".join(f"{x:.1f}" for x in per_fwd_node) + f" (sum {sum(per_fwd_node):.1f}).\n")
         f.write(f"\nKernel source sha256 (`python bench.py --source-hash`): `{h}`\n")
     say(f"  {wl}: persistent median {med:.1f} us, bench {line['value']:.1f} us")
     return dict(median_us=med, clock_mhz=line.get("core_clock_mhz"))
@@ -289,10 +288,14 @@ def stats_of(wl):
     """Algorithmic bytes and flops of a workload's plan (host only)."""
     sys.path.insert(0, ROOT)
     import workloads
+    from . import _lib as L
     from . import graphs as G
     d = workloads.default_dims(wl)
-    st = G.build(wl, d).build(num_cus=256).stats()
-    return dict(bytes=float(st.bytes), flops=float(st.flops))
+    plan = G.build(wl, d).build(num_cus=256)
+    st = plan.stats()
+    w = plan.instructions()
+    live = w[:, L.W_OPCODE] != L.I_NOOP
+    return dict(bytes=float(st.bytes), flops=float(st.flops), nodes=len(set(w[live, L.W_NODE].tolist())))
 
 
 if __name__ == "__main__":
