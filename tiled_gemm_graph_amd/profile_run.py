@@ -47,8 +47,14 @@ def say(msg):
     print(f"[profile_run {time.strftime('%H:%M:%S')}] {msg}", flush=True)
 
 
+SUMMARIZE_ONLY = False   # --summarize-only: re-read the logs and raw output of an earlier run
+
+
 def run(cmd, log_path, limit):
     """Run one step from /tmp under its own kill timer; returns (rc, stdout)."""
+    if SUMMARIZE_ONLY:
+        with open(log_path) as f:
+            return 0, f.read()
     env = dict(os.environ, TMPDIR="/tmp")
     full = ["timeout", "-s", "KILL", str(limit)] + cmd
     say("$ " + " ".join(cmd))
@@ -58,6 +64,18 @@ def run(cmd, log_path, limit):
         lf.write(p.stdout)
     say(f"  exit {p.returncode}")
     return p.returncode, p.stdout
+
+
+def bench_constants():
+    """WARM_SECONDS and AB_ROUNDS of bench.py (read from its source)."""
+    out = {}
+    with open(BENCH) as f:
+        for ln in f:
+            for k in ("WARM_SECONDS", "AB_ROUNDS"):
+                if ln.startswith(k + " ="):
+                    out[k] = float(ln.split("=", 1)[1].split("#")[0]) if k == "WARM_SECONDS" \
+                        else int(ln.split("=", 1)[1].split("#")[0])
+    return out
 
 
 def bench_json(stdout):
@@ -92,7 +110,16 @@ def kernel_trace(wl, out, prof, steps, warmup, h):
     if not dur or line is None:
         say(f"  no kernel trace for {wl} (rc {rc})")
         return None
-    sel = [x[1] / 1000.0 for x in dur[1 + warmup:1 + warmup + steps]]
+    # persistent launches: parity forward, the warm-up of WARM_SECONDS, then
+    # AB_ROUNDS blocks of warmup + steps forwards (the first is the headline
+    # block), then one traced forward; keep the timed `steps` of each block
+    rounds = bench_constants()["AB_ROUNDS"]
+    blk = warmup + steps
+    end = len(dur) - 1
+    sel = []
+    for j in range(rounds):
+        stop = end - (rounds - 1 - j) * blk
+        sel += [x[1] / 1000.0 for x in dur[stop - steps:stop]]
     med = statistics.median(sel)
     n_nodes = stats_of(wl)["nodes"]
     per_fwd_node = []
@@ -105,8 +132,9 @@ def kernel_trace(wl, out, prof, steps, warmup, h):
     with open(os.path.join(prof, f"{KERNEL}_{wl}_kernel_trace.md"), "w") as f:
         f.write(f"# {KERNEL} — {wl}: {line['config']['workload']}, kernel trace\n\n")
         f.write("Command (the repository at /root/repo):\n\n```\n" + fmt_cmd(cmd, 600) + "\n```\n\n")
-        f.write(f"Persistent launches in launch order: 1 parity forward, {warmup} warmup, {steps} timed, "
-                f"1 traced forward. The {steps} timed launches:\n\n")
+        f.write(f"Persistent launches in launch order: 1 parity forward, the forwards of a one-second warm-up, "
+                f"{rounds} blocks of {warmup} untimed and {steps} timed forwards (alternating with blocks of "
+                f"per-op forwards), 1 traced forward. The timed launches of the {rounds} blocks:\n\n")
         f.write("| kernel | timed dispatches | median us | min us | max us |\n|---|---|---|---|---|\n")
         f.write(f"| {KERNEL} | {len(sel)} | {med:.1f} | {min(sel):.1f} | {max(sel):.1f} |\n\n")
         f.write(f"Bench line of the same run (HIP events on the launch stream over the timed region, under "
@@ -142,9 +170,15 @@ def pmc_pass(tag, counters, prog, out, limit=180):
     return rc, d, cmd
 
 
-def mean_counter(d, name, kernel, skip=0):
+def mean_counter(d, name, kernel, big_only=False):
+    """Mean of a counter over the dispatches of ``kernel`` (with
+    ``big_only``, over those within half of the largest value: the copy
+    calibration run also issues a few tiny copies)."""
     c = PS.counters(d, kernel)
-    vals = [v[name] for _, v in list(c.items())[skip:] if name in v]
+    vals = [v[name] for _, v in c.items() if name in v]
+    if vals and big_only:
+        top = max(vals)
+        vals = [v for v in vals if v >= 0.5 * top]
     return (statistics.mean(vals), len(vals), (max(vals) - min(vals)) / max(statistics.mean(vals), 1e-9)) \
         if vals else (None, 0, 0.0)
 
@@ -153,8 +187,8 @@ def copy_scales(out):
     prog = ["python3", BENCH, "--copy-mib", "1024", "--steps", "3"]
     rf, df, cf = pmc_pass("fetch_copy", ["FETCH_SIZE"], prog, out)
     rw, dw, cw = pmc_pass("write_copy", ["WRITE_SIZE"], prog, out)
-    fk, _, _ = mean_counter(df, "FETCH_SIZE", "copyBuffer")
-    wk, _, _ = mean_counter(dw, "WRITE_SIZE", "copyBuffer")
+    fk, _, _ = mean_counter(df, "FETCH_SIZE", "copyBuffer", big_only=True)
+    wk, _, _ = mean_counter(dw, "WRITE_SIZE", "copyBuffer", big_only=True)
     if not fk or not wk:
         return None
     return dict(fetch=1048576.0 / fk, write=1048576.0 / wk, fetch_kib=fk, write_kib=wk, cmds=(cf, cw))
@@ -259,11 +293,17 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--skip", nargs="*", default=[], choices=["trace", "hbm", "mfma", "nodes"])
+    ap.add_argument("--summarize-only", action="store_true",
+                    help="write the summaries from the logs and raw output already under --out")
+    ap.add_argument("--source-hash", default=None,
+                    help="with --summarize-only: the kernel-source hash the raw output was taken on")
     a = ap.parse_args(argv)
+    global SUMMARIZE_ONLY
+    SUMMARIZE_ONLY = a.summarize_only
     out = os.path.abspath(a.out)
     os.makedirs(out, exist_ok=True)
     os.makedirs(a.profiles, exist_ok=True)
-    h = source_hash()
+    h = a.source_hash if (a.summarize_only and a.source_hash) else source_hash()
     say(f"kernel sources {h[:16]}..., workloads {a.workloads}")
     scales = None if "hbm" in a.skip else copy_scales(out)
     bound = dict(mlp3="mfma", decode="hbm", prefill="mfma", decode_gemm="hbm", layer="mfma", decode_kv="hbm")
