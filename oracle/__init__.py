@@ -10,9 +10,11 @@ Contents
 
 ``ops``       plain numpy definitions of every op the graphs use (GEMM,
               bias, ReLU, residual, RMSNorm, SiLU-mul, rotary embedding,
-              causal grouped-query attention), evaluated in fp32 by default.
-``graphs``    the five workload graphs evaluated op by op from the same
-              fp16/bf16 input bytes the GPU consumes.
+              causal grouped-query attention, one-token attention over a KV
+              cache with the rotary append), evaluated in fp32 by default.
+``graphs``    the workload graphs (the five configurations and the decode
+              layer with KV-cache attention) evaluated op by op from the
+              same fp16/bf16 input bytes the GPU consumes.
 ``schedule``  a brute-force re-derivation of the instruction list, tensor
               slots and dependency counters from a graph description and
               per-node tile parameters (MegaKittens Internals, sections
