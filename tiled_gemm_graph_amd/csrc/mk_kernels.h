@@ -1425,7 +1425,7 @@ __device__ __forceinline__ void attention_tile(const KArgs& a, const mk_instr& i
   constexpr int D = 128, KBLK = 64, NH = NT / 256;
   constexpr int KS = D + kLdsPad;      // K tile row: 136 elements
   constexpr int VS = KBLK + kLdsPad;   // V^T tile row: 72 elements
-  constexpr int HALF_ELEMS = KBLK * KS + D * VS;
+  constexpr int HALF_ELEMS = KBLK * KS + D * VS;  // a half's K / V^T staging (elements)
   static_assert(NH * HALF_ELEMS * 2 <= kSmemBytes && (4 * 64 * 64 + 2 * 4 * 64) * 4 <= kSmemBytes,
                 "attention LDS");
   const int t = threadIdx.x, lane = t & 63, wave = (t >> 6) & 3, hh = t >> 8, g = lane >> 5, l32 = lane & 31;
@@ -1478,65 +1478,76 @@ __device__ __forceinline__ void attention_tile(const KArgs& a, const mk_instr& i
         *reinterpret_cast<u32x2*>(Vt + (dblk * 8 + n) * VS + kq * 4) = u32x2{pick2(v[0], v[1], n), pick2(v[2], v[3], n)};
     }
     __syncthreads();
-    if (!live) continue;
-    // S^T for 64 keys x 32 queries: two 32-key blocks
-    f32x16 sacc[2];
+    if (live) {
+      const u16* ksb = Ks;
+      const u16* vtb = Vt;
+      // S^T for 64 keys x 32 queries: two 32-key blocks
+      f32x16 sacc[2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) sacc[kb][e] = 0.f;
+        for (int e = 0; e < 16; ++e) sacc[kb][e] = 0.f;
 #pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        const u32x4 kf = *reinterpret_cast<const u32x4*>(Ks + (kb * 32 + l32) * KS + s * 16 + g * 8);
-        sacc[kb] = mfma32<DT>(kf, qf[s], sacc[kb]);
+        for (int s = 0; s < 8; ++s) {
+          const u32x4 kf = *reinterpret_cast<const u32x4*>(ksb + (kb * 32 + l32) * KS + s * 16 + g * 8);
+          sacc[kb] = mfma32<DT>(kf, qf[s], sacc[kb]);
+        }
       }
-    }
-    // mask, scale, running max
-    float mloc = -INFINITY;
+      // mask (only blocks that reach past the end or the wave's first
+      // query), running max of the raw scores, then the scale folded into
+      // the exponent: p = 2^(s c - m), m in scaled units (c > 0)
+      const bool edge = kb0 + KBLK > kend || (causal && kb0 + KBLK - 1 > q0 + wave * 32);
+      float mloc = -INFINITY;
+      if (edge) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int key = kb0 + kb * 32 + 8 * (e >> 2) + 4 * g + (e & 3);
-        float sv = sacc[kb][e] * c;
-        if (key >= kend || (causal && key > qrow)) sv = -INFINITY;
-        sacc[kb][e] = sv;
-        mloc = fmaxf(mloc, sv);
+          for (int e = 0; e < 16; ++e) {
+            const int key = kb0 + kb * 32 + 8 * (e >> 2) + 4 * g + (e & 3);
+            if (key >= kend || (causal && key > qrow)) sacc[kb][e] = -INFINITY;
+          }
       }
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
-    const float mnew = fmaxf(mrun, mloc);
-    const float muse = mnew == -INFINITY ? 0.f : mnew;
-    const float alpha = exp2f(mrun - muse);
-    mrun = mnew;
-    float psum = 0.f;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const float p = exp2f(sacc[kb][e] - muse);
-        sacc[kb][e] = p;
-        psum += p;
+        for (int e = 0; e < 16; ++e) mloc = fmaxf(mloc, sacc[kb][e]);
+      mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
+      const float mnew = fmaxf(mrun, mloc * c);
+      const float muse = mnew == -INFINITY ? 0.f : mnew;
+      const float alpha = exp2f(mrun - muse);
+      mrun = mnew;
+      float psum = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const float p = exp2f(fmaf(sacc[kb][e], c, -muse));
+          sacc[kb][e] = p;
+          psum += p;
+        }
+      lsum = lsum * alpha + psum;
+      if (__any(alpha != 1.f)) {   // the running max moved for some lane of the wave
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) o[db][e] *= alpha;
       }
-    lsum = lsum * alpha + psum;
+      // O^T += V^T P^T over four 16-key substeps
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+      for (int st = 0; st < 4; ++st) {
+        const int kb = st >> 1, hf = st & 1;
+        float pv[8];
 #pragma unroll
-      for (int e = 0; e < 16; ++e) o[db][e] *= alpha;
-    // O^T += V^T P^T over four 16-key substeps
+        for (int e = 0; e < 8; ++e) pv[e] = sacc[kb][hf * 8 + e];
+        const u32x4 pf = pack8<DT>(pv);
+        const int kbase = kb * 32 + hf * 16 + 4 * g;  // keys kbase..+3 and kbase+8..+3
 #pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      const int kb = st >> 1, hf = st & 1;
-      float pv[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) pv[e] = sacc[kb][hf * 8 + e];
-      const u32x4 pf = pack8<DT>(pv);
-      const int kbase = kb * 32 + hf * 16 + 4 * g;  // keys kbase..+3 and kbase+8..+3
-#pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        const u16* vrow = Vt + (db * 32 + l32) * VS;
-        const u32x2 v0 = *reinterpret_cast<const u32x2*>(vrow + kbase);
-        const u32x2 v1 = *reinterpret_cast<const u32x2*>(vrow + kbase + 8);
-        o[db] = mfma32<DT>(u32x4{v0.x, v0.y, v1.x, v1.y}, pf, o[db]);
+        for (int db = 0; db < 4; ++db) {
+          const u16* vrow = vtb + (db * 32 + l32) * VS;
+          const u32x2 v0 = *reinterpret_cast<const u32x2*>(vrow + kbase);
+          const u32x2 v1 = *reinterpret_cast<const u32x2*>(vrow + kbase + 8);
+          o[db] = mfma32<DT>(u32x4{v0.x, v0.y, v1.x, v1.y}, pf, o[db]);
+        }
       }
     }
   }
