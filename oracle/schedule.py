@@ -67,6 +67,16 @@ Lowering and tiling spec (the compiler implements the same rules):
   the whole sequence even under the causal mask, so every q block of a kv
   head shares one dependency set and each k/v tile arrives on one counter.
 ``add`` / ``relu`` ops, tile params er, ec: row-major (er x ec) tiles.
+``decode_attention`` op (one new token over a KV cache, "Implementing a
+  Mega Kernel for B300", section 2), tile param bq = C keys per chunk:
+  partial fp32 tensor P [1, NC, Hq, d + 4] (NC = ceil(S_max / C)) appended
+  to the graph; a partial node of NC x Hkv instructions, chunk c outer, kv
+  head g inner, coords (c, g), each reading the q columns of g's G = Hq /
+  Hkv query heads, k_new and v_new of g, cache rows [cC, min(S, cC + C)) x
+  g's columns of both caches, and the position; writing P (chunk c, heads
+  of g, all d + 4).  Then a combine node of Hkv instructions, coords (g),
+  reading P (all chunks, heads of g) and the position, writing o's columns
+  of g's query heads.
 """
 from __future__ import annotations
 
@@ -77,9 +87,9 @@ from typing import Dict, List, Optional, Sequence, Tuple
 import numpy as np
 
 # opcodes
-NOOP, GEMM, GEMV, REDUCE, RMSNORM, ATTENTION, EW_ADD, EW_RELU = range(8)
+NOOP, GEMM, GEMV, REDUCE, RMSNORM, ATTENTION, EW_ADD, EW_RELU, ATTN_PARTIAL, ATTN_COMBINE = range(10)
 OPCODE_NAMES = ["NOOP", "GEMM", "GEMV", "REDUCE", "RMSNORM", "ATTENTION",
-                "EW_ADD", "EW_RELU"]
+                "EW_ADD", "EW_RELU", "ATTN_PARTIAL", "ATTN_COMBINE"]
 # epilogue / role flags
 BIAS, RELU, RESIDUAL, SILU_MUL, RMSNORM_INPUT, ROPE, PARTIAL = (
     1, 2, 4, 8, 16, 32, 64)
@@ -91,7 +101,7 @@ MAX_SRC, MAX_DST = 16, 8
 # among the counter's arrivals in instruction order; larger counters carry
 # rank -1.
 SLICE_MAX = 256
-DTYPE_BYTES = {"f16": 2, "bf16": 2, "f32": 4}
+DTYPE_BYTES = {"f16": 2, "bf16": 2, "f32": 4, "i32": 4}
 
 
 @dataclasses.dataclass
@@ -239,6 +249,8 @@ def lower(g: Graph, ncu: int = 256) -> List[Node]:
             for c0 in range(ncu, len(ins), 2 * ncu):
                 ins[c0:c0 + ncu] = ins[c0:c0 + ncu][::-1]
             nodes.append(Node(oi, ATTENTION, 0, op.out, [q, k, v], ins))
+        elif op.kind == "decode_attention":
+            nodes.extend(_lower_decode_attention(g, oi, op))
         elif op.kind in ("add", "relu"):
             a = op.ins["a"]
             M, N = a.rows, a.cols
@@ -258,6 +270,37 @@ def lower(g: Graph, ncu: int = 256) -> List[Node]:
         else:
             raise ValueError(op.kind)
     return nodes
+
+
+def _lower_decode_attention(g: Graph, oi: int, op: Op) -> List[Node]:
+    q, kn, vn = op.ins["q"], op.ins["k_new"], op.ins["v_new"]
+    kc, vc, ps = op.ins["k_cache"], op.ins["v_cache"], op.ins["pos"]
+    Hq, Hkv, d = int(op.attrs["heads"]), int(op.attrs["kv_heads"]), int(op.attrs["head_dim"])
+    G, S, C = Hq // Hkv, kc.rows, op.tile["bq"]
+    NC, W = _cdiv(S, C), d + 4
+    pt = g.tensor(f"attention partials of op {oi}", "f32", (1, NC, Hq, W), "intermediate")
+    pos_box = g.full(ps.tensor)
+    pos_box = tuple((a, b) for a, b in zip(pos_box.lo, pos_box.hi))
+    parts = []
+    for c in range(NC):
+        r0, r1 = c * C, min(S, c * C + C)
+        for kh in range(Hkv):
+            reads = [(q.tensor, q.box(0, 1, kh * G * d, (kh + 1) * G * d)),
+                     (kn.tensor, kn.box(0, 1, kh * d, (kh + 1) * d)),
+                     (vn.tensor, vn.box(0, 1, kh * d, (kh + 1) * d)),
+                     (kc.tensor, kc.box(r0, r1, kh * d, (kh + 1) * d)),
+                     (vc.tensor, vc.box(r0, r1, kh * d, (kh + 1) * d)),
+                     (ps.tensor, pos_box)]
+            writes = [(pt, ((0, 1), (c, c + 1), (kh * G, (kh + 1) * G), (0, W)))]
+            parts.append(Instr((c, kh, 0, 0), reads, writes))
+    o = g.full(op.out)
+    comb = []
+    for kh in range(Hkv):
+        comb.append(Instr((kh, 0, 0, 0),
+                          [(pt, ((0, 1), (0, NC), (kh * G, (kh + 1) * G), (0, W))), (ps.tensor, pos_box)],
+                          [(op.out, o.box(0, 1, kh * G * d, (kh + 1) * G * d))]))
+    return [Node(oi, ATTN_PARTIAL, 0, pt, [q, kn, vn, kc, vc, ps], parts),
+            Node(oi, ATTN_COMBINE, 0, op.out, [g.full(pt), ps], comb)]
 
 
 def _position_column(p: int, hd: int, rope_cols: int) -> int:
@@ -767,9 +810,48 @@ def layer_graph(d: Dict[str, int], tiles: Sequence[Dict[str, int]]) -> Graph:
     return g
 
 
+def decode_kv_graph(d: Dict[str, int], tiles: Sequence[Dict[str, int]]) -> Graph:
+    """The decode layer with attention over a KV cache (bf16): RMSNorm-input
+    QKV GEMV; decode attention of the new token over the cache (q, k_new,
+    v_new the [Q | K | V] column blocks of qkv); O + residual; RMSNorm-input
+    gate_up with SiLU-mul; down + residual.  ``tiles`` in op order (5)."""
+    g = Graph()
+    M, H, nq, nkv, I, hd = d["m"], d["hidden"], d["n_q"], d["n_kv"], d["inter"], d["head_dim"]
+    x = g.tensor("x", "bf16", (M, H), "input")
+    g1 = g.tensor("g1", "bf16", (H,), "weight")
+    Wqkv = g.tensor("Wqkv", "bf16", (H, nq + 2 * nkv), "weight")
+    Wo = g.tensor("Wo", "bf16", (nq, H), "weight")
+    g2 = g.tensor("g2", "bf16", (H,), "weight")
+    Wgu = g.tensor("Wgu", "bf16", (H, 2 * I), "weight")
+    Wd = g.tensor("Wd", "bf16", (I, H), "weight")
+    kc = g.tensor("k_cache", "bf16", (d["s_max"], nkv), "input")
+    vc = g.tensor("v_cache", "bf16", (d["s_max"], nkv), "input")
+    pos = g.tensor("pos", "i32", (1,), "input")
+    qkv = g.tensor("qkv", "bf16", (M, nq + 2 * nkv), "intermediate")
+    o = g.tensor("o", "bf16", (M, nq), "intermediate")
+    h = g.tensor("h", "bf16", (M, H), "intermediate")
+    a = g.tensor("a", "bf16", (M, I), "intermediate")
+    out = g.tensor("out", "bf16", (M, H), "output")
+    g.ops.append(Op("gemm", dict(a=g.full(x), b=g.full(Wqkv), gamma=g.full(g1)), qkv,
+                    RMSNORM_INPUT, dict(tiles[0])))
+    g.ops.append(Op("decode_attention",
+                    dict(q=g.cols(qkv, 0, nq), k_new=g.cols(qkv, nq, nq + nkv),
+                         v_new=g.cols(qkv, nq + nkv, nq + 2 * nkv), k_cache=g.full(kc),
+                         v_cache=g.full(vc), pos=g.full(pos)),
+                    o, 0, dict(tiles[1]), dict(heads=nq // hd, kv_heads=nkv // hd, head_dim=hd)))
+    g.ops.append(Op("gemm", dict(a=g.full(o), b=g.full(Wo), residual=g.full(x)), h,
+                    RESIDUAL, dict(tiles[2])))
+    g.ops.append(Op("gemm", dict(a=g.full(h), b=g.full(Wgu), gamma=g.full(g2)), a,
+                    RMSNORM_INPUT | SILU_MUL, dict(tiles[3])))
+    g.ops.append(Op("gemm", dict(a=g.full(a), b=g.full(Wd), residual=g.full(h)), out,
+                    RESIDUAL, dict(tiles[4])))
+    return g
+
+
 def workload_graph(workload: str, d: Dict[str, int],
                    tiles: Sequence[Dict[str, int]]) -> Graph:
     if workload == "mlp3":
         return mlp3_graph(d["layers"], d["m"], d["h"], tiles[0])
     return dict(prefill=prefill_graph, decode_gemm=decode_gemm_graph,
-                decode=decode_graph, layer=layer_graph)[workload](d, tiles)
+                decode=decode_graph, layer=layer_graph,
+                decode_kv=decode_kv_graph)[workload](d, tiles)

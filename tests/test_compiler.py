@@ -121,6 +121,18 @@ def _compare(wl, dims, tiles=None, reuse=0, ncu=256, sync=0):
     return plan, sc
 
 
+@pytest.mark.parametrize("size", ["small", "full"])
+def test_decode_kv_lists_match_oracle(size):
+    # the decode layer with split-KV attention: partial and combine nodes,
+    # the cache and position reads, the partial tensor's dependency sets
+    dims = workloads.small_dims("decode_kv") if size == "small" else workloads.default_dims("decode_kv")
+    plan, sc = _compare("decode_kv", dims)
+    ops = {int(r[3]) for r in plan.decoded()}
+    assert {L.I_ATTN_PARTIAL, L.I_ATTN_COMBINE} <= ops
+    for bq in (64, 256):
+        _compare("decode_kv", dims, tiles=[None, dict(bq=bq)])
+
+
 @pytest.mark.parametrize("wl", workloads.WORKLOADS)
 def test_full_size_lists_match_oracle(wl):
     dims = workloads.default_dims(wl)
