@@ -253,12 +253,18 @@ struct Compiler {
       t.bn = silu ? bbn / 2 : bbn;   // tile.bn counts output columns
       t.split = bs;
       // REDUCE tiles of at most 16384 fp32 sums (64 KB of LDS), so that
-      // the eight-wave REDUCE body fits beside its per-thread partials
+      // the eight-wave REDUCE body fits beside its per-thread partials; and
+      // rows halved (down to 32) while that leaves CUs without a REDUCE
+      // instruction: the node is latency-bound, so more, smaller tiles
+      // finish sooner
+      const bool auto_rows = t.rbm <= 0;
       if (t.rbm <= 0) t.rbm = std::min(t.bm, 128);
       if (t.rbn <= 0) {
         const int cap = 16384 / (t.rbm * (silu ? 2 : 1));
         t.rbn = std::max(8, std::min(t.bn, cap / 8 * 8));
       }
+      if (t.split > 1 && auto_rows)
+        while (t.rbm > 32 && cdiv(std::max<I64>(M, 1), t.rbm) * cdiv(N, t.rbn) < ncu) t.rbm /= 2;
       return t;
     }
     if (t.bm <= 0 || t.bn <= 0) {
