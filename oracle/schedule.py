@@ -31,11 +31,10 @@ Lowering and tiling spec (the compiler implements the same rules):
   Kc = roundup(ceil(K/S), 64) rows (every chunk must be non-empty).
   Tiles run in groups, chunk index s fastest, each tile repeated ``dup``
   times (the CTA-pair duplicate of section 04).  GEMM-body nodes cut the
-  TM x TN tile grid into groups of gm = min(TM, 4) rows by
+  TM x TN tile grid into groups of gm = min(TM, 32) rows by
   gn = min(TN, max(1, B // (gm * S))) columns, B = ncu // 8 when ncu is a
   multiple of 8, else 32; groups are taken row by row and the tiles of a
-  group row by row (one group is one XCD's share of a wave: the persistent
-  kernel deals its workgroups to the 8 XCDs in blocks of B).  GEMV-body
+  group row by row.  GEMV-body
   nodes run row-major over (tm, tn).  Placement: a GEMM-body node with at
   least ncu instructions starts on a multiple of ncu // 8 (when ncu is a
   multiple of 8), the gap before it being Noops.
@@ -361,7 +360,7 @@ def _grouped_tiles(TM: int, TN: int, S: int, ncu: int) -> List[Tuple[int, int]]:
     if TM == 0 or TN == 0:
         return []
     B = ncu // 8 if ncu % 8 == 0 else 32
-    gm = min(TM, 4)
+    gm = min(TM, 32)
     gn = min(TN, max(1, B // (gm * S)))
     order = []
     for gi in range(_cdiv(TM, gm)):
