@@ -44,8 +44,8 @@
 extern "C" {
 #endif
 
-#define MK_ABI_VERSION 4
-#define MK_MAX_TENSORS 64       /* graph tensors incl. views and internals */
+#define MK_ABI_VERSION 5
+#define MK_MAX_TENSORS 256      /* graph tensors incl. views and internals */
 #define MK_MAX_SRC 16           /* counters one instruction waits on       */
 #define MK_MAX_DST 8            /* counters one instruction arrives on     */
 #define MK_INSTR_WORDS 64       /* int32 words per instruction record      */

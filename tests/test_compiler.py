@@ -25,7 +25,7 @@ def test_library_exports_every_declared_symbol():
     for n in names:
         assert hasattr(lib, n), n
     assert set(L.EXPORTS) <= set(names)
-    assert lib.mk_abi_version() == 4
+    assert lib.mk_abi_version() == 5
 
 
 def test_struct_layout_matches_decoder(tmp_path):
@@ -362,3 +362,19 @@ def test_noalloc_size_limit_checked_before_any_gpu_call():
         plan.run_noalloc([0] * 64, stream=0)
     assert ei.value.status == L.MK_E_LIMIT
     assert "64" in str(ei.value) or "67108864" in str(ei.value)
+
+
+def test_layer_stack_limits():
+    # Prefill decoder layers in sequence: five fit the 48 node descriptors
+    # the persistent kernel keeps in LDS (45 lowered nodes, 81 tensor slots
+    # of MK_MAX_TENSORS = 256); a sixth builds but is refused at run time.
+    d = workloads.default_dims("layer")
+    p5 = G.layer_stack(d, 5).build(num_cus=256)
+    assert p5.stats().n_slots == 81
+    with pytest.raises(L.MkError) as e:
+        p5.run([], stream=0)            # no GPU here: any error but "unsupported"
+    assert e.value.status != L.MK_E_UNSUPPORTED
+    p6 = G.layer_stack(d, 6).build(num_cus=256)
+    with pytest.raises(L.MkError) as e:
+        p6.run([], stream=0)
+    assert e.value.status == L.MK_E_UNSUPPORTED and "48 lowered nodes" in str(e.value)

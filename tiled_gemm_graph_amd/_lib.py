@@ -24,7 +24,7 @@ EP_BIAS, EP_RELU, EP_RESIDUAL, EP_SILU_MUL, EP_RMSNORM_INPUT, EP_ROPE, EP_PARTIA
     1, 2, 4, 8, 16, 32, 64)
 (I_NOOP, I_GEMM, I_GEMV, I_REDUCE, I_RMSNORM, I_ATTENTION, I_EW_ADD, I_EW_RELU, I_ATTN_PARTIAL,
  I_ATTN_COMBINE) = range(10)
-MAX_TENSORS, MAX_SRC, MAX_DST, INSTR_WORDS, NODE_WORDS = 64, 16, 8, 64, 64
+MAX_TENSORS, MAX_SRC, MAX_DST, INSTR_WORDS, NODE_WORDS = 256, 16, 8, 64, 64
 
 # word offsets of mk_instr (mirrors the struct; checked by tests)
 W_OPCODE, W_FLAGS, W_NODE, W_NSRC, W_NDST = 0, 1, 2, 3, 4
@@ -130,7 +130,7 @@ def load() -> ctypes.CDLL:
         f = getattr(L, name)
         f.argtypes = args
         f.restype = res
-    if L.mk_abi_version() != 4:
+    if L.mk_abi_version() != 5:
         raise ImportError("libmk.so ABI version mismatch")
     _lib = L
     return L

@@ -187,6 +187,46 @@ def build(workload: str, dims: Dict[str, int], tiles: Optional[Sequence[dict]] =
     raise KeyError(workload)
 
 
+def layer_stack(dims: Dict[str, int], n_layers: int, tiles: Optional[Sequence[dict]] = None) -> Graph:
+    """``n_layers`` of the prefill decoder layer in sequence (the layer
+    graph above, each with its own weights): tensors ``x``, per layer l the
+    weights ``g1_l, Wq_l, Wkv_l, Wo_l, g2_l, Wgu_l, Wd_l`` and the layer's
+    output ``out_l`` (the graph output for the last layer), which is the next
+    layer's input."""
+    g = Graph()
+    S, H = dims["seq"], dims["hidden"]
+    Hq, Hkv, hd, I = dims["heads"], dims["kv_heads"], dims["head_dim"], dims["inter"]
+    nq, nkv = Hq * hd, Hkv * hd
+    cur = g.tensor("x", "bf16", (S, H), "input")
+    for l in range(n_layers):
+        g1 = g.tensor(f"g1_{l}", "bf16", (H,), "weight")
+        Wq = g.tensor(f"Wq_{l}", "bf16", (H, nq), "weight")
+        Wkv = g.tensor(f"Wkv_{l}", "bf16", (H, 2 * nkv), "weight")
+        Wo = g.tensor(f"Wo_{l}", "bf16", (nq, H), "weight")
+        g2 = g.tensor(f"g2_{l}", "bf16", (H,), "weight")
+        Wgu = g.tensor(f"Wgu_{l}", "bf16", (H, 2 * I), "weight")
+        Wd = g.tensor(f"Wd_{l}", "bf16", (I, H), "weight")
+        xn = g.tensor(f"xn_{l}", "bf16", (S, H), "intermediate")
+        q = g.tensor(f"q_{l}", "bf16", (S, nq), "intermediate")
+        kv = g.tensor(f"kv_{l}", "bf16", (S, 2 * nkv), "intermediate")
+        o = g.tensor(f"o_{l}", "bf16", (S, nq), "intermediate")
+        h1 = g.tensor(f"h1_{l}", "bf16", (S, H), "intermediate")
+        hn = g.tensor(f"hn_{l}", "bf16", (S, H), "intermediate")
+        a = g.tensor(f"a_{l}", "bf16", (S, I), "intermediate")
+        out = g.tensor(f"out_{l}", "bf16", (S, H), "output" if l == n_layers - 1 else "intermediate")
+        g.rmsnorm(cur, g1, xn, tile=_t(tiles, 0))
+        g.gemm(xn, Wq, q, L.EP_ROPE, head_dim=hd, rope_cols=nq, tile=_t(tiles, 1))
+        g.gemm(xn, Wkv, kv, L.EP_ROPE, head_dim=hd, rope_cols=nkv, tile=_t(tiles, 2))
+        g.attention(q, g.cols(kv, 0, nkv), g.cols(kv, nkv, 2 * nkv), o, Hq, Hkv, hd, True,
+                    tile=_t(tiles, 3))
+        g.gemm(o, Wo, h1, L.EP_RESIDUAL, residual=cur, tile=_t(tiles, 4))
+        g.rmsnorm(h1, g2, hn, tile=_t(tiles, 5))
+        g.gemm(hn, Wgu, a, L.EP_SILU_MUL, tile=_t(tiles, 6))
+        g.gemm(a, Wd, out, L.EP_RESIDUAL, residual=h1, tile=_t(tiles, 7))
+        cur = out
+    return g
+
+
 def graph_inputs(workload: str, dims: Dict[str, int], inputs: Dict[str, "object"]) -> Dict[str, "object"]:
     """The graph's input and weight tensors from a workload's inputs: the
     layer's Wqkv is handed over as its q and k|v column blocks."""
