@@ -365,16 +365,42 @@ def test_noalloc_size_limit_checked_before_any_gpu_call():
 
 
 def test_layer_stack_limits():
-    # Prefill decoder layers in sequence: five fit the 48 node descriptors
-    # the persistent kernel keeps in LDS (45 lowered nodes, 81 tensor slots
-    # of MK_MAX_TENSORS = 256); a sixth builds but is refused at run time.
+    # Prefill decoder layers in sequence (9 lowered nodes each).  Up to 48
+    # nodes the persistent kernel keeps every node descriptor in LDS; beyond,
+    # a window of 48 consecutive ids per workgroup, which must hold the
+    # nodes of three consecutive records of a CU: fine for these layers
+    # (every node has at least 256 instructions), refused for the work queue.
     d = workloads.default_dims("layer")
-    p5 = G.layer_stack(d, 5).build(num_cus=256)
-    assert p5.stats().n_slots == 81
+    p14 = G.layer_stack(d, 14).build(num_cus=256)      # 126 nodes, 225 slots
+    assert p14.stats().n_nodes == 126 and p14.stats().n_slots == 225
     with pytest.raises(L.MkError) as e:
-        p5.run([], stream=0)            # no GPU here: any error but "unsupported"
+        p14.run([], stream=0)           # no GPU here: any error but "unsupported"
     assert e.value.status != L.MK_E_UNSUPPORTED
-    p6 = G.layer_stack(d, 6).build(num_cus=256)
+    pq = G.layer_stack(d, 6).build(num_cus=256, queue=1)
     with pytest.raises(L.MkError) as e:
-        p6.run([], stream=0)
-    assert e.value.status == L.MK_E_UNSUPPORTED and "48 lowered nodes" in str(e.value)
+        pq.run([], stream=0)
+    assert e.value.status == L.MK_E_UNSUPPORTED and "static placement" in str(e.value)
+    with pytest.raises(L.MkError) as e:
+        G.layer_stack(d, 15).build(num_cus=256)         # 241 data + rope tables > 256
+    assert e.value.status == L.MK_E_LIMIT
+
+
+def test_node_window_refuses_records_spanning_48_nodes():
+    # 60 tiny nodes (one instruction each, placed on CU i mod C): on 4 CUs
+    # three consecutive records of a CU span 9 nodes, fine; on 25 CUs CU 0
+    # holds nodes 0, 25 and 50, a span of 51 the window refuses
+    g = G.Graph()
+    cur = g.tensor("x", "f16", (64, 64), "input")
+    w = g.tensor("w", "f16", (64, 64), "weight")
+    for i in range(60):
+        y = g.tensor(f"y{i}", "f16", (64, 64), "output" if i == 59 else "intermediate")
+        g.gemm(cur, w, y, 0, tile=dict(bm=64, bn=64, gemv=0))
+        cur = y
+    ok = g.build(num_cus=4)
+    with pytest.raises(L.MkError) as e:
+        ok.run([], stream=0)
+    assert e.value.status != L.MK_E_UNSUPPORTED
+    bad = g.build(num_cus=25)
+    with pytest.raises(L.MkError) as e:
+        bad.run([], stream=0)
+    assert e.value.status == L.MK_E_UNSUPPORTED and "node window" in str(e.value)

@@ -1132,6 +1132,35 @@ struct Compiler {
     return o;
   }
 
+  // The persistent kernel keeps at most 48 node descriptors in LDS.  A plan
+  // of more nodes runs with a window of 48 consecutive node ids per
+  // workgroup, which must hold the nodes of every three consecutive records
+  // of a CU (the running one and the two fetched ahead); the work queue
+  // hands out records in an order this cannot bound.
+  void check_node_window() {
+    constexpr I64 kWindow = 48;
+    if ((I64)p.nodes.size() <= kWindow) return;
+    if (p.opts.queue) {
+      unsup("plans of more than 48 lowered nodes run in static placement only");
+      return;
+    }
+    const I64 n_iters = cdiv(p.n_instr, ncu);
+    for (I64 c = 0; c < ncu; ++c)
+      for (I64 it = 0; it < n_iters; ++it) {
+        int lo = -1, hi = -1;
+        for (I64 k = it; k < std::min(n_iters, it + 3); ++k) {
+          const mk_instr& r = p.records[(size_t)(k * ncu + c)];
+          if (r.opcode == MK_I_NOOP) continue;
+          lo = lo < 0 ? r.node : std::min(lo, r.node);
+          hi = std::max(hi, r.node);
+        }
+        if (lo >= 0 && hi - lo >= kWindow) {
+          unsup("three consecutive records of a CU span 48 or more lowered nodes (the LDS node window)");
+          return;
+        }
+      }
+  }
+
   void emit() {
     const I64 n_iters = cdiv(p.n_instr, ncu);
     p.records.assign((size_t)(n_iters * ncu), mk_instr{});
@@ -1279,11 +1308,11 @@ struct Compiler {
     p.n_graph_tensors = (int)g.t.size();
     p.ops = g.ops;
     lower();
-    if (p.nodes.size() > 48) unsup("more than 48 lowered nodes (the LDS node cache)");
     place();
     assign_slots();
     derive_barriers();
     emit();
+    check_node_window();
     algorithmic_counts();
     const_tables();
     p.stats.reserved = unsupported.empty() ? 0 : 1;

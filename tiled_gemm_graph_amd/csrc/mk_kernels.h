@@ -2078,7 +2078,52 @@ struct Loop {
   int vcu;
   int* idx;             // work-queue mode: record index of each slot, -1 = none
   int* seen;            // [kSeenSlots] counters this workgroup saw complete in this run
+  int* node_tag;        // [kMaxNodes] node id held by each descriptor slot (plans of more nodes)
 };
+
+// Node descriptors.  A plan of at most kMaxNodes nodes has all of them in
+// LDS (copied at launch).  A larger plan keeps a window: descriptor id in
+// slot id % kMaxNodes, its id in node_tag.  A workgroup's in-flight records
+// (the current one and the two fetched ahead) then need nodes that lie
+// within kMaxNodes of each other, which the compiler checks for every CU
+// (and it runs such plans in static placement only).
+__device__ __forceinline__ const mk_node& node_of(const Loop& L, int id) { return L.nodes[id % kMaxNodes]; }
+
+// Wave 0: make node ids lo..hi present (hi - lo < kMaxNodes).  On a miss,
+// every missing id of [lo, lo + kMaxNodes) is loaded, sixteen descriptors
+// per memory round trip.
+__device__ __forceinline__ void ensure_nodes(const Loop& L, int lo, int hi) {
+  if (L.a.n_nodes <= kMaxNodes || lo < 0) return;
+  bool miss = false;
+  for (int id = lo; id <= hi; ++id) miss |= L.node_tag[id % kMaxNodes] != id;
+  if (!miss) return;
+  const int lane = threadIdx.x & 63;
+  const int end = min(lo + kMaxNodes, L.a.n_nodes);
+  mk_node* slots = const_cast<mk_node*>(L.nodes);
+  for (int id0 = lo; id0 < end; id0 += 16) {
+    int v[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const int id = id0 + k;
+      v[k] = id < end && L.node_tag[id % kMaxNodes] != id ? reinterpret_cast<const int*>(L.a.nodes + id)[lane] : 0;
+    }
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const int id = id0 + k;
+      if (id < end && L.node_tag[id % kMaxNodes] != id)
+        reinterpret_cast<int*>(&slots[id % kMaxNodes])[lane] = v[k];
+    }
+  }
+  // tags after every lane's words are in place (one wave: LDS operations in order)
+  for (int id = lo + lane; id < end; id += 64) L.node_tag[id % kMaxNodes] = id;
+}
+
+// Node id of a record word set (lane 2 holds `node`, lane 0 `opcode`); -1
+// for a Noop.
+__device__ __forceinline__ int rec_node(int w) {
+  const int op = __builtin_amdgcn_readlane(w, 0), nd = __builtin_amdgcn_readlane(w, 2);
+  return op == MK_I_NOOP ? -1 : nd;
+}
 
 // Record index of local iteration it (the slot it % 3 holds it), and
 // whether there is one.  Static placement: column vcu of the list.  Work
@@ -2261,6 +2306,19 @@ __device__ __forceinline__ void store_ahead(const Loop& L, int it, int w, int tk
     if (threadIdx.x == 0) L.idx[(it + 2) % 3] = tk;
   } else if (it > 0 && it + 2 < L.a.n_iters) {
     reinterpret_cast<int*>(&L.slots[(it + 2) % 3])[threadIdx.x & 63] = w;
+    if (L.a.n_nodes > kMaxNodes) {
+      // the window holds the nodes of records it .. it + 2 (record it may
+      // still be running: the GEMV streak stores ahead before its body)
+      int lo = -1, hi = -1;
+      for (int k = 0; k < 3; ++k) {
+        const mk_instr& c = L.slots[(it + k) % 3];
+        const int nd = k == 2 ? rec_node(w) : (c.opcode == MK_I_NOOP ? -1 : c.node);
+        if (nd < 0) continue;
+        lo = lo < 0 ? nd : min(lo, nd);
+        hi = max(hi, nd);
+      }
+      ensure_nodes(L, lo, hi);
+    }
   }
 }
 
@@ -2276,7 +2334,7 @@ __device__ __forceinline__ bool generic_iter(const Loop& L, int it, int& w) {
   if constexpr ((OPS & kOpOther) != 0 && NT == kThreads) {
     if (in.opcode == MK_I_ATTN_PARTIAL) {
       // the KV cache rows are requested before the counters clear
-      const mk_node& nd = L.nodes[in.node];
+      const mk_node& nd = node_of(L, in.node);
       AttnPrefetch f;
       attn_partial_prefetch(a, in, nd, f);
       if (!wait_sources(L, in, it, gidx, w, tk)) return false;
@@ -2292,7 +2350,7 @@ __device__ __forceinline__ bool generic_iter(const Loop& L, int it, int& w) {
   }
   if (!wait_sources(L, in, it, gidx, w, tk)) return false;
   if (in.opcode != MK_I_NOOP) {
-    const mk_node& nd = L.nodes[in.node];
+    const mk_node& nd = node_of(L, in.node);
     if (tr) stamp(a, gidx, 1, wall_clock64());
     run_instr<OPS, NT>(a, in, nd, L.smem);
     if (tr) stamp(a, gidx, 2, wall_clock64());
@@ -2325,12 +2383,12 @@ __device__ __forceinline__ int gemv_streak(const Loop& L, int& it, int& w) {
   int s0 = 0;
   {
     const mk_instr& in = L.slots[it % 3];
-    gemv_prologue(a, in, L.nodes[in.node], B);
+    gemv_prologue(a, in, node_of(L, in.node), B);
   }
   for (;;) {
     const int gidx = rec_index(L, it);
     const mk_instr& in = L.slots[it % 3];
-    const mk_node& nd = L.nodes[in.node];
+    const mk_node& nd = node_of(L, in.node);
     const bool tr = a.trace && threadIdx.x == 0;
     if (tr) stamp(a, gidx, 0, wall_clock64());
     int tk = -1;
@@ -2347,9 +2405,9 @@ __device__ __forceinline__ int gemv_streak(const Loop& L, int& it, int& w) {
     const mk_node* nxd = nullptr;
     if (has_rec(L, it + 1)) {
       const mk_instr& c = L.slots[(it + 1) % 3];
-      if (c.opcode == MK_I_GEMV && L.nodes[c.node].dtype == nd.dtype) {
+      if (c.opcode == MK_I_GEMV && node_of(L, c.node).dtype == nd.dtype) {
         nx = &c;
-        nxd = &L.nodes[c.node];
+        nxd = &node_of(L, c.node);
       }
     }
     s0 = gemv_body_rows<DT>(a, in, nd, L.smem, B, nx, nxd, s0);
@@ -2376,17 +2434,20 @@ __global__ void __launch_bounds__(NT, 1) mk_persistent(mkd::KArgs args) {
   __shared__ int s_flag;
   __shared__ int s_idx[3];
   __shared__ int s_seen[mkd::kSeenSlots];
+  __shared__ int s_node_tag[mkd::kMaxNodes];
   __shared__ __attribute__((aligned(16))) char smem[mkd::kSmemBytes];
   const int t = threadIdx.x;
   const int b = blockIdx.x;
   if (t < mkd::kSeenSlots) s_seen[t] = -1;
+  if (t < mkd::kMaxNodes) s_node_tag[t] = -1;
   // Workgroup b runs column b of the placement, so consecutive instructions
   // land on different XCDs (b % 8), as a grid launch would place them.
   // Keeping 32 consecutive instructions on one XCD instead (for L2 sharing)
   // measured 0-3 % slower on every workload.
   const int vcu = b;
-  for (int i = t; i < a.n_nodes * 64; i += NT)
-    reinterpret_cast<int*>(s_nodes)[i] = reinterpret_cast<const int*>(a.nodes)[i];
+  if (a.n_nodes <= mkd::kMaxNodes)
+    for (int i = t; i < a.n_nodes * 64; i += NT)
+      reinterpret_cast<int*>(s_nodes)[i] = reinterpret_cast<const int*>(a.nodes)[i];
   if (a.queue) {
     // clear the other ticket word for the next run; take iterations 0 and 1
     if (b == 0 && t < 8)
@@ -2414,13 +2475,27 @@ __global__ void __launch_bounds__(NT, 1) mk_persistent(mkd::KArgs args) {
     clk[0] = wall_clock64();
     clk[1] = __builtin_amdgcn_s_memtime();
   }
-  const mkd::Loop L{a, s_in, s_nodes, &s_flag, smem, vcu, s_idx, s_seen};
+  const mkd::Loop L{a, s_in, s_nodes, &s_flag, smem, vcu, s_idx, s_seen, s_node_tag};
+  if (a.n_nodes > mkd::kMaxNodes) {
+    // a windowed plan (static placement): the nodes of records 0 .. 2
+    if (t < 64) {
+      int lo = -1, hi = -1;
+      for (int r = 0; r < 3 && r < a.n_iters; ++r) {
+        if (s_in[r].opcode == MK_I_NOOP) continue;
+        const int nd = s_in[r].node;
+        lo = lo < 0 ? nd : min(lo, nd);
+        hi = max(hi, nd);
+      }
+      mkd::ensure_nodes(L, lo, hi);
+    }
+    __syncthreads();
+  }
   int it = 0, w = 0;
   while (mkd::has_rec(L, it)) {
     const mk_instr& in = s_in[it % 3];
     if constexpr ((OPS & mkd::kOpGemv) != 0) {
       if (in.opcode == MK_I_GEMV) {
-        const int st = s_nodes[in.node].dtype == MK_BF16 ? mkd::gemv_streak<MK_BF16>(L, it, w)
+        const int st = mkd::node_of(L, in.node).dtype == MK_BF16 ? mkd::gemv_streak<MK_BF16>(L, it, w)
                                                         : mkd::gemv_streak<MK_F16>(L, it, w);
         if (st < 0) return;
         continue;
