@@ -72,6 +72,16 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
+// The thread index, read afresh at each use: the empty volatile asm keeps
+// the compiler from hoisting values derived from it out of the persistent
+// loop, where every body's per-thread offsets would otherwise stay live (and
+// spill) across all the other bodies of the kernel.
+__device__ __forceinline__ int tid() {
+  int t = threadIdx.x;
+  asm volatile("" : "+v"(t));
+  return t;
+}
+
 // ---------------------------------------------------------------- numerics
 __device__ __forceinline__ float bf16_to_f(u16 h) { return __uint_as_float((uint32_t)h << 16); }
 __device__ __forceinline__ float f16_to_f(u16 h) { return (float)__builtin_bit_cast(_Float16, h); }
@@ -143,9 +153,9 @@ __device__ __forceinline__ float wave_sum(float v) {
 template <int NT = kThreads>
 __device__ __forceinline__ float block_sum(float v, float* red) {
   v = wave_sum(v);
-  const int w = threadIdx.x >> 6;
+  const int w = tid() >> 6;
   __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[w] = v;
+  if ((tid() & 63) == 0) red[w] = v;
   __syncthreads();
   float s = red[0];
 #pragma unroll
@@ -165,7 +175,7 @@ __device__ __forceinline__ void lds_barrier() {
 // masking), so waits inside a branch are executed only by the waves that
 // take it.  Each wave's vector-memory counter is its own; a wait emitted in
 // code that every wave runs would also drain the other waves' streams.
-__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6); }
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(tid() >> 6); }
 
 // A value every lane holds the same (record and node fields read from LDS),
 // moved to a scalar register: loop bounds and branches on it become scalar
@@ -277,7 +287,7 @@ __device__ __forceinline__ void gemm_tile(const KArgs& a, const mk_instr& in, co
 
   u16* As = reinterpret_cast<u16*>(smem);
   u16* Bs = As + 2 * A_STAGE;
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int t = tid(), lane = t & 63, wave = t >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int flags = uni(in.flags);
   const bool silu = flags & MK_EP_SILU_MUL;
@@ -516,16 +526,28 @@ __device__ __forceinline__ void bare_barrier() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-// NW waves (4 or 8) in a (NW / 2) x 2 grid, each WM x WN = BM / (NW / 2) x
-// BN / 2.  With eight waves two share each SIMD, so one wave's MFMAs run
-// while the other issues loads or waits at a barrier.
+// Four waves: a 2 x 2 grid, each wave WM x WN = BM / 2 x BN / 2 over the
+// whole K range.  Eight waves (two per SIMD, so one wave's MFMAs run while
+// the other issues loads or waits at a barrier), with MK_GEMM_KSPLIT
+// (default): the same 2 x 2 grid of WM x WN blocks, each held by a pair of
+// waves w and w + 4 that take the first and the second half of every
+// 64-deep K stage (sub-steps 0-1 and 2-3) and add their sums in the
+// epilogue.  A wave's block is then twice as large as in a 4 x 2 grid of
+// eight waves, so each MFMA needs a quarter fewer LDS operand bytes.
+// Without it: a 4 x 2 grid of eight whole-K waves.
+#ifndef MK_GEMM_KSPLIT
+#define MK_GEMM_KSPLIT 1
+#endif
 template <int BM, int BN, int DT, int NW = 4>
 __device__ __forceinline__ void gemm_packed_tile(const KArgs& a, const mk_instr& in, const mk_node& nd,
                                                  char* smem) {
   constexpr int NT = NW * 64;
   constexpr int ROWB = 128;                         // bytes per LDS row: 64 k values
   constexpr int A_BYTES = BM * ROWB, STAGE = (BM + BN) * ROWB;
-  constexpr int WGM = NW / 2;                       // wave rows (two wave columns)
+  constexpr bool KS = NW == 8 && MK_GEMM_KSPLIT;    // wave pairs split each K stage
+  constexpr int NB = KS ? NW / 2 : NW;              // waves (or pairs) with distinct blocks
+  constexpr int WGM = NB / 2;                       // wave rows (two wave columns)
+  constexpr int SUB = KS ? 2 : 4;                   // 16-deep sub-steps per stage per wave
   constexpr int WM = BM / WGM, WN = BN / 2, FM = WM / 32, FN = WN / 32;
   static_assert(FM >= 1 && FN >= 1, "every wave holds whole 32 x 32 blocks");
   constexpr int A_LOADS = BM / (8 * NW), B_LOADS = BN / (8 * NW);  // 16-byte loads per thread per stage
@@ -533,8 +555,10 @@ __device__ __forceinline__ void gemm_packed_tile(const KArgs& a, const mk_instr&
   constexpr int ST = (kSmemBytes / STAGE) < 4 ? (kSmemBytes / STAGE) : 4;
   static_assert(ST >= 2, "two stages must fit in LDS");
   constexpr int L = A_LOADS + B_LOADS;                 // loads per thread per stage
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int t = tid(), lane = t & 63, wave = t >> 6;
+  const int blk = KS ? (wave & 3) : wave;           // output block of this wave
+  const int kh = KS ? (wave >> 2) : 0;              // K half of the stage (pairs)
+  const int wm = blk >> 1, wn = blk & 1;
   const int flags = uni(in.flags);
   const int M = uni(nd.M), N = uni(nd.N), K = uni(nd.K);
   const int r0 = uni(in.r0), c0 = uni(in.c0), k0 = uni(in.k0), k1 = uni(in.k1);
@@ -584,10 +608,11 @@ __device__ __forceinline__ void gemm_packed_tile(const KArgs& a, const mk_instr&
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-  // Operand fragments of the four 16-deep sub-steps of a stage,
-  // double-buffered: the LDS reads of sub-step kk + 1 are in flight during
-  // kk's MFMAs, and those of the next stage's first sub-step during this
-  // stage's last one, so no sub-step waits out a whole LDS round trip.
+  // Operand fragments of a wave's 16-deep sub-steps of a stage (four, or
+  // two in a K-split pair), double-buffered: the LDS reads of the next
+  // sub-step are in flight during this one's MFMAs, and those of the next
+  // stage's first sub-step during this stage's last one, so no sub-step
+  // waits out a whole LDS round trip.
   u32x4 af[2][FM], bf[2][FN];
   auto frags = [&](const char* __restrict__ st, int kk, int b) __attribute__((always_inline)) {
     const int c = kk * 2 + (lane >> 5);
@@ -602,9 +627,10 @@ __device__ __forceinline__ void gemm_packed_tile(const KArgs& a, const mk_instr&
       bf[b][j] = *reinterpret_cast<const u32x4*>(st + A_BYTES + row * ROWB + ((c ^ ((row >> 1) & 7)) << 4));
     }
   };
-  auto mma = [&](int kk, int q) __attribute__((always_inline)) {
+  // MFMA q of the sub-step whose fragments are in buffer b
+  auto mma = [&](int b, int q) __attribute__((always_inline)) {
     const int i = q / FN, j = q % FN;
-    acc[i][j] = mfma32<DT>(af[kk & 1][i], bf[kk & 1][j], acc[i][j]);
+    acc[i][j] = mfma32<DT>(af[b][i], bf[b][j], acc[i][j]);
   };
   // Wait until stage s has landed in this wave, leaving the `younger`
   // stages issued after it in flight (each stage is L loads per thread),
@@ -631,10 +657,12 @@ __device__ __forceinline__ void gemm_packed_tile(const KArgs& a, const mk_instr&
     if (s < nk)
 #pragma unroll
       for (int q = 0; q < L; ++q) load_one(s, s, q);
+  // sub-steps of this wave: kb, kb + 1, ... kb + SUB - 1 (wave-uniform)
+  const int kb = uni(kh * 2);
   if (nk > 0) {
     land(min(ST - 1, nk - 1));
     bare_barrier();
-    frags(smem, 0, 0);
+    frags(smem, kb, 0);
   }
   // Stage kt in buffer U = kt % ST (a compile-time index in each copy).  One
   // straight path for every stage (the last one waits for nothing and reads
@@ -644,18 +672,18 @@ __device__ __forceinline__ void gemm_packed_tile(const KArgs& a, const mk_instr&
     constexpr int u = decltype(U)::value;
     const char* __restrict__ cur = smem + u * STAGE;
 #pragma unroll
-    for (int kk = 0; kk < 3; ++kk) {
-      frags(cur, kk + 1, (kk + 1) & 1);
+    for (int kk = 0; kk < SUB - 1; ++kk) {
+      frags(cur, kb + kk + 1, (kk + 1) & 1);
 #pragma unroll
-      for (int q = 0; q < NQ; ++q) mma(kk, q);
+      for (int q = 0; q < NQ; ++q) mma(kk & 1, q);
     }
     land(min(ST - 2, nk - 2 - kt));
     bare_barrier();
-    frags(smem + ((u + 1) % ST) * STAGE, 0, 0);
+    frags(smem + ((u + 1) % ST) * STAGE, kb, 0);
     const bool more = kt + ST < nk;
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
-      mma(3, q);
+      mma((SUB - 1) & 1, q);
       if (more) {
 #pragma unroll
         for (int l = q * L / NQ; l < (q + 1) * L / NQ; ++l) load_one(kt + ST, u, l);
@@ -688,12 +716,21 @@ __device__ __forceinline__ void gemm_packed_tile(const KArgs& a, const mk_instr&
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
     __syncthreads();   // the previous strip (or the last K stage) is consumed
+    // a K-split pair: the first half's sums are stored, then the second
+    // half adds its own (same lane, same element)
 #pragma unroll
-    for (int jj = 0; jj < FN; ++jj)
+    for (int h = 0; h < (KS ? 2 : 1); ++h) {
+      if (h == 1) __syncthreads();
+      if (kh == h) {
 #pragma unroll
-      for (int e = 0; e < 16; ++e)
-        Cs[(wm * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3)) * CS + wn * WN + jj * 32 + (lane & 31)] =
-            acc[i][jj][e];
+        for (int jj = 0; jj < FN; ++jj)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            float* c = &Cs[(wm * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3)) * CS + wn * WN + jj * 32 + (lane & 31)];
+            *c = h ? *c + acc[i][jj][e] : acc[i][jj][e];
+          }
+      }
+    }
     __syncthreads();
     for (int u = t; u < UNITS; u += NT) {
       const int sr = u / (BN / 8), w = (u % (BN / 8)) * 8;   // strip row, weight column
@@ -762,7 +799,7 @@ struct GemvShape {
 __device__ __forceinline__ GemvShape gemv_shape(const mk_instr& in, const mk_node& nd) {
   GemvShape g;
   const bool silu = in.flags & MK_EP_SILU_MUL;
-  const int tw = (int)threadIdx.x - 64;
+  const int tw = tid() - 64;
   g.bw = in.c1 - in.c0;
   g.wc = silu ? 2 * g.bw : g.bw;
   g.ncg = g.wc / 8;
@@ -879,7 +916,7 @@ template <int DT, int MAXR>
 __device__ __forceinline__ void gemv_packed_prepare(const KArgs& a, const mk_node& nd, int flags, int r0,
                                                     int c0, int rows, int bw, int wc, const float* sq,
                                                     PackedEp& ep) {
-  const int npair = bw >> 1, u = threadIdx.x & 63;
+  const int npair = bw >> 1, u = tid() & 63;
   if (u >= rows * npair) return;
   const int m = u / npair, q = (u - m * npair) * 2, gr = r0 + m;
   const bool rot = (flags & MK_EP_ROPE) && c0 + q < nd.rope_cols;
@@ -918,8 +955,8 @@ __device__ __forceinline__ void gemv_store_packed(const KArgs& a, const mk_node&
   const int hd = nd.head_dim, hh = hd >> 1;
   const int npair = bw >> 1;
   u16* O = buf<u16>(a, nd.out);
-  for (int u = threadIdx.x; u < rows * npair; u += 64) {
-    const bool first = u == (int)threadIdx.x;
+  for (int u = tid(); u < rows * npair; u += 64) {
+    const bool first = u == tid();
     float v[2], cs = 0.f, sn = 0.f;
     long off[2];
     bool rot;
@@ -992,7 +1029,7 @@ template <int DT, int MAXR, int S0>
 __device__ __forceinline__ void gemv_body(const KArgs& a, const mk_instr& in, const mk_node& nd, char* smem,
                                           u32x4 (&B)[kGemvBufs][kGemvBatch], const mk_instr* nx,
                                           const mk_node* nxd) {
-  const int t = threadIdx.x;
+  const int t = tid();
   const int flags = in.flags;
   const bool silu = flags & MK_EP_SILU_MUL, rms = flags & MK_EP_RMSNORM_INPUT;
   const int N = nd.N, r0 = in.r0, rows = in.r1 - in.r0, c0 = in.c0, k0 = in.k0;
@@ -1212,7 +1249,7 @@ __device__ __forceinline__ int gemv_body_rows(const KArgs& a, const mk_instr& in
 // ---------------------------------------------------------------- REDUCE
 template <int DT, int NT = kThreads>
 __device__ __forceinline__ void reduce_tile(const KArgs& a, const mk_instr& in, const mk_node& nd, char* smem) {
-  const int t = threadIdx.x;
+  const int t = tid();
   const int flags = in.flags;
   const bool silu = flags & MK_EP_SILU_MUL, rms = flags & MK_EP_RMSNORM_INPUT;
   const int N = nd.N, S = nd.split, K = nd.K;
@@ -1307,7 +1344,7 @@ __device__ __forceinline__ void reduce_tile(const KArgs& a, const mk_instr& in, 
 template <int DT, int CPT, int NT = kThreads>
 __device__ __forceinline__ void rmsnorm_rows(const KArgs& a, const mk_instr& in, const mk_node& nd, char* smem) {
   constexpr int RMAX = 16 / CPT;                // rows per group
-  const int t = threadIdx.x, H = nd.N, w = wave_id();
+  const int t = tid(), H = nd.N, w = wave_id();
   constexpr int NW = NT / 64;
   float* part = reinterpret_cast<float*>(smem);  // [NW waves][RMAX] sums of squares
   const u16* X = buf<const u16>(a, nd.a);
@@ -1379,7 +1416,7 @@ __device__ __forceinline__ void rmsnorm_rows(const KArgs& a, const mk_instr& in,
 
 template <int DT, int NT = kThreads>
 __device__ __forceinline__ void rmsnorm_tile(const KArgs& a, const mk_instr& in, const mk_node& nd, char* smem) {
-  const int t = threadIdx.x;
+  const int t = tid();
   const int H = nd.N;
   const int cpt = (H / 8 + NT - 1) / NT;   // 16-byte chunks per thread and row
   if (cpt <= 1) return rmsnorm_rows<DT, 1, NT>(a, in, nd, smem);
@@ -1428,7 +1465,7 @@ __device__ __forceinline__ void attention_tile(const KArgs& a, const mk_instr& i
   constexpr int HALF_ELEMS = KBLK * KS + D * VS;  // a half's K / V^T staging (elements)
   static_assert(NH * HALF_ELEMS * 2 <= kSmemBytes && (4 * 64 * 64 + 2 * 4 * 64) * 4 <= kSmemBytes,
                 "attention LDS");
-  const int t = threadIdx.x, lane = t & 63, wave = (t >> 6) & 3, hh = t >> 8, g = lane >> 5, l32 = lane & 31;
+  const int t = tid(), lane = t & 63, wave = (t >> 6) & 3, hh = t >> 8, g = lane >> 5, l32 = lane & 31;
   const int t4 = t & 255;
   u16* Ks = reinterpret_cast<u16*>(smem) + hh * HALF_ELEMS;   // [64][136]
   u16* Vt = Ks + KBLK * KS;                                    // [128][72]
@@ -1633,7 +1670,7 @@ struct AttnPrefetch {
 // for kl < nr (the chunk's rows); zero beyond.
 __device__ __forceinline__ void attn_issue_kv(const KArgs& a, const mk_node& nd, int g, int j0, int nr, int ps,
                                               u32x4* kr, u32x4* vr) {
-  const int lane = threadIdx.x & 63, w = wave_id();
+  const int lane = tid() & 63, w = wave_id();
   const int sub = lane >> 4, part = lane & 15;
   const u16* Kc = buf<const u16>(a, nd.bias) + (long)g * kAttnD + part * 8;
   const u16* Vc = buf<const u16>(a, nd.gamma) + (long)g * kAttnD + part * 8;
@@ -1656,8 +1693,8 @@ __device__ __forceinline__ void attn_partial_prefetch(const KArgs& a, const mk_i
   f.p = uni(*buf<const int>(a, nd.part));
   const int pc = min(max(f.p, 0), S - 1);     // the table row stays in bounds for any p
   const float* tab = buf<const float>(a, nd.aux) + (long)pc * kAttnD;   // [cos | sin] of position p
-  f.cs = tab[threadIdx.x & 63];
-  f.sn = tab[64 + (threadIdx.x & 63)];
+  f.cs = tab[tid() & 63];
+  f.sn = tab[64 + (tid() & 63)];
   attn_issue_kv(a, nd, uni(in.c0), j0, uni(in.r1) - j0, 0, f.kr, f.vr);
 }
 
@@ -1666,7 +1703,7 @@ __device__ __forceinline__ void attn_partial_run(const KArgs& a, const mk_instr&
                                                  AttnPrefetch& f) {
   constexpr int D = kAttnD, HALF = 64, KPASS = kAttnPass, GR = kAttnGroups;
   static_assert((8 * D + D + 8 * 256 + 32) * 4 + 256 * D * 2 <= kSmemBytes, "decode attention LDS");
-  const int t = threadIdx.x, lane = t & 63, w = wave_id();
+  const int t = tid(), lane = t & 63, w = wave_id();
   const int sub = lane >> 4, part = lane & 15;   // key within a group of four; dimensions 8 part .. 8 part + 7
   const int g = uni(in.c0), G = uni(in.c1), S = uni(nd.seq), Hq = uni(nd.heads);
   const int p = f.p;
@@ -1857,7 +1894,7 @@ __device__ __forceinline__ void attn_partial_tile(const KArgs& a, const mk_instr
 template <int DT>
 __device__ __forceinline__ void attn_combine_tile(const KArgs& a, const mk_instr& in, const mk_node& nd) {
   constexpr int D = 128, W = D + 4, B = 32;
-  const int t = threadIdx.x;
+  const int t = tid();
   const int g = uni(in.c0), G = uni(in.c1), S = uni(nd.seq), Hq = uni(nd.heads), C = uni(nd.K);
   const int p = uni(*buf<const int>(a, nd.part));
   u16* O = buf<u16>(a, nd.out) + (long)g * G * D;
@@ -1907,7 +1944,7 @@ __device__ __forceinline__ void attn_combine_tile(const KArgs& a, const mk_instr
 // ----------------------------------------------------------- elementwise
 template <int DT, int NT = kThreads>
 __device__ __forceinline__ void elementwise_tile(const KArgs& a, const mk_instr& in, const mk_node& nd) {
-  const int t = threadIdx.x;
+  const int t = tid();
   const bool add = in.opcode == MK_I_EW_ADD;
   const int wcols = in.c1 - in.c0, units = (in.r1 - in.r0) * (wcols / 8);
   const u16* A = buf<const u16>(a, nd.a);
@@ -1971,13 +2008,12 @@ __device__ __forceinline__ void run_body(const KArgs& a, const mk_instr& in, con
     case MK_I_GEMM:
       if constexpr (!(OPS & kOpGemm)) break;
       else if constexpr (NT == 512) {
-        ArgsK* ak = (ArgsK*)&a;
-        InstrL* il = (InstrL*)&in;
-        NodeL* nl = (NodeL*)&nd;
-        CharL* sl = (CharL*)smem;
-        if (nd.tile_m == 256 && nd.tile_n == 128) gemm_packed_call<256, 128, DT, 8>(ak, il, nl, sl);
-        else if (nd.tile_m == 128 && nd.tile_n == 256) gemm_packed_call<128, 256, DT, 8>(ak, il, nl, sl);
-        else gemm_packed_call<128, 128, DT, 8>(ak, il, nl, sl);
+        // inline: the K loop keeps its operand offsets in registers, and a
+        // call would save and restore the callee-saved registers it uses
+        // (about 300 bytes per lane) through scratch memory on every tile
+        if (nd.tile_m == 256 && nd.tile_n == 128) gemm_packed_tile<256, 128, DT, 8>(a, in, nd, smem);
+        else if (nd.tile_m == 128 && nd.tile_n == 256) gemm_packed_tile<128, 256, DT, 8>(a, in, nd, smem);
+        else gemm_packed_tile<128, 128, DT, 8>(a, in, nd, smem);
       } else {
         ArgsK* ak = (ArgsK*)&a;
         InstrL* il = (InstrL*)&in;
@@ -2029,7 +2065,7 @@ __device__ __forceinline__ void run_instr(const KArgs& a, const mk_instr& in, co
 
 // ----------------------------------------------------- counters and waits
 __device__ __forceinline__ void copy_words(int* dst, const int* src) {
-  if (threadIdx.x < 64) dst[threadIdx.x] = src[threadIdx.x];
+  if (tid() < 64) dst[tid()] = src[tid()];
 }
 
 // Arrival on the destination counters, lane k of the controller wave
@@ -2037,7 +2073,7 @@ __device__ __forceinline__ void copy_words(int* dst, const int* src) {
 // get an agent-scope add (the counter layout of mk.h).  Callers have made
 // the instruction's results visible at agent scope first.
 __device__ __forceinline__ void arrive(const KArgs& a, const mk_instr& in) {
-  const int lane = threadIdx.x & 63;
+  const int lane = tid() & 63;
   if (lane < in.n_dst) {
     int* c = a.counters + (long)in.dst_id[lane] * a.ctr_stride;
     const int rank = in.dst_rank[lane];
@@ -2053,7 +2089,7 @@ __device__ __forceinline__ void release_dests(const KArgs& a, const mk_instr& in
   __syncthreads();
   if (wave_id() == 0 && in.n_dst) {
     // GEMM tiles stored through to the coherent level: completion suffices
-    if (threadIdx.x == 0 && in.opcode != MK_I_GEMM) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    if (tid() == 0 && in.opcode != MK_I_GEMM) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     arrive(a, in);
   }
 }
@@ -2097,7 +2133,7 @@ __device__ __forceinline__ void ensure_nodes(const Loop& L, int lo, int hi) {
   bool miss = false;
   for (int id = lo; id <= hi; ++id) miss |= L.node_tag[id % kMaxNodes] != id;
   if (!miss) return;
-  const int lane = threadIdx.x & 63;
+  const int lane = tid() & 63;
   const int end = min(lo + kMaxNodes, L.a.n_nodes);
   mk_node* slots = const_cast<mk_node*>(L.nodes);
   for (int id0 = lo; id0 < end; id0 += 16) {
@@ -2147,7 +2183,7 @@ __device__ __forceinline__ bool has_rec(const Loop& L, int it) {
 __device__ __forceinline__ int take_ticket(const KArgs& a, int vcu) {
   const int q = a.queue == 2 ? (vcu & 7) : 0;
   int tk = 0;
-  if ((threadIdx.x & 63) == 0)
+  if ((tid() & 63) == 0)
     tk = __hip_atomic_fetch_add(a.ticket + 2 * q + (a.epoch & 1), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   tk = __shfl(tk, 0, 64);
   const long idx = a.queue == 2 ? (long)tk * 8 + q : (long)tk;
@@ -2162,11 +2198,11 @@ __device__ __forceinline__ void stamp(const KArgs& a, int gidx, int k, unsigned 
 // the load is unconditional).
 __device__ __forceinline__ int fetch_ahead(const Loop& L, int it) {
   const long r = min(it + 2, L.a.n_iters - 1);
-  return reinterpret_cast<const int*>(L.a.instrs + r * L.a.ncu + L.vcu)[threadIdx.x & 63];
+  return reinterpret_cast<const int*>(L.a.instrs + r * L.a.ncu + L.vcu)[tid() & 63];
 }
 // Wave 0, work-queue mode: this lane's word of record tk (0 when tk < 0).
 __device__ __forceinline__ int fetch_record(const Loop& L, int tk) {
-  return tk >= 0 ? reinterpret_cast<const int*>(L.a.instrs + tk)[threadIdx.x & 63] : 0;
+  return tk >= 0 ? reinterpret_cast<const int*>(L.a.instrs + tk)[tid() & 63] : 0;
 }
 
 // Start of iteration it.  Wave 0 issues the load of record it + 2 (used at
@@ -2185,7 +2221,7 @@ constexpr int kSeenSlots = 64;   // direct-mapped record of counters seen comple
 constexpr int kPollNapMax = 8;   // longest pause between polls, in units of 64 cycles
 __device__ __forceinline__ bool poll_sources(const Loop& L, const mk_instr& in, int gidx) {
   const KArgs& a = L.a;
-  const int lane = threadIdx.x & 63;
+  const int lane = tid() & 63;
   const int ns = in.n_src;
   // A counter only grows during a run, so one this workgroup has already
   // seen complete (and acquired) is not polled again: later instructions on
@@ -2284,7 +2320,7 @@ __device__ __forceinline__ bool wait_sources(const Loop& L, const mk_instr& in, 
       if (it > 0) w = fetch_ahead(L, it);
       ok = poll_sources(L, in, gidx);
     }
-    if (threadIdx.x == 0) *L.flag = ok;
+    if (tid() == 0) *L.flag = ok;
   }
   lds_barrier();
   return *L.flag != 0;
@@ -2302,10 +2338,10 @@ __device__ __forceinline__ bool wait_sources(const Loop& L, const mk_instr& in, 
 __device__ __forceinline__ void store_ahead(const Loop& L, int it, int w, int tk) {
   if (wave_id() != 0) return;
   if (L.a.queue) {
-    if (tk >= 0) reinterpret_cast<int*>(&L.slots[(it + 2) % 3])[threadIdx.x & 63] = w;
-    if (threadIdx.x == 0) L.idx[(it + 2) % 3] = tk;
+    if (tk >= 0) reinterpret_cast<int*>(&L.slots[(it + 2) % 3])[tid() & 63] = w;
+    if (tid() == 0) L.idx[(it + 2) % 3] = tk;
   } else if (it > 0 && it + 2 < L.a.n_iters) {
-    reinterpret_cast<int*>(&L.slots[(it + 2) % 3])[threadIdx.x & 63] = w;
+    reinterpret_cast<int*>(&L.slots[(it + 2) % 3])[tid() & 63] = w;
     if (L.a.n_nodes > kMaxNodes) {
       // the window holds the nodes of records it .. it + 2 (record it may
       // still be running: the GEMV streak stores ahead before its body)
@@ -2328,7 +2364,7 @@ __device__ __forceinline__ bool generic_iter(const Loop& L, int it, int& w) {
   const KArgs& a = L.a;
   const int gidx = rec_index(L, it);
   const mk_instr& in = L.slots[it % 3];
-  const bool tr = a.trace && threadIdx.x == 0 && in.opcode != MK_I_NOOP;
+  const bool tr = a.trace && tid() == 0 && in.opcode != MK_I_NOOP;
   if (tr) stamp(a, gidx, 0, wall_clock64());
   int tk = -1;
   if constexpr ((OPS & kOpOther) != 0 && NT == kThreads) {
@@ -2389,7 +2425,7 @@ __device__ __forceinline__ int gemv_streak(const Loop& L, int& it, int& w) {
     const int gidx = rec_index(L, it);
     const mk_instr& in = L.slots[it % 3];
     const mk_node& nd = node_of(L, in.node);
-    const bool tr = a.trace && threadIdx.x == 0;
+    const bool tr = a.trace && tid() == 0;
     if (tr) stamp(a, gidx, 0, wall_clock64());
     int tk = -1;
     if (!wait_sources(L, in, it, gidx, w, tk)) return -1;
@@ -2436,7 +2472,7 @@ __global__ void __launch_bounds__(NT, 1) mk_persistent(mkd::KArgs args) {
   __shared__ int s_seen[mkd::kSeenSlots];
   __shared__ int s_node_tag[mkd::kMaxNodes];
   __shared__ __attribute__((aligned(16))) char smem[mkd::kSmemBytes];
-  const int t = threadIdx.x;
+  const int t = mkd::tid();
   const int b = blockIdx.x;
   if (t < mkd::kSeenSlots) s_seen[t] = -1;
   if (t < mkd::kMaxNodes) s_node_tag[t] = -1;
