@@ -1974,20 +1974,6 @@ __device__ __forceinline__ void elementwise_tile(const KArgs& a, const mk_instr&
 // same tile ran 8-16 % slower than in a one-tile kernel.  The pointers keep
 // their address spaces (kernel arguments, LDS), so every access in the body
 // stays a scalar or an LDS access.
-typedef __attribute__((address_space(4))) const KArgs ArgsK;
-typedef __attribute__((address_space(3))) const mk_instr InstrL;
-typedef __attribute__((address_space(3))) const mk_node NodeL;
-typedef __attribute__((address_space(3))) char CharL;
-
-template <int BM, int BN, int DT, int NW = 4>
-__device__ __attribute__((noinline)) void gemm_packed_call(ArgsK* a, InstrL* in, NodeL* nd, CharL* smem) {
-  gemm_packed_tile<BM, BN, DT, NW>(*(const KArgs*)a, *(const mk_instr*)in, *(const mk_node*)nd, (char*)smem);
-}
-template <int BM, int BN, int DT>
-__device__ __attribute__((noinline)) void gemm_call(ArgsK* a, InstrL* in, NodeL* nd, CharL* smem) {
-  gemm_tile<BM, BN, DT>(*(const KArgs*)a, *(const mk_instr*)in, *(const mk_node*)nd, (char*)smem);
-}
-
 // Op families compiled into a kernel instance.  A plan runs on the smallest
 // instance whose families cover its instructions: leaving the other bodies
 // out keeps their registers and code away from the loop that runs.
@@ -2006,27 +1992,23 @@ __device__ __forceinline__ void run_body(const KArgs& a, const mk_instr& in, con
   if (!(op_family(in.opcode) & OPS)) return;
   switch (in.opcode) {
     case MK_I_GEMM:
+      // The tile bodies are inlined: a call would save and restore the
+      // callee-saved registers a body uses (300-550 bytes per lane) through
+      // scratch memory on every tile.
       if constexpr (!(OPS & kOpGemm)) break;
       else if constexpr (NT == 512) {
-        // inline: the K loop keeps its operand offsets in registers, and a
-        // call would save and restore the callee-saved registers it uses
-        // (about 300 bytes per lane) through scratch memory on every tile
         if (nd.tile_m == 256 && nd.tile_n == 128) gemm_packed_tile<256, 128, DT, 8>(a, in, nd, smem);
         else if (nd.tile_m == 128 && nd.tile_n == 256) gemm_packed_tile<128, 256, DT, 8>(a, in, nd, smem);
         else gemm_packed_tile<128, 128, DT, 8>(a, in, nd, smem);
       } else {
-        ArgsK* ak = (ArgsK*)&a;
-        InstrL* il = (InstrL*)&in;
-        NodeL* nl = (NodeL*)&nd;
-        CharL* sl = (CharL*)smem;
         if (nd.layout == 2) {
-          if (nd.tile_m == 256 && nd.tile_n == 128) gemm_packed_call<256, 128, DT>(ak, il, nl, sl);
-          else if (nd.tile_m == 128 && nd.tile_n == 256) gemm_packed_call<128, 256, DT>(ak, il, nl, sl);
-          else gemm_packed_call<128, 128, DT>(ak, il, nl, sl);
-        } else if (nd.tile_m == 128 && nd.tile_n == 128) gemm_call<128, 128, DT>(ak, il, nl, sl);
-        else if (nd.tile_m == 64 && nd.tile_n == 128) gemm_call<64, 128, DT>(ak, il, nl, sl);
-        else if (nd.tile_m == 128 && nd.tile_n == 64) gemm_call<128, 64, DT>(ak, il, nl, sl);
-        else gemm_call<64, 64, DT>(ak, il, nl, sl);
+          if (nd.tile_m == 256 && nd.tile_n == 128) gemm_packed_tile<256, 128, DT>(a, in, nd, smem);
+          else if (nd.tile_m == 128 && nd.tile_n == 256) gemm_packed_tile<128, 256, DT>(a, in, nd, smem);
+          else gemm_packed_tile<128, 128, DT>(a, in, nd, smem);
+        } else if (nd.tile_m == 128 && nd.tile_n == 128) gemm_tile<128, 128, DT>(a, in, nd, smem);
+        else if (nd.tile_m == 64 && nd.tile_n == 128) gemm_tile<64, 128, DT>(a, in, nd, smem);
+        else if (nd.tile_m == 128 && nd.tile_n == 64) gemm_tile<128, 64, DT>(a, in, nd, smem);
+        else gemm_tile<64, 64, DT>(a, in, nd, smem);
       }
       break;
     case MK_I_GEMV:
