@@ -31,6 +31,7 @@ sys.path.insert(0, ROOT)
 METRIC = "µs/forward + TFLOP/s (% MFMA peak) or GB/s (% HBM) per graph, 1 MI355X"
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 PEAK_MFMA_TFLOPS = 2500.0   # MI355X dense fp16/bf16 MFMA
+NOMINAL_CLOCK_MHZ = 2400.0   # the clock the nominal peak is quoted at
 WARM_SECONDS = 1.0          # forwards run before the timed blocks of each graph
 AB_ROUNDS = 3               # per-op blocks (and megakernel blocks) in the interleaved comparison
 
@@ -285,7 +286,7 @@ def line_for(head, steps, warmup, graphs=None):
         if k in head:
             line[k] = head[k]
     if "core_clock_mhz" in head:
-        line["peak_at_measured_clock_tflops"] = PEAK_MFMA_TFLOPS * head["core_clock_mhz"] / 2400.0
+        line["peak_at_measured_clock_tflops"] = PEAK_MFMA_TFLOPS * head["core_clock_mhz"] / NOMINAL_CLOCK_MHZ
     if graphs is not None:
         line["graphs"] = graphs
     return line
@@ -328,6 +329,41 @@ def copy_calibration(mib, steps):
                       "gbps": 2 * n / (ms * 1e-3) / 1e9}), flush=True)
 
 
+def mfma_probe(steps):
+    """The MFMA rate this part sustains when only MFMAs run (mk_probe_mfma):
+    operands held in registers and changing every instruction, drawn like
+    the prefill workload's (A ~ N(0, 1), B ~ N(0, 1/8192)), one workgroup of
+    eight waves per CU.  Under the power limit this sits well below the
+    nominal peak, and it is the ceiling any GEMM body here can reach."""
+    import ctypes
+    import torch
+    from tiled_gemm_graph_amd import _lib as L
+    lib = L.load()
+    blocks = torch.cuda.get_device_properties(0).multi_processor_count
+    iters = 4000
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    res = {}
+    for name, tdt, code in (("f16", torch.float16, L.MK_F16), ("bf16", torch.bfloat16, L.MK_BF16)):
+        g = torch.Generator(device="cuda").manual_seed(0)
+        v = torch.randn(blocks * 512, 16, 8, generator=g, device="cuda")
+        v[:, 8:, :] /= math.sqrt(8192.0)
+        ops = v.to(tdt).contiguous()
+        out = torch.empty(blocks * 512, device="cuda")
+
+        def launch():
+            L.check(lib.mk_probe_mfma(ctypes.c_void_p(ops.data_ptr()), ctypes.c_void_p(out.data_ptr()),
+                                      blocks, iters, code, stream))
+        warm_up(launch, WARM_SECONDS)
+        ms = time_forwards(launch, steps, 0)
+        assert torch.isfinite(out).all()
+        tf = blocks * iters * 2097152 / (ms * 1e-3) / 1e12
+        res[name] = {"tflops": round(tf, 1), "frac_of_nominal": round(tf / PEAK_MFMA_TFLOPS, 4),
+                     "us_per_launch": round(ms * 1e3, 1),
+                     "clock_if_pipes_saturated_mhz": round(NOMINAL_CLOCK_MHZ * tf / PEAK_MFMA_TFLOPS)}
+    print(json.dumps({"mfma_probe": res, "blocks": blocks, "iters": iters, "steps": steps,
+                      "operands": "A ~ N(0,1), B ~ N(0,1/8192), 8 A and 8 B fragments cycled"}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -346,6 +382,8 @@ def main():
                          "level boundary, for A/B comparison")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="only time a plain copy of this many MiB (counter calibration)")
+    ap.add_argument("--mfma-probe", action="store_true",
+                    help="only measure the sustained MFMA rate with random operands")
     ap.add_argument("--node-trace", action="store_true",
                     help="with --workload: print the per-node timeline of one traced forward")
     ap.add_argument("--source-hash", action="store_true",
@@ -364,6 +402,9 @@ def main():
         sys.exit(2)
     if args.copy_mib:
         copy_calibration(args.copy_mib, args.steps)
+        return
+    if args.mfma_probe:
+        mfma_probe(args.steps)
         return
     if args.node_trace:
         if not args.workload:

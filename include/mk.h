@@ -501,6 +501,24 @@ mk_status mk_plan_epoch(const mk_plan *p, int64_t *epoch);
  * the current device. */
 mk_status mk_wall_clock_khz(int32_t *khz);
 
+/* Calibration, not part of the path: the MFMA rate this part sustains
+ * when nothing but v_mfma_f32_32x32x16_{f16,bf16} runs, as a measured
+ * ceiling beside the nominal peak (the measurement discipline of
+ * "Hand-writing a Blackwell GEMM", "How I measured": rates against what
+ * the hardware delivers, on realistic data).  `blocks` workgroups of 512
+ * threads (one per CU); thread t of workgroup b reads 16 sixteen-byte
+ * operand fragments at ops[(b * 512 + t) * 16 ..] (caller-owned device
+ * memory of blocks * 131072 bytes, fp16 or bf16 values per `dtype`) into
+ * registers, then issues iters * 8 MFMAs that cycle through 8 A and 8 B
+ * fragments into 4 independent accumulators, and writes one float per
+ * thread to out[b * 512 + t] (device, blocks * 2048 bytes).  One launch is
+ * blocks * iters * 2097152 flops.  Asynchronous on `stream`; the caller
+ * times it.  MK_E_INVALID for null pointers, blocks outside 1..65535,
+ * iters < 1 or a dtype other than MK_F16 / MK_BF16; MK_E_HIP on a launch
+ * error. */
+mk_status mk_probe_mfma(const void *ops, float *out, int32_t blocks, int32_t iters, int32_t dtype,
+                        void *stream);
+
 const char *mk_last_error(void);
 int32_t mk_abi_version(void);
 

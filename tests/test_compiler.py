@@ -28,6 +28,16 @@ def test_library_exports_every_declared_symbol():
     assert lib.mk_abi_version() == 5
 
 
+def test_mfma_probe_rejects_bad_arguments():
+    # argument checks come before any device call, so they run without a GPU
+    lib = L.load()
+    buf = ctypes.create_string_buffer(64)
+    p = ctypes.cast(buf, ctypes.c_void_p)
+    for args in [(None, p, 1, 1, L.MK_F16), (p, None, 1, 1, L.MK_F16), (p, p, 0, 1, L.MK_F16),
+                 (p, p, 65536, 1, L.MK_F16), (p, p, 1, 0, L.MK_F16), (p, p, 1, 1, L.MK_F32)]:
+        assert lib.mk_probe_mfma(*args, None) == L.MK_E_INVALID, args
+
+
 def test_struct_layout_matches_decoder(tmp_path):
     src = tmp_path / "layout.c"
     src.write_text("""

@@ -10,6 +10,8 @@ bug would fail, through the C ABI.
 
 Every case prints its name and shapes before touching the GPU.
 """
+import ctypes
+
 import numpy as np
 import pytest
 import torch
@@ -169,3 +171,31 @@ def test_megakittens_mlp_bf16_unfused_pooled():
     torch.cuda.synchronize()
     assert_parity(to_np(bufs["y2"]), OG.mlp3(inp), "bf16", "MegaKittens MLP")
     _counters_ok(plan, 2)
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+def test_mfma_probe_counts_every_product(dt):
+    # The calibration probe (mk_probe_mfma) must really issue its MFMAs.  A
+    # 32 x 32 x 16 product summed over its 1024 outputs is sum_k (sum of A's
+    # column k) * (sum of B's row k), and a lane holds the same k values of
+    # its A and B fragments, so a wave's total follows from the operands
+    # alone; with small integers every partial sum is exact in fp32.
+    blocks, iters = 2, 3
+    say(f"[gpu] mfma probe {dt} blocks={blocks} iters={iters}")
+    g = torch.Generator().manual_seed(7)
+    v = torch.randint(-2, 3, (blocks * 512, 16, 8), generator=g).double()
+    tdt = torch.float16 if dt == "f16" else torch.bfloat16
+    ops = v.to(tdt).cuda()
+    out = torch.empty(blocks * 512, device="cuda")
+    lib = L.load()
+    code = L.MK_F16 if dt == "f16" else L.MK_BF16
+    L.check(lib.mk_probe_mfma(ctypes.c_void_p(ops.data_ptr()), ctypes.c_void_p(out.data_ptr()),
+                              blocks, iters, code, None))
+    torch.cuda.synchronize()
+    got = out.cpu().double().view(blocks * 8, 64).sum(1)
+    x = v.view(blocks * 8, 2, 32, 16, 8)          # wave, lane half, lane, fragment, element
+    col_a = x[:, :, :, :8, :].sum(2)              # wave, half, A fragment, element
+    row_b = x[:, :, :, 8:, :].sum(2)              # wave, half, B fragment, element
+    pairs = [(0, 0), (1, 3), (2, 6), (3, 1), (4, 4), (5, 7), (6, 2), (7, 5)]
+    want = sum((col_a[:, :, a, :] * row_b[:, :, b, :]).sum((1, 2)) for a, b in pairs) * iters
+    assert torch.equal(got, want), (got[:4], want[:4])

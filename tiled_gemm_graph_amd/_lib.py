@@ -84,6 +84,7 @@ EXPORTS = [
     "mk_plan_check", "mk_plan_stats_get", "mk_plan_instructions", "mk_plan_nodes",
     "mk_plan_barriers", "mk_plan_slots", "mk_plan_op_tile", "mk_plan_read_counters",
     "mk_plan_epoch", "mk_plan_weight_layout", "mk_plan_pack_weight", "mk_wall_clock_khz",
+    "mk_probe_mfma",
     "mk_last_error", "mk_abi_version",
 ]
 
@@ -123,6 +124,7 @@ def load() -> ctypes.CDLL:
         "mk_plan_weight_layout": ([vp, c_int32, i32p, i64p], c_int),
         "mk_plan_pack_weight": ([vp, c_int32, vp, vp, vp], c_int),
         "mk_wall_clock_khz": ([i32p], c_int),
+        "mk_probe_mfma": ([vp, vp, c_int32, c_int32, c_int32, vp], c_int),
         "mk_last_error": ([], c_char_p),
         "mk_abi_version": ([], c_int32),
     }

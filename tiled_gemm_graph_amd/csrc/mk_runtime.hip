@@ -41,6 +41,39 @@ constexpr size_t kTicketPad = 32;   // int32 words after the counter slots
 // The array behind megakernel_run_noalloc (64 MiB per GPU, see below).
 static __device__ __align__(256) unsigned char scratch[(size_t)64 << 20];
 
+// MFMA issue-rate probe (mk_probe_mfma): operands in registers, changing
+// every instruction, four independent accumulators per wave, two waves per
+// SIMD; 96 KB of LDS keeps it to one workgroup per CU.
+template <int DT>
+__global__ void __launch_bounds__(512, 1) mk_probe_mfma_kernel(const mkd::u32x4* __restrict__ ops, float* __restrict__ out,
+                                                              int iters) {
+  __shared__ int pin[24 * 1024];
+  const int t = threadIdx.x;
+  if (t == 0) pin[0] = 0;
+  __syncthreads();
+  const mkd::u32x4* p = ops + ((size_t)blockIdx.x * 512 + t) * 16;
+  mkd::u32x4 A[8], B[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    A[j] = p[j];
+    B[j] = p[8 + j];
+  }
+  mkd::f32x16 c0 = {}, c1 = {}, c2 = {}, c3 = {};
+  for (int i = 0; i < iters; ++i) {
+#pragma unroll
+    for (int j = 0; j < 8; j += 4) {
+      c0 = mkd::mfma32<DT>(A[j], B[j], c0);
+      c1 = mkd::mfma32<DT>(A[j + 1], B[(j + 3) & 7], c1);
+      c2 = mkd::mfma32<DT>(A[j + 2], B[(j + 6) & 7], c2);
+      c3 = mkd::mfma32<DT>(A[j + 3], B[(j + 1) & 7], c3);
+    }
+  }
+  float sum = 0.f;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) sum += c0[e] + c1[e] + c2[e] + c3[e];
+  out[(size_t)blockIdx.x * 512 + t] = sum + (float)pin[0];
+}
+
 // Fill n 32-bit words with v (the NaN poison of debug_poison runs).
 __global__ void mk_fill_kernel(uint32_t* __restrict__ p, size_t n, uint32_t v) {
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
@@ -684,6 +717,20 @@ mk_status mk_plan_pack_weight(mk_plan* p, int32_t tensor, const void* src, void*
                      static_cast<const unsigned short*>(src), static_cast<unsigned short*>(dst), (long)pk->K,
                      (long)pk->N, ld, pk->bn, pk->wc, (long)pk->tiles, pk->silu ? 1 : 0, pk->head_dim,
                      (long)pk->rope_cols);
+  HIPCHK(hipGetLastError());
+  return MK_OK;
+}
+
+mk_status mk_probe_mfma(const void* ops, float* out, int32_t blocks, int32_t iters, int32_t dtype, void* stream) {
+  if (!ops || !out) { set_error("null argument"); return MK_E_INVALID; }
+  if (blocks < 1 || blocks > 65535 || iters < 1) { set_error("blocks must be 1..65535 and iters >= 1"); return MK_E_INVALID; }
+  if (dtype != MK_F16 && dtype != MK_BF16) { set_error("dtype must be MK_F16 or MK_BF16"); return MK_E_INVALID; }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const mkd::u32x4* o = static_cast<const mkd::u32x4*>(ops);
+  if (dtype == MK_BF16)
+    hipLaunchKernelGGL(mk_probe_mfma_kernel<MK_BF16>, dim3(blocks), dim3(512), 0, s, o, out, iters);
+  else
+    hipLaunchKernelGGL(mk_probe_mfma_kernel<MK_F16>, dim3(blocks), dim3(512), 0, s, o, out, iters);
   HIPCHK(hipGetLastError());
   return MK_OK;
 }
