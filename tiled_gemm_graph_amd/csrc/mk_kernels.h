@@ -1282,7 +1282,52 @@ __device__ __forceinline__ void reduce_tile(const KArgs& a, const mk_instr& in, 
   // thread order, so the result is the same on every run.
   int tpu = 1;
   while (tpu * 2 * units <= NT && tpu * 2 <= S) tpu *= 2;
-  for (int u0 = 0; u0 < units; u0 += NT / tpu) {
+  if (tpu == 1) {
+    // One thread per unit, planes in order.  A thread takes up to UB units
+    // at once and loads plane p of all of them together, unconditionally
+    // (a unit past the tile re-reads unit 0), so a plane costs one memory
+    // round trip for UB units.
+    constexpr int UB = 4;
+    for (int u0 = t; u0 < units; u0 += NT * UB) {
+      const float* src[UB];
+#pragma unroll
+      for (int b = 0; b < UB; ++b) {
+        const int u = u0 + b * NT < units ? u0 + b * NT : 0;
+        const int m = u / ncg, w = (u % ncg) * 8;
+        const int gc = (silu && w >= bw) ? N + c0 + (w - bw) : c0 + w;
+        src[b] = P + (long)(r0 + m) * ldp + gc;
+      }
+      float acc[UB][8];
+#pragma unroll
+      for (int b = 0; b < UB; ++b)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[b][e] = 0.f;
+      for (int p = 0; p < S; ++p) {
+        float4 x[UB][2];
+#pragma unroll
+        for (int b = 0; b < UB; ++b) {
+          x[b][0] = *reinterpret_cast<const float4*>(src[b] + p * plane);
+          x[b][1] = *reinterpret_cast<const float4*>(src[b] + p * plane + 4);
+        }
+#pragma unroll
+        for (int b = 0; b < UB; ++b) {
+          acc[b][0] += x[b][0].x; acc[b][1] += x[b][0].y; acc[b][2] += x[b][0].z; acc[b][3] += x[b][0].w;
+          acc[b][4] += x[b][1].x; acc[b][5] += x[b][1].y; acc[b][6] += x[b][1].z; acc[b][7] += x[b][1].w;
+        }
+      }
+#pragma unroll
+      for (int b = 0; b < UB; ++b) {
+        const int u = u0 + b * NT;
+        if (u < units) {
+          const int m = u / ncg, w = (u % ncg) * 8;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) sum[m * wc + w + e] = acc[b][e];
+        }
+      }
+    }
+    __syncthreads();
+  }
+  for (int u0 = 0; tpu > 1 && u0 < units; u0 += NT / tpu) {
     const int u = u0 + t / tpu, sub = t % tpu;
     float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     if (u < units) {
@@ -1336,14 +1381,16 @@ __device__ __forceinline__ void reduce_tile(const KArgs& a, const mk_instr& in, 
 }
 
 // --------------------------------------------------------------- RMSNORM
-// Rows [r0, r1) of y = x * rsqrt(mean(x^2) + eps) * gamma, up to 16
-// 16-byte chunks per thread in registers: the loads of a whole group of
+// Rows [r0, r1) of y = x * rsqrt(mean(x^2) + eps) * gamma, RMAX rows of
+// CPT 16-byte chunks per thread in registers: the loads of a whole group of
 // rows are in flight together, each wave adds up the squares of every row,
 // and one barrier exchanges the wave sums, so a group costs one memory
-// round trip instead of two per row.
-template <int DT, int CPT, int NT = kThreads>
+// round trip instead of two per row.  The loads are unconditional (a row
+// past the tile re-reads its last row, a chunk past the row end its last
+// chunk): a load under a branch would make the compiler wait for the one
+// before it, one memory round trip per row.
+template <int DT, int CPT, int NT = kThreads, int RMAX = 16 / CPT>
 __device__ __forceinline__ void rmsnorm_rows(const KArgs& a, const mk_instr& in, const mk_node& nd, char* smem) {
-  constexpr int RMAX = 16 / CPT;                // rows per group
   const int t = tid(), H = nd.N, w = wave_id();
   constexpr int NW = NT / 64;
   float* part = reinterpret_cast<float*>(smem);  // [NW waves][RMAX] sums of squares
@@ -1353,8 +1400,8 @@ __device__ __forceinline__ void rmsnorm_rows(const KArgs& a, const mk_instr& in,
   u32x4 gv[CPT];
 #pragma unroll
   for (int c = 0; c < CPT; ++c) {
-    const int k = (t + c * NT) * 8;
-    if (k < H) gv[c] = *reinterpret_cast<const u32x4*>(G + k);
+    const int k = min((t + c * NT) * 8, H - 8);
+    gv[c] = *reinterpret_cast<const u32x4*>(G + k);
   }
   for (int g0 = in.r0; g0 < in.r1; g0 += RMAX) {
     const int nr = min(RMAX, in.r1 - g0);
@@ -1363,8 +1410,8 @@ __device__ __forceinline__ void rmsnorm_rows(const KArgs& a, const mk_instr& in,
     for (int rr = 0; rr < RMAX; ++rr)
 #pragma unroll
       for (int c = 0; c < CPT; ++c) {
-        const int k = (t + c * NT) * 8;
-        if (rr < nr && k < H) xv[rr][c] = *reinterpret_cast<const u32x4*>(X + (long)(g0 + rr) * nd.a.ld + k);
+        const int k = min((t + c * NT) * 8, H - 8);
+        xv[rr][c] = *reinterpret_cast<const u32x4*>(X + (long)(g0 + min(rr, nr - 1)) * nd.a.ld + k);
       }
 #pragma unroll
     for (int rr = 0; rr < RMAX; ++rr) {
@@ -1419,9 +1466,12 @@ __device__ __forceinline__ void rmsnorm_tile(const KArgs& a, const mk_instr& in,
   const int t = tid();
   const int H = nd.N;
   const int cpt = (H / 8 + NT - 1) / NT;   // 16-byte chunks per thread and row
-  if (cpt <= 1) return rmsnorm_rows<DT, 1, NT>(a, in, nd, smem);
-  if (cpt <= 2) return rmsnorm_rows<DT, 2, NT>(a, in, nd, smem);
-  if (cpt <= 4) return rmsnorm_rows<DT, 4, NT>(a, in, nd, smem);
+  // groups of up to 16 chunks per thread, halved for tiles of few rows (a
+  // group's rows past the tile are loaded too)
+  const bool few = in.r1 - in.r0 <= 8 / cpt;
+  if (cpt <= 1) return few ? rmsnorm_rows<DT, 1, NT, 8>(a, in, nd, smem) : rmsnorm_rows<DT, 1, NT>(a, in, nd, smem);
+  if (cpt <= 2) return few ? rmsnorm_rows<DT, 2, NT, 4>(a, in, nd, smem) : rmsnorm_rows<DT, 2, NT>(a, in, nd, smem);
+  if (cpt <= 4) return few ? rmsnorm_rows<DT, 4, NT, 2>(a, in, nd, smem) : rmsnorm_rows<DT, 4, NT>(a, in, nd, smem);
   // wider rows: one row at a time, streamed
   float* scratch = reinterpret_cast<float*>(smem);
   const u16* X = buf<const u16>(a, nd.a);
