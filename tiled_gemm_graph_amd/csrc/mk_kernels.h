@@ -608,6 +608,12 @@ __device__ __forceinline__ void gemm_packed_tile(const KArgs& a, const mk_instr&
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
+  // No load the compiler issued may still be in flight when the K loop
+  // starts: one that was (a record fetched ahead, another body's prefetch
+  // whose register the loop reuses) would make it wait for every
+  // outstanding load, the stages in flight included, on each pass.
+  wait_vmcnt_lgkm0<0>();
+
   // Operand fragments of a wave's 16-deep sub-steps of a stage (four, or
   // two in a K-split pair), double-buffered: the LDS reads of the next
   // sub-step are in flight during this one's MFMAs, and those of the next
@@ -1541,28 +1547,41 @@ __device__ __forceinline__ void attention_tile(const KArgs& a, const mk_instr& i
     for (int e = 0; e < 16; ++e) o[db][e] = 0.f;
   float mrun = -INFINITY, lsum = 0.f;
 
+  // K and V rows of a key block, one block ahead: the loads of block j + 1
+  // are issued once block j is in LDS, so they are in flight during block
+  // j's MFMAs and softmax.  Thread: 4 K chunks (key cidx >> 4, 8 dims at
+  // (cidx & 15) * 8 for cidx = t4 + 256 i) and 8 dims of 4 keys of V.
+  const int dblk = t4 & 15, kq = t4 >> 4;
+  u32x4 kpre[4], vpre[4];
+  auto load_kv = [&](int kb) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int cidx = t4 + 256 * i, key = cidx >> 4, dc = (cidx & 15) * 8;
+      kpre[i] = *reinterpret_cast<const u32x4*>(Kp + (long)min(kb + key, S - 1) * ldk + dc);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      vpre[r] = *reinterpret_cast<const u32x4*>(Vp + (long)min(kb + kq * 4 + r, S - 1) * ldv + dblk * 8);
+  };
+  if (hh * KBLK < kend) load_kv(hh * KBLK);
+
   for (int kbp = 0; kbp < kend; kbp += NH * KBLK) {
     const int kb0 = kbp + hh * KBLK;   // this half's key block
     const bool live = kb0 < kend;      // uniform per wave
     __syncthreads();
     if (live) {
-      // stage K [64][128] and V^T [128][64]
+      // stage K [64][128] and V^T [128][64] from the registers, then
+      // request the half's next block
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int cidx = t4 + 256 * i, key = cidx >> 4, dc = (cidx & 15) * 8;
-        const int gk = min(kb0 + key, S - 1);
-        *reinterpret_cast<u32x4*>(Ks + key * KS + dc) = *reinterpret_cast<const u32x4*>(Kp + (long)gk * ldk + dc);
-      }
-      const int dblk = t4 & 15, kq = t4 >> 4;  // 8 d x 4 keys per thread
-      u32x4 v[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int gk = min(kb0 + kq * 4 + r, S - 1);
-        v[r] = *reinterpret_cast<const u32x4*>(Vp + (long)gk * ldv + dblk * 8);
+        *reinterpret_cast<u32x4*>(Ks + key * KS + dc) = kpre[i];
       }
 #pragma unroll
       for (int n = 0; n < 8; ++n)
-        *reinterpret_cast<u32x2*>(Vt + (dblk * 8 + n) * VS + kq * 4) = u32x2{pick2(v[0], v[1], n), pick2(v[2], v[3], n)};
+        *reinterpret_cast<u32x2*>(Vt + (dblk * 8 + n) * VS + kq * 4) =
+            u32x2{pick2(vpre[0], vpre[1], n), pick2(vpre[2], vpre[3], n)};
+      if (kb0 + NH * KBLK < kend) load_kv(kb0 + NH * KBLK);
     }
     __syncthreads();
     if (live) {
@@ -1638,6 +1657,8 @@ __device__ __forceinline__ void attention_tile(const KArgs& a, const mk_instr& i
       }
     }
   }
+  // (no K/V prefetch is left in flight: the last block issues none)
+  __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0); expcnt, lgkmcnt not waited
   lsum += __shfl_xor(lsum, 32, 64);
   if constexpr (NH == 2) {
     // the second half hands its (o, m, l) to the first: o' = o0 2^(m0 - M)
