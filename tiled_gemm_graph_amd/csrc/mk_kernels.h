@@ -517,6 +517,21 @@ __device__ __forceinline__ void wait_vmcnt_lgkm0() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0070);
 }
 
+// wait_vmcnt_lgkm0 with a wave-uniform count n (0 .. 63) known only at run
+// time: a chain of scalar compares, for the few waits of a tile's prologue.
+template <int K = 0>
+__device__ __forceinline__ void wait_vmcnt_rt(int n) {
+  if constexpr (K > 63) {
+    wait_vmcnt_lgkm0<0>();
+  } else {
+    if (n <= K) {
+      wait_vmcnt_lgkm0<K>();
+      return;
+    }
+    wait_vmcnt_rt<K + 1>(n);
+  }
+}
+
 // Workgroup barrier with no memory fence: the caller has already waited
 // for the operations the barrier publishes (LDS is coherent within the CU);
 // the signal fences keep the compiler from moving memory accesses across it.
@@ -540,7 +555,7 @@ __device__ __forceinline__ void bare_barrier() {
 #endif
 template <int BM, int BN, int DT, int NW = 4>
 __device__ __forceinline__ void gemm_packed_tile(const KArgs& a, const mk_instr& in, const mk_node& nd,
-                                                 char* smem) {
+                                                 char* smem, bool bpre = false) {
   constexpr int NT = NW * 64;
   constexpr int ROWB = 128;                         // bytes per LDS row: 64 k values
   constexpr int A_BYTES = BM * ROWB, STAGE = (BM + BN) * ROWB;
@@ -658,15 +673,22 @@ __device__ __forceinline__ void gemm_packed_tile(const KArgs& a, const mk_instr&
   // are in flight, and waiting for stage kt + 1 leaves ST - 2 younger ones.
   constexpr int NQ = FM * FN;   // MFMAs per sub-step
   const int nk = (k1 - k0) / 64;
+  // With bpre the weight slices of stages 0 .. ST - 1 are already in LDS
+  // (issued before the counter wait, complete after the wait above), and
+  // these stages load A only: waiting for stage s then leaves A_LOADS per
+  // younger prologue stage and L per younger loop stage in flight.
+  const int pl = bpre ? A_LOADS : L;   // loads per prologue stage
 #pragma unroll
   for (int s = 0; s < ST; ++s)
     if (s < nk)
 #pragma unroll
-      for (int q = 0; q < L; ++q) load_one(s, s, q);
+      for (int q = 0; q < L; ++q)
+        if (q < A_LOADS || !bpre) load_one(s, s, q);
   // sub-steps of this wave: kb, kb + 1, ... kb + SUB - 1 (wave-uniform)
   const int kb = uni(kh * 2);
   if (nk > 0) {
-    land(min(ST - 1, nk - 1));
+    if (bpre) wait_vmcnt_rt(pl * min(ST - 1, nk - 1));
+    else land(min(ST - 1, nk - 1));
     bare_barrier();
     frags(smem, kb, 0);
   }
@@ -683,7 +705,14 @@ __device__ __forceinline__ void gemm_packed_tile(const KArgs& a, const mk_instr&
 #pragma unroll
       for (int q = 0; q < NQ; ++q) mma(kk & 1, q);
     }
-    land(min(ST - 2, nk - 2 - kt));
+    if (bpre && kt + 1 < ST) {
+      // stage kt + 1 is a prologue stage: younger are the prologue stages
+      // after it (A only) and the loop stages issued so far (one per stage
+      // before kt)
+      wait_vmcnt_rt(pl * max(0, min(ST - 2 - kt, nk - 2 - kt)) + L * max(0, min(kt, nk - ST)));
+    } else {
+      land(min(ST - 2, nk - 2 - kt));
+    }
     bare_barrier();
     frags(smem + ((u + 1) % ST) * STAGE, kb, 0);
     const bool more = kt + ST < nk;
@@ -778,6 +807,36 @@ __device__ __forceinline__ void gemm_packed_tile(const KArgs& a, const mk_instr&
         for (int e = 0; e < 8; ++e) o[e] = src[x + e];
       });
     }
+  }
+}
+
+// The weight slices of a packed GEMM tile's first K stages, issued into
+// their LDS stage buffers before the tile's counters clear (a packed
+// weight is a caller input no instruction writes).  Waves 1 .. NW - 1
+// issue them, so that wave 0's counter polls do not queue behind the
+// loads; the same rows, chunks and LDS addresses as the tile body's own B
+// loads.  The tile body then loads A only for these stages.
+template <int BM, int BN, int NW>
+__device__ __forceinline__ void gemm_packed_prefetch_b(const KArgs& a, const mk_instr& in, const mk_node& nd,
+                                                       char* smem) {
+  constexpr int ROWB = 128, A_BYTES = BM * ROWB, STAGE = (BM + BN) * ROWB;
+  constexpr int ST = (kSmemBytes / STAGE) < 4 ? (kSmemBytes / STAGE) : 4;
+  constexpr int NB = BN / 8;   // 1 KB loads (8 weight rows) per stage
+  const int w = wave_id();
+  if (w == 0) return;
+  const int lane = tid() & 63;
+  const int K = uni(nd.K), k0 = uni(in.k0), k1 = uni(in.k1);
+  const int nk = (k1 - k0) / 64;
+  const long nkt = K / 64;
+  const char* b_sb = uni_ptr(buf<const u16>(a, nd.b) + ((long)uni(in.coord[1]) * nkt + k0 / 64) * (long)BN * 64);
+  const unsigned smem_lds = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)smem);
+  for (int j = w - 1; j < NB; j += NW - 1) {
+    const int row = 8 * j + (lane >> 3);
+    const int c = (lane & 7) ^ ((row >> 1) & 7);
+    const unsigned vo = (unsigned)(row * 64 + c * 8) * 2u;
+#pragma unroll
+    for (int st = 0; st < ST; ++st)
+      if (st < nk) g2lds16_sb(b_sb + (long)st * (BN * 128), vo, smem_lds + st * STAGE + A_BYTES + (8 * j) * ROWB);
   }
 }
 
@@ -2059,7 +2118,8 @@ __host__ __device__ constexpr unsigned op_family(int opcode) {
 // bodies, each of which then runs on all eight waves (the GEMV bodies, the
 // row-major GEMM tile and decode attention exist with four waves only).
 template <unsigned OPS, int DT, int NT>
-__device__ __forceinline__ void run_body(const KArgs& a, const mk_instr& in, const mk_node& nd, char* smem) {
+__device__ __forceinline__ void run_body(const KArgs& a, const mk_instr& in, const mk_node& nd, char* smem,
+                                         bool bpre = false) {
   if (!(op_family(in.opcode) & OPS)) return;
   switch (in.opcode) {
     case MK_I_GEMM:
@@ -2068,14 +2128,14 @@ __device__ __forceinline__ void run_body(const KArgs& a, const mk_instr& in, con
       // scratch memory on every tile.
       if constexpr (!(OPS & kOpGemm)) break;
       else if constexpr (NT == 512) {
-        if (nd.tile_m == 256 && nd.tile_n == 128) gemm_packed_tile<256, 128, DT, 8>(a, in, nd, smem);
-        else if (nd.tile_m == 128 && nd.tile_n == 256) gemm_packed_tile<128, 256, DT, 8>(a, in, nd, smem);
-        else gemm_packed_tile<128, 128, DT, 8>(a, in, nd, smem);
+        if (nd.tile_m == 256 && nd.tile_n == 128) gemm_packed_tile<256, 128, DT, 8>(a, in, nd, smem, bpre);
+        else if (nd.tile_m == 128 && nd.tile_n == 256) gemm_packed_tile<128, 256, DT, 8>(a, in, nd, smem, bpre);
+        else gemm_packed_tile<128, 128, DT, 8>(a, in, nd, smem, bpre);
       } else {
         if (nd.layout == 2) {
-          if (nd.tile_m == 256 && nd.tile_n == 128) gemm_packed_tile<256, 128, DT>(a, in, nd, smem);
-          else if (nd.tile_m == 128 && nd.tile_n == 256) gemm_packed_tile<128, 256, DT>(a, in, nd, smem);
-          else gemm_packed_tile<128, 128, DT>(a, in, nd, smem);
+          if (nd.tile_m == 256 && nd.tile_n == 128) gemm_packed_tile<256, 128, DT>(a, in, nd, smem, bpre);
+          else if (nd.tile_m == 128 && nd.tile_n == 256) gemm_packed_tile<128, 256, DT>(a, in, nd, smem, bpre);
+          else gemm_packed_tile<128, 128, DT>(a, in, nd, smem, bpre);
         } else if (nd.tile_m == 128 && nd.tile_n == 128) gemm_tile<128, 128, DT>(a, in, nd, smem);
         else if (nd.tile_m == 64 && nd.tile_n == 128) gemm_tile<64, 128, DT>(a, in, nd, smem);
         else if (nd.tile_m == 128 && nd.tile_n == 64) gemm_tile<128, 64, DT>(a, in, nd, smem);
@@ -2111,9 +2171,21 @@ __device__ __forceinline__ void run_body(const KArgs& a, const mk_instr& in, con
 }
 
 template <unsigned OPS, int NT>
-__device__ __forceinline__ void run_instr(const KArgs& a, const mk_instr& in, const mk_node& nd, char* smem) {
-  if (nd.dtype == MK_BF16) run_body<OPS, MK_BF16, NT>(a, in, nd, smem);
-  else run_body<OPS, MK_F16, NT>(a, in, nd, smem);
+__device__ __forceinline__ void run_instr(const KArgs& a, const mk_instr& in, const mk_node& nd, char* smem,
+                                          bool bpre = false) {
+  if (nd.dtype == MK_BF16) run_body<OPS, MK_BF16, NT>(a, in, nd, smem, bpre);
+  else run_body<OPS, MK_F16, NT>(a, in, nd, smem, bpre);
+}
+
+// Before a packed GEMM tile's counter wait: its first weight stages
+// (gemm_packed_prefetch_b), in the tile shape and wave count it runs with.
+template <int NT>
+__device__ __forceinline__ void prefetch_gemm_weights(const KArgs& a, const mk_instr& in, const mk_node& nd,
+                                                      char* smem) {
+  constexpr int NW = NT / 64;
+  if (nd.tile_m == 256 && nd.tile_n == 128) gemm_packed_prefetch_b<256, 128, NW>(a, in, nd, smem);
+  else if (nd.tile_m == 128 && nd.tile_n == 256) gemm_packed_prefetch_b<128, 256, NW>(a, in, nd, smem);
+  else gemm_packed_prefetch_b<128, 128, NW>(a, in, nd, smem);
 }
 
 // ----------------------------------------------------- counters and waits
@@ -2437,11 +2509,23 @@ __device__ __forceinline__ bool generic_iter(const Loop& L, int it, int& w) {
       return true;
     }
   }
+  // a packed GEMM tile's first weight stages go out before its counters
+  // clear (the previous body has left the LDS arena)
+  bool bpre = false;
+  if constexpr ((OPS & kOpGemm) != 0) {
+    if (in.opcode == MK_I_GEMM) {
+      const mk_node& nd = node_of(L, in.node);
+      if (nd.layout == 2) {
+        prefetch_gemm_weights<NT>(a, in, nd, L.smem);
+        bpre = true;
+      }
+    }
+  }
   if (!wait_sources(L, in, it, gidx, w, tk)) return false;
   if (in.opcode != MK_I_NOOP) {
     const mk_node& nd = node_of(L, in.node);
     if (tr) stamp(a, gidx, 1, wall_clock64());
-    run_instr<OPS, NT>(a, in, nd, L.smem);
+    run_instr<OPS, NT>(a, in, nd, L.smem, bpre);
     if (tr) stamp(a, gidx, 2, wall_clock64());
     release_dests(a, in);
     if (tr) stamp(a, gidx, 3, wall_clock64());
