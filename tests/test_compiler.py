@@ -375,23 +375,23 @@ def test_noalloc_size_limit_checked_before_any_gpu_call():
 
 
 def test_layer_stack_limits():
-    # Prefill decoder layers in sequence (9 lowered nodes each).  Up to 48
+    # Prefill decoder layers in sequence (8 lowered nodes each).  Up to 48
     # nodes the persistent kernel keeps every node descriptor in LDS; beyond,
     # a window of 48 consecutive ids per workgroup, which must hold the
     # nodes of three consecutive records of a CU: fine for these layers
     # (every node has at least 256 instructions), refused for the work queue.
     d = workloads.default_dims("layer")
-    p14 = G.layer_stack(d, 14).build(num_cus=256)      # 126 nodes, 225 slots
-    assert p14.stats().n_nodes == 126 and p14.stats().n_slots == 225
+    p15 = G.layer_stack(d, 15).build(num_cus=256)      # 120 nodes, 226 slots
+    assert p15.stats().n_nodes == 120 and p15.stats().n_slots == 226
     with pytest.raises(L.MkError) as e:
-        p14.run([], stream=0)           # no GPU here: any error but "unsupported"
+        p15.run([], stream=0)           # no GPU here: any error but "unsupported"
     assert e.value.status != L.MK_E_UNSUPPORTED
-    pq = G.layer_stack(d, 6).build(num_cus=256, queue=1)
+    pq = G.layer_stack(d, 7).build(num_cus=256, queue=1)   # 56 nodes
     with pytest.raises(L.MkError) as e:
         pq.run([], stream=0)
     assert e.value.status == L.MK_E_UNSUPPORTED and "static placement" in str(e.value)
     with pytest.raises(L.MkError) as e:
-        G.layer_stack(d, 15).build(num_cus=256)         # 241 data + rope tables > 256
+        G.layer_stack(d, 16).build(num_cus=256)         # 257 graph tensors
     assert e.value.status == L.MK_E_LIMIT
 
 

@@ -230,7 +230,7 @@ struct Compiler {
       for (const Cand& c : cands) {
         if (t.bm > 0 && c.bm != t.bm) continue;
         if (t.bn > 0 && c.bn != t.bn * (silu ? 2 : 1)) continue;
-        if (rope && (c.bn / 2) % hd) continue;
+        if (rope && c.bn % hd) continue;
         const I64 bn_out = silu ? c.bn / 2 : c.bn;
         const I64 tiles = cdiv(std::max<I64>(M, 1), c.bm) * cdiv(N, bn_out);
         for (I64 sp = 1; sp <= 16; ++sp) {
@@ -381,8 +381,10 @@ struct Compiler {
       if (t.dup != 1) unsup("duplicated tiles are a host profile only");
       if ((fl & MK_EP_ROPE) && S == 1) {
         const int hd = op.attrs.head_dim;
-        if ((hd != 64 && hd != 128) || (bnk / 2) % hd)
-          unsup("ROPE on a packed GEMM tile needs head_dim 64 or 128 within half a tile");
+        // the epilogue reads a rotary partner (half a head away) from the
+        // tile's fp32 LDS strip, so a tile must hold whole heads
+        if ((hd != 64 && hd != 128) || bnk % hd)
+          unsup("ROPE on a packed GEMM tile needs head_dim 64 or 128 and whole heads in a tile");
       }
     } else {
       int bnk = t.bn * (silu ? 2 : 1);
