@@ -459,11 +459,11 @@ __device__ __forceinline__ void gemm_tile(const KArgs& a, const mk_instr& in, co
 // of a load fills LDS byte L * 16 of its 1 KB block and fetches the chunk
 // that belongs there.
 //
-// Four waves in 2 x 2, each WM x WN = BM/2 x BN/2 of v_mfma_f32_32x32x16
-// tiles.  The epilogue runs from the accumulators: the packing puts the
-// gate and up columns of one output (SILU_MUL) WN/2 columns apart inside a
-// wave's half, and a rotary partner is head_dim/2 columns away in the same
-// wave, so both partners of every pair are in the same lane.
+// Waves hold WM x WN blocks of v_mfma_f32_32x32x16 tiles (the layouts are
+// below).  The epilogue goes through an fp32 LDS strip of the whole tile
+// width: the packing puts the gate and up columns of one output (SILU_MUL)
+// WN/2 columns apart inside a wave column's half, and a rotary partner is
+// head_dim/2 columns away in the same tile (tiles hold whole heads).
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef const __attribute__((address_space(1))) void gbl_void_t;
 
