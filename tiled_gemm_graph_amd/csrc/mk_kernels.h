@@ -2509,10 +2509,13 @@ __device__ __forceinline__ bool generic_iter(const Loop& L, int it, int& w) {
       return true;
     }
   }
-  // a packed GEMM tile's first weight stages go out before its counters
-  // clear (the previous body has left the LDS arena)
+  // A packed GEMM tile's first weight stages go out before its counters
+  // clear: every body has left the LDS arena by its release barrier.  Not
+  // in instances with GEMV bodies: there the controller wave may still read
+  // the GEMV's sums from LDS, without a barrier, when the other waves reach
+  // the next instruction.
   bool bpre = false;
-  if constexpr ((OPS & kOpGemm) != 0) {
+  if constexpr ((OPS & kOpGemm) != 0 && (OPS & kOpGemv) == 0) {
     if (in.opcode == MK_I_GEMM) {
       const mk_node& nd = node_of(L, in.node);
       if (nd.layout == 2) {
