@@ -199,3 +199,48 @@ def test_mfma_probe_counts_every_product(dt):
     pairs = [(0, 0), (1, 3), (2, 6), (3, 1), (4, 4), (5, 7), (6, 2), (7, 5)]
     want = sum((col_a[:, :, a, :] * row_b[:, :, b, :]).sum((1, 2)) for a, b in pairs) * iters
     assert torch.equal(got, want), (got[:4], want[:4])
+
+
+def test_gemv_then_packed_gemm_in_one_plan():
+    # A GEMV node and an independent packed GEMM node in one plan (the
+    # four-wave instance with every body): a CU's GEMM tile comes right
+    # after its GEMV instruction, while the GEMV's controller wave may still
+    # read its sums from LDS and store them.  The GEMM tile must not touch
+    # the LDS arena before its own barrier (no weight prefetch in this
+    # instance).  Both outputs against the oracle, two runs.
+    g = G.Graph()
+    v = g.tensor("v", "bf16", (1, 1024), "input")
+    w1 = g.tensor("w1", "bf16", (1024, 2048), "weight")
+    g.tensor("y1", "bf16", (1, 2048), "output")
+    X = g.tensor("X", "bf16", (256, 1024), "input")
+    w2 = g.tensor("w2", "bf16", (1024, 4096), "weight")
+    g.tensor("y2", "bf16", (256, 4096), "output")
+    g.gemm(v, w1, g.ids["y1"])
+    g.gemm(X, w2, g.ids["y2"])
+    plan = g.build()
+    t0, t1 = plan.op_tile(0), plan.op_tile(1)
+    assert t0["gemv"] == 1 and t1["gemv"] == 0 and t1["layout"] == 2
+    say(f"[gpu] GEMV then packed GEMM: {plan.stats().n_instr} instructions, tiles {t0['bn']} / "
+        f"{t1['bm']}x{t1['bn']}")
+    gen = torch.Generator().manual_seed(11)
+    mk = lambda *s, std=1.0: (torch.randn(*s, generator=gen) * std).to(torch.bfloat16)
+    host = dict(v=mk(1, 1024), w1=mk(1024, 2048, std=1024 ** -0.5), X=mk(256, 1024),
+                w2=mk(1024, 4096, std=1024 ** -0.5))
+    bufs = {k: t.cuda() for k, t in host.items()}
+    for name in plan.packed_weights():
+        dst = torch.empty(plan.weight_layout(name)[1] // 2, dtype=torch.bfloat16, device="cuda")
+        plan.pack_weight(name, bufs[name], dst)
+        bufs[name] = dst
+    bufs["y1"] = torch.empty(1, 2048, dtype=torch.bfloat16, device="cuda")
+    bufs["y2"] = torch.empty(256, 4096, dtype=torch.bfloat16, device="cuda")
+    f = lambda t: t.double().numpy()
+    ref1 = f(host["v"]) @ f(host["w1"])
+    ref2 = f(host["X"]) @ f(host["w2"])
+    for run in range(2):
+        bufs["y1"].fill_(float("nan"))
+        bufs["y2"].fill_(float("nan"))
+        plan.run(bufs)
+        plan.check()
+        torch.cuda.synchronize()
+        assert_parity(to_np(bufs["y1"]), ref1, "bf16", f"GEMV run {run}")
+        assert_parity(to_np(bufs["y2"]), ref2, "bf16", f"packed GEMM run {run}")
