@@ -14,6 +14,7 @@
 #include <string>
 #include <vector>
 
+#include "mk_instances.h"
 #include "mk_internal.h"
 #include "mk_kernels.h"
 
@@ -177,32 +178,41 @@ bool wide_ok(const mk_plan* p) {
   }
   return any;
 }
+// Entry point of a kernel instance; the instances live in three units of
+// their own (mk_instances.h).  Every (persistent, ops, nt) the selection
+// below asks for is held by one of them.
+const void* instance(bool persistent, unsigned ops, int nt) {
+  const void* f = mk::instances_wide(persistent, ops, nt);
+  if (!f) f = mk::instances_gemv(persistent, ops, nt);
+  if (!f) f = mk::instances_gemm(persistent, ops, nt);
+  if (!f) f = mk::instances_all_p(persistent, ops, nt);
+  if (!f) f = mk::instances_all_n(persistent, ops, nt);
+  return f;
+}
 Launch persistent_for(unsigned ops, bool wide) {
-  if (wide && (ops & ~(mkd::kOpGemm | mkd::kOpOther)) == 0) {
-    if (ops == mkd::kOpGemm) return {reinterpret_cast<const void*>(mk_persistent<mkd::kOpGemm, 512>), 512};
-    return {reinterpret_cast<const void*>(mk_persistent<mkd::kOpGemm | mkd::kOpOther, 512>), 512};
+  using namespace mkd;
+  if (wide && (ops & ~(kOpGemm | kOpOther)) == 0) {
+    if (ops == kOpGemm) return {instance(true, kOpGemm, 512), 512};
+    return {instance(true, kOpGemm | kOpOther, 512), 512};
   }
-  if ((ops & ~mkd::kOpGemv) == 0) return {reinterpret_cast<const void*>(mk_persistent<mkd::kOpGemv>), 256};
-  if ((ops & ~mkd::kOpGemm) == 0) return {reinterpret_cast<const void*>(mk_persistent<mkd::kOpGemm>), 256};
-  if ((ops & mkd::kOpGemv) == 0)
-    return {reinterpret_cast<const void*>(mk_persistent<mkd::kOpGemm | mkd::kOpOther>), 256};
-  if ((ops & mkd::kOpGemm) == 0)
-    return {reinterpret_cast<const void*>(mk_persistent<mkd::kOpGemv | mkd::kOpOther>), 256};
-  return {reinterpret_cast<const void*>(mk_persistent<mkd::kOpAll>), 256};
+  if ((ops & ~kOpGemv) == 0) return {instance(true, kOpGemv, 256), 256};
+  if ((ops & ~kOpGemm) == 0) return {instance(true, kOpGemm, 256), 256};
+  if ((ops & kOpGemv) == 0) return {instance(true, kOpGemm | kOpOther, 256), 256};
+  if ((ops & kOpGemm) == 0) return {instance(true, kOpGemv | kOpOther, 256), 256};
+  return {instance(true, kOpAll, 256), 256};
 }
 Launch node_kernel_for(unsigned ops, bool wide) {
-  if (wide && (ops & mkd::kOpGemv) == 0) {
-    if (ops == mkd::kOpGemm) return {reinterpret_cast<const void*>(mk_node_kernel<mkd::kOpGemm, 512>), 512};
-    if (ops == mkd::kOpOther) return {reinterpret_cast<const void*>(mk_node_kernel<mkd::kOpOther, 512>), 512};
-    return {reinterpret_cast<const void*>(mk_node_kernel<mkd::kOpGemm | mkd::kOpOther, 512>), 512};
+  using namespace mkd;
+  if (wide && (ops & kOpGemv) == 0) {
+    if (ops == kOpGemm) return {instance(false, kOpGemm, 512), 512};
+    if (ops == kOpOther) return {instance(false, kOpOther, 512), 512};
+    return {instance(false, kOpGemm | kOpOther, 512), 512};
   }
-  if ((ops & ~mkd::kOpGemv) == 0) return {reinterpret_cast<const void*>(mk_node_kernel<mkd::kOpGemv>), 256};
-  if ((ops & ~mkd::kOpGemm) == 0) return {reinterpret_cast<const void*>(mk_node_kernel<mkd::kOpGemm>), 256};
-  if ((ops & mkd::kOpGemv) == 0)
-    return {reinterpret_cast<const void*>(mk_node_kernel<mkd::kOpGemm | mkd::kOpOther>), 256};
-  if ((ops & mkd::kOpGemm) == 0)
-    return {reinterpret_cast<const void*>(mk_node_kernel<mkd::kOpGemv | mkd::kOpOther>), 256};
-  return {reinterpret_cast<const void*>(mk_node_kernel<mkd::kOpAll>), 256};
+  if ((ops & ~kOpGemv) == 0) return {instance(false, kOpGemv, 256), 256};
+  if ((ops & ~kOpGemm) == 0) return {instance(false, kOpGemm, 256), 256};
+  if ((ops & kOpGemv) == 0) return {instance(false, kOpGemm | kOpOther, 256), 256};
+  if ((ops & kOpGemm) == 0) return {instance(false, kOpGemv | kOpOther, 256), 256};
+  return {instance(false, kOpAll, 256), 256};
 }
 
 using mk::set_error;
