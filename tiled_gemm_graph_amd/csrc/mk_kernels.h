@@ -846,10 +846,11 @@ __device__ __forceinline__ void gemm_packed_prefetch_b(const KArgs& a, const mk_
 // the activation chunk in LDS, sums the partial products and stores and
 // releases the result.  Waves 1-3 stream the weights: thread tw owns 16-byte
 // column group tw % ncg of the weight tile and K rows kr, kr + kpar, ...
-// (kpar = 192 / ncg), and keeps two batches of kGemvBatch chunks in flight
-// in registers.  Their stream runs on across consecutive GEMV instructions:
-// the loads that follow the last batches of instruction i are batches 0 and
-// 1 of instruction i + 1, issued before that instruction's counters clear.
+// (kpar = 192 / ncg), and keeps a ring of kGemvBufs batches of kGemvBatch
+// chunks in flight in registers.  Their stream runs on across consecutive
+// GEMV instructions: the loads that follow the last batches of instruction i
+// are the first batches of instruction i + 1, issued before that
+// instruction's counters clear.
 // The vector-memory counter is per wave and retires in order, so the
 // controller's small dependent loads and its release never wait behind the
 // weight stream.  Weight loads are unconditional (rows past the chunk
@@ -1087,10 +1088,14 @@ __device__ __forceinline__ void gemv_store_packed(const KArgs& a, const mk_node&
   }
 }
 
-// Body after the counter wait.  In the weight waves B[(k + S0) % kGemvBufs]
-// holds (in flight) batch k of `in`; on return B[(k + S0 + nb) % kGemvBufs]
-// holds batch k of `nx` (or redundant re-reads of `in` when nx is null).
-template <int DT, int MAXR, int S0>
+// Body after the counter wait.  In the weight waves B[k] holds (in flight)
+// batch k of `in`; on return B[k] holds batch k of `nx` (or redundant
+// re-reads of `in` when nx is null).  The stream of an instruction takes a
+// whole number of ring turns, so every instruction starts at buffer 0 and
+// all of them run one copy of this code: with the start buffer as a template
+// parameter, consecutive instructions ran different copies and each paid its
+// own instruction-cache misses.
+template <int DT, int MAXR>
 __device__ __forceinline__ void gemv_body(const KArgs& a, const mk_instr& in, const mk_node& nd, char* smem,
                                           u32x4 (&B)[kGemvBufs][kGemvBatch], const mk_instr* nx,
                                           const mk_node* nxd) {
@@ -1173,14 +1178,17 @@ __device__ __forceinline__ void gemv_body(const KArgs& a, const mk_instr& in, co
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc[m][e] = 0.f;
     // Loads target "virtual" batches: v < nb is batch v of this
-    // instruction, v >= nb batch v - nb of the next one (clamped to its last
-    // batch), or a redundant re-read of this tile when there is no next GEMV.
+    // instruction, v >= nr (nb rounded up to whole ring turns) batch v - nr
+    // of the next one (clamped to its last batch); the virtual batches in
+    // between, and all past nb when there is no next GEMV, re-read this
+    // tile's last batch (cache hits that keep the loads per step fixed).
+    const int nr = (g.nb + kGemvBufs - 1) / kGemvBufs * kGemvBufs;
     const GemvStream sc = gemv_stream(a, in, nd, g);
     const GemvStream sn = nx ? gemv_stream(a, *nx, *nxd, gemv_shape(*nx, *nxd)) : sc;
-    const int nshift = nx ? g.nb : 0;
+    const int nshift = nx ? nr : 0;
     const float* xk = xs + (g.active && g.kr < g.kn ? g.kr : 0);
     auto load_v = [&](int v, u32x4* dst) __attribute__((always_inline)) {
-      const bool nxt = v >= g.nb;
+      const bool nxt = v >= nr;
       GemvStream st;
       st.p = nxt ? sn.p : sc.p;
       st.step = nxt ? sn.step : sc.step;
@@ -1188,17 +1196,16 @@ __device__ __forceinline__ void gemv_body(const KArgs& a, const mk_instr& in, co
       st.nb = nxt ? sn.nb : sc.nb;
       gemv_load(st, nxt ? v - nshift : v, dst);
     };
-    // Virtual batch v lives in B[(v + S0) % kGemvBufs].  Batch v is consumed,
-    // then its buffer receives batch v + kGemvBufs; steps past the end
-    // re-request the batch the buffer already holds, so the number of loads
-    // per step is fixed and each wait leaves the younger batches in flight.
-    for (int v0 = 0; v0 < g.nb; v0 += kGemvBufs) {
+    // Virtual batch v lives in B[v % kGemvBufs].  Batch v is consumed (if
+    // v < nb), then its buffer receives virtual batch v + kGemvBufs, so the
+    // number of loads per step is fixed and each wait leaves the younger
+    // batches in flight.
+    for (int v0 = 0; v0 < nr; v0 += kGemvBufs) {
 #pragma unroll
       for (int k = 0; k < kGemvBufs; ++k) {
         const int v = v0 + k;
-        u32x4* buf_k = B[(k + S0) % kGemvBufs];
-        if (v < g.nb) gemv_fma_batch<DT, MAXR>(buf_k, v, xk, g.kpar, sc.rv, xstride, rows, acc);
-        load_v(v < g.nb ? v + kGemvBufs : v, buf_k);
+        if (v < g.nb) gemv_fma_batch<DT, MAXR>(B[k], v, xk, g.kpar, sc.rv, xstride, rows, acc);
+        load_v(v + kGemvBufs, B[k]);
       }
     }
     if (g.active) {
@@ -1287,28 +1294,12 @@ __device__ __forceinline__ void gemv_body(const KArgs& a, const mk_instr& in, co
   }
 }
 
-template <int DT, int MAXR, int S = 0>
-__device__ __forceinline__ void gemv_body_s0(const KArgs& a, const mk_instr& in, const mk_node& nd, char* smem,
-                                             u32x4 (&B)[kGemvBufs][kGemvBatch], const mk_instr* nx,
-                                             const mk_node* nxd, int s0) {
-  if constexpr (S + 1 < kGemvBufs) {
-    if (s0 != S) {
-      gemv_body_s0<DT, MAXR, S + 1>(a, in, nd, smem, B, nx, nxd, s0);
-      return;
-    }
-  }
-  gemv_body<DT, MAXR, S>(a, in, nd, smem, B, nx, nxd);
-}
-
-// Runs `in` with its stream starting at buffer s0; returns the buffer where
-// the next instruction's stream starts.
 template <int DT>
-__device__ __forceinline__ int gemv_body_rows(const KArgs& a, const mk_instr& in, const mk_node& nd, char* smem,
-                                              u32x4 (&B)[kGemvBufs][kGemvBatch], const mk_instr* nx,
-                                              const mk_node* nxd, int s0) {
-  if (in.r1 - in.r0 == 1) gemv_body_s0<DT, 1>(a, in, nd, smem, B, nx, nxd, s0);
-  else gemv_body_s0<DT, 8>(a, in, nd, smem, B, nx, nxd, s0);
-  return (s0 + gemv_shape(in, nd).nb) % kGemvBufs;
+__device__ __forceinline__ void gemv_body_rows(const KArgs& a, const mk_instr& in, const mk_node& nd, char* smem,
+                                               u32x4 (&B)[kGemvBufs][kGemvBatch], const mk_instr* nx,
+                                               const mk_node* nxd) {
+  if (in.r1 - in.r0 == 1) gemv_body<DT, 1>(a, in, nd, smem, B, nx, nxd);
+  else gemv_body<DT, 8>(a, in, nd, smem, B, nx, nxd);
 }
 
 // ---------------------------------------------------------------- REDUCE
@@ -2146,7 +2137,7 @@ __device__ __forceinline__ void run_body(const KArgs& a, const mk_instr& in, con
       if constexpr (OPS & kOpGemv) {
         u32x4 B[kGemvBufs][kGemvBatch];
         gemv_prologue(a, in, nd, B);
-        gemv_body_rows<DT>(a, in, nd, smem, B, nullptr, nullptr, 0);
+        gemv_body_rows<DT>(a, in, nd, smem, B, nullptr, nullptr);
       }
       break;
     default:
@@ -2556,7 +2547,6 @@ template <int DT>
 __device__ __forceinline__ int gemv_streak(const Loop& L, int& it, int& w) {
   const KArgs& a = L.a;
   u32x4 B[kGemvBufs][kGemvBatch];
-  int s0 = 0;
   {
     const mk_instr& in = L.slots[it % 3];
     gemv_prologue(a, in, node_of(L, in.node), B);
@@ -2586,7 +2576,7 @@ __device__ __forceinline__ int gemv_streak(const Loop& L, int& it, int& w) {
         nxd = &node_of(L, c.node);
       }
     }
-    s0 = gemv_body_rows<DT>(a, in, nd, L.smem, B, nx, nxd, s0);
+    gemv_body_rows<DT>(a, in, nd, L.smem, B, nx, nxd);
     if (a.queue) store_ahead(L, it, w, tk);
     if (tr) stamp(a, gidx, 2, wall_clock64());
     release_gemv(a, in, nd);
