@@ -216,6 +216,16 @@ __device__ __forceinline__ void store_f32x8_wt(float* p, const float* s) {
   store16_wt(p, lo);
   store16_wt(p + 4, hi);
 }
+__device__ __forceinline__ void store_u16_wt(u16* p, u16 v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_u32_wt(void* p, uint32_t v) {
+  __hip_atomic_store(reinterpret_cast<uint32_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_f32x2_wt(float* p, float x, float y) {
+  const uint64_t v = (uint64_t)__float_as_uint(x) | ((uint64_t)__float_as_uint(y) << 32);
+  __hip_atomic_store(reinterpret_cast<uint64_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 // WT: store through to the device-coherent level (GEMM and GEMV outputs,
 // released without an L2 write-back).
@@ -1809,14 +1819,14 @@ __device__ __forceinline__ void attn_issue_kv(const KArgs& a, const mk_node& nd,
 }
 
 __device__ __forceinline__ void attn_partial_prefetch(const KArgs& a, const mk_instr& in, const mk_node& nd,
-                                                      AttnPrefetch& f) {
+                                                      AttnPrefetch& f, bool kv = true) {
   const int j0 = uni(in.r0), S = uni(nd.seq);
   f.p = uni(*buf<const int>(a, nd.part));
   const int pc = min(max(f.p, 0), S - 1);     // the table row stays in bounds for any p
   const float* tab = buf<const float>(a, nd.aux) + (long)pc * kAttnD;   // [cos | sin] of position p
   f.cs = tab[tid() & 63];
   f.sn = tab[64 + (tid() & 63)];
-  attn_issue_kv(a, nd, uni(in.c0), j0, uni(in.r1) - j0, 0, f.kr, f.vr);
+  if (kv) attn_issue_kv(a, nd, uni(in.c0), j0, uni(in.r1) - j0, 0, f.kr, f.vr);
 }
 
 template <int DT, int G8>
@@ -1862,13 +1872,13 @@ __device__ __forceinline__ void attn_partial_run(const KArgs& a, const mk_instr&
       u16* Vw = buf<u16>(a, nd.gamma) + (long)p * nd.gamma.ld + (long)g * D;
       const float x1 = to_f<DT>(Kn[t]), x2 = to_f<DT>(Kn[t + HALF]);
       const u16 y1 = from_f<DT>(x1 * cs - x2 * sn), y2 = from_f<DT>(x2 * cs + x1 * sn);
-      Kw[t] = y1;
-      Kw[t + HALF] = y2;
+      store_u16_wt(Kw + t, y1);
+      store_u16_wt(Kw + t + HALF, y2);
       knb[t] = y1;
       knb[t + HALF] = y2;
       const u16 v1 = Vn[t], v2 = Vn[t + HALF];
-      Vw[t] = v1;
-      Vw[t + HALF] = v2;
+      store_u16_wt(Vw + t, v1);
+      store_u16_wt(Vw + t + HALF, v2);
       vnb[t] = v1;
       vnb[t + HALF] = v2;
     }
@@ -1982,13 +1992,11 @@ __device__ __forceinline__ void attn_partial_run(const KArgs& a, const mk_instr&
 #pragma unroll
     for (int hh = 0; hh < G8; ++hh)
       if (hh == h) { hm = mx[hh]; hl = ls[hh]; }
+    // stores through to the device-coherent level (8-byte aligned: rows
+    // of D + 4 floats), so the release needs no L2 write-back
     float* dst = P + (long)(g * G + h) * (D + 4);
-    dst[2 * dp] = o0;
-    dst[2 * dp + 1] = o1;
-    if (dp == 0) {
-      dst[D] = hm;
-      dst[D + 1] = hl;
-    }
+    store_f32x2_wt(dst + 2 * dp, o0, o1);
+    if (dp == 0) store_f32x2_wt(dst + D, hm, hl);
   }
 }
 
@@ -2012,15 +2020,16 @@ __device__ __forceinline__ void attn_partial_tile(const KArgs& a, const mk_instr
 // M = max m_c, o = sum 2^(m_c - M) o_c / sum 2^(m_c - M) l_c.  A thread
 // holds two output elements of one head and requests the (o, m, l) of 32
 // chunks at once; more chunks are merged 32 at a time with a running max.
+// p is the position (a graph input, read before the counters clear).
+// Outputs are stored through to the device-coherent level.
 template <int DT>
-__device__ __forceinline__ void attn_combine_tile(const KArgs& a, const mk_instr& in, const mk_node& nd) {
+__device__ __forceinline__ void attn_combine_tile(const KArgs& a, const mk_instr& in, const mk_node& nd, int p) {
   constexpr int D = 128, W = D + 4, B = 32;
   const int t = tid();
   const int g = uni(in.c0), G = uni(in.c1), S = uni(nd.seq), Hq = uni(nd.heads), C = uni(nd.K);
-  const int p = uni(*buf<const int>(a, nd.part));
   u16* O = buf<u16>(a, nd.out) + (long)g * G * D;
   if (p < 0 || p >= S) {
-    for (int u = t; u < G * D; u += kThreads) O[u] = 0;
+    for (int u = t; u < G * D; u += kThreads) store_u16_wt(O + u, 0);
     return;
   }
   const int nc = p / C + 1;
@@ -2057,8 +2066,8 @@ __device__ __forceinline__ void attn_combine_tile(const KArgs& a, const mk_instr
       M = Mb;
     }
     const float inv = 1.f / den;
-    O[h * D + 2 * dp] = from_f<DT>(n0 * inv);
-    O[h * D + 2 * dp + 1] = from_f<DT>(n1 * inv);
+    store_u32_wt(O + h * D + 2 * dp,
+                 (uint32_t)from_f<DT>(n0 * inv) | ((uint32_t)from_f<DT>(n1 * inv) << 16));
   }
 }
 
@@ -2150,7 +2159,7 @@ __device__ __forceinline__ void run_body(const KArgs& a, const mk_instr& in, con
             if constexpr (NT == kThreads) attn_partial_tile<DT>(a, in, nd, smem);
             break;
           case MK_I_ATTN_COMBINE:
-            if constexpr (NT == kThreads) attn_combine_tile<DT>(a, in, nd);
+            if constexpr (NT == kThreads) attn_combine_tile<DT>(a, in, nd, uni(*buf<const int>(a, nd.part)));
             break;
           case MK_I_EW_ADD:
           case MK_I_EW_RELU: elementwise_tile<DT, NT>(a, in, nd); break;
@@ -2204,17 +2213,18 @@ __device__ __forceinline__ void release_dests(const KArgs& a, const mk_instr& in
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (wave_id() == 0 && in.n_dst) {
-    // GEMM tiles stored through to the coherent level: completion suffices
-    if (tid() == 0 && in.opcode != MK_I_GEMM) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    // GEMM tiles and decode attention stored through to the coherent level:
+    // completion suffices
+    const bool wt = in.opcode == MK_I_GEMM || in.opcode == MK_I_ATTN_PARTIAL || in.opcode == MK_I_ATTN_COMBINE;
+    if (tid() == 0 && !wt) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     arrive(a, in);
   }
 }
 
 }  // namespace mkd
 
-// One workgroup per CU; instruction `it * ncu + vcu` in iteration `it`.
-// Workgroups are dealt to the 8 XCDs round-robin, so the virtual CU index
-// groups each XCD's workgroups into one contiguous block of the placement.
+// One workgroup per CU; instruction `it * ncu + vcu` in iteration `it`
+// (workgroup b runs column vcu = b of the placement).
 // Records sit in three LDS slots and are loaded two iterations ahead, so
 // iteration it always sees its own record and the next one (the two-slot
 // instruction pipeline of MegaKittens Internals, section 09, one deeper);
@@ -2485,14 +2495,36 @@ __device__ __forceinline__ bool generic_iter(const Loop& L, int it, int& w) {
   int tk = -1;
   if constexpr ((OPS & kOpOther) != 0 && NT == kThreads) {
     if (in.opcode == MK_I_ATTN_PARTIAL) {
-      // the KV cache rows are requested before the counters clear
+      // The KV cache rows are requested before the counters clear, except
+      // the controller wave's: its counter polls would retire behind them
+      // (the vector-memory counter retires in order), so it requests its
+      // rows after the wait, beside the q loads that need a round trip
+      // then anyway.
       const mk_node& nd = node_of(L, in.node);
       AttnPrefetch f;
-      attn_partial_prefetch(a, in, nd, f);
+      attn_partial_prefetch(a, in, nd, f, wave_id() != 0);
       if (!wait_sources(L, in, it, gidx, w, tk)) return false;
+      if (wave_id() == 0) {
+        const int j0 = uni(in.r0);
+        attn_issue_kv(a, nd, uni(in.c0), j0, uni(in.r1) - j0, 0, f.kr, f.vr);
+      }
       if (tr) stamp(a, gidx, 1, wall_clock64());
       if (nd.dtype == MK_BF16) attn_partial_dispatch<MK_BF16>(a, in, nd, L.smem, f);
       else attn_partial_dispatch<MK_F16>(a, in, nd, L.smem, f);
+      if (tr) stamp(a, gidx, 2, wall_clock64());
+      release_dests(a, in);
+      if (tr) stamp(a, gidx, 3, wall_clock64());
+      store_ahead(L, it, w, tk);
+      return true;
+    }
+    if (in.opcode == MK_I_ATTN_COMBINE) {
+      // the position is a graph input: read before the counters clear
+      const mk_node& nd = node_of(L, in.node);
+      const int p = uni(*buf<const int>(a, nd.part));
+      if (!wait_sources(L, in, it, gidx, w, tk)) return false;
+      if (tr) stamp(a, gidx, 1, wall_clock64());
+      if (nd.dtype == MK_BF16) attn_combine_tile<MK_BF16>(a, in, nd, p);
+      else attn_combine_tile<MK_F16>(a, in, nd, p);
       if (tr) stamp(a, gidx, 2, wall_clock64());
       release_dests(a, in);
       if (tr) stamp(a, gidx, 3, wall_clock64());
