@@ -2393,6 +2393,10 @@ __device__ __forceinline__ bool poll_sources(const Loop& L, const mk_instr& in, 
     const long long t0 = wall_clock64();
     int nap = 1;
     for (;;) {
+      // the abort flag is read with the counters, in the same round trip
+      // (read only after a poll that found a counter short, it doubled the
+      // time each unsuccessful poll takes)
+      const int abort = __hip_atomic_load(a.err + 6, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       int ready = 1, seen = 0, want = 0, who = 0;
 #pragma unroll
       for (int j = 0; j < kPollGroups; ++j)
@@ -2408,7 +2412,7 @@ __device__ __forceinline__ bool poll_sources(const Loop& L, const mk_instr& in, 
             }
           }
       if (ready) break;
-      if (__hip_atomic_load(a.err + 6, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) { ok = 0; break; }
+      if (abort) { ok = 0; break; }
       if (wall_clock64() - t0 > a.spin_ticks) {
         if (atomicCAS(a.err, 0, (int)MK_E_DEADLOCK) == 0) {
           a.err[1] = L.vcu; a.err[2] = gidx; a.err[3] = who; a.err[4] = seen; a.err[5] = want;
