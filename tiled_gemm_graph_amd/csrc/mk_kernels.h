@@ -227,6 +227,26 @@ __device__ __forceinline__ void store_f32x2_wt(float* p, float x, float y) {
   __hip_atomic_store(reinterpret_cast<uint64_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Loads that read from the device-coherent level (agent scope, like the
+// counter polls): they never return a line another XCD has since
+// rewritten.  A body that reads every value produced in the run through
+// them needs no cache invalidation after its counter wait (see
+// coherent_reads).
+__device__ __forceinline__ u32x4 ld16_coh(const void* p) {
+  const uint64_t* q = reinterpret_cast<const uint64_t*>(p);
+  const uint64_t lo = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const uint64_t hi = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return u32x4{(uint32_t)lo, (uint32_t)(lo >> 32), (uint32_t)hi, (uint32_t)(hi >> 32)};
+}
+__device__ __forceinline__ u16 ld_u16_coh(const u16* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float2 ld_f32x2_coh(const float* p) {
+  const uint64_t v = __hip_atomic_load(reinterpret_cast<const uint64_t*>(p), __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+  return float2{__uint_as_float((uint32_t)v), __uint_as_float((uint32_t)(v >> 32))};
+}
+
 // WT: store through to the device-coherent level (GEMM and GEMV outputs,
 // released without an L2 write-back).
 template <int DT, bool WT = false, typename Raw>
@@ -1003,8 +1023,8 @@ __device__ __forceinline__ void gemv_packed_prepare(const KArgs& a, const mk_nod
     const int c = packed_col(nd, rot, c0 + q + e);
     ep.off[e] = (long)gr * nd.out.ld + c;
     float x = 0.f;
-    if (flags & MK_EP_BIAS) x += to_f<DT>(buf<const u16>(a, nd.bias)[(long)gr * nd.bias.ld + c]);
-    if (flags & MK_EP_RESIDUAL) x += to_f<DT>(buf<const u16>(a, nd.res)[(long)gr * nd.res.ld + c]);
+    if (flags & MK_EP_BIAS) x += to_f<DT>(ld_u16_coh(buf<const u16>(a, nd.bias) + (long)gr * nd.bias.ld + c));
+    if (flags & MK_EP_RESIDUAL) x += to_f<DT>(ld_u16_coh(buf<const u16>(a, nd.res) + (long)gr * nd.res.ld + c));
     ep.add[e] = x;
   }
   ep.pair = !rot && ep.off[1] == ep.off[0] + 1 && (ep.off[0] & 1) == 0;
@@ -1071,8 +1091,8 @@ __device__ __forceinline__ void gemv_store_packed(const KArgs& a, const mk_node&
         off[e] = (long)gr * nd.out.ld + c;
         float x = sum[m * wc + q + e] * sc;
         if (silu_mul) x = silu(x) * (sum[m * wc + bw + q + e] * sc);
-        if (flags & MK_EP_BIAS) x += to_f<DT>(buf<const u16>(a, nd.bias)[(long)gr * nd.bias.ld + c]);
-        if (flags & MK_EP_RESIDUAL) x += to_f<DT>(buf<const u16>(a, nd.res)[(long)gr * nd.res.ld + c]);
+        if (flags & MK_EP_BIAS) x += to_f<DT>(ld_u16_coh(buf<const u16>(a, nd.bias) + (long)gr * nd.bias.ld + c));
+        if (flags & MK_EP_RESIDUAL) x += to_f<DT>(ld_u16_coh(buf<const u16>(a, nd.res) + (long)gr * nd.res.ld + c));
         v[e] = x;
       }
       if (rot) {
@@ -1138,7 +1158,7 @@ __device__ __forceinline__ void gemv_body(const KArgs& a, const mk_instr& in, co
       const int i = t + j * kThreads;
       if (i < nch) {
         const int m = i / kc8, kc = (i - m * kc8) * 8;
-        xv[j] = *reinterpret_cast<const u32x4*>(A + (long)m * nd.a.ld + kc);
+        xv[j] = ld16_coh(A + (long)m * nd.a.ld + kc);
         if (rms) gv[j] = *reinterpret_cast<const u32x4*>(buf<const u16>(a, nd.gamma) + k0 + kc);
       }
     }
@@ -1858,7 +1878,7 @@ __device__ __forceinline__ void attn_partial_run(const KArgs& a, const mk_instr&
       const int h = u / HALF, i = u - h * HALF;
       float y1 = 0.f, y2 = 0.f;               // heads G .. G8 - 1 score zero
       if (h < G) {
-        const float x1 = to_f<DT>(Q[h * D + i]), x2 = to_f<DT>(Q[h * D + i + HALF]);
+        const float x1 = to_f<DT>(ld_u16_coh(Q + h * D + i)), x2 = to_f<DT>(ld_u16_coh(Q + h * D + i + HALF));
         y1 = (x1 * cs - x2 * sn) * c;
         y2 = (x2 * cs + x1 * sn) * c;
       }
@@ -1870,13 +1890,13 @@ __device__ __forceinline__ void attn_partial_run(const KArgs& a, const mk_instr&
       const u16* Vn = buf<const u16>(a, nd.res) + (long)g * D;
       u16* Kw = buf<u16>(a, nd.bias) + (long)p * nd.bias.ld + (long)g * D;
       u16* Vw = buf<u16>(a, nd.gamma) + (long)p * nd.gamma.ld + (long)g * D;
-      const float x1 = to_f<DT>(Kn[t]), x2 = to_f<DT>(Kn[t + HALF]);
+      const float x1 = to_f<DT>(ld_u16_coh(Kn + t)), x2 = to_f<DT>(ld_u16_coh(Kn + t + HALF));
       const u16 y1 = from_f<DT>(x1 * cs - x2 * sn), y2 = from_f<DT>(x2 * cs + x1 * sn);
       store_u16_wt(Kw + t, y1);
       store_u16_wt(Kw + t + HALF, y2);
       knb[t] = y1;
       knb[t + HALF] = y2;
-      const u16 v1 = Vn[t], v2 = Vn[t + HALF];
+      const u16 v1 = ld_u16_coh(Vn + t), v2 = ld_u16_coh(Vn + t + HALF);
       store_u16_wt(Vw + t, v1);
       store_u16_wt(Vw + t + HALF, v2);
       vnb[t] = v1;
@@ -2043,8 +2063,8 @@ __device__ __forceinline__ void attn_combine_tile(const KArgs& a, const mk_instr
 #pragma unroll
       for (int q = 0; q < B; ++q) {
         const long off = (long)min(c0 + q, nc - 1) * cst;         // past nc: a repeat, weighted zero
-        o[q] = *reinterpret_cast<const float2*>(ph + off + 2 * dp);
-        ml[q] = *reinterpret_cast<const float2*>(ph + off + D);
+        o[q] = ld_f32x2_coh(ph + off + 2 * dp);
+        ml[q] = ld_f32x2_coh(ph + off + D);
       }
       float Mb = M;
 #pragma unroll
@@ -2345,6 +2365,17 @@ __device__ __forceinline__ int fetch_record(const Loop& L, int tk) {
 constexpr int kPollGroups = 2;
 constexpr int kSeenSlots = 64;   // direct-mapped record of counters seen complete (by id)
 constexpr int kPollNapMax = 8;   // longest pause between polls, in units of 64 cycles
+// Bodies that read every value produced in the run through coherent loads
+// (ld16_coh and the like): packed-tile GEMVs (activation, bias, residual)
+// and decode attention (q, k_new, v_new; the partials).  Their other reads
+// are weights, graph inputs and constant tables, which no instruction of
+// the run writes (the compiler rejects a produced GEMV weight and requires
+// the KV caches and the position to be inputs).
+__device__ __forceinline__ bool coherent_reads(const Loop& L, const mk_instr& in) {
+  if (in.opcode == MK_I_ATTN_PARTIAL || in.opcode == MK_I_ATTN_COMBINE) return true;
+  return in.opcode == MK_I_GEMV && (node_of(L, in.node).layout != 0 || (in.flags & MK_EP_PARTIAL));
+}
+
 __device__ __forceinline__ bool poll_sources(const Loop& L, const mk_instr& in, int gidx) {
   const KArgs& a = L.a;
   const int lane = tid() & 63;
@@ -2430,8 +2461,14 @@ __device__ __forceinline__ bool poll_sources(const Loop& L, const mk_instr& in, 
     }
     if (!__all(ok)) return false;
   }
-  if (lane == 0) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  if (lane < ns && ((todo >> lane) & 1)) L.seen[in.src_id[lane] & (kSeenSlots - 1)] = in.src_id[lane];
+  // The acquire's cache invalidation (about 1 us at every wait) is skipped
+  // for bodies that read produced values only through coherent loads; their
+  // counters are then not marked seen, so a later instruction of another
+  // kind polls them again and takes the acquire itself.
+  if (!coherent_reads(L, in)) {
+    if (lane == 0) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    if (lane < ns && ((todo >> lane) & 1)) L.seen[in.src_id[lane] & (kSeenSlots - 1)] = in.src_id[lane];
+  }
   return true;
 }
 // Work-queue mode: the ticket for iteration it + 2 is taken before the poll
