@@ -1839,14 +1839,14 @@ __device__ __forceinline__ void attn_issue_kv(const KArgs& a, const mk_node& nd,
 }
 
 __device__ __forceinline__ void attn_partial_prefetch(const KArgs& a, const mk_instr& in, const mk_node& nd,
-                                                      AttnPrefetch& f, bool kv = true) {
+                                                      AttnPrefetch& f) {
   const int j0 = uni(in.r0), S = uni(nd.seq);
   f.p = uni(*buf<const int>(a, nd.part));
   const int pc = min(max(f.p, 0), S - 1);     // the table row stays in bounds for any p
   const float* tab = buf<const float>(a, nd.aux) + (long)pc * kAttnD;   // [cos | sin] of position p
   f.cs = tab[tid() & 63];
   f.sn = tab[64 + (tid() & 63)];
-  if (kv) attn_issue_kv(a, nd, uni(in.c0), j0, uni(in.r1) - j0, 0, f.kr, f.vr);
+  attn_issue_kv(a, nd, uni(in.c0), j0, uni(in.r1) - j0, 0, f.kr, f.vr);
 }
 
 template <int DT, int G8>
@@ -2536,17 +2536,32 @@ __device__ __forceinline__ bool generic_iter(const Loop& L, int it, int& w) {
   int tk = -1;
   if constexpr ((OPS & kOpOther) != 0 && NT == kThreads) {
     if (in.opcode == MK_I_ATTN_PARTIAL) {
-      // The KV cache rows are requested before the counters clear, except
-      // the controller wave's: its counter polls would retire behind them
-      // (the vector-memory counter retires in order), so it requests its
-      // rows after the wait, beside the q loads that need a round trip
-      // then anyway.
+      // The position, its rotary row and the KV cache rows are requested
+      // before the counters clear, except by the controller wave: its
+      // counter polls would retire behind them (the vector-memory counter
+      // retires in order), and the rotary row's address waits on the
+      // position.  Wave 1 hands the controller the position and the rotary
+      // pair of each lane through LDS (lane i of every wave uses pair i);
+      // the controller requests its KV rows after the wait, beside the q
+      // loads that need a round trip then anyway.
+      __shared__ float s_rot[2 * 64 + 1];
       const mk_node& nd = node_of(L, in.node);
       AttnPrefetch f;
-      attn_partial_prefetch(a, in, nd, f, wave_id() != 0);
-      if (!wait_sources(L, in, it, gidx, w, tk)) return false;
+      if (wave_id() != 0) {
+        attn_partial_prefetch(a, in, nd, f);
+        if (wave_id() == 1) {
+          const int lane = tid() & 63;
+          s_rot[lane] = f.cs;
+          s_rot[64 + lane] = f.sn;
+          if (lane == 0) s_rot[128] = __int_as_float(f.p);
+        }
+      }
+      if (!wait_sources(L, in, it, gidx, w, tk)) return false;   // its barrier publishes s_rot
       if (wave_id() == 0) {
-        const int j0 = uni(in.r0);
+        const int lane = tid() & 63, j0 = uni(in.r0);
+        f.cs = s_rot[lane];
+        f.sn = s_rot[64 + lane];
+        f.p = uni(__float_as_int(s_rot[128]));
         attn_issue_kv(a, nd, uni(in.c0), j0, uni(in.r1) - j0, 0, f.kr, f.vr);
       }
       if (tr) stamp(a, gidx, 1, wall_clock64());
