@@ -293,7 +293,14 @@ typedef struct {
   int32_t layout;            /* weight: 0 row-major [K, Nb]; 1 packed GEMV
                                 column tiles [tiles][K][tile_n]; 2 packed
                                 GEMM tiles [tiles][K/64][tile_n][64]       */
-  int32_t reserved[MK_NODE_WORDS - 20 - 8 * 4 - 2 - 2 - 1];
+  int32_t lines_own;         /* 1: every tensor this node reads that the run
+                                writes is written in whole 128-byte lines,
+                                each by instructions its readers wait on, in
+                                a slot of its own (row-major GEMM nodes
+                                only); their counter waits then skip the
+                                cache invalidation when all buffers are
+                                128-byte aligned                           */
+  int32_t reserved[MK_NODE_WORDS - 20 - 8 * 4 - 2 - 2 - 1 - 1];
 } mk_node;
 
 typedef struct mk_graph mk_graph;

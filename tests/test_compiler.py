@@ -51,12 +51,14 @@ int main(void) {
     offsetof(mk_instr, src_target)/4, offsetof(mk_instr, dst_id)/4, offsetof(mk_instr, dst_rank)/4,
     sizeof(mk_tile), sizeof(mk_op_attrs));
   printf("%zu %zu %zu\\n", sizeof(mk_build_options), sizeof(mk_plan_stats), sizeof(mk_run_error));
+  printf("%zu %zu\\n", offsetof(mk_node, layout)/4, offsetof(mk_node, lines_own)/4);
   return 0;
 }
 """)
     exe = tmp_path / "layout"
     subprocess.check_call(["gcc", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)])
-    l1, l2 = subprocess.check_output([str(exe)]).decode().split("\n")[:2]
+    l1, l2, l3 = subprocess.check_output([str(exe)]).decode().split("\n")[:3]
+    assert [int(x) for x in l3.split()] == [L.N_LAYOUT, L.N_LINES_OWN]
     v = [int(x) for x in l1.split()]
     assert v[:2] == [256, 256]
     assert v[2:11] == [L.W_OPCODE, L.W_NSRC, L.W_COORD, L.W_R0, L.W_SPLIT, L.W_SRC_ID,
@@ -348,6 +350,40 @@ def test_small_m_gemm_on_a_produced_b_is_not_a_gemv():
     assert plan.stats().reserved == 0
     forced = _produced_b_graph(tile=dict(gemv=1)).build()
     assert forced.stats().reserved == 1
+
+
+def _gemm_chain(n_out, widths, reuse=0):
+    # x [1024, 64] -> widths[0] -> widths[1] ... -> n_out, row-major tiles
+    g = G.Graph()
+    cur = g.tensor("x", "f16", (1024, 64), "input")
+    k = 64
+    for i, wdt in enumerate(list(widths) + [n_out]):
+        w = g.tensor(f"w{i}", "f16", (k, wdt), "weight")
+        last = i == len(widths)
+        y = g.tensor(f"y{i}", "f16", (1024, wdt), "output" if last else "intermediate")
+        g.gemm(cur, w, y, tile=dict(layout=1, bm=64, bn=64))   # row-major 64 x 64 tiles
+        cur, k = y, wdt
+    return g.build(reuse=reuse)
+
+
+def test_lines_own_marks_gemm_nodes_that_may_skip_the_invalidation():
+    # A row-major GEMM node may skip the cache invalidation of its counter
+    # waits when every tensor it reads that the run writes is written in
+    # whole 128-byte lines in a slot of its own.
+    mlp = G.build("mlp3", workloads.default_dims("mlp3"), None).build()
+    assert list(mlp.nodes()[:, L.N_LINES_OWN]) == [1, 1, 1]
+    # rows of 1000 fp16 values (2000 bytes) end mid-line: the reader of
+    # that tensor keeps the invalidation, the first node (inputs only) not
+    odd = _gemm_chain(64, [1000])
+    assert list(odd.nodes()[:, L.N_LINES_OWN]) == [1, 0]
+    # slot reuse: y3 takes y0's slot (node 2's 256 tiles lie between y0's
+    # last reader and y3's writer), so the readers of y0 and y3 keep it
+    re = _gemm_chain(64, [1024, 1024, 1024, 1024], reuse=1)
+    assert re.stats().n_reuse_barriers > 0
+    assert list(re.nodes()[:, L.N_LINES_OWN]) == [1, 0, 1, 1, 0]
+    # packed tiles, GEMVs and other bodies never carry the mark
+    dec = G.build("decode", workloads.default_dims("decode"), None).build()
+    assert not dec.nodes()[:, L.N_LINES_OWN].any()
 
 
 def test_new_build_options_are_validated():

@@ -34,6 +34,8 @@ W_SRC_ID = 16
 W_SRC_TGT = W_SRC_ID + MAX_SRC
 W_DST_ID = W_SRC_TGT + MAX_SRC
 W_DST_RANK = W_DST_ID + MAX_DST
+# node descriptor words (mk_node)
+N_LAYOUT, N_LINES_OWN = 56, 57
 SLICE_MAX = 256  # counters with at most this target are one slot per arrival
 
 

@@ -1305,6 +1305,55 @@ struct Compiler {
     }
   }
 
+  // Row-major GEMM nodes whose counter waits may skip the cache
+  // invalidation (mk_node.lines_own).  Every tensor such a node reads that
+  // the run writes must be written in whole 128-byte lines (row length and
+  // every write box's column range multiples of 128 bytes) and hold its
+  // slot alone (no reuse).  A reader of any byte of such a line then waits
+  // on every writer of that line, so no cache of the device can have taken
+  // the line before it was complete (caches start each launch clean).  The
+  // KV caches, which decode attention appends to, count as written.
+  void mark_lines_own() {
+    std::map<int, std::vector<Box>> writes;
+    for (const Node& n : p.nodes)
+      for (const Instr& in : n.ins)
+        for (const Access& w : in.writes) writes[w.tensor].push_back(w.box);
+    std::set<int> appended, shared;
+    for (const OpRec& op : p.ops)
+      if (op.kind == MK_OP_DECODE_ATTENTION && op.in.size() > 4) {
+        appended.insert(edge_of(p.tensors, op.in[3]).tensor);
+        appended.insert(edge_of(p.tensors, op.in[4]).tensor);
+      }
+    for (const auto& ev : reuse_events) {
+      shared.insert(ev.second.second);
+      shared.insert(p.nodes[ev.first].out);
+    }
+    std::map<int, bool> own;   // tensor -> lines written whole, slot alone
+    auto lines_ok = [&](int t) {
+      auto it = own.find(t);
+      if (it != own.end()) return it->second;
+      bool ok = !appended.count(t) && !shared.count(t);
+      const I64 es = dtype_bytes(p.tensors[t].dt);
+      if (ok && (p.tensors[t].shape[3] * es) % 128) ok = false;
+      for (const Box& b : writes[t])
+        if ((b.lo[3] * es) % 128 || (b.hi[3] * es) % 128) ok = false;
+      own[t] = ok;
+      return ok;
+    };
+    for (Node& n : p.nodes) {
+      n.desc.lines_own = 0;
+      if (n.opcode != MK_I_GEMM || n.desc.layout != 0) continue;
+      bool ok = true;
+      for (const Instr& in : n.ins) {
+        for (const Access& r : in.reads)
+          if ((writes.count(r.tensor) || appended.count(r.tensor)) && !lines_ok(r.tensor)) ok = false;
+        if (!ok) break;
+      }
+      n.desc.lines_own = ok ? 1 : 0;
+    }
+    for (size_t ni = 0; ni < p.nodes.size(); ++ni) p.node_descs[ni].lines_own = p.nodes[ni].desc.lines_own;
+  }
+
   void run() {
     p.tensors = g.t;
     p.n_graph_tensors = (int)g.t.size();
@@ -1314,6 +1363,7 @@ struct Compiler {
     assign_slots();
     derive_barriers();
     emit();
+    mark_lines_own();
     check_node_window();
     algorithmic_counts();
     const_tables();

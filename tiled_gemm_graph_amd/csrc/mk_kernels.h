@@ -61,6 +61,7 @@ struct KArgs {
   int* ticket;              // work-queue mode: two ticket words, run e uses e & 1
   int queue;                // 1: instructions taken from the work queue
   int n_instr;              // list length (work-queue mode)
+  int lines_ok;             // every buffer 128-byte aligned (mk_node.lines_own applies)
   void* bufs[MK_MAX_TENSORS];
 };
 
@@ -2365,15 +2366,22 @@ __device__ __forceinline__ int fetch_record(const Loop& L, int tk) {
 constexpr int kPollGroups = 2;
 constexpr int kSeenSlots = 64;   // direct-mapped record of counters seen complete (by id)
 constexpr int kPollNapMax = 8;   // longest pause between polls, in units of 64 cycles
-// Bodies that read every value produced in the run through coherent loads
-// (ld16_coh and the like): packed-tile GEMVs (activation, bias, residual)
-// and decode attention (q, k_new, v_new; the partials).  Their other reads
-// are weights, graph inputs and constant tables, which no instruction of
-// the run writes (the compiler rejects a produced GEMV weight and requires
-// the KV caches and the position to be inputs).
-__device__ __forceinline__ bool coherent_reads(const Loop& L, const mk_instr& in) {
+// Instructions whose counter wait needs no cache invalidation:
+// * bodies that read every value produced in the run through coherent loads
+//   (ld16_coh and the like): packed-tile GEMVs (activation, bias, residual)
+//   and decode attention (q, k_new, v_new; the partials).  Their other
+//   reads are weights, graph inputs and constant tables, which no
+//   instruction of the run writes (the compiler rejects a produced GEMV
+//   weight and requires the KV caches and the position to be inputs);
+// * row-major GEMM tiles of nodes whose produced inputs are written in
+//   whole 128-byte lines that they wait on (mk_node.lines_own), when every
+//   buffer is 128-byte aligned: no cache can hold such a line from before
+//   its last write.
+__device__ __forceinline__ bool skip_invalidate(const Loop& L, const mk_instr& in) {
   if (in.opcode == MK_I_ATTN_PARTIAL || in.opcode == MK_I_ATTN_COMBINE) return true;
-  return in.opcode == MK_I_GEMV && (node_of(L, in.node).layout != 0 || (in.flags & MK_EP_PARTIAL));
+  const mk_node& nd = node_of(L, in.node);
+  if (in.opcode == MK_I_GEMV) return nd.layout != 0 || (in.flags & MK_EP_PARTIAL);
+  return in.opcode == MK_I_GEMM && nd.lines_own && L.a.lines_ok;
 }
 
 __device__ __forceinline__ bool poll_sources(const Loop& L, const mk_instr& in, int gidx) {
@@ -2462,10 +2470,10 @@ __device__ __forceinline__ bool poll_sources(const Loop& L, const mk_instr& in, 
     if (!__all(ok)) return false;
   }
   // The acquire's cache invalidation (about 1 us at every wait) is skipped
-  // for bodies that read produced values only through coherent loads; their
-  // counters are then not marked seen, so a later instruction of another
-  // kind polls them again and takes the acquire itself.
-  if (!coherent_reads(L, in)) {
+  // where skip_invalidate allows; those counters are then not marked seen,
+  // so a later instruction of another kind polls them again and takes the
+  // acquire itself.
+  if (!skip_invalidate(L, in)) {
     if (lane == 0) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     if (lane < ns && ((todo >> lane) & 1)) L.seen[in.src_id[lane] & (kSeenSlots - 1)] = in.src_id[lane];
   }

@@ -341,6 +341,14 @@ unsigned ops_of(const mk_plan* p) {
   return ops;
 }
 
+// 1 when every buffer slot starts a 128-byte line: the condition under
+// which nodes marked lines_own skip the cache invalidation of their waits.
+int lines_aligned(const mk_plan* p, const mkd::KArgs& a) {
+  for (size_t s = 0; s < p->slot_owner.size(); ++s)
+    if (reinterpret_cast<uintptr_t>(a.bufs[s]) % 128) return 0;
+  return 1;
+}
+
 mk_status fill_args(mk_plan* p, void* const* buffers, int n_buffers, mkd::KArgs& a) {
   std::memset(&a, 0, sizeof(a));
   if (n_buffers < p->n_graph_tensors) {
@@ -364,6 +372,7 @@ mk_status fill_args(mk_plan* p, void* const* buffers, int n_buffers, mkd::KArgs&
       a.bufs[s] = buffers[tid];
     }
   }
+  a.lines_ok = lines_aligned(p, a);
   a.instrs = p->dev->d_instrs;
   a.nodes = p->dev->d_nodes;
   a.counters = p->dev->d_counters;
@@ -572,6 +581,7 @@ mk_status megakernel_run_noalloc(mk_plan* p, void* const* buffers, int n_buffers
     }
     a.bufs[k] = buffers[tid];
   }
+  a.lines_ok = lines_aligned(p, a);
   int rate_khz = 0;
   HIPCHK(hipDeviceGetAttribute(&rate_khz, hipDeviceAttributeWallClockRate, dev));
   if (rate_khz <= 0) rate_khz = 100000;
