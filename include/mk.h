@@ -365,7 +365,10 @@ void mk_plan_destroy(mk_plan *p);
  * id i for every caller-owned tensor (inputs, weights, outputs), 16-byte
  * aligned; entries of views and intermediates are ignored; n_buffers is at
  * least the number of graph tensors.  A weight the plan packs
- * (mk_plan_weight_layout) is passed as its packed buffer.
+ * (mk_plan_weight_layout) is passed as its packed buffer.  When every
+ * buffer is 128-byte aligned (torch allocations are), nodes marked
+ * lines_own skip the cache invalidation after their counter waits; with
+ * any buffer less aligned they keep it, and the results are the same.
  *
  * Residency: with opts.cooperative = 0 the launch is an ordinary one, and
  * the kernel's LDS use allows one workgroup per CU, so all num_cus
