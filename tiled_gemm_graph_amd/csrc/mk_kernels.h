@@ -1,12 +1,14 @@
 // Device side of the tile-graph megakernel for gfx950 (CDNA4).
 //
-// One persistent workgroup of 256 threads (4 wave64s) per compute unit walks
-// its share of the host-compiled instruction list ("MegaKittens Internals",
-// sections 05 and 08-11; "Beating torch.compile with Megakernels in CuTe DSL",
-// "Cooperative Kernel"): fetch the 256-byte record, wait until every source
-// counter reaches epoch * target (acquire, agent scope), run the tile body,
-// make the tile's stores visible (release, agent scope) and add 1 to every
-// destination counter.  Every wait is bounded in time: on expiry the
+// One persistent workgroup of 256 threads (4 wave64s), or 512 (8 wave64s)
+// for plans of packed GEMM tiles, per compute unit walks its share of the
+// host-compiled instruction list ("MegaKittens Internals", sections 05 and
+// 08-11; "Beating torch.compile with Megakernels in CuTe DSL", "Cooperative
+// Kernel"): fetch the 256-byte record, wait until every source counter
+// reaches its target for this run (acquire, agent scope; its cache
+// invalidation is skipped where skip_invalidate shows it unneeded), run the
+// tile body, make the tile's stores visible (release, agent scope) and
+// arrive on every destination counter.  Every wait is bounded in time: on expiry the
 // workgroup records the failure, raises a shared abort flag that every other
 // wait polls, and the whole grid drains.
 //
@@ -232,7 +234,7 @@ __device__ __forceinline__ void store_f32x2_wt(float* p, float x, float y) {
 // counter polls): they never return a line another XCD has since
 // rewritten.  A body that reads every value produced in the run through
 // them needs no cache invalidation after its counter wait (see
-// coherent_reads).
+// skip_invalidate).
 __device__ __forceinline__ u32x4 ld16_coh(const void* p) {
   const uint64_t* q = reinterpret_cast<const uint64_t*>(p);
   const uint64_t lo = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
