@@ -161,6 +161,12 @@ def test_megakittens_mlp_bf16_unfused_pooled():
     say(f"[gpu] MegaKittens MLP bf16 unfused reuse=1: {st.n_instr} instrs, {st.n_slots} slots, "
         f"{st.n_reuse_barriers} reuse barriers")
     assert st.n_reuse_barriers > 0
+    # GEMM nodes on both sides of the cache-invalidation skip: those whose
+    # inputs hold their slots alone skip it, the one reading a pooled slot
+    # keeps it
+    nodes = plan.nodes()
+    own = nodes[nodes[:, 0] == L.I_GEMM, L.N_LINES_OWN]
+    assert own.any() and not own.all(), own
     ew = [r for r in plan.decoded() if r[3] in (L.I_EW_ADD, L.I_EW_RELU)]
     assert len(ew) == 6 * (1024 // 256) * (1024 // 128)
     bufs = {k: v.cuda().contiguous() for k, v in inp.items()}
